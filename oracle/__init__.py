@@ -1,0 +1,313 @@
+"""CPU oracle for the batch-1 GQA decode step (test infrastructure only).
+
+Thin ctypes wrapper around ``liboracle.so`` (built from ``oracle.c`` by ``oracle/build.py``).
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import this package; the
+HIP library and its Python binding never do.  Arrays go in and come out as numpy arrays; all
+floating-point results are float64.  See ``oracle.c`` for what each function computes and which
+passage of the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OR_F32, OR_BF16, OR_I8 = 0, 1, 2
+
+_P = C.c_void_p
+_I64 = C.c_int64
+_I32 = C.c_int32
+_D = C.c_double
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b  # noqa: F401  (build script lives beside the source)
+            _b.build()
+        _lib = C.CDLL(_LIB_PATH)
+        sig = {
+            "or_round_bf16": (None, [_P, _P, _I64]),
+            "or_to_bf16_bits": (None, [_P, _P, _I64]),
+            "or_bf16_bits_to_double": (None, [_P, _P, _I64]),
+            "or_params_per_layer": (_I64, [_I64, _I64, _I64, _I64, _I64, _I32]),
+            "or_params_total": (_I64, [_I64] * 7 + [_I32, _I32]),
+            "or_kv_bytes_per_layer_token": (_I64, [_I64, _I64, _I64]),
+            "or_rmsnorm": (None, [_P, _P, _I64, _D, _P]),
+            "or_silu": (None, [_P, _P, _I64]),
+            "or_rope": (None, [_P, _I32, _I64, _D]),
+            "or_gemv": (None, [_P, _I32, _P, _P, _I64, _I64, _P]),
+            "or_quantize_rows": (None, [_P, _I64, _I64, _P, _P]),
+            "or_attention": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+            "or_attention_online": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+            "or_attention_partitioned": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P]),
+            "or_pool_offset": (_I64, [_I32, _I32, _I32, _P, _I32, _I32, _I32]),
+            "or_pool_scatter": (None, [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P]),
+            "or_decode_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P]),
+            "or_argmax": (_I64, [_P, _I64]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(_lib, name)
+            fn.restype = res
+            fn.argtypes = args
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+# ---- number formats ------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    x = _f64(x)
+    out = np.empty_like(x)
+    lib().or_round_bf16(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    x = _f64(x)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().or_to_bf16_bits(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, dtype=np.float64)
+    lib().or_bf16_bits_to_double(_ptr(bits), _ptr(out), bits.size)
+    return out
+
+
+# ---- shapes ---------------------------------------------------------------------------------
+
+def params_per_layer(hidden, hq, hkv, d, ffn, qk_norm=1) -> int:
+    return int(lib().or_params_per_layer(hidden, hq, hkv, d, ffn, qk_norm))
+
+
+def params_total(n_layers, hidden, hq, hkv, d, ffn, vocab, tied, qk_norm=1) -> int:
+    return int(lib().or_params_total(n_layers, hidden, hq, hkv, d, ffn, vocab, tied, qk_norm))
+
+
+def kv_bytes_per_layer_token(hkv, d, elem) -> int:
+    return int(lib().or_kv_bytes_per_layer_token(hkv, d, elem))
+
+
+# ---- ops -------------------------------------------------------------------------------------
+
+def rmsnorm(x, gamma, eps) -> np.ndarray:
+    x = _f64(x)
+    g = _f32(gamma)
+    out = np.empty_like(x)
+    lib().or_rmsnorm(_ptr(x), _ptr(g), x.size, float(eps), _ptr(out))
+    return out
+
+
+def silu(z) -> np.ndarray:
+    z = _f64(z)
+    out = np.empty_like(z)
+    lib().or_silu(_ptr(z), _ptr(out), z.size)
+    return out
+
+
+def rope(v, pos, theta) -> np.ndarray:
+    """Rotates a copy of one head vector v[D] (or every row of v[..., D]) to position pos."""
+    v = _f64(v).copy()
+    d = v.shape[-1]
+    flat = v.reshape(-1, d)
+    for i in range(flat.shape[0]):
+        row = np.ascontiguousarray(flat[i])
+        lib().or_rope(_ptr(row), d, int(pos), float(theta))
+        flat[i] = row
+    return flat.reshape(v.shape)
+
+
+def _wtype(w):
+    if w.dtype == np.float32:
+        return OR_F32
+    if w.dtype == np.uint16:
+        return OR_BF16
+    if w.dtype == np.int8:
+        return OR_I8
+    raise TypeError(f"unsupported weight dtype {w.dtype} (float32, uint16 bf16 bits, int8)")
+
+
+def gemv(w, x, scale=None) -> np.ndarray:
+    """y = W x; w is float32, uint16 (bf16 bits) or int8 codes (then scale[n] is required)."""
+    w = np.ascontiguousarray(w)
+    n, k = w.shape
+    x = _f64(x)
+    assert x.size == k
+    wt = _wtype(w)
+    s = _f32(scale) if wt == OR_I8 else None
+    y = np.empty(n, dtype=np.float64)
+    lib().or_gemv(_ptr(w), wt, _ptr(s), _ptr(x), n, k, _ptr(y))
+    return y
+
+
+def quantize_rows(w):
+    """Per-row symmetric int8: returns (codes int8 [n, k], scales float32 [n])."""
+    w = _f32(w)
+    n, k = w.shape
+    q = np.empty((n, k), dtype=np.int8)
+    s = np.empty(n, dtype=np.float32)
+    lib().or_quantize_rows(_ptr(w), n, k, _ptr(q), _ptr(s))
+    return q, s
+
+
+def _attn_args(q, K, V):
+    q = _f64(q)
+    K = _f32(K)
+    V = _f32(V)
+    hq, d = q.shape
+    t, hkv, d2 = K.shape
+    assert d2 == d and V.shape == K.shape and hq % hkv == 0
+    return q, K, V, t, hq, hkv, d
+
+
+def attention(q, K, V) -> np.ndarray:
+    """Two-pass causal GQA attention of q[Hq, D] over logical K, V [T, Hkv, D]."""
+    q, K, V, t, hq, hkv, d = _attn_args(q, K, V)
+    out = np.empty((hq, d), dtype=np.float64)
+    lib().or_attention(_ptr(q), _ptr(K), _ptr(V), t, hq, hkv, d, _ptr(out))
+    return out
+
+
+def attention_online(q, K, V) -> np.ndarray:
+    q, K, V, t, hq, hkv, d = _attn_args(q, K, V)
+    out = np.empty((hq, d), dtype=np.float64)
+    lib().or_attention_online(_ptr(q), _ptr(K), _ptr(V), t, hq, hkv, d, _ptr(out))
+    return out
+
+
+def attention_partitioned(q, K, V, part) -> np.ndarray:
+    q, K, V, t, hq, hkv, d = _attn_args(q, K, V)
+    out = np.empty((hq, d), dtype=np.float64)
+    lib().or_attention_partitioned(_ptr(q), _ptr(K), _ptr(V), t, hq, hkv, d, int(part), _ptr(out))
+    return out
+
+
+def argmax(x) -> int:
+    x = _f64(x)
+    return int(lib().or_argmax(_ptr(x), x.size))
+
+
+# ---- paged KV ---------------------------------------------------------------------------------
+
+def pool_offset(pos, head, r, block_table, hkv, d, page) -> int:
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    return int(lib().or_pool_offset(pos, head, r, _ptr(bt), hkv, d, page))
+
+
+def pool_scatter(logical, pos0, block_table, num_pages, page):
+    """Expected pool contents (one layer, K or V) after writing logical [n, Hkv, D] rows at
+    pos0..pos0+n-1; elements are copied bit for bit, untouched slots stay zero."""
+    logical = np.ascontiguousarray(logical)
+    n, hkv, d = logical.shape
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    pool = np.zeros((num_pages, hkv, page, d), dtype=logical.dtype)
+    lib().or_pool_scatter(_ptr(logical), logical.itemsize, pos0, n, _ptr(bt), hkv, d, page,
+                          _ptr(pool))
+    return pool
+
+
+# ---- whole model --------------------------------------------------------------------------------
+
+class _ORModel(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "qk_norm",
+        "embed_type", "proj_type", "lm_type", "act_bf16", "kv_bf16", "max_ctx")] + [
+        ("eps", C.c_double), ("theta", C.c_double),
+        ("embed", C.c_void_p), ("lm_head", C.c_void_p), ("lm_scale", C.c_void_p),
+        ("final_norm", C.c_void_p),
+    ] + [(n, C.c_void_p) for n in (
+        "qkv", "qkv_scale", "o", "o_scale", "gate_up", "gate_up_scale", "down", "down_scale",
+        "in_norm", "post_norm", "q_norm", "k_norm", "k_cache", "v_cache")]
+
+
+class Model:
+    """Host-side model for ``or_decode_step``.
+
+    ``weights`` is a dict: ``embed`` [V, d] (float32 or uint16 bf16 bits), ``lm_head`` (same
+    convention, or int8 codes with ``lm_scale``; ``None`` when tied), ``final_norm`` [d] float32,
+    and per-layer lists ``qkv``, ``o``, ``gate_up``, ``down`` (float32 / uint16 / int8 with
+    ``*_scale`` lists) and ``in_norm``, ``post_norm``, ``q_norm``, ``k_norm`` (float32).
+    The KV cache is held here as logical float32 arrays [max_ctx, Hkv, D] per layer.
+    """
+
+    def __init__(self, cfg: dict, weights: dict, max_ctx: int):
+        self.cfg = dict(cfg)
+        self.w = weights
+        L = cfg["n_layers"]
+        hkv, d = cfg["n_kv_heads"], cfg["head_dim"]
+        self.k_cache = [np.zeros((max_ctx, hkv, d), dtype=np.float32) for _ in range(L)]
+        self.v_cache = [np.zeros((max_ctx, hkv, d), dtype=np.float32) for _ in range(L)]
+        self._keep = []
+        lm = weights.get("lm_head")
+        if lm is None:
+            lm = weights["embed"]
+        s = _ORModel()
+        s.n_layers, s.hidden = L, cfg["hidden"]
+        s.n_q_heads, s.n_kv_heads, s.head_dim = cfg["n_q_heads"], hkv, d
+        s.ffn, s.vocab, s.qk_norm = cfg["ffn"], cfg["vocab"], int(cfg.get("qk_norm", 1))
+        s.embed_type = _wtype(weights["embed"])
+        s.proj_type = _wtype(weights["qkv"][0])
+        s.lm_type = _wtype(lm)
+        s.act_bf16 = int(cfg["act_bf16"])
+        s.kv_bf16 = int(cfg["kv_bf16"])
+        s.max_ctx = max_ctx
+        s.eps, s.theta = float(cfg["eps"]), float(cfg["theta"])
+        s.embed = self._hold(weights["embed"])
+        s.lm_head = self._hold(lm)
+        s.lm_scale = self._hold(weights.get("lm_scale")) if s.lm_type == OR_I8 else None
+        s.final_norm = self._hold(_f32(weights["final_norm"]))
+        for key in ("qkv", "o", "gate_up", "down"):
+            setattr(s, key, self._ptr_array([np.ascontiguousarray(a) for a in weights[key]]))
+            sc = weights.get(key + "_scale")
+            setattr(s, key + "_scale", self._ptr_array([_f32(a) for a in sc]) if sc else None)
+        for key in ("in_norm", "post_norm", "q_norm", "k_norm"):
+            setattr(s, key, self._ptr_array([_f32(a) for a in weights[key]]))
+        s.k_cache = self._ptr_array(self.k_cache)
+        s.v_cache = self._ptr_array(self.v_cache)
+        self._s = s
+
+    def _hold(self, a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        self._keep.append(a)
+        return a.ctypes.data
+
+    def _ptr_array(self, arrays):
+        arr = (C.c_void_p * len(arrays))(*[self._hold(a) for a in arrays])
+        self._keep.append(arr)
+        return C.cast(arr, C.c_void_p).value
+
+    def step(self, pos, token=None, embedding=None, want_logits=True):
+        """Runs one decode step; returns (hidden [d] f64, logits [V] f64 or None, argmax or None)."""
+        d, v = self.cfg["hidden"], self.cfg["vocab"]
+        hidden = np.empty(d, dtype=np.float64)
+        logits = np.empty(v, dtype=np.float64) if want_logits else None
+        am = C.c_int32(-1)
+        emb = _f64(embedding) if embedding is not None else None
+        rc = lib().or_decode_step(C.byref(self._s), -1 if token is None else int(token), _ptr(emb),
+                                  int(pos), _ptr(hidden), _ptr(logits),
+                                  C.byref(am) if want_logits else None)
+        if rc != 0:
+            raise ValueError("or_decode_step rejected its arguments")
+        return hidden, logits, (am.value if want_logits else None)

@@ -1,0 +1,512 @@
+/*
+ * oracle.c - plain, slow CPU reference for the batch-1 GQA decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the package entry file and the
+ * benchmark's CPU-baseline leg may load or call this library.  The HIP library never does, and
+ * the two share no code, headers, tables or helpers.
+ *
+ * Arithmetic: every dot product, sum of squares and softmax sum is accumulated in fp64 and each
+ * function returns fp64 results.  Stored tensors are read exactly as stored (bf16 widened by the
+ * 16-bit shift, int8 codes as integers, fp32 as is).  Where the pages fix a narrower precision the
+ * oracle applies it at the same place:
+ *   - the int8 quantiser computes its scale and codes in fp32 (scale = max|row| / 127);
+ *   - on the bf16 path, tensors that cross an op boundary in bf16 ([Qwen3-runtime] §0.1: bf16 in
+ *     and out, fp32 inside reductions) are rounded to bf16 there, and the KV cache stores the
+ *     rounded values; on the fp32 path the KV cache stores fp32-rounded values.
+ *
+ * Sources, cited by page title and section:
+ *   [Qwen3-runtime]  "从 Qwen3 数学到 CUDA Kernel：0.6B 推理运行时的完整实现与优化" (chengzipai.xyz)
+ *   [ETE]            "EdgeTransformerEngine" (thomasli.cn/cuda-engine.html)
+ *
+ * Pins (what checks this file against something other than itself) live in the CPU tests:
+ * library routines (torch rms_norm / silu / bfloat16 casts, numpy matmul, scipy softmax), closed
+ * forms (complex-exponential RoPE, constant-vector RMSNorm), invariants (rotation norm, softmax
+ * shift invariance, bijective paging) and brute force on tiny inputs.  Every exported function
+ * below has at least one such pin; none is "parity unpinned".
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).  OpenMP only splits
+ * independent output rows or heads across threads; each row's arithmetic order is sequential.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+
+/* ------------------------------------------------------------------------------------------ */
+/* Number formats                                                                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* bf16 -> value: the bf16 bits are the upper half of an fp32 word ([ETE], the passage on bf16 as a
+ * storage format: widening is a 16-bit left shift). */
+static double bf16_bits_to_double(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Rounds a value to the nearest bf16 number, ties to even, directly from fp64 (8 significant
+ * bits, fp32's exponent range; below 2^-126 the spacing is the subnormal step 2^-133).  Overflow
+ * rounds to infinity.  This is a reading: the pages show only the widening direction. */
+static double round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  double a = fabs(v);
+  if (a < ldexp(1.0, -126)) return ldexp(nearbyint(ldexp(v, 133)), -133);
+  int e;
+  double m = frexp(v, &e); /* v = m * 2^e, 0.5 <= |m| < 1 */
+  double r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+  if (fabs(r) >= ldexp(1.0, 128)) return v > 0 ? INFINITY : -INFINITY;
+  return r;
+}
+
+static uint16_t bf16_bits_of(double rounded) {
+  float f = (float)rounded; /* exact: rounded is a bf16 value */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if (isnan(rounded)) return (uint16_t)0x7FC0;
+  return (uint16_t)(u >> 16);
+}
+
+static double round_f32(double v) { return (double)(float)v; }
+
+void or_round_bf16(const double* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = round_bf16(in[i]);
+}
+
+void or_to_bf16_bits(const double* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_bits_of(round_bf16(in[i]));
+}
+
+void or_bf16_bits_to_double(const uint16_t* in, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_bits_to_double(in[i]);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Shapes and byte counts ([Qwen3-runtime] §1.1 and §3.3)                                      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Parameters of one layer: the packed QKV matrix (Q width Hq*D, K and V width Hkv*D each), the O
+ * matrix, packed gate and up, down, the input and post-attention gammas and the per-head Q/K
+ * gammas. */
+int64_t or_params_per_layer(int64_t hidden, int64_t hq, int64_t hkv, int64_t d, int64_t ffn,
+                            int32_t qk_norm) {
+  int64_t q_w = hq * d, kv_w = hkv * d;
+  int64_t mats = (q_w + 2 * kv_w) * hidden  /* W_q, W_k, W_v */
+                 + hidden * q_w             /* W_o */
+                 + 2 * ffn * hidden         /* W_gate, W_up */
+                 + hidden * ffn;            /* W_down */
+  int64_t norms = 2 * hidden + (qk_norm ? 2 * d : 0);
+  return mats + norms;
+}
+
+/* All layers plus the embedding (counted once when the LM head is tied) plus the final norm. */
+int64_t or_params_total(int64_t n_layers, int64_t hidden, int64_t hq, int64_t hkv, int64_t d,
+                        int64_t ffn, int64_t vocab, int32_t tied, int32_t qk_norm) {
+  return n_layers * or_params_per_layer(hidden, hq, hkv, d, ffn, qk_norm) +
+         vocab * hidden * (tied ? 1 : 2) + hidden;
+}
+
+/* KV bytes of one layer and one token at batch 1: K and V (the first factor 2), Hkv heads of D
+ * elements each, elem bytes per element ([Qwen3-runtime] §3.3). */
+int64_t or_kv_bytes_per_layer_token(int64_t hkv, int64_t d, int64_t elem) {
+  return 2 * hkv * d * elem;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Elementwise pieces                                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/* RMSNorm without mean subtraction ([Qwen3-runtime] §2.1): y = x / sqrt(mean(x^2) + eps) * gamma. */
+void or_rmsnorm(const double* x, const float* gamma, int64_t n, double eps, double* y) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
+  double inv = 1.0 / sqrt(ss / (double)n + eps);
+  for (int64_t i = 0; i < n; ++i) y[i] = x[i] * inv * (double)gamma[i];
+}
+
+/* SiLU ([Qwen3-runtime] §2.7): silu(z) = z * sigmoid(z). */
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+void or_silu(const double* z, double* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = silu(z[i]);
+}
+
+/* Half-rotation RoPE at position pos ([Qwen3-runtime] §2.4): the two halves of a head vector are
+ * paired, a = v[i], b = v[i + D/2], and rotated by the angle pos * theta_i with
+ * theta_i = base^(-2i/D):  a' = a cos - b sin,  b' = b cos + a sin.  The frequency formula and the
+ * sign convention were lost from the page; this is the reading taken. */
+void or_rope(double* v, int32_t d, int64_t pos, double base) {
+  int32_t h = d / 2;
+  for (int32_t i = 0; i < h; ++i) {
+    double ang = (double)pos * pow(base, -2.0 * (double)i / (double)d);
+    double c = cos(ang), s = sin(ang);
+    double a = v[i], b = v[i + h];
+    v[i] = a * c - b * s;
+    v[i + h] = b * c + a * s;
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Projections ([Qwen3-runtime] §4.1: at batch 1 every linear layer is a GEMV)                   */
+/* ------------------------------------------------------------------------------------------ */
+
+/* y[n] = sum_k W[n][k] x[k] for W of type wt (OR_F32, OR_BF16, or OR_I8 codes).  For OR_I8 the
+ * per-row scale multiplies the integer-weighted sum once: y = s_n * sum_k q_nk x_k, which equals
+ * sum_k (q_nk s_n) x_k in exact arithmetic ([Qwen3-runtime] §13.1, the group-scale step, read per
+ * row as [ETE] quantises per row). */
+void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int64_t n, int64_t k,
+             double* y) {
+  if (wt == OR_F32) {
+    const float* W = (const float*)w;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      double s = 0.0;
+      for (int64_t c = 0; c < k; ++c) s += (double)W[r * k + c] * x[c];
+      y[r] = s;
+    }
+  } else if (wt == OR_BF16) {
+    const uint16_t* W = (const uint16_t*)w;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      double s = 0.0;
+      for (int64_t c = 0; c < k; ++c) s += bf16_bits_to_double(W[r * k + c]) * x[c];
+      y[r] = s;
+    }
+  } else {
+    const int8_t* W = (const int8_t*)w;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      double s = 0.0;
+      for (int64_t c = 0; c < k; ++c) s += (double)W[r * k + c] * x[c];
+      y[r] = s * (double)scale[r];
+    }
+  }
+}
+
+/* Symmetric per-row int8 quantisation ([ETE], the int8 passage: symmetric, one scale per row).
+ * In fp32 as the scheme states: scale = max|w_row| / 127; code = w / scale rounded to nearest
+ * (ties to even: a reading), clamped to [-127, 127].  A zero row gets scale 0 and zero codes. */
+void or_quantize_rows(const float* w, int64_t n, int64_t k, int8_t* q, float* s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    const float* row = w + r * k;
+    float mx = 0.0f;
+    for (int64_t c = 0; c < k; ++c) {
+      float a = fabsf(row[c]);
+      if (a > mx) mx = a;
+    }
+    float sc = mx / 127.0f;
+    s[r] = sc;
+    for (int64_t c = 0; c < k; ++c) {
+      float v = 0.0f;
+      if (sc != 0.0f) {
+        v = rintf(row[c] / sc);
+        if (v > 127.0f) v = 127.0f;
+        if (v < -127.0f) v = -127.0f;
+      }
+      q[r * k + c] = (int8_t)v;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Attention ([Qwen3-runtime] §2.5-2.6, §9.1; [ETE] the online-softmax passage)                */
+/* ------------------------------------------------------------------------------------------ */
+
+/* The plain definition, two passes.  q: [hq][d]; K, V: logical [t][hkv][d] (values as stored).
+ * Query head h reads kv head h / (hq / hkv) ([Qwen3-runtime] §2.5).  Scores s_j = q.k_j / sqrt(d)
+ * over every key j < t (the causal range of the new token); softmax with the maximum subtracted;
+ * out = sum_j p_j v_j. */
+void or_attention(const double* q, const float* K, const float* V, int64_t t, int32_t hq,
+                  int32_t hkv, int32_t d, double* out) {
+  int32_t group = hq / hkv;
+  double rs = sqrt((double)d);
+#pragma omp parallel for schedule(dynamic)
+  for (int32_t h = 0; h < hq; ++h) {
+    int32_t g = h / group;
+    const double* qh = q + (int64_t)h * d;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(t > 0 ? t : 1));
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < t; ++j) {
+      const float* kj = K + (j * hkv + g) * d;
+      double dot = 0.0;
+      for (int32_t r = 0; r < d; ++r) dot += qh[r] * (double)kj[r];
+      s[j] = dot / rs;
+      if (s[j] > mx) mx = s[j];
+    }
+    double* o = out + (int64_t)h * d;
+    for (int32_t r = 0; r < d; ++r) o[r] = 0.0;
+    double den = 0.0;
+    for (int64_t j = 0; j < t; ++j) {
+      double w = exp(s[j] - mx);
+      den += w;
+      const float* vj = V + (j * hkv + g) * d;
+      for (int32_t r = 0; r < d; ++r) o[r] += w * (double)vj[r];
+    }
+    for (int32_t r = 0; r < d; ++r) o[r] /= den;
+    free(s);
+  }
+}
+
+/* One online-softmax update of the state (m, l, acc) with a new score and value row
+ * ([ETE], the (m, l, acc) passage; [Qwen3-runtime] §9.1, the scalar state update). */
+static void online_update(double score, const float* v, int32_t d, double* m, double* l,
+                          double* acc) {
+  double nm = score > *m ? score : *m;
+  double old_scale = exp(*m - nm);
+  double new_scale = exp(score - nm);
+  *l = *l * old_scale + new_scale;
+  for (int32_t r = 0; r < d; ++r) acc[r] = acc[r] * old_scale + (double)v[r] * new_scale;
+  *m = nm;
+}
+
+/* State of one contiguous range [j0, j1) of keys for query head h: m starts at -1e30, l and acc
+ * at 0 ([ETE]: the initialisation kernel's values). */
+static void partition_state(const double* qh, const float* K, const float* V, int64_t j0,
+                            int64_t j1, int32_t g, int32_t hkv, int32_t d, double* m, double* l,
+                            double* acc) {
+  double rs = sqrt((double)d);
+  *m = -1e30;
+  *l = 0.0;
+  for (int32_t r = 0; r < d; ++r) acc[r] = 0.0;
+  for (int64_t j = j0; j < j1; ++j) {
+    const float* kj = K + (j * hkv + g) * d;
+    double dot = 0.0;
+    for (int32_t r = 0; r < d; ++r) dot += qh[r] * (double)kj[r];
+    online_update(dot / rs, V + (j * hkv + g) * d, d, m, l, acc);
+  }
+}
+
+/* Single-pass online form over all t keys, then out = acc / l ([ETE]: the finalisation kernel). */
+void or_attention_online(const double* q, const float* K, const float* V, int64_t t, int32_t hq,
+                         int32_t hkv, int32_t d, double* out) {
+  int32_t group = hq / hkv;
+  for (int32_t h = 0; h < hq; ++h) {
+    double m, l;
+    double* o = out + (int64_t)h * d;
+    partition_state(q + (int64_t)h * d, K, V, 0, t, h / group, hkv, d, &m, &l, o);
+    for (int32_t r = 0; r < d; ++r) o[r] /= l;
+  }
+}
+
+/* Split form ([Qwen3-runtime] §9.1, §10.2): keys cut into contiguous partitions of `part`
+ * positions, each reduced to (m_p, l_p, o_p) with o_p unnormalised; then M = max_p m_p, each state
+ * rescaled by exp(m_p - M), L = sum l_p e^(m_p-M), O = sum o_p e^(m_p-M), out = O / L. */
+void or_attention_partitioned(const double* q, const float* K, const float* V, int64_t t,
+                              int32_t hq, int32_t hkv, int32_t d, int64_t part, double* out) {
+  int32_t group = hq / hkv;
+  int64_t np = (t + part - 1) / part;
+  double* ms = (double*)malloc(sizeof(double) * (size_t)np);
+  double* ls = (double*)malloc(sizeof(double) * (size_t)np);
+  double* os = (double*)malloc(sizeof(double) * (size_t)(np * d));
+  for (int32_t h = 0; h < hq; ++h) {
+    for (int64_t p = 0; p < np; ++p) {
+      int64_t j0 = p * part, j1 = j0 + part < t ? j0 + part : t;
+      partition_state(q + (int64_t)h * d, K, V, j0, j1, h / group, hkv, d, &ms[p], &ls[p],
+                      os + p * d);
+    }
+    double M = -INFINITY;
+    for (int64_t p = 0; p < np; ++p)
+      if (ms[p] > M) M = ms[p];
+    double L = 0.0;
+    double* o = out + (int64_t)h * d;
+    for (int32_t r = 0; r < d; ++r) o[r] = 0.0;
+    for (int64_t p = 0; p < np; ++p) {
+      double w = exp(ms[p] - M);
+      L += ls[p] * w;
+      for (int32_t r = 0; r < d; ++r) o[r] += os[p * d + r] * w;
+    }
+    for (int32_t r = 0; r < d; ++r) o[r] /= L;
+  }
+  free(ms);
+  free(ls);
+  free(os);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Paged KV addressing ([Qwen3-runtime] §7.2: logical page = p / page, slot = p % page, physical  */
+/* page from the block table).  The intra-page layout is not on the page; the reading taken is  */
+/* one contiguous page x D tile per (physical page, kv head).                                   */
+/* ------------------------------------------------------------------------------------------ */
+
+int64_t or_pool_offset(int32_t pos, int32_t head, int32_t r, const int32_t* block_table,
+                       int32_t hkv, int32_t d, int32_t page) {
+  int64_t phys = block_table[pos / page];
+  int64_t slot = pos % page;
+  return ((phys * hkv + head) * page + slot) * d + r;
+}
+
+/* Places logical rows [n][hkv][d] (elem bytes each, copied bit for bit) of positions
+ * pos0..pos0+n-1 into a pool buffer by or_pool_offset. */
+void or_pool_scatter(const void* logical, int32_t elem, int32_t pos0, int32_t n,
+                     const int32_t* block_table, int32_t hkv, int32_t d, int32_t page,
+                     void* pool) {
+  const unsigned char* src = (const unsigned char*)logical;
+  unsigned char* dst = (unsigned char*)pool;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t g = 0; g < hkv; ++g)
+      for (int32_t r = 0; r < d; ++r) {
+        int64_t off = or_pool_offset(pos0 + i, g, r, block_table, hkv, d, page);
+        memcpy(dst + off * elem, src + (((int64_t)i * hkv + g) * d + r) * elem, (size_t)elem);
+      }
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* One decode step of the whole model                                                          */
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct or_model {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t qk_norm;
+  int32_t embed_type, proj_type, lm_type; /* OR_F32 / OR_BF16 / OR_I8 */
+  int32_t act_bf16;                       /* 1: bf16 op-boundary rounding (the bf16 path) */
+  int32_t kv_bf16;                        /* 1: the KV cache stores bf16 values, else fp32 */
+  int32_t max_ctx;
+  double eps, theta;
+  const void* embed;
+  const void* lm_head;
+  const float* lm_scale;
+  const float* final_norm;
+  const void* const* qkv;
+  const float* const* qkv_scale;
+  const void* const* o;
+  const float* const* o_scale;
+  const void* const* gate_up;
+  const float* const* gate_up_scale;
+  const void* const* down;
+  const float* const* down_scale;
+  const float* const* in_norm;
+  const float* const* post_norm;
+  const float* const* q_norm;
+  const float* const* k_norm;
+  float* const* k_cache; /* per layer, logical [max_ctx][Hkv][D] */
+  float* const* v_cache;
+} or_model;
+
+static double act_round(const or_model* m, double v) { return m->act_bf16 ? round_bf16(v) : v; }
+static double kv_round(const or_model* m, double v) {
+  return m->kv_bf16 ? round_bf16(v) : round_f32(v);
+}
+
+/* The step of [ETE] (its GPU block pipeline) with the math of [Qwen3-runtime] §2.1-2.7:
+ *   x = E[token] (or the given embedding row)
+ *   per layer:  h = RMSNorm(x, g_in);  [q|k|v] = W_qkv h  (Q rows, then K, then V)
+ *               per Q and K head: RMSNorm over D (when qk_norm), then RoPE at pos
+ *               append k, v at logical position pos (so attention covers 0..pos)
+ *               o_h = attention(q_h, K[0..pos], V[0..pos]) for every Q head
+ *               x += W_o concat(o_h)
+ *               h2 = RMSNorm(x, g_post);  [g|u] = W_gu h2;  a = silu(g) * u;  x += W_down a
+ *   hidden = x;  logits = W_lm RMSNorm(x, g_final);  argmax = lowest index of the maximum.
+ * Rounding to bf16 (act_bf16) at: each RMSNorm output that feeds a projection, the rotated Q,
+ * the attention output, the SwiGLU output and the logits; K/V are stored by kv_round.  On the
+ * fp32 path the logits are rounded to fp32 (their output type) before the argmax.
+ * Returns 0, or -1 on a bad argument. */
+int32_t or_decode_step(const or_model* m, int32_t token, const double* emb, int32_t pos,
+                       double* hidden_out, double* logits_out, int32_t* argmax_out) {
+  const int64_t dm = m->hidden, hq = m->n_q_heads, hkv = m->n_kv_heads, d = m->head_dim;
+  const int64_t f = m->ffn, v = m->vocab;
+  const int64_t qw = hq * d, kw = hkv * d, nqkv = qw + 2 * kw;
+  if (pos < 0 || pos >= m->max_ctx || d > 256) return -1;
+  if (!emb && (token < 0 || token >= v)) return -1;
+
+  double* x = (double*)calloc((size_t)dm, sizeof(double));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(dm > f ? dm : f));
+  double* qkv = (double*)malloc(sizeof(double) * (size_t)nqkv);
+  double* att = (double*)malloc(sizeof(double) * (size_t)qw);
+  double* y = (double*)malloc(sizeof(double) * (size_t)(dm > 2 * f ? dm : 2 * f));
+  double* a = (double*)malloc(sizeof(double) * (size_t)f);
+
+  if (emb) {
+    for (int64_t i = 0; i < dm; ++i) x[i] = emb[i];
+  } else if (m->embed_type == OR_BF16) {
+    const uint16_t* E = (const uint16_t*)m->embed;
+    for (int64_t i = 0; i < dm; ++i) x[i] = bf16_bits_to_double(E[(int64_t)token * dm + i]);
+  } else {
+    const float* E = (const float*)m->embed;
+    for (int64_t i = 0; i < dm; ++i) x[i] = (double)E[(int64_t)token * dm + i];
+  }
+
+  for (int32_t l = 0; l < m->n_layers; ++l) {
+    /* attention block */
+    or_rmsnorm(x, m->in_norm[l], dm, m->eps, h);
+    for (int64_t i = 0; i < dm; ++i) h[i] = act_round(m, h[i]);
+    or_gemv(m->qkv[l], m->proj_type, m->qkv_scale ? m->qkv_scale[l] : NULL, h, nqkv, dm, qkv);
+
+    double* q = qkv;            /* [hq][d] */
+    double* kx = qkv + qw;      /* [hkv][d] */
+    double* vx = qkv + qw + kw; /* [hkv][d] */
+    double tmp[256];
+    for (int64_t hh = 0; hh < hq; ++hh) {
+      double* qh = q + hh * d;
+      if (m->qk_norm) {
+        or_rmsnorm(qh, m->q_norm[l], d, m->eps, tmp);
+        memcpy(qh, tmp, sizeof(double) * (size_t)d);
+      }
+      or_rope(qh, (int32_t)d, pos, m->theta);
+      for (int64_t r = 0; r < d; ++r) qh[r] = act_round(m, qh[r]);
+    }
+    float* kc = m->k_cache[l];
+    float* vc = m->v_cache[l];
+    for (int64_t g = 0; g < hkv; ++g) {
+      double* kh = kx + g * d;
+      if (m->qk_norm) {
+        or_rmsnorm(kh, m->k_norm[l], d, m->eps, tmp);
+        memcpy(kh, tmp, sizeof(double) * (size_t)d);
+      }
+      or_rope(kh, (int32_t)d, pos, m->theta);
+      for (int64_t r = 0; r < d; ++r) {
+        kc[((int64_t)pos * hkv + g) * d + r] = (float)kv_round(m, kh[r]);
+        vc[((int64_t)pos * hkv + g) * d + r] = (float)kv_round(m, vx[g * d + r]);
+      }
+    }
+    or_attention(q, kc, vc, (int64_t)pos + 1, (int32_t)hq, (int32_t)hkv, (int32_t)d, att);
+    for (int64_t i = 0; i < qw; ++i) att[i] = act_round(m, att[i]);
+    or_gemv(m->o[l], m->proj_type, m->o_scale ? m->o_scale[l] : NULL, att, dm, qw, y);
+    for (int64_t i = 0; i < dm; ++i) x[i] += y[i];
+
+    /* MLP block */
+    or_rmsnorm(x, m->post_norm[l], dm, m->eps, h);
+    for (int64_t i = 0; i < dm; ++i) h[i] = act_round(m, h[i]);
+    or_gemv(m->gate_up[l], m->proj_type, m->gate_up_scale ? m->gate_up_scale[l] : NULL, h, 2 * f,
+            dm, y);
+    for (int64_t i = 0; i < f; ++i) a[i] = act_round(m, silu(y[i]) * y[f + i]);
+    or_gemv(m->down[l], m->proj_type, m->down_scale ? m->down_scale[l] : NULL, a, dm, f, y);
+    for (int64_t i = 0; i < dm; ++i) x[i] += y[i];
+  }
+
+  if (hidden_out)
+    for (int64_t i = 0; i < dm; ++i) hidden_out[i] = x[i];
+
+  if (logits_out || argmax_out) {
+    double* lg = (double*)malloc(sizeof(double) * (size_t)v);
+    or_rmsnorm(x, m->final_norm, dm, m->eps, h);
+    for (int64_t i = 0; i < dm; ++i) h[i] = act_round(m, h[i]);
+    or_gemv(m->lm_head, m->lm_type, m->lm_scale, h, v, dm, lg);
+    for (int64_t i = 0; i < v; ++i) lg[i] = m->act_bf16 ? round_bf16(lg[i]) : round_f32(lg[i]);
+    if (argmax_out) {
+      int32_t best = -1;
+      for (int64_t i = 0; i < v; ++i)
+        if (!isnan(lg[i]) && (best < 0 || lg[i] > lg[best])) best = (int32_t)i;
+      *argmax_out = best;
+    }
+    if (logits_out) memcpy(logits_out, lg, sizeof(double) * (size_t)v);
+    free(lg);
+  }
+  free(x);
+  free(h);
+  free(qkv);
+  free(att);
+  free(y);
+  free(a);
+  return 0;
+}
+
+/* Index of the largest value, the lowest index on ties, NaN never chosen (-1 if all NaN). */
+int64_t or_argmax(const double* x, int64_t n) {
+  int64_t best = -1;
+  for (int64_t i = 0; i < n; ++i)
+    if (!isnan(x[i]) && (best < 0 || x[i] > x[best])) best = i;
+  return best;
+}
