@@ -1,0 +1,174 @@
+// common.h - device primitives and kernel argument blocks shared by the HIP kernels (gfx950).
+//
+// Wave64 throughout.  Reductions use DPP row operations inside each 16-lane row and
+// v_readlane across rows, so they need every lane of the wave active (callers reduce in
+// converged code, idle lanes contributing the neutral element).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qd {
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;  // tokens per KV page
+
+enum WType : int { W_F32 = 0, W_BF16 = 1, W_I8 = 2 };
+
+// ---- bf16 <-> fp32 -------------------------------------------------------------------------
+// bf16 is the upper half of an fp32 word: widening is a 16-bit shift.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// ---- DPP wave reductions ---------------------------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of a group gets the group sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  if (N >= 8) v += dpp<kDppHalfMirror>(v);
+  if (N >= 16) v += dpp<kDppMirror>(v);
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  if (N >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if (N >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Full-wave sum; the result is wave-uniform.  Fixed association order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)),
+               fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+// ---- split-KV partition sizing (shared by the host launcher and the kernels) -----------------
+// Fixed partitions when part_fixed > 0; otherwise the partition length grows with the context
+// so that Hkv * n_part stays near target_wgs work-groups, with a floor of 64 tokens.
+__host__ __device__ inline int part_tokens_for(int ctx, int part_fixed, int n_kv_heads,
+                                               int target_wgs) {
+  if (part_fixed > 0) return part_fixed;
+  long long want = ((long long)ctx * n_kv_heads + target_wgs - 1) / target_wgs;
+  int p = (int)(((want + 63) / 64) * 64);
+  return p < 64 ? 64 : p;
+}
+__host__ __device__ inline int n_parts_for(int ctx, int part_tokens) {
+  return (ctx + part_tokens - 1) / part_tokens;
+}
+
+// ---- kernel argument blocks (passed by value) -----------------------------------------------
+
+// Step descriptor in device memory: written by the embedding kernel, read by the later kernels
+// of the step, so a replayed graph needs only the embedding node's arguments updated.
+struct StepDesc {
+  int32_t pos;
+  int32_t ctx;    // pos + 1
+  int32_t error;  // sticky: 1 after an out-of-range token id
+  int32_t pad;
+};
+
+struct GemvArgs {
+  const void* w;          // [rows x k] (rows = n, or 2n for SwiGLU)
+  const float* scale;     // [rows] for int8 codes
+  const void* x;          // input vector [k] (when gamma == nullptr)
+  int32_t x_bf16;         // x element type
+  int32_t round_h;        // round the normalised input to bf16
+  const float* xn;        // fp32 input to normalise (when gamma != nullptr)
+  const float* gamma;     // RMSNorm gamma [k] or nullptr
+  float eps;
+  int32_t y_bf16;         // output element type for EPI_STORE / EPI_SWIGLU
+  void* y;                // output [n]
+  float* resid;           // EPI_RESID: resid[n] += W x
+  float* hidden_copy;     // optional: work-group 0 copies xn here (the step's hidden output)
+  int64_t n;              // output rows
+  int64_t k;              // input length
+};
+
+struct AttnArgs {
+  const void* q;              // [Hq x D] (bf16 or fp32)
+  int32_t q_bf16;
+  const void* k_pool;         // [P][Hkv][16][D] (bf16 or fp32)
+  const void* v_pool;
+  const int32_t* block_table;
+  const StepDesc* desc;       // ctx from here when non-null
+  int32_t ctx_arg;            // ctx when desc == nullptr
+  int32_t n_q_heads, n_kv_heads;
+  int32_t part_fixed, target_wgs;
+  int32_t max_parts;          // scratch stride (partitions per head)
+  float* part_acc;            // [Hq][max_parts][D] unnormalised accumulators
+  float* part_ml;             // [Hq][max_parts][2]: running max (log2 units) and denominator
+  void* out;                  // [Hq x D] (when a single partition covers the context)
+  int32_t out_bf16;
+  float qscale;               // log2(e) / sqrt(D)
+};
+
+struct RopeAppendArgs {
+  const float* qkv;           // [(Hq + 2 Hkv) D] fp32
+  const float* q_gamma;       // [D] or nullptr (no Q/K norm)
+  const float* k_gamma;
+  float eps;
+  const float* table;         // [max_pos][D/2][2] (cos, sin)
+  const StepDesc* desc;
+  int32_t pos_arg;
+  void* q_out;
+  int32_t q_bf16;
+  void* k_pool;
+  void* v_pool;
+  int32_t kv_bf16;
+  const int32_t* block_table;
+  int32_t n_q_heads, n_kv_heads;
+};
+
+struct EmbedArgs {
+  const void* table;          // [V x d] (bf16 or fp32), used when emb == nullptr
+  int32_t table_bf16;
+  const void* emb;            // caller's embedding row (act dtype) or nullptr
+  const int32_t* token;       // device token id
+  float* x;                   // [d] fp32 residual stream
+  StepDesc* desc;             // written: pos, ctx (nullable)
+  int32_t pos;
+  int32_t vocab;
+  int32_t d;
+};
+
+}  // namespace qd

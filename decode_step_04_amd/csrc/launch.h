@@ -1,0 +1,42 @@
+// launch.h - host-side launchers of the HIP kernels (internal to the library).
+//
+// Each launcher enqueues one kernel on `stream` and returns hipGetLastError() of the launch.
+// Shapes have been validated by the caller (runtime.hip); the launchers only derive grids.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace qd {
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+// Grid cap of the GEMV: enough resident waves per CU to keep many dwordx4 loads in flight.
+constexpr int kGemvMaxWgs = 2048;
+
+hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s);
+
+// Split-KV partition kernel over `grid_parts` partitions per KV head (surplus ones exit early).
+hipError_t launch_attention(int head_dim, bool kv_bf16, int group, const AttnArgs& a,
+                            int grid_parts, hipStream_t s);
+hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_rope_append(int head_dim, const RopeAppendArgs& a, hipStream_t s);
+hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+const void* embed_kernel_fn();
+
+hipError_t launch_argmax(const void* x, int x_bf16, int64_t n, int32_t* out, hipStream_t s);
+hipError_t launch_quantize(const void* w, int src_bf16, int8_t* q, float* scale, int64_t n,
+                           int64_t k, hipStream_t s);
+hipError_t launch_kv_copy(void* pool, void* linear, const int32_t* block_table, int pos0, int n,
+                          int n_kv_heads, int head_dim, int elem, int to_pool, hipStream_t s);
+hipError_t launch_rope_table(float* table, int max_pos, int head_dim, float theta, hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+hipError_t launch_convert(void* dst, int dst_type, const void* src, int src_type, int64_t n,
+                          hipStream_t s);
+hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y, int y_bf16,
+                          int n, hipStream_t s);
+
+}  // namespace qd

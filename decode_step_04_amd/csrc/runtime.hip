@@ -1,0 +1,1186 @@
+// runtime.hip - the C ABI of include/qdec.h: validation, context lifecycle, uploads, paged KV,
+// the decode-step driver, HIP graph capture/replay, the event profiler and op-level entry points.
+//
+// [Qwen3-runtime] = the page "从 Qwen3 数学到 CUDA Kernel：0.6B 推理运行时的完整实现与优化".
+// [ETE] = the page "EdgeTransformerEngine".
+//
+// Rules kept here ([Qwen3-runtime] §5.1-5.2; [ETE], its list of limitations):
+//   - every argument is validated on the host before anything is enqueued;
+//   - every HIP call is checked and mapped to QDEC_E_HIP with its message;
+//   - all device memory is allocated in qdec_create; the step only enqueues kernels on the
+//     caller's stream, so it can be captured and replayed at fixed addresses.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "launch.h"
+#include "qdec.h"
+
+#define QDEC_API extern "C" __attribute__((visibility("default")))
+
+using namespace qd;
+
+namespace {
+
+thread_local std::string g_err;  // last error of context-free calls on this thread
+
+constexpr int kTargetWgs = 1024;  // split-KV work-groups aimed for when partitions are automatic
+constexpr int kNumSlots = 11;
+
+qdec_status fail(std::string* dst, qdec_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (dst) *dst = buf;
+  g_err = buf;
+  return s;
+}
+
+int elem_size(int dtype) { return dtype == QDEC_F32 ? 4 : dtype == QDEC_BF16 ? 2 : 1; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Mat {
+  void* data = nullptr;
+  float* scale = nullptr;
+  int64_t rows = 0, cols = 0;
+  int dtype = QDEC_F32;
+  int64_t bytes() const {
+    return rows * cols * elem_size(dtype) + (dtype == QDEC_I8_ROW ? rows * 4 : 0);
+  }
+};
+
+struct Layer {
+  Mat qkv, o, gu, down;
+  float* in_norm = nullptr;
+  float* post_norm = nullptr;
+  float* q_norm = nullptr;
+  float* k_norm = nullptr;
+  void* k_pool = nullptr;
+  void* v_pool = nullptr;
+};
+
+int64_t max_parts_for(const qdec_config& c, int part_fixed) {
+  if (part_fixed > 0) return (c.max_context + part_fixed - 1) / part_fixed;
+  int64_t mx = 1;
+  for (int t = 1; t <= c.max_context; ++t)
+    mx = std::max<int64_t>(mx, n_parts_for(t, part_tokens_for(t, 0, c.n_kv_heads, kTargetWgs)));
+  return mx;
+}
+
+}  // namespace
+
+struct qdec_ctx {
+  qdec_config cfg{};
+  int device = 0;
+  int part_fixed = 0;
+  int max_parts = 1;
+  std::vector<void*> allocs;
+  int64_t device_bytes = 0;
+  Mat embed, lm;
+  bool lm_alias = false;
+  float* final_norm = nullptr;
+  std::vector<Layer> layers;
+  int32_t* block_table = nullptr;
+  int32_t n_logical = 0;
+  float* rope = nullptr;
+  float* x = nullptr;
+  float* qkv = nullptr;
+  void* q = nullptr;
+  void* attn = nullptr;
+  void* act = nullptr;
+  void* logits = nullptr;
+  float* part_acc = nullptr;
+  float* part_ml = nullptr;
+  StepDesc* desc = nullptr;
+  std::vector<uint8_t> uploaded;  // (n_layers + 1) x kNumSlots; row n_layers = global slots
+  std::string err;
+  // graph of everything after the embedding kernel
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  qdec_step graph_templ{};
+  // event profiler
+  bool prof = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_class;
+  int ev_used = 0;
+  double prof_ms[QDEC_K_COUNT] = {};
+  int64_t prof_n[QDEC_K_COUNT] = {};
+
+  qdec_status hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return QDEC_OK;
+    return fail(&err, QDEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  }
+  template <typename T>
+  qdec_status alloc(T** p, int64_t bytes, const char* what) {
+    *p = nullptr;
+    if (bytes <= 0) return QDEC_OK;
+    void* d = nullptr;
+    hipError_t e = hipMalloc(&d, (size_t)bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(&err, QDEC_E_NOMEM, "hipMalloc of %lld bytes for %s failed: %s",
+                  (long long)bytes, what, hipGetErrorString(e));
+    }
+    allocs.push_back(d);
+    device_bytes += bytes;
+    *p = static_cast<T*>(d);
+    return QDEC_OK;
+  }
+  uint8_t& slot(int layer, int which) { return uploaded[(size_t)layer * kNumSlots + which]; }
+  bool act_bf16() const { return cfg.act_dtype == QDEC_BF16; }
+  bool kv_bf16() const { return cfg.kv_dtype == QDEC_BF16; }
+};
+
+// =====================================================================================
+// configuration
+// =====================================================================================
+
+static qdec_status validate(const qdec_config* c, std::string* why) {
+  if (!c) return fail(why, QDEC_E_INVAL, "config is NULL");
+  if (c->n_layers < 1 || c->n_layers > 4096)
+    return fail(why, QDEC_E_INVAL, "n_layers %d out of [1, 4096]", c->n_layers);
+  if (c->hidden <= 0 || c->ffn <= 0 || c->vocab <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0)
+    return fail(why, QDEC_E_INVAL, "sizes must be positive");
+  if (c->hidden % 64 || c->ffn % 64)
+    return fail(why, QDEC_E_UNSUPPORTED, "hidden (%d) and ffn (%d) must be multiples of 64",
+                c->hidden, c->ffn);
+  if (c->hidden > 16384 || c->ffn > 16384)
+    return fail(why, QDEC_E_UNSUPPORTED, "hidden and ffn are limited to 16384 (LDS staging)");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(why, QDEC_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are implemented",
+                c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(why, QDEC_E_INVAL, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > 8)
+    return fail(why, QDEC_E_UNSUPPORTED, "more than 8 query heads per KV head");
+  if ((int64_t)c->n_q_heads * c->head_dim > 16384)
+    return fail(why, QDEC_E_UNSUPPORTED, "n_q_heads * head_dim is limited to 16384");
+  if (c->vocab > (1 << 30)) return fail(why, QDEC_E_UNSUPPORTED, "vocab above 2^30");
+  if ((c->tied_lm_head != 0 && c->tied_lm_head != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
+    return fail(why, QDEC_E_INVAL, "tied_lm_head and qk_norm must be 0 or 1");
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps))
+    return fail(why, QDEC_E_INVAL, "rms_eps must be positive and finite");
+  if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
+    return fail(why, QDEC_E_INVAL, "rope_theta must be finite and above 1");
+  auto dt_ok = [](int d) { return d == QDEC_F32 || d == QDEC_BF16 || d == QDEC_I8_ROW; };
+  if (!dt_ok(c->proj_dtype) || !dt_ok(c->lm_head_dtype) || !dt_ok(c->act_dtype) ||
+      !dt_ok(c->kv_dtype))
+    return fail(why, QDEC_E_INVAL, "unknown dtype value");
+  if (c->act_dtype == QDEC_F32) {
+    if (c->proj_dtype != QDEC_F32 || c->lm_head_dtype != QDEC_F32 || c->kv_dtype != QDEC_F32)
+      return fail(why, QDEC_E_UNSUPPORTED, "the fp32 path needs fp32 projections, LM head and KV");
+  } else if (c->act_dtype == QDEC_BF16) {
+    if (c->proj_dtype == QDEC_F32 || c->lm_head_dtype == QDEC_F32 || c->kv_dtype != QDEC_BF16)
+      return fail(why, QDEC_E_UNSUPPORTED,
+                  "the bf16 path needs bf16 or int8-row projections / LM head and a bf16 KV cache");
+  } else {
+    return fail(why, QDEC_E_UNSUPPORTED, "act_dtype must be F32 or BF16");
+  }
+  if (c->page_size != kPage)
+    return fail(why, QDEC_E_UNSUPPORTED, "page_size %d: only 16 is implemented", c->page_size);
+  if (c->num_pages < 1 || c->max_context < 1)
+    return fail(why, QDEC_E_INVAL, "num_pages and max_context must be positive");
+  if ((int64_t)c->num_pages * kPage < c->max_context)
+    return fail(why, QDEC_E_INVAL, "max_context %d exceeds num_pages * page_size", c->max_context);
+  if (c->max_context > (1 << 24)) return fail(why, QDEC_E_UNSUPPORTED, "max_context above 2^24");
+  if (c->partition_size < 0 || c->partition_size % 64)
+    return fail(why, QDEC_E_INVAL, "partition_size must be 0 or a positive multiple of 64");
+  return QDEC_OK;
+}
+
+static void fill_info(const qdec_config& c, qdec_info* o) {
+  const int64_t d = c.hidden, hq = c.n_q_heads, hkv = c.n_kv_heads, hd = c.head_dim, f = c.ffn,
+                v = c.vocab, L = c.n_layers;
+  const int64_t mats = (hq + 2 * hkv) * hd * d + d * hq * hd + 2 * f * d + d * f;
+  const int64_t rows = (hq + 2 * hkv) * hd + d + 2 * f + d;
+  const int64_t norms = 2 * d + (c.qk_norm ? 2 * hd : 0);
+  memset(o, 0, sizeof *o);
+  o->params_per_layer = mats + norms;
+  o->params_total = L * (mats + norms) + v * d * (c.tied_lm_head ? 1 : 2) + d;
+  o->layer_matrix_bytes = L * mats * elem_size(c.proj_dtype);
+  o->layer_scale_bytes = c.proj_dtype == QDEC_I8_ROW ? L * rows * 4 : 0;
+  o->lm_head_bytes = v * d * elem_size(c.lm_head_dtype) + (c.lm_head_dtype == QDEC_I8_ROW ? v * 4 : 0);
+  o->kv_bytes_per_layer_token = 2 * hkv * hd * elem_size(c.kv_dtype);
+  o->kv_pool_bytes = L * 2 * (int64_t)c.num_pages * kPage * hkv * hd * elem_size(c.kv_dtype);
+  const int pf = c.partition_size;
+  const int64_t mp = max_parts_for(c, pf);
+  o->partition_tokens = pf > 0 ? pf : part_tokens_for(c.max_context, 0, (int)hkv, kTargetWgs);
+  o->max_partitions = (int32_t)mp;
+  const int ae = elem_size(c.act_dtype);
+  const bool lm_alias = c.tied_lm_head && c.lm_head_dtype == c.act_dtype;
+  o->device_bytes = v * d * ae + (lm_alias ? 0 : o->lm_head_bytes) + d * 4 +
+                    o->layer_matrix_bytes + o->layer_scale_bytes + L * norms * 4 + o->kv_pool_bytes +
+                    (int64_t)c.num_pages * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
+                    (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ae +
+                    hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc);
+}
+
+QDEC_API qdec_status qdec_config_validate(const qdec_config* cfg, char* msg, size_t len) {
+  std::string why;
+  qdec_status s = validate(cfg, &why);
+  if (msg && len) {
+    snprintf(msg, len, "%s", s == QDEC_OK ? "ok" : why.c_str());
+  }
+  return s;
+}
+
+QDEC_API qdec_status qdec_config_info(const qdec_config* cfg, qdec_info* out) {
+  if (!out) return fail(nullptr, QDEC_E_INVAL, "out is NULL");
+  qdec_status s = validate(cfg, nullptr);
+  if (s != QDEC_OK) return s;
+  fill_info(*cfg, out);
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_bytes_model(const qdec_config* c, int32_t context, int32_t with_logits,
+                                      qdec_bytes* o) {
+  if (!o) return fail(nullptr, QDEC_E_INVAL, "out is NULL");
+  qdec_status s = validate(c, nullptr);
+  if (s != QDEC_OK) return s;
+  if (context < 1 || context > c->max_context)
+    return fail(nullptr, QDEC_E_RANGE, "context %d outside [1, %d]", context, c->max_context);
+  const int64_t d = c->hidden, hq = c->n_q_heads, hkv = c->n_kv_heads, hd = c->head_dim,
+                f = c->ffn, v = c->vocab, L = c->n_layers, T = context;
+  const int64_t we = elem_size(c->proj_dtype), ke = elem_size(c->kv_dtype),
+                ae = elem_size(c->act_dtype), le = elem_size(c->lm_head_dtype);
+  const int64_t sc = c->proj_dtype == QDEC_I8_ROW ? 4 : 0;
+  memset(o, 0, sizeof *o);
+  o->embed = d * ae;
+  o->qkv = L * ((hq + 2 * hkv) * hd * (d * we + sc) + d * 4);
+  o->rope_append = L * ((c->qk_norm ? 2 * hd * 4 : 0) + 2 * hkv * hd * ke);
+  o->attention = L * (T * 2 * hkv * hd * ke);
+  o->merge = 0;
+  o->o_proj = L * (d * (hq * hd * we + sc));
+  o->gate_up = L * (2 * f * (d * we + sc) + d * 4);
+  o->down = L * (d * (f * we + sc));
+  if (with_logits) {
+    o->lm_head = v * (d * le + (c->lm_head_dtype == QDEC_I8_ROW ? 4 : 0)) + d * 4 + v * ae;
+    o->argmax = v * ae;
+  }
+  o->total = o->embed + o->qkv + o->rope_append + o->attention + o->o_proj + o->gate_up + o->down +
+             o->lm_head;
+  const int part = c->partition_size > 0 ? c->partition_size
+                                         : part_tokens_for(context, 0, (int)hkv, kTargetWgs);
+  const int64_t np = n_parts_for(context, part);
+  o->scratch = np > 1 ? L * hq * np * (hd + 2) * 4 * 2 : 0;
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// lifecycle
+// =====================================================================================
+
+QDEC_API const char* qdec_status_string(qdec_status s) {
+  switch (s) {
+    case QDEC_OK: return "ok";
+    case QDEC_E_INVAL: return "invalid argument";
+    case QDEC_E_UNSUPPORTED: return "unsupported";
+    case QDEC_E_STATE: return "wrong state";
+    case QDEC_E_RANGE: return "out of range";
+    case QDEC_E_NOMEM: return "out of device memory";
+    case QDEC_E_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+QDEC_API const char* qdec_last_error(const qdec_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_err.c_str();
+}
+
+static void release(qdec_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->device);
+  (void)hipDeviceSynchronize();
+  if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  for (void* p : c->allocs) (void)hipFree(p);
+  delete c;
+}
+
+QDEC_API void qdec_destroy(qdec_ctx* ctx) { release(ctx); }
+
+QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ctx** out) {
+  if (!out) return fail(nullptr, QDEC_E_INVAL, "out is NULL");
+  *out = nullptr;
+  std::string why;
+  qdec_status s = validate(cfg, &why);
+  if (s != QDEC_OK) return s;
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(nullptr, QDEC_E_HIP, "no HIP device: %s", hipGetErrorString(he));
+  }
+  if (device < 0 || device >= ndev)
+    return fail(nullptr, QDEC_E_INVAL, "device %d out of [0, %d)", device, ndev);
+  he = hipSetDevice(device);
+  if (he != hipSuccess) return fail(nullptr, QDEC_E_HIP, "hipSetDevice: %s", hipGetErrorString(he));
+
+  qdec_ctx* c = new qdec_ctx();
+  c->cfg = *cfg;
+  c->device = device;
+  c->part_fixed = cfg->partition_size;
+  c->max_parts = (int)max_parts_for(*cfg, cfg->partition_size);
+  const int64_t d = cfg->hidden, hq = cfg->n_q_heads, hkv = cfg->n_kv_heads, hd = cfg->head_dim,
+                f = cfg->ffn, v = cfg->vocab, L = cfg->n_layers;
+  const int ae = elem_size(cfg->act_dtype);
+  c->uploaded.assign((size_t)(L + 1) * kNumSlots, 0);
+
+#define TRY(x)                  \
+  do {                          \
+    qdec_status s_ = (x);       \
+    if (s_ != QDEC_OK) {        \
+      g_err = c->err;           \
+      release(c);               \
+      return s_;                \
+    }                           \
+  } while (0)
+
+  auto make_mat = [&](Mat& m, int64_t rows, int64_t cols, int dtype, const char* what) {
+    m.rows = rows;
+    m.cols = cols;
+    m.dtype = dtype;
+    qdec_status st = c->alloc(&m.data, rows * cols * elem_size(dtype), what);
+    if (st == QDEC_OK && dtype == QDEC_I8_ROW) st = c->alloc(&m.scale, rows * 4, what);
+    return st;
+  };
+
+  TRY(make_mat(c->embed, v, d, cfg->act_dtype, "embedding"));
+  c->lm_alias = cfg->tied_lm_head && cfg->lm_head_dtype == cfg->act_dtype;
+  if (c->lm_alias)
+    c->lm = c->embed;
+  else
+    TRY(make_mat(c->lm, v, d, cfg->lm_head_dtype, "LM head"));
+  TRY(c->alloc(&c->final_norm, d * 4, "final norm"));
+  c->layers.resize((size_t)L);
+  const int64_t pool_bytes = (int64_t)cfg->num_pages * kPage * hkv * hd * elem_size(cfg->kv_dtype);
+  for (auto& ly : c->layers) {
+    TRY(make_mat(ly.qkv, (hq + 2 * hkv) * hd, d, cfg->proj_dtype, "QKV"));
+    TRY(make_mat(ly.o, d, hq * hd, cfg->proj_dtype, "O"));
+    TRY(make_mat(ly.gu, 2 * f, d, cfg->proj_dtype, "gate-up"));
+    TRY(make_mat(ly.down, d, f, cfg->proj_dtype, "down"));
+    TRY(c->alloc(&ly.in_norm, d * 4, "norm"));
+    TRY(c->alloc(&ly.post_norm, d * 4, "norm"));
+    if (cfg->qk_norm) {
+      TRY(c->alloc(&ly.q_norm, hd * 4, "q norm"));
+      TRY(c->alloc(&ly.k_norm, hd * 4, "k norm"));
+    }
+    TRY(c->alloc(&ly.k_pool, pool_bytes, "K pool"));
+    TRY(c->alloc(&ly.v_pool, pool_bytes, "V pool"));
+    TRY(c->hip(hipMemset(ly.k_pool, 0, (size_t)pool_bytes), "hipMemset K pool"));
+    TRY(c->hip(hipMemset(ly.v_pool, 0, (size_t)pool_bytes), "hipMemset V pool"));
+  }
+  TRY(c->alloc(&c->block_table, (int64_t)cfg->num_pages * 4, "block table"));
+  TRY(c->alloc(&c->rope, (int64_t)cfg->max_context * (hd / 2) * 8, "RoPE table"));
+  TRY(c->alloc(&c->x, d * 4, "residual"));
+  TRY(c->alloc(&c->qkv, (hq + 2 * hkv) * hd * 4, "qkv"));
+  TRY(c->alloc(&c->q, hq * hd * ae, "q"));
+  TRY(c->alloc(&c->attn, hq * hd * ae, "attention output"));
+  TRY(c->alloc(&c->act, f * ae, "SwiGLU output"));
+  TRY(c->alloc(&c->logits, v * ae, "logits"));
+  TRY(c->alloc(&c->part_acc, hq * (int64_t)c->max_parts * hd * 4, "split-KV scratch"));
+  TRY(c->alloc(&c->part_ml, hq * (int64_t)c->max_parts * 8, "split-KV scratch"));
+  TRY(c->alloc(&c->desc, (int64_t)sizeof(StepDesc), "step descriptor"));
+  TRY(c->hip(hipMemset(c->desc, 0, sizeof(StepDesc)), "hipMemset descriptor"));
+  TRY(c->hip(launch_rope_table(c->rope, cfg->max_context, (int)hd, cfg->rope_theta, nullptr),
+             "RoPE table kernel"));
+  TRY(c->hip(hipDeviceSynchronize(), "hipDeviceSynchronize after create"));
+#undef TRY
+  *out = c;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_info_get(const qdec_ctx* ctx, qdec_info* out) {
+  if (!ctx || !out) return fail(nullptr, QDEC_E_INVAL, "NULL argument");
+  fill_info(ctx->cfg, out);
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// weights
+// =====================================================================================
+
+static bool is_global(int which) {
+  return which == QDEC_W_EMBED || which == QDEC_W_LM_HEAD || which == QDEC_W_FINAL_NORM;
+}
+
+// Resolves a slot to a matrix or a gamma vector and its expected shape.
+static qdec_status resolve(qdec_ctx* c, int32_t layer, int32_t which, Mat** mat, float** vec,
+                           int64_t* rows, int64_t* cols) {
+  *mat = nullptr;
+  *vec = nullptr;
+  if (which < 0 || which >= kNumSlots) return fail(&c->err, QDEC_E_INVAL, "unknown weight slot %d", which);
+  if (!is_global(which) && (layer < 0 || layer >= c->cfg.n_layers))
+    return fail(&c->err, QDEC_E_INVAL, "layer %d out of [0, %d)", layer, c->cfg.n_layers);
+  const int64_t d = c->cfg.hidden, hd = c->cfg.head_dim;
+  Layer* ly = is_global(which) ? nullptr : &c->layers[(size_t)layer];
+  switch (which) {
+    case QDEC_W_EMBED: *mat = &c->embed; break;
+    case QDEC_W_LM_HEAD: *mat = &c->lm; break;
+    case QDEC_W_FINAL_NORM: *vec = c->final_norm; *rows = 1; *cols = d; return QDEC_OK;
+    case QDEC_W_IN_NORM: *vec = ly->in_norm; *rows = 1; *cols = d; return QDEC_OK;
+    case QDEC_W_POST_NORM: *vec = ly->post_norm; *rows = 1; *cols = d; return QDEC_OK;
+    case QDEC_W_Q_NORM:
+    case QDEC_W_K_NORM:
+      if (!c->cfg.qk_norm) return fail(&c->err, QDEC_E_INVAL, "qk_norm is off: no Q/K gamma slot");
+      *vec = which == QDEC_W_Q_NORM ? ly->q_norm : ly->k_norm;
+      *rows = 1;
+      *cols = hd;
+      return QDEC_OK;
+    case QDEC_W_QKV: *mat = &ly->qkv; break;
+    case QDEC_W_O: *mat = &ly->o; break;
+    case QDEC_W_GATE_UP: *mat = &ly->gu; break;
+    default: *mat = &ly->down; break;
+  }
+  *rows = (*mat)->rows;
+  *cols = (*mat)->cols;
+  return QDEC_OK;
+}
+
+static qdec_status copy_in(qdec_ctx* c, void* dst, const void* src, int64_t bytes, int src_dev,
+                           hipStream_t s) {
+  return c->hip(hipMemcpyAsync(dst, src, (size_t)bytes,
+                               src_dev ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice, s),
+                "hipMemcpyAsync (upload)");
+}
+
+// Fills `m` from src of src_dtype (conversion or quantisation on the device).
+static qdec_status fill_mat(qdec_ctx* c, Mat& m, const void* src, int src_dtype, int src_dev,
+                            hipStream_t s) {
+  const int64_t n = m.rows * m.cols;
+  if (m.dtype == src_dtype) return copy_in(c, m.data, src, n * elem_size(src_dtype), src_dev, s);
+  if (!src_dev)
+    return fail(&c->err, QDEC_E_UNSUPPORTED,
+                "converting a host source needs a device copy first (src_is_device = 1)");
+  if (m.dtype == QDEC_I8_ROW)
+    return c->hip(launch_quantize(src, src_dtype == QDEC_BF16, static_cast<int8_t*>(m.data),
+                                  m.scale, m.rows, m.cols, s),
+                  "quantize kernel");
+  return c->hip(launch_convert(m.data, m.dtype == QDEC_BF16 ? W_BF16 : W_F32, src,
+                               src_dtype == QDEC_BF16 ? W_BF16 : W_F32, n, s),
+                "convert kernel");
+}
+
+QDEC_API qdec_status qdec_upload(qdec_ctx* c, int32_t layer, int32_t which, const void* src,
+                                 int32_t src_dtype, int64_t rows, int64_t cols,
+                                 int32_t src_is_device, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (!src) return fail(&c->err, QDEC_E_INVAL, "src is NULL");
+  if (src_dtype != QDEC_F32 && src_dtype != QDEC_BF16)
+    return fail(&c->err, QDEC_E_INVAL, "src_dtype must be F32 or BF16");
+  if (src_is_device && !aligned(src, 16))
+    return fail(&c->err, QDEC_E_INVAL, "device source must be 16-byte aligned");
+  Mat* m;
+  float* vec;
+  int64_t er, ec;
+  qdec_status st = resolve(c, layer, which, &m, &vec, &er, &ec);
+  if (st != QDEC_OK) return st;
+  if (rows != er || cols != ec)
+    return fail(&c->err, QDEC_E_INVAL, "shape %lldx%lld, expected %lldx%lld", (long long)rows,
+                (long long)cols, (long long)er, (long long)ec);
+  if (which == QDEC_W_LM_HEAD && c->cfg.tied_lm_head)
+    return fail(&c->err, QDEC_E_INVAL, "tied LM head: upload QDEC_W_EMBED instead");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
+  const int lrow = is_global(which) ? c->cfg.n_layers : layer;
+  if (vec) {
+    if (src_dtype == QDEC_F32)
+      st = copy_in(c, vec, src, cols * 4, src_is_device, s);
+    else if (!src_is_device)
+      return fail(&c->err, QDEC_E_UNSUPPORTED, "bf16 gamma from the host needs a device copy");
+    else
+      st = c->hip(launch_convert(vec, W_F32, src, W_BF16, cols, s), "convert kernel");
+    if (st == QDEC_OK) c->slot(lrow, which) = 1;
+    return st;
+  }
+  if (m->dtype == QDEC_I8_ROW && m->cols % 16)
+    return fail(&c->err, QDEC_E_UNSUPPORTED, "int8 rows need cols %% 16 == 0");
+  st = fill_mat(c, *m, src, src_dtype, src_is_device, s);
+  if (st != QDEC_OK) return st;
+  c->slot(lrow, which) = 1;
+  if (which == QDEC_W_EMBED && c->cfg.tied_lm_head) {
+    if (!c->lm_alias) {
+      st = fill_mat(c, c->lm, src, src_dtype, src_is_device, s);
+      if (st != QDEC_OK) return st;
+    }
+    c->slot(lrow, QDEC_W_LM_HEAD) = 1;
+  }
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_upload_i8(qdec_ctx* c, int32_t layer, int32_t which,
+                                    const int8_t* codes, const float* scales, int64_t rows,
+                                    int64_t cols, int32_t src_is_device, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (!codes || !scales) return fail(&c->err, QDEC_E_INVAL, "codes/scales NULL");
+  Mat* m;
+  float* vec;
+  int64_t er, ec;
+  qdec_status st = resolve(c, layer, which, &m, &vec, &er, &ec);
+  if (st != QDEC_OK) return st;
+  if (!m || m->dtype != QDEC_I8_ROW) return fail(&c->err, QDEC_E_INVAL, "slot is not int8-row");
+  if (which == QDEC_W_LM_HEAD && c->cfg.tied_lm_head && c->lm_alias)
+    return fail(&c->err, QDEC_E_INVAL, "tied LM head aliases the embedding");
+  if (rows != er || cols != ec) return fail(&c->err, QDEC_E_INVAL, "shape mismatch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
+  if ((st = copy_in(c, m->data, codes, rows * cols, src_is_device, s)) != QDEC_OK) return st;
+  if ((st = copy_in(c, m->scale, scales, rows * 4, src_is_device, s)) != QDEC_OK) return st;
+  c->slot(is_global(which) ? c->cfg.n_layers : layer, which) = 1;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_weight_ptr(const qdec_ctx* c0, int32_t layer, int32_t which,
+                                     void** data, float** scales) {
+  qdec_ctx* c = const_cast<qdec_ctx*>(c0);
+  if (!c || !data) return fail(nullptr, QDEC_E_INVAL, "NULL argument");
+  Mat* m;
+  float* vec;
+  int64_t r, k;
+  qdec_status st = resolve(c, layer, which, &m, &vec, &r, &k);
+  if (st != QDEC_OK) return st;
+  *data = m ? m->data : vec;
+  if (scales) *scales = m ? m->scale : nullptr;
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// paged KV
+// =====================================================================================
+
+QDEC_API qdec_status qdec_kv_set_block_table(qdec_ctx* c, const int32_t* table, int32_t n_logical,
+                                             void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (!table) return fail(&c->err, QDEC_E_INVAL, "table is NULL");
+  if (n_logical < 1 || n_logical > c->cfg.num_pages)
+    return fail(&c->err, QDEC_E_INVAL, "n_logical %d out of [1, %d]", n_logical, c->cfg.num_pages);
+  std::vector<uint8_t> used((size_t)c->cfg.num_pages, 0);
+  for (int i = 0; i < n_logical; ++i) {
+    const int32_t p = table[i];
+    if (p < 0 || p >= c->cfg.num_pages)
+      return fail(&c->err, QDEC_E_INVAL, "block_table[%d] = %d out of [0, %d)", i, p,
+                  c->cfg.num_pages);
+    if (used[(size_t)p]) return fail(&c->err, QDEC_E_INVAL, "physical page %d mapped twice", p);
+    used[(size_t)p] = 1;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  qdec_status st;
+  if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
+  if ((st = c->hip(hipMemcpyAsync(c->block_table, table, (size_t)n_logical * 4,
+                                  hipMemcpyHostToDevice, s),
+                   "hipMemcpyAsync (block table)")) != QDEC_OK)
+    return st;
+  if ((st = c->hip(hipStreamSynchronize(s), "hipStreamSynchronize")) != QDEC_OK) return st;
+  c->n_logical = n_logical;
+  return QDEC_OK;
+}
+
+static qdec_status kv_copy(qdec_ctx* c, int32_t layer, int32_t pos0, int32_t n, void* k, void* v,
+                           void* stream, int to_pool) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(&c->err, QDEC_E_INVAL, "layer out of range");
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16))
+    return fail(&c->err, QDEC_E_INVAL, "k/v must be non-NULL and 16-byte aligned");
+  if (pos0 < 0 || n < 0) return fail(&c->err, QDEC_E_INVAL, "negative position or count");
+  if (c->n_logical == 0) return fail(&c->err, QDEC_E_STATE, "no block table set");
+  if ((int64_t)pos0 + n > (int64_t)c->n_logical * kPage || (int64_t)pos0 + n > c->cfg.max_context)
+    return fail(&c->err, QDEC_E_RANGE, "positions [%d, %d) not mapped", pos0, pos0 + n);
+  if (n == 0) return QDEC_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  qdec_status st;
+  if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
+  const Layer& ly = c->layers[(size_t)layer];
+  const int es = elem_size(c->cfg.kv_dtype);
+  if ((st = c->hip(launch_kv_copy(ly.k_pool, k, c->block_table, pos0, n, c->cfg.n_kv_heads,
+                                  c->cfg.head_dim, es, to_pool, s),
+                   "kv copy kernel")) != QDEC_OK)
+    return st;
+  return c->hip(launch_kv_copy(ly.v_pool, v, c->block_table, pos0, n, c->cfg.n_kv_heads,
+                               c->cfg.head_dim, es, to_pool, s),
+                "kv copy kernel");
+}
+
+QDEC_API qdec_status qdec_kv_write(qdec_ctx* c, int32_t layer, int32_t pos0, int32_t n,
+                                   const void* k, const void* v, void* stream) {
+  return kv_copy(c, layer, pos0, n, const_cast<void*>(k), const_cast<void*>(v), stream, 1);
+}
+
+QDEC_API qdec_status qdec_kv_read(qdec_ctx* c, int32_t layer, int32_t pos0, int32_t n, void* k,
+                                  void* v, void* stream) {
+  return kv_copy(c, layer, pos0, n, k, v, stream, 0);
+}
+
+QDEC_API qdec_status qdec_kv_pool_ptr(const qdec_ctx* c, int32_t layer, void** k_pool,
+                                      void** v_pool) {
+  if (!c || !k_pool || !v_pool) return fail(nullptr, QDEC_E_INVAL, "NULL argument");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(nullptr, QDEC_E_INVAL, "layer out of range");
+  *k_pool = c->layers[(size_t)layer].k_pool;
+  *v_pool = c->layers[(size_t)layer].v_pool;
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// the decode step
+// =====================================================================================
+
+static qdec_status check_step(qdec_ctx* c, const qdec_step* st, bool check_pos) {
+  if (!st) return fail(&c->err, QDEC_E_INVAL, "step is NULL");
+  if (st->reserved != 0) return fail(&c->err, QDEC_E_INVAL, "step.reserved must be 0");
+  if (!st->token_embedding && !st->token_id)
+    return fail(&c->err, QDEC_E_INVAL, "need token_embedding or token_id");
+  if (st->token_embedding && !aligned(st->token_embedding, 4))
+    return fail(&c->err, QDEC_E_INVAL, "token_embedding misaligned");
+  if (st->hidden_out && !aligned(st->hidden_out, 16))
+    return fail(&c->err, QDEC_E_INVAL, "hidden_out must be 16-byte aligned");
+  if (st->logits_out && !aligned(st->logits_out, 4))
+    return fail(&c->err, QDEC_E_INVAL, "logits_out misaligned");
+  const int L = c->cfg.n_layers;
+  for (int l = 0; l <= L; ++l)
+    for (int w = 0; w < kNumSlots; ++w) {
+      bool need;
+      if (l == L)
+        need = is_global(w);
+      else
+        need = !is_global(w) && (c->cfg.qk_norm || (w != QDEC_W_Q_NORM && w != QDEC_W_K_NORM));
+      if (need && !c->slot(l, w))
+        return fail(&c->err, QDEC_E_STATE, "weight slot %d of layer %d not uploaded", w,
+                    l == L ? -1 : l);
+    }
+  if (c->n_logical == 0) return fail(&c->err, QDEC_E_STATE, "no block table set");
+  if (check_pos) {
+    if (st->pos < 0 || st->pos >= c->cfg.max_context)
+      return fail(&c->err, QDEC_E_RANGE, "pos %d outside [0, %d)", st->pos, c->cfg.max_context);
+    if (st->pos / kPage >= c->n_logical)
+      return fail(&c->err, QDEC_E_RANGE, "pos %d beyond the block table (%d pages)", st->pos,
+                  c->n_logical);
+  }
+  return QDEC_OK;
+}
+
+// Records one launch for the event profiler (eager steps only).
+struct ProfScope {
+  qdec_ctx* c;
+  hipStream_t s;
+  int cls;
+  bool on;
+  ProfScope(qdec_ctx* c_, hipStream_t s_, int cls_, bool graph)
+      : c(c_), s(s_), cls(cls_), on(c_->prof && !graph && c_->ev_used + 2 <= (int)c_->ev.size()) {
+    if (on) (void)hipEventRecord(c->ev[(size_t)c->ev_used], s);
+  }
+  void done() {
+    if (!on) return;
+    (void)hipEventRecord(c->ev[(size_t)c->ev_used + 1], s);
+    c->ev_class[(size_t)c->ev_used / 2] = cls;
+    c->ev_used += 2;
+  }
+};
+
+// Enqueues every kernel of the step after the embedding.  In graph mode the split-KV grid covers
+// max_context and the merge always runs; the kernels take ctx from the device descriptor in both
+// modes, so eager and replayed steps compute the same values.
+static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s,
+                                  bool graph) {
+  const qdec_config& k = c->cfg;
+  const int64_t d = k.hidden, hq = k.n_q_heads, hkv = k.n_kv_heads, hd = k.head_dim, f = k.ffn;
+  const bool ab = c->act_bf16();
+  const int wt = k.proj_dtype == QDEC_F32 ? W_F32 : k.proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+  const int ctxlen = pos + 1;
+  const int part = part_tokens_for(ctxlen, c->part_fixed, (int)hkv, kTargetWgs);
+  const int np = n_parts_for(ctxlen, part);
+  const int grid_parts = graph ? c->max_parts : np;
+  const int group = (int)(hq / hkv);
+  qdec_status rs;
+#define LAUNCH(cls, call)                                   \
+  do {                                                      \
+    ProfScope ps_(c, s, cls, graph);                        \
+    if ((rs = c->hip((call), #cls)) != QDEC_OK) return rs;  \
+    ps_.done();                                             \
+  } while (0)
+
+  for (int64_t l = 0; l < k.n_layers; ++l) {
+    const Layer& ly = c->layers[(size_t)l];
+    GemvArgs g{};
+    g.w = ly.qkv.data;
+    g.scale = ly.qkv.scale;
+    g.xn = c->x;
+    g.gamma = ly.in_norm;
+    g.eps = k.rms_eps;
+    g.round_h = ab;
+    g.y = c->qkv;
+    g.y_bf16 = 0;
+    g.n = (hq + 2 * hkv) * hd;
+    g.k = d;
+    LAUNCH(QDEC_K_QKV, launch_gemv(wt, EPI_STORE, true, g, s));
+
+    RopeAppendArgs r{};
+    r.qkv = c->qkv;
+    r.q_gamma = ly.q_norm;
+    r.k_gamma = ly.k_norm;
+    r.eps = k.rms_eps;
+    r.table = c->rope;
+    r.desc = c->desc;
+    r.q_out = c->q;
+    r.q_bf16 = ab;
+    r.k_pool = ly.k_pool;
+    r.v_pool = ly.v_pool;
+    r.kv_bf16 = c->kv_bf16();
+    r.block_table = c->block_table;
+    r.n_q_heads = (int)hq;
+    r.n_kv_heads = (int)hkv;
+    LAUNCH(QDEC_K_ROPE_APPEND, launch_rope_append((int)hd, r, s));
+
+    AttnArgs at{};
+    at.q = c->q;
+    at.q_bf16 = ab;
+    at.k_pool = ly.k_pool;
+    at.v_pool = ly.v_pool;
+    at.block_table = c->block_table;
+    at.desc = c->desc;
+    at.n_q_heads = (int)hq;
+    at.n_kv_heads = (int)hkv;
+    at.part_fixed = c->part_fixed;
+    at.target_wgs = kTargetWgs;
+    at.max_parts = c->max_parts;
+    at.part_acc = c->part_acc;
+    at.part_ml = c->part_ml;
+    at.out = c->attn;
+    at.out_bf16 = ab;
+    at.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+    LAUNCH(QDEC_K_ATTENTION, launch_attention((int)hd, c->kv_bf16(), group, at, grid_parts, s));
+    if (graph || np > 1) LAUNCH(QDEC_K_MERGE, launch_attention_merge((int)hd, at, s));
+
+    GemvArgs o{};
+    o.w = ly.o.data;
+    o.scale = ly.o.scale;
+    o.x = c->attn;
+    o.x_bf16 = ab;
+    o.resid = c->x;
+    o.n = d;
+    o.k = hq * hd;
+    LAUNCH(QDEC_K_O_PROJ, launch_gemv(wt, EPI_RESID, false, o, s));
+
+    GemvArgs gu{};
+    gu.w = ly.gu.data;
+    gu.scale = ly.gu.scale;
+    gu.xn = c->x;
+    gu.gamma = ly.post_norm;
+    gu.eps = k.rms_eps;
+    gu.round_h = ab;
+    gu.y = c->act;
+    gu.y_bf16 = ab;
+    gu.n = f;
+    gu.k = d;
+    LAUNCH(QDEC_K_GATE_UP, launch_gemv(wt, EPI_SWIGLU, true, gu, s));
+
+    GemvArgs dn{};
+    dn.w = ly.down.data;
+    dn.scale = ly.down.scale;
+    dn.x = c->act;
+    dn.x_bf16 = ab;
+    dn.resid = c->x;
+    dn.n = d;
+    dn.k = f;
+    LAUNCH(QDEC_K_DOWN, launch_gemv(wt, EPI_RESID, false, dn, s));
+  }
+
+  const bool want_logits = st->logits_out || st->argmax_out;
+  if (want_logits) {
+    void* lg = st->logits_out ? st->logits_out : c->logits;
+    const int lt = k.lm_head_dtype == QDEC_F32 ? W_F32 : k.lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+    GemvArgs h{};
+    h.w = c->lm.data;
+    h.scale = c->lm.scale;
+    h.xn = c->x;
+    h.gamma = c->final_norm;
+    h.eps = k.rms_eps;
+    h.round_h = ab;
+    h.y = lg;
+    h.y_bf16 = ab;
+    h.hidden_copy = st->hidden_out;
+    h.n = k.vocab;
+    h.k = d;
+    LAUNCH(QDEC_K_LM_HEAD, launch_gemv(lt, EPI_STORE, true, h, s));
+    if (st->argmax_out) LAUNCH(QDEC_K_ARGMAX, launch_argmax(lg, ab, k.vocab, st->argmax_out, s));
+  } else if (st->hidden_out) {
+    if ((rs = c->hip(launch_copy(st->hidden_out, c->x, d * 4, s), "hidden copy")) != QDEC_OK)
+      return rs;
+  }
+#undef LAUNCH
+  return QDEC_OK;
+}
+
+static qdec_status enqueue_embed(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s) {
+  EmbedArgs e{};
+  e.table = c->embed.data;
+  e.table_bf16 = c->act_bf16();
+  e.emb = st->token_embedding;
+  e.token = st->token_id;
+  e.x = c->x;
+  e.desc = c->desc;
+  e.pos = pos;
+  e.vocab = c->cfg.vocab;
+  e.d = c->cfg.hidden;
+  ProfScope ps(c, s, QDEC_K_EMBED, false);
+  qdec_status r = c->hip(launch_embed(e, s), "embedding kernel");
+  if (r == QDEC_OK) ps.done();
+  return r;
+}
+
+QDEC_API qdec_status qdec_decode_step(qdec_ctx* c, const qdec_step* st, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  qdec_status r = check_step(c, st, true);
+  if (r != QDEC_OK) return r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  if (c->prof) c->ev_used = 0;
+  if ((r = enqueue_embed(c, st, st->pos, s)) != QDEC_OK) return r;
+  return enqueue_layers(c, st, st->pos, s, false);
+}
+
+QDEC_API qdec_status qdec_graph_reset(qdec_ctx* c) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (c->gexec) (void)hipGraphExecDestroy(c->gexec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  c->gexec = nullptr;
+  c->graph = nullptr;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_graph_capture(qdec_ctx* c, const qdec_step* templ, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  qdec_status r = check_step(c, templ, false);
+  if (r != QDEC_OK) return r;
+  qdec_graph_reset(c);
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  if (!c->cap_stream &&
+      (r = c->hip(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking),
+                  "hipStreamCreateWithFlags")) != QDEC_OK)
+    return r;
+  // the capture stream must not start before earlier work on the caller's stream (uploads)
+  if ((r = c->hip(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize")) !=
+      QDEC_OK)
+    return r;
+  if ((r = c->hip(hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal),
+                  "hipStreamBeginCapture")) != QDEC_OK)
+    return r;
+  qdec_status er = enqueue_layers(c, templ, 0, c->cap_stream, true);
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamEndCapture(c->cap_stream, &g);
+  if (er != QDEC_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return er;
+  }
+  if ((r = c->hip(e, "hipStreamEndCapture")) != QDEC_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return r;
+  }
+  hipGraphExec_t ex = nullptr;
+  if ((r = c->hip(hipGraphInstantiate(&ex, g, nullptr, nullptr, 0), "hipGraphInstantiate")) !=
+      QDEC_OK) {
+    (void)hipGraphDestroy(g);
+    return r;
+  }
+  c->graph = g;
+  c->gexec = ex;
+  c->graph_templ = *templ;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_graph_replay(qdec_ctx* c, int32_t pos, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (!c->gexec) return fail(&c->err, QDEC_E_STATE, "no captured graph");
+  qdec_step st = c->graph_templ;
+  st.pos = pos;
+  qdec_status r = check_step(c, &st, true);
+  if (r != QDEC_OK) return r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  // the embedding kernel carries pos and runs in stream order ahead of the graph
+  const bool prof = c->prof;
+  c->prof = false;
+  r = enqueue_embed(c, &st, pos, s);
+  c->prof = prof;
+  if (r != QDEC_OK) return r;
+  return c->hip(hipGraphLaunch(c->gexec, s), "hipGraphLaunch");
+}
+
+QDEC_API qdec_status qdec_device_error(qdec_ctx* c, int32_t* flag, void* stream) {
+  if (!c || !flag) return fail(nullptr, QDEC_E_INVAL, "NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StepDesc h{};
+  qdec_status r;
+  if ((r = c->hip(hipMemcpyAsync(&h, c->desc, sizeof h, hipMemcpyDeviceToHost, s), "read flag")) !=
+      QDEC_OK)
+    return r;
+  if ((r = c->hip(hipStreamSynchronize(s), "hipStreamSynchronize")) != QDEC_OK) return r;
+  *flag = h.error;
+  if (h.error) {
+    const int32_t zero = 0;
+    if ((r = c->hip(hipMemcpyAsync(&c->desc->error, &zero, 4, hipMemcpyHostToDevice, s),
+                    "clear flag")) != QDEC_OK)
+      return r;
+    if ((r = c->hip(hipStreamSynchronize(s), "hipStreamSynchronize")) != QDEC_OK) return r;
+  }
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// event profiler
+// =====================================================================================
+
+QDEC_API qdec_status qdec_profile_enable(qdec_ctx* c, int32_t enable) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  qdec_status r;
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  for (int k = 0; k < QDEC_K_COUNT; ++k) {
+    c->prof_ms[k] = 0;
+    c->prof_n[k] = 0;
+  }
+  c->ev_used = 0;
+  if (enable && c->ev.empty()) {
+    const size_t n = 2 * (size_t)(8 * c->cfg.n_layers + 4);
+    for (size_t i = 0; i < n; ++i) {
+      hipEvent_t e;
+      if ((r = c->hip(hipEventCreate(&e), "hipEventCreate")) != QDEC_OK) return r;
+      c->ev.push_back(e);
+    }
+    c->ev_class.assign(n / 2, 0);
+  }
+  c->prof = enable != 0;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_profile_collect(qdec_ctx* c, double* ms, int64_t* launches) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  qdec_status r;
+  for (int i = 0; i + 1 < c->ev_used; i += 2) {
+    if ((r = c->hip(hipEventSynchronize(c->ev[(size_t)i + 1]), "hipEventSynchronize")) != QDEC_OK)
+      return r;
+    float t = 0.f;
+    if ((r = c->hip(hipEventElapsedTime(&t, c->ev[(size_t)i], c->ev[(size_t)i + 1]),
+                    "hipEventElapsedTime")) != QDEC_OK)
+      return r;
+    const int cls = c->ev_class[(size_t)i / 2];
+    c->prof_ms[cls] += t;
+    c->prof_n[cls] += 1;
+  }
+  c->ev_used = 0;
+  for (int k = 0; k < QDEC_K_COUNT; ++k) {
+    if (ms) ms[k] = c->prof_ms[k];
+    if (launches) launches[k] = c->prof_n[k];
+  }
+  return QDEC_OK;
+}
+
+// =====================================================================================
+// op-level entry points
+// =====================================================================================
+
+static int wt_of(int32_t dt) { return dt == QDEC_F32 ? W_F32 : dt == QDEC_BF16 ? W_BF16 : W_I8; }
+
+QDEC_API qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale,
+                                  const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
+                                  int64_t n, int64_t k, void* stream) {
+  if (!w || !x || !y) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (w_dtype < QDEC_F32 || w_dtype > QDEC_I8_ROW) return fail(nullptr, QDEC_E_INVAL, "bad w_dtype");
+  if ((w_dtype == QDEC_I8_ROW) != (w_scale != nullptr))
+    return fail(nullptr, QDEC_E_INVAL, "w_scale is required for (and only for) I8_ROW");
+  if ((x_dtype != QDEC_F32 && x_dtype != QDEC_BF16) || (y_dtype != QDEC_F32 && y_dtype != QDEC_BF16))
+    return fail(nullptr, QDEC_E_INVAL, "x/y dtype must be F32 or BF16");
+  if (n < 1 || k < 1) return fail(nullptr, QDEC_E_INVAL, "n and k must be positive");
+  if (k > 16384) return fail(nullptr, QDEC_E_UNSUPPORTED, "k above 16384 (LDS staging)");
+  if ((k * elem_size(w_dtype)) % 16) return fail(nullptr, QDEC_E_INVAL, "rows must be 16-byte multiples");
+  if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4) || (w_scale && !aligned(w_scale, 4)))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer");
+  GemvArgs a{};
+  a.w = w;
+  a.scale = w_scale;
+  a.x = x;
+  a.x_bf16 = x_dtype == QDEC_BF16;
+  a.y = y;
+  a.y_bf16 = y_dtype == QDEC_BF16;
+  a.n = n;
+  a.k = k;
+  hipError_t e = launch_gemv(wt_of(w_dtype), EPI_STORE, false, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "gemv launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_quantize_rows(const void* w, int32_t w_dtype, int8_t* codes,
+                                           float* scales, int64_t n, int64_t k, void* stream) {
+  if (!w || !codes || !scales) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (w_dtype != QDEC_F32 && w_dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad w_dtype");
+  if (n < 1 || k < 1 || k % 16) return fail(nullptr, QDEC_E_INVAL, "need n, k > 0 and k %% 16 == 0");
+  if (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 4))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer");
+  hipError_t e = launch_quantize(w, w_dtype == QDEC_BF16, codes, scales, n, k,
+                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_rmsnorm(const float* x, const float* gamma, float eps, void* y,
+                                     int32_t y_dtype, int32_t n, void* stream) {
+  if (!x || !gamma || !y) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (n < 1 || !(eps > 0.f)) return fail(nullptr, QDEC_E_INVAL, "need n > 0 and eps > 0");
+  if (y_dtype != QDEC_F32 && y_dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad y_dtype");
+  hipError_t e = launch_rmsnorm(x, gamma, eps, y, y_dtype == QDEC_BF16, n,
+                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "rmsnorm launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_rope_table(float* table, int32_t max_pos, int32_t head_dim,
+                                        float theta, void* stream) {
+  if (!table) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (max_pos < 1 || (head_dim != 64 && head_dim != 128) || !(theta > 1.f))
+    return fail(nullptr, QDEC_E_INVAL, "bad sizes");
+  hipError_t e = launch_rope_table(table, max_pos, head_dim, theta, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "rope table launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_qk_norm_rope_append(
+    const float* qkv, const float* q_gamma, const float* k_gamma, float eps, const float* table,
+    int32_t pos, void* q_out, int32_t q_dtype, void* k_pool, void* v_pool, int32_t kv_dtype,
+    const int32_t* block_table, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+    int32_t page_size, void* stream) {
+  if (!qkv || !table || !q_out || !k_pool || !v_pool || !block_table)
+    return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if ((q_gamma == nullptr) != (k_gamma == nullptr))
+    return fail(nullptr, QDEC_E_INVAL, "q_gamma and k_gamma must both be set or both NULL");
+  if (head_dim != 64 && head_dim != 128) return fail(nullptr, QDEC_E_UNSUPPORTED, "head_dim");
+  if (page_size != kPage) return fail(nullptr, QDEC_E_UNSUPPORTED, "page_size must be 16");
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || pos < 0)
+    return fail(nullptr, QDEC_E_INVAL, "bad head counts or position");
+  if ((q_dtype != QDEC_F32 && q_dtype != QDEC_BF16) || (kv_dtype != QDEC_F32 && kv_dtype != QDEC_BF16))
+    return fail(nullptr, QDEC_E_INVAL, "bad dtype");
+  RopeAppendArgs a{};
+  a.qkv = qkv;
+  a.q_gamma = q_gamma;
+  a.k_gamma = k_gamma;
+  a.eps = eps;
+  a.table = table;
+  a.pos_arg = pos;
+  a.q_out = q_out;
+  a.q_bf16 = q_dtype == QDEC_BF16;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_bf16 = kv_dtype == QDEC_BF16;
+  a.block_table = block_table;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  hipError_t e = launch_rope_append(head_dim, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "rope/append launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+static int op_part(int32_t ctx_len, int32_t n_kv_heads, int32_t partition_size) {
+  return part_tokens_for(ctx_len, partition_size, n_kv_heads, kTargetWgs);
+}
+
+QDEC_API qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_heads,
+                                                 int32_t head_dim, int32_t partition_size,
+                                                 size_t* bytes) {
+  if (!bytes) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (ctx_len < 1 || n_q_heads < 1 || head_dim < 1 || partition_size < 0 || partition_size % 64)
+    return fail(nullptr, QDEC_E_INVAL, "bad sizes");
+  // the automatic size depends on n_kv_heads; take the largest count it can produce (Hkv = 1)
+  const int part = partition_size > 0 ? partition_size : op_part(ctx_len, 1, 0);
+  const int64_t np = n_parts_for(ctx_len, part);
+  if (np <= 1) {
+    *bytes = 0;
+    return QDEC_OK;
+  }
+  const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
+  *bytes = (size_t)(acc + (int64_t)n_q_heads * np * 8);
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const void* k_pool,
+                                       const void* v_pool, int32_t kv_dtype,
+                                       const int32_t* block_table, int32_t ctx_len,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int32_t page_size, int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, void* out, int32_t out_dtype,
+                                       void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (head_dim != 64 && head_dim != 128) return fail(nullptr, QDEC_E_UNSUPPORTED, "head_dim");
+  if (page_size != kPage) return fail(nullptr, QDEC_E_UNSUPPORTED, "page_size must be 16");
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8)
+    return fail(nullptr, QDEC_E_INVAL, "bad head counts");
+  if (ctx_len < 1) return fail(nullptr, QDEC_E_INVAL, "ctx_len must be positive");
+  if (partition_size < 0 || partition_size % 64)
+    return fail(nullptr, QDEC_E_INVAL, "partition_size must be 0 or a multiple of 64");
+  if ((q_dtype != QDEC_F32 && q_dtype != QDEC_BF16) || (kv_dtype != QDEC_F32 && kv_dtype != QDEC_BF16) ||
+      (out_dtype != QDEC_F32 && out_dtype != QDEC_BF16))
+    return fail(nullptr, QDEC_E_INVAL, "bad dtype");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(nullptr, QDEC_E_INVAL, "pools must be 16-byte aligned");
+  const int part = op_part(ctx_len, n_kv_heads, partition_size);
+  const int np = n_parts_for(ctx_len, part);
+  size_t need = 0;
+  if (np > 1) {
+    const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
+    need = (size_t)(acc + (int64_t)n_q_heads * np * 8);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+      return fail(nullptr, QDEC_E_INVAL, "workspace of %zu bytes (256-byte aligned) required", need);
+  }
+  AttnArgs a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == QDEC_BF16;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.desc = nullptr;
+  a.ctx_arg = ctx_len;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.part_fixed = partition_size;
+  a.target_wgs = kTargetWgs;
+  a.max_parts = np;
+  if (np > 1) {
+    a.part_acc = static_cast<float*>(workspace);
+    const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
+    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
+  }
+  a.out = out;
+  a.out_bf16 = out_dtype == QDEC_BF16;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_attention(head_dim, kv_dtype == QDEC_BF16, n_q_heads / n_kv_heads, a, np, s);
+  if (e == hipSuccess && np > 1) e = launch_attention_merge(head_dim, a, s);
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "attention launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_argmax(const void* x, int32_t x_dtype, int64_t n, int32_t* out,
+                                    void* stream) {
+  if (!x || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (x_dtype != QDEC_F32 && x_dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad dtype");
+  if (n < 1 || n > (int64_t)1 << 31) return fail(nullptr, QDEC_E_INVAL, "n out of range");
+  hipError_t e = launch_argmax(x, x_dtype == QDEC_BF16, n, out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "argmax launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_copy(void* dst, const void* src, int64_t bytes, void* stream) {
+  if (!dst || !src) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (bytes < 0 || bytes % 16 || !aligned(dst, 16) || !aligned(src, 16))
+    return fail(nullptr, QDEC_E_INVAL, "bytes and pointers must be multiples of 16");
+  hipError_t e = launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "copy launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}

@@ -1,0 +1,86 @@
+"""Helpers that marshal a model's tensors into a qdec context (no arithmetic of the method).
+
+``config_for`` fills a ``qdec_config`` from a shape dict (see ``synth``); ``upload_weights``
+hands every tensor of a weight dict to ``qdec_upload`` (the library converts / quantises on the
+device); ``prefill_kv`` writes logical K/V rows through the block table with ``qdec_kv_write``.
+"""
+from __future__ import annotations
+
+from . import qdec as Q
+
+
+def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
+               partition_size: int = 0) -> Q.qdec_config:
+    """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights/activations/KV) or 'w8a16'
+    (int8 per-row projections and LM head, bf16 activations and KV)."""
+    if path == "fp32":
+        proj = lm = act = kv = Q.F32
+    elif path == "bf16":
+        proj = lm = act = kv = Q.BF16
+    elif path == "w8a16":
+        proj = lm = Q.I8_ROW
+        act = kv = Q.BF16
+    else:
+        raise ValueError(path)
+    return Q.make_config(
+        n_layers=shape["n_layers"], hidden=shape["hidden"], n_q_heads=shape["n_q_heads"],
+        n_kv_heads=shape["n_kv_heads"], head_dim=shape["head_dim"], ffn=shape["ffn"],
+        vocab=shape["vocab"], tied_lm_head=int(shape["tied"]), qk_norm=int(shape["qk_norm"]),
+        rms_eps=shape["eps"], rope_theta=shape["theta"], proj_dtype=proj, lm_head_dtype=lm,
+        act_dtype=act, kv_dtype=kv, page_size=16, num_pages=num_pages, max_context=max_context,
+        partition_size=partition_size)
+
+
+def _dt(t):
+    import torch
+
+    if t.dtype == torch.float32:
+        return Q.F32
+    if t.dtype == torch.bfloat16:
+        return Q.BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def upload_weights(ctx, weights: dict, device="cuda", stream=None):
+    """Uploads a weight dict (torch tensors, or numpy float32 arrays for the tiny model).
+    Tensors are moved to `device` first so every conversion runs on the GPU."""
+    import numpy as np
+    import torch
+
+    keep = []
+
+    def dev(a):
+        if isinstance(a, np.ndarray):
+            a = torch.from_numpy(a)
+        t = a.to(device).contiguous()
+        keep.append(t)
+        return t
+
+    def up(layer, which, a):
+        t = dev(a)
+        rows, cols = (1, t.numel()) if t.dim() == 1 else tuple(t.shape)
+        Q.qdec_upload(ctx, layer, which, t, _dt(t), rows, cols, 1, stream)
+
+    up(0, Q.W_EMBED, weights["embed"])
+    if weights.get("lm_head") is not None:
+        up(0, Q.W_LM_HEAD, weights["lm_head"])
+    up(0, Q.W_FINAL_NORM, weights["final_norm"])
+    for l in range(len(weights["qkv"])):
+        up(l, Q.W_IN_NORM, weights["in_norm"][l])
+        up(l, Q.W_POST_NORM, weights["post_norm"][l])
+        if weights.get("q_norm"):
+            up(l, Q.W_Q_NORM, weights["q_norm"][l])
+            up(l, Q.W_K_NORM, weights["k_norm"][l])
+        up(l, Q.W_QKV, weights["qkv"][l])
+        up(l, Q.W_O, weights["o"][l])
+        up(l, Q.W_GATE_UP, weights["gate_up"][l])
+        up(l, Q.W_DOWN, weights["down"][l])
+    torch.cuda.synchronize()
+    del keep
+
+
+def prefill_kv(ctx, kv_layers, stream=None):
+    """kv_layers: list over layers of (K, V) device tensors [n, Hkv, D] in the KV dtype,
+    written at positions 0..n-1."""
+    for l, (k, v) in enumerate(kv_layers):
+        Q.qdec_kv_write(ctx, l, 0, k.shape[0], k.contiguous(), v.contiguous(), stream)

@@ -1,0 +1,154 @@
+"""The C-ABI library on a host without a GPU: it loads, exports every declared symbol, and its
+host-only logic (capability gate, sizes, byte model, argument validation) behaves as documented.
+No test here launches a kernel."""
+import json
+import os
+import re
+
+import pytest
+
+from decode_step_04_amd import loader, synth
+from decode_step_04_amd import qdec as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MIB = 2**20
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "qdec.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qdec_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = Q.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 30
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(Q.exported_names()) == declared
+
+
+def test_only_the_abi_is_exported():
+    out = os.popen(f"nm -D --defined-only {Q._LIB_PATH}").read().split("\n")
+    text_syms = [ln.split()[-1] for ln in out if " T " in ln]
+    assert text_syms and all(s.startswith("qdec_") for s in text_syms), text_syms
+
+
+def cfg(shape=synth.QWEN3_0P6B, path="bf16", num_pages=512, max_context=8192, **over):
+    c = loader.config_for(shape, path=path, num_pages=num_pages, max_context=max_context)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("shape,path", [(synth.TINY, "fp32"), (synth.QWEN3_0P6B, "bf16"),
+                                        (synth.QWEN3_0P6B, "w8a16"), (synth.DENSE_8B, "bf16"),
+                                        (synth.DENSE_8B, "w8a16")])
+def test_benchmark_configs_pass_the_gate(shape, path):
+    st, msg = Q.qdec_config_validate(cfg(shape, path))
+    assert st == Q.OK, msg
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), Q.E_UNSUPPORTED), (dict(head_dim=256), Q.E_UNSUPPORTED),
+    (dict(n_kv_heads=3), Q.E_INVAL), (dict(n_q_heads=32, n_kv_heads=2), Q.E_UNSUPPORTED),
+    (dict(page_size=32), Q.E_UNSUPPORTED), (dict(hidden=1000), Q.E_UNSUPPORTED),
+    (dict(ffn=0), Q.E_INVAL), (dict(n_layers=0), Q.E_INVAL), (dict(rms_eps=0.0), Q.E_INVAL),
+    (dict(rope_theta=1.0), Q.E_INVAL), (dict(max_context=8193), Q.E_INVAL),
+    (dict(partition_size=100), Q.E_INVAL), (dict(kv_dtype=Q.F32), Q.E_UNSUPPORTED),
+    (dict(proj_dtype=Q.F32), Q.E_UNSUPPORTED), (dict(act_dtype=Q.I8_ROW), Q.E_UNSUPPORTED),
+    (dict(proj_dtype=7), Q.E_INVAL), (dict(tied_lm_head=2), Q.E_INVAL),
+    (dict(qk_norm=-1), Q.E_INVAL), (dict(vocab=-5), Q.E_INVAL),
+])
+def test_gate_rejects(over, status):
+    st, msg = Q.qdec_config_validate(cfg(**over))
+    assert st == status, msg
+    assert msg and msg != "ok"
+
+
+def test_fp32_path_must_be_fp32_throughout():
+    st, _ = Q.qdec_config_validate(cfg(synth.TINY, "fp32", num_pages=8, max_context=64,
+                                       kv_dtype=Q.BF16))
+    assert st == Q.E_UNSUPPORTED
+
+
+def test_info_reproduces_the_printed_qwen3_numbers():
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "qwen3_0p6b_shape_pins.json")))
+    info = Q.qdec_config_info(cfg())
+    assert info.params_per_layer == g["params_per_layer"]["value"]
+    assert info.params_total == g["params_total"]["value"]
+    assert info.kv_bytes_per_layer_token == 4096
+    assert info.kv_pool_bytes == g["kv_mib_T8192_28_layers"]["value"] * MIB  # 512 pages x 16
+    assert info.layer_matrix_bytes == g["layer_weight_mib_per_token"]["value"] * MIB
+    assert info.lm_head_bytes == g["lm_head_mib_per_token"]["value"] * MIB
+    w8 = Q.qdec_config_info(cfg(path="w8a16"))
+    assert w8.layer_matrix_bytes * 2 == info.layer_matrix_bytes
+    assert w8.layer_scale_bytes == 28 * (4096 + 1024 + 6144 + 1024) * 4
+    assert w8.lm_head_bytes == 151936 * 1024 + 151936 * 4
+
+
+def test_bytes_model_components():
+    c = cfg(max_context=8192)
+    b = Q.qdec_bytes_model(c, 4096, 1)
+    assert b.attention == 28 * 4096 * 4096                      # T keys and values, 28 layers
+    assert b.rope_append == 28 * (2 * 128 * 4 + 4096)            # q/k gammas + one K/V row
+    layer = b.qkv + b.o_proj + b.gate_up + b.down
+    assert layer == 840 * MIB + 28 * 2 * 1024 * 4                # matrices + in/post gammas
+    assert b.lm_head == 151936 * 1024 * 2 + 1024 * 4 + 151936 * 2
+    assert b.total == (b.embed + b.qkv + b.rope_append + b.attention + b.o_proj + b.gate_up
+                       + b.down + b.lm_head)
+    nolog = Q.qdec_bytes_model(c, 4096, 0)
+    assert nolog.lm_head == 0 and nolog.total == b.total - b.lm_head
+    with pytest.raises(Q.QdecError):
+        Q.qdec_bytes_model(c, 0, 1)
+    with pytest.raises(Q.QdecError):
+        Q.qdec_bytes_model(c, 8193, 1)
+
+
+def test_op_entry_points_validate_before_touching_the_gpu():
+    with pytest.raises(Q.QdecError) as e:
+        Q.qdec_op_gemv(None, Q.BF16, None, 16, Q.BF16, 16, Q.F32, 4, 64)
+    assert e.value.status == Q.E_INVAL
+    with pytest.raises(Q.QdecError) as e:      # scale given for a bf16 matrix
+        Q.qdec_op_gemv(256, Q.BF16, 256, 256, Q.BF16, 256, Q.F32, 4, 64)
+    assert e.value.status == Q.E_INVAL
+    with pytest.raises(Q.QdecError) as e:      # row of 60 bf16 = 120 bytes, not a 16B multiple
+        Q.qdec_op_gemv(256, Q.BF16, None, 256, Q.BF16, 256, Q.F32, 4, 60)
+    assert e.value.status == Q.E_INVAL
+    with pytest.raises(Q.QdecError) as e:
+        Q.qdec_op_quantize_rows(256, Q.F32, 256, 256, 4, 24)
+    assert e.value.status == Q.E_INVAL
+    with pytest.raises(Q.QdecError) as e:
+        Q.qdec_op_attention(256, Q.F32, 256, 256, Q.BF16, 256, 100, 32, 8, 96, 512, None, 0, 256,
+                            Q.F32)
+    assert e.value.status == Q.E_UNSUPPORTED
+    with pytest.raises(Q.QdecError) as e:      # several partitions but no workspace
+        Q.qdec_op_attention(256, Q.F32, 256, 256, Q.BF16, 256, 4096, 32, 8, 128, 512, None, 0,
+                            256, Q.F32)
+    assert e.value.status == Q.E_INVAL
+    with pytest.raises(Q.QdecError) as e:
+        Q.qdec_op_copy(256, 256, 24)
+    assert e.value.status == Q.E_INVAL
+    assert "16" in Q.qdec_last_error()
+
+
+def test_attention_workspace_sizes():
+    assert Q.qdec_op_attention_workspace(512, 32, 128, 512) == 0           # one partition
+    ws = Q.qdec_op_attention_workspace(8192, 32, 128, 512)
+    assert ws == 32 * 16 * 128 * 4 + 32 * 16 * 8
+    assert Q.qdec_op_attention_workspace(131072, 32, 128, 512) == 32 * 256 * (128 + 2) * 4
+
+
+def test_status_strings():
+    assert Q.qdec_status_string(Q.OK) == "ok"
+    assert Q.qdec_status_string(Q.E_RANGE) == "out of range"
+
+
+def test_create_without_a_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: creation is covered by the GPU tests")
+    with pytest.raises(Q.QdecError) as e:
+        Q.qdec_create(cfg(synth.TINY, "fp32", num_pages=8, max_context=64))
+    assert e.value.status == Q.E_HIP
