@@ -1,0 +1,260 @@
+"""Benchmark of the batch-1 GQA decode step on one MI355X.
+
+Workload (default): Qwen3-0.6B shape (28 layers, hidden 1024, 16 Q / 8 KV heads, D 128, FFN 3072,
+vocab 151936 tied), bf16 weights and KV cache, random-init N(0, 0.02) weights, KV positions
+0..T-2 pre-filled with N(0, 1) values through a randomly permuted block table (pages of 16),
+one decode step at pos T-1 with T = 4096, logits + greedy argmax included.  A "step" is the
+whole hot path (embedding, 28 layers of norm/QKV/RoPE+append/split-KV attention/merge/O/norm/
+gate-up+SwiGLU/down, final norm, LM head, argmax); the timed steps are HIP-graph replays at the
+same position (each replay appends the same slot again).
+
+Prints one JSON line: tokens/s, ms per step, achieved algorithmic HBM bandwidth of the whole step,
+the roofline of the dominant kernel (event-timed live, per launch), per-kernel times, a parity
+check of the timed step against the CPU oracle, and the oracle's own rate on the host CPU.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs peak (Qwen3-0.6B shape, 4K ctx)"
+KERNEL_SOURCES = {  # kernel class -> source file whose change invalidates stored counters
+    "qkv": "gemv.hip", "o_proj": "gemv.hip", "gate_up": "gemv.hip", "down": "gemv.hip",
+    "lm_head": "gemv.hip", "attention": "attention.hip", "merge": "attention.hip",
+    "rope_append": "misc.hip", "embed": "misc.hip", "argmax": "misc.hip",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--model", choices=["0.6b", "8b"], default="0.6b")
+    p.add_argument("--path", choices=["bf16", "w8a16"], default="bf16")
+    p.add_argument("--act", choices=["f32", "bf16"], default=None,
+                   help="activation precision at op boundaries (default f32 for bf16 weights, "
+                        "bf16 for w8a16)")
+    p.add_argument("--ctx", type=int, default=None, help="context T (default 4096 / 8192 for 8b)")
+    p.add_argument("--profile-steps", type=int, default=20)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="wall-clock budget of the CPU-oracle baseline (0 disables it)")
+    p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="only run the library's copy kernel on 1 GiB (counter calibration)")
+    return p.parse_args()
+
+
+def sha_of(fname):
+    with open(os.path.join(ROOT, "decode_step_04_amd", "csrc", fname), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kclass, workload):
+    """Per-launch HBM bytes of kernel class `kclass` from the committed rocprofv3 counter summary,
+    or None when absent or taken from a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tab = json.load(f)
+    ent = tab.get(workload, {}).get(kclass)
+    if not ent or ent.get("source_sha") != sha_of(KERNEL_SOURCES[kclass]):
+        return None
+    return ent["bytes_per_launch"]
+
+
+def copy_calibration():
+    import torch
+
+    from decode_step_04_amd import qdec as Q
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        Q.qdec_op_copy(b, a, n)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        Q.qdec_op_copy(b, a, n)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 20
+    print(json.dumps({"copy_bytes_each_way": n, "copy_ms": dt * 1e3,
+                      "copy_gbps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path does not shard across GPUs)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calib:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    from decode_step_04_amd import loader, synth
+    from decode_step_04_amd import qdec as Q
+
+    shape = synth.QWEN3_0P6B if args.model == "0.6b" else synth.DENSE_8B
+    T = args.ctx or (4096 if args.model == "0.6b" else 8192)
+    dev = "cuda"
+    n_pages = (T + 15) // 16
+    cfg = loader.config_for(shape, path=args.path, num_pages=n_pages, max_context=T,
+                            act=args.act)
+    act_name = "bf16" if cfg.act_dtype == Q.BF16 else "f32"
+    ctx = Q.qdec_create(cfg, 0)
+    w = synth.bf16_model(shape, seed=0, device=dev)
+    loader.upload_weights(ctx, w, dev)
+    table = synth.block_table(n_pages, n_pages, seed=2)
+    Q.qdec_kv_set_block_table(ctx, table)
+    kv = synth.kv_prefill(shape, T - 1, seed=1, device=dev)
+    loader.prefill_kv(ctx, kv)
+    tok_id = synth.token_id(shape["vocab"], seed=3)
+    tok = torch.tensor([tok_id], dtype=torch.int32, device=dev)
+    logits = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=dev)
+    hidden = torch.empty(shape["hidden"], dtype=torch.float32, device=dev)
+    amax = torch.empty(1, dtype=torch.int32, device=dev)
+    pos = T - 1
+    step = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax)
+    torch.cuda.synchronize()
+
+    # eager warm-up, then capture the step into a graph
+    for _ in range(3):
+        Q.qdec_decode_step(ctx, step)
+    torch.cuda.synchronize()
+    Q.qdec_graph_capture(ctx, step)
+    for _ in range(args.warmup):
+        Q.qdec_graph_replay(ctx, pos)
+    torch.cuda.synchronize()
+
+    # timed region: graph replays
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        Q.qdec_graph_replay(ctx, pos)
+    torch.cuda.synchronize()
+    graph_s = (time.perf_counter() - t0) / args.steps
+
+    # eager steps for comparison
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        Q.qdec_decode_step(ctx, step)
+    torch.cuda.synchronize()
+    eager_s = (time.perf_counter() - t0) / args.steps
+
+    # per-kernel durations with HIP events on the step's stream
+    Q.qdec_profile_enable(ctx, 1)
+    for _ in range(args.profile_steps):
+        Q.qdec_decode_step(ctx, step)
+        prof = Q.qdec_profile_collect(ctx)
+    Q.qdec_profile_enable(ctx, 0)
+    bm = Q.qdec_bytes_model(cfg, T, 1)
+    per_step_ms = {k: v[0] / args.profile_steps for k, v in prof.items()}
+    launches = {k: v[1] // args.profile_steps for k, v in prof.items()}
+    kernels = {}
+    for k in Q.K_NAMES:
+        if launches[k] == 0:
+            continue
+        b = getattr(bm, k)
+        avg_us = per_step_ms[k] * 1e3 / launches[k]
+        kernels[k] = {"launches_per_step": launches[k], "avg_us": round(avg_us, 3),
+                      "ms_per_step": round(per_step_ms[k], 4),
+                      "bytes_per_launch": b // launches[k],
+                      "gbps": round(b / launches[k] / (avg_us * 1e-6) / 1e9, 1) if b else None}
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dominant]
+    workload = f"{shape['name']}-{args.path}-act{act_name}-ctx{T}"
+    traffic = load_traffic(dominant, workload)
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": dk["gbps"],
+                "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(dk["gbps"] / PEAK_HBM_GBPS, 4) if dk["gbps"] else None,
+                "bytes_per_launch": dk["bytes_per_launch"], "avg_launch_us": dk["avg_us"],
+                "traffic": traffic}
+
+    # parity of the timed step against the oracle, and the oracle's own rate
+    parity = None
+    cpu = None
+    if not args.no_parity or args.cpu_seconds > 0:
+        import oracle
+
+        Q.qdec_graph_replay(ctx, pos)
+        torch.cuda.synchronize()
+        g_hidden = hidden.cpu().numpy().astype(np.float64)
+        g_logits = synth.bf16_to_f32(logits).astype(np.float64)
+        g_arg = int(amax.item())
+        hw = synth.host_weights(w)
+        if args.path == "w8a16":
+            for key in ("qkv", "o", "gate_up", "down"):
+                qs = [oracle.quantize_rows(oracle.bf16_bits_to_f64(b).astype(np.float32))
+                      for b in hw[key]]
+                hw[key] = [q for q, _ in qs]
+                hw[key + "_scale"] = [s for _, s in qs]
+            lm_src = hw["lm_head"] if hw.get("lm_head") is not None else hw["embed"]
+            q, s = oracle.quantize_rows(oracle.bf16_bits_to_f64(lm_src).astype(np.float32))
+            hw["lm_head"], hw["lm_scale"] = q, s
+        om = oracle.Model(dict(shape, act_bf16=int(cfg.act_dtype == Q.BF16), kv_bf16=1,
+                               logits_bf16=1), hw, max_ctx=T)
+        for l, (k, v) in enumerate(kv):
+            om.k_cache[l][: T - 1] = k.float().cpu().numpy()
+            om.v_cache[l][: T - 1] = v.float().cpu().numpy()
+        del kv
+        t0 = time.perf_counter()
+        oh, ol, oa = om.step(pos, token=tok_id)
+        first = time.perf_counter() - t0
+        rel = float(np.linalg.norm(g_hidden - oh) / np.linalg.norm(oh))
+        parity = {"hidden_rel_l2": rel, "logits_max_abs": float(np.max(np.abs(g_logits - ol))),
+                  "argmax_gpu": g_arg, "argmax_oracle": oa,
+                  "argmax_valid": bool(ol[g_arg] >= ol.max() - 2 * 2.0**-8 * abs(ol.max())),
+                  "ok": rel <= 1.5e-2 and float(np.max(np.abs(g_logits - ol))) <= 5e-2}
+        if args.cpu_seconds > 0:
+            n, spent = 1, first
+            while spent < args.cpu_seconds and n < 50:
+                t0 = time.perf_counter()
+                om.step(pos, token=tok_id)
+                spent += time.perf_counter() - t0
+                n += 1
+            threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+            cpu = {"value": round(n / spent, 4), "unit": "tokens/s", "cores": threads,
+                   "kind": "oracle",
+                   "sample": f"{n} full decode steps of the same workload (same weights, KV and "
+                             f"position) on {threads} OpenMP threads, {spent:.1f} s"}
+
+    Q.qdec_destroy(ctx)
+    tok_s = 1.0 / graph_s
+    out = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_s * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{shape['name']} batch-1 decode step, ctx {T}, {args.path} "
+                               "weights, bf16 KV, graph replay",
+                   "context": T, "batch": 1, "weights": args.path, "kv_cache": "bf16",
+                   "activations": act_name,
+                   "page_size": 16, "block_table": "random permutation",
+                   "parallelism": "single GPU"},
+        "hbm_gbps": round(bm.total / graph_s / 1e9, 1),
+        "hbm_frac": round(bm.total / graph_s / 1e9 / PEAK_HBM_GBPS, 4),
+        "bytes_per_step": bm.total,
+        "eager_ms_per_step": round(eager_s * 1e3, 5),
+        "roofline": roofline,
+        "kernels": kernels,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

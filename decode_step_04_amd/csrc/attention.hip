@@ -7,18 +7,30 @@
 // g = h / (Hq / Hkv), scores s_j = q_h . k_j / sqrt(D) over positions j < ctx, and
 // out_h = sum_j softmax(s)_j v_j.
 //
-// How ([Qwen3-runtime] §9.1, §10.1-10.2; [ETE] the (m, l, acc) passage):
-//   k_attn_part: one work-group per (kv head g, partition).  A partition is a contiguous range of
-//   whole 16-token pages.  The G = Hq / Hkv query heads of g are all handled by the same lanes, so
-//   every K/V element is loaded from HBM once and used for all G heads (the GQA reuse of §2.5).
-//   Each wave takes every 4th page of the partition; a page tile of one head (16 x D, contiguous
-//   in the pool) is read with one 16-byte load per lane per 1 KiB, so lane l holds EPL
-//   consecutive dims of one token per load: token row = l / LPT, dims (l % LPT) * EPL.  Scores
-//   are reduced over the LPT lanes of a token with DPP, and every token row keeps its own fp32
-//   online state (m, l, acc[dims]) per head.  Rows, then waves (through LDS), are combined with
-//   the exact rescaling of §9.1.  With one partition the normalised output is written directly
-//   (the short path of §10.1); otherwise the unnormalised state goes to scratch.
-//   k_attn_merge: per query head, M = max m_p, out = sum acc_p 2^(m_p - M) / sum l_p 2^(m_p - M).
+// k_attn: one work-group (4 waves) per (kv head g, partition), a partition being part_tokens
+// consecutive positions (whole 16-token pages).
+//   - Loads are ordered for the shortest dependent chain: ctx, the partition's block-table
+//     entries (read ahead of ctx; every entry below bt_len is a valid page number) and the QKV
+//     rows are requested together, then each wave requests its first K/V page tile before doing
+//     anything else, so HBM latency overlaps the prologue.
+//   - Fused prologue (model path, [Qwen3-runtime] §2.3-2.4, §7.1-7.2): the work-group RMS-
+//     normalises and rotates the G = Hq/Hkv query heads of g (one wave per head: lane l holds
+//     the RoPE pair (l, l + D/2), so the norm is one wave reduction and the rotation needs no
+//     data exchange).  The work-group whose partition holds the new position also normalises and
+//     rotates K of head g, stores K and V at (bt[pos/16], pos%16) -- the paged append -- and uses
+//     the same values in registers for that slot.
+//   - Page loop ([Qwen3-runtime] §10.1-10.2): each wave takes every 4th page; a 16 x D page tile
+//     of one head is contiguous and read with one 16-byte load per lane per 1 KiB, so lane l
+//     holds EPL consecutive dims of one token per load (token row l / LPT).  Scores are reduced
+//     over the LPT lanes of a token with DPP; each token row keeps fp32 (m, l, acc) per head
+//     ([ETE], the online-softmax passage) and all G heads use the same K/V registers, so each
+//     K/V byte is read once for the whole query group ([Qwen3-runtime] §2.5).
+//   - Rows, then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With one partition
+//     the normalised output is written directly (the short path of §10.1); otherwise the
+//     unnormalised state goes to scratch for k_attn_merge.
+// k_attn_merge: one work-group per query head.  The (m, l) pairs of all partitions and the
+// accumulators are requested together; M = max m_p, w_p = 2^(m_p - M), out = sum w_p acc_p /
+// sum w_p l_p, reductions through LDS.
 //
 // Scores are kept in log2 units: q is pre-multiplied by log2(e)/sqrt(D), so exp(s - m) becomes
 // exp2(s' - m') (one v_exp_f32).  The initial running max is -1e30 as in [ETE]; masked tokens
@@ -38,7 +50,6 @@ struct Geo {
   static_assert(LPT >= 8 && LPT <= 32, "lane layout");
 };
 
-// Sum over aligned groups of N lanes, N in {8, 16, 32}.
 template <int N>
 __device__ __forceinline__ float lanes_sum(float v) {
   if constexpr (N <= 16) {
@@ -62,42 +73,161 @@ __device__ __forceinline__ void widen16(const uint4 w, float (&f)[EPL]) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, bool KVB, int G>
-__global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
+// Per-head RMSNorm (gamma may be null) and rotate-half RoPE of one D-vector by one wave; lane l
+// holds the pair (x0, x1) = (v[l], v[l + D/2]) (zeros for l >= D/2) and gets the rotated pair.
+template <int D>
+__device__ __forceinline__ void norm_rope(float x0, float x1, const float* gamma, float eps,
+                                          float2 cs, int lane, float& y0, float& y1) {
+  constexpr int HALF = D / 2;
+  if (gamma != nullptr) {
+    const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+    const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
+    if (lane < HALF) {
+      x0 = x0 * rinv * gamma[lane];
+      x1 = x1 * rinv * gamma[lane + HALF];
+    }
+  }
+  y0 = x0 * cs.x - x1 * cs.y;
+  y1 = x1 * cs.x + x0 * cs.y;
+}
+
+template <int D, bool KVB, int G, bool FUSED>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   using Gm = Geo<D, KVB>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPI = Gm::TPI, NI = Gm::NI, ELEM = Gm::ELEM;
+  constexpr int HALF = D / 2;
+  constexpr int NPH = 4;            // block-table entries per wave read ahead of ctx
+  __shared__ float sq[G][D];        // scaled query heads
+  __shared__ float skv[2][D];       // K and V of the new token (as stored)
   __shared__ float sm_acc[4][G][D];
   __shared__ float sm_m[4][G];
   __shared__ float sm_l[4][G];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
-  const int part = part_tokens_for(ctx, a.part_fixed, a.n_kv_heads, a.target_wgs);
-  const int np = n_parts_for(ctx, part);
   const int hkv = a.n_kv_heads;
   const int g = blockIdx.x % hkv;
   const int pi = blockIdx.x / hkv;
+  const int part = a.part_tokens;
+  const int ppp = part / kPage;                  // pages per partition
+  const int pg_first = pi * ppp;
+
+  // ---- independent loads: block-table entries, ctx, the QKV rows of the prologue ----
+  int phys[NPH];
+  const int npw = (ppp + 3 - wave) / 4;          // pages of this wave in a full partition
+#pragma unroll
+  for (int j = 0; j < NPH; ++j) {
+    const int idx = pg_first + wave + 4 * j;
+    phys[j] = (j < npw && idx < a.bt_len) ? a.block_table[idx] : 0;
+  }
+  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
+  float qx0[2] = {0.f, 0.f}, qx1[2] = {0.f, 0.f};  // this wave's query heads (h = wave, wave+4)
+  float kx0 = 0.f, kx1 = 0.f, vx0 = 0.f, vx1 = 0.f;
+  if constexpr (FUSED) {
+    if (lane < HALF) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int h = wave + 4 * t;
+        if (h < G) {
+          const float* src = a.qkv + (int64_t)(g * G + h) * D;
+          qx0[t] = src[lane];
+          qx1[t] = src[lane + HALF];
+        }
+      }
+      if (wave == 3) {
+        const float* ks = a.qkv + (int64_t)(a.n_q_heads + g) * D;
+        const float* vs = a.qkv + (int64_t)(a.n_q_heads + hkv + g) * D;
+        kx0 = ks[lane];
+        kx1 = ks[lane + HALF];
+        vx0 = vs[lane];
+        vx1 = vs[lane + HALF];
+      }
+    }
+  }
+  const int pos = ctx - 1;
+  const int np = n_parts_for(ctx, part);
   if (pi >= np) return;
   const int tok0 = pi * part;
   const int tok1 = min(ctx, tok0 + part);
-  const int pg0 = tok0 / kPage, pg1 = (tok1 + kPage - 1) / kPage;
+  const int pg1 = (tok1 + kPage - 1) / kPage;    // one past the last page of the partition
+  const bool has_new = FUSED && (pos >= tok0) && (pos < tok1);
+
+  // ---- first page tile of this wave, requested before the prologue ----
+  const int64_t tile_bytes = (int64_t)kPage * D * ELEM;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  uint4 kw[NI], vw[NI];
+  int pg = pg_first + wave;
+  if (pg < pg1) {
+    const int64_t tile = ((int64_t)phys[0] * hkv + g) * tile_bytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
+  }
+
+  // ---- prologue: query heads (and the new K/V) into LDS ----
+  if constexpr (FUSED) {
+    const float2 cs = (lane < HALF)
+                          ? reinterpret_cast<const float2*>(a.rope_table)[(int64_t)pos * HALF + lane]
+                          : make_float2(1.f, 0.f);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int h = wave + 4 * t;
+      if (h < G) {
+        float y0, y1;
+        norm_rope<D>(qx0[t], qx1[t], a.q_gamma, a.eps, cs, lane, y0, y1);
+        if (lane < HALF) {
+          if (a.round_q) {
+            y0 = round_bf16(y0);
+            y1 = round_bf16(y1);
+          }
+          sq[h][lane] = y0 * a.qscale;
+          sq[h][lane + HALF] = y1 * a.qscale;
+        }
+      }
+    }
+    if (has_new && wave == 3) {
+      float y0, y1;
+      norm_rope<D>(kx0, kx1, a.k_gamma, a.eps, cs, lane, y0, y1);
+      if (lane < HALF) {
+        float v0 = vx0, v1 = vx1;
+        const int64_t phys_new = a.block_table[pos / kPage];
+        const int64_t off = ((phys_new * hkv + g) * kPage + pos % kPage) * D + lane;
+        if constexpr (KVB) {
+          y0 = round_bf16(y0); y1 = round_bf16(y1); v0 = round_bf16(v0); v1 = round_bf16(v1);
+          uint16_t* kp = static_cast<uint16_t*>(a.k_pool);
+          uint16_t* vp = static_cast<uint16_t*>(a.v_pool);
+          kp[off] = f32_to_bf16(y0); kp[off + HALF] = f32_to_bf16(y1);
+          vp[off] = f32_to_bf16(v0); vp[off + HALF] = f32_to_bf16(v1);
+        } else {
+          float* kp = static_cast<float*>(a.k_pool);
+          float* vp = static_cast<float*>(a.v_pool);
+          kp[off] = y0; kp[off + HALF] = y1;
+          vp[off] = v0; vp[off + HALF] = v1;
+        }
+        skv[0][lane] = y0; skv[0][lane + HALF] = y1;
+        skv[1][lane] = v0; skv[1][lane + HALF] = v1;
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+      const int idx = g * G * D + i;
+      const float v = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[idx])
+                               : static_cast<const float*>(a.q)[idx];
+      sq[i / D][i % D] = v * a.qscale;
+    }
+  }
+  __syncthreads();
 
   const int dsub = (lane % LPT) * EPL;
   const int trow = lane / LPT;
-
-  // query slices of the G grouped heads, pre-scaled to log2 units
   float q[G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int hq = g * G + h;
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int idx = hq * D + dsub + e;
-      const float v = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[idx])
-                               : static_cast<const float*>(a.q)[idx];
-      q[h][e] = v * a.qscale;
-    }
-  }
+    for (int e = 0; e < EPL; ++e) q[h][e] = sq[h][dsub + e];
   float m[G], l[G], acc[G][EPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -107,38 +237,42 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  const int64_t tile_bytes = (int64_t)kPage * D * ELEM;
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-
-  for (int pg = pg0 + wave; pg < pg1; pg += 4) {
-    const int64_t phys = a.block_table[pg];
-    const int64_t tile = (phys * hkv + g) * tile_bytes;
-    uint4 kw[NI], vw[NI];
+  for (int j = 0; pg < pg1; pg += 4, ++j) {
+    if (j > 0) {
+      // select chain instead of phys[j]: a runtime index would put the array in scratch memory
+      const int64_t ph = j == 1 ? phys[1] : j == 2 ? phys[2] : j == 3 ? phys[3]
+                                                                      : a.block_table[pg];
+      const int64_t tile = (ph * hkv + g) * tile_bytes;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
+      for (int i = 0; i < NI; ++i)
+        kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
-
-    // scores of this lane's token row for every load slot i and head h
+      for (int i = 0; i < NI; ++i)
+        vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
+    }
     float s[G][NI];
+    float kf[NI][EPL], vf[NI][EPL];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      float kf[EPL];
-      widen16<KVB, EPL>(kw[i], kf);
+      widen16<KVB, EPL>(kw[i], kf[i]);
+      widen16<KVB, EPL>(vw[i], vf[i]);
       const int tok = pg * kPage + i * TPI + trow;
+      if (has_new && tok == pos) {  // the appended slot: use the values just computed
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          kf[i][e] = skv[0][dsub + e];
+          vf[i][e] = skv[1][dsub + e];
+        }
+      }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float p = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
+        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[i][e], p);
         p = lanes_sum<LPT>(p);
         s[h][i] = (tok < tok1) ? p : -INFINITY;
       }
     }
-    // online update ([ETE]: new max, rescale the old state, add the new terms)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float mx = m[h];
@@ -152,10 +286,8 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
       for (int i = 0; i < NI; ++i) {
         const float p = fast_exp2(s[h][i] - mx);
         l[h] += p;
-        float vf[EPL];
-        widen16<KVB, EPL>(vw[i], vf);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
       }
       m[h] = mx;
     }
@@ -223,60 +355,100 @@ __global__ __launch_bounds__(256) void k_attn_part(AttnArgs a) {
   }
 }
 
-// One work-group of D threads per query head.
+// One work-group of 256 threads per query head.  Dynamic LDS: 2 * max_parts floats.
 template <int D>
-__global__ __launch_bounds__(128) void k_attn_merge(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  extern __shared__ float sml[];  // [max_parts] weights 2^(m_p - M), then [max_parts] l_p
+  __shared__ float red[4];
+  __shared__ float part_o[256 / D][D];
   const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
-  const int part = part_tokens_for(ctx, a.part_fixed, a.n_kv_heads, a.target_wgs);
-  const int np = n_parts_for(ctx, part);
-  if (np <= 1) return;  // the partition kernel already wrote the output
-  const int hq = blockIdx.x, r = threadIdx.x;
+  const int np = n_parts_for(ctx, a.part_tokens);
+  if (np <= 1) return;  // the partition kernel wrote the output itself
+  const int hq = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NG = 256 / D;            // partition groups for the accumulator pass
+  const int r = tid % D, grp = tid / D;
   const int64_t base = (int64_t)hq * a.max_parts;
-  float M = -1e30f;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, a.part_ml[(base + p) * 2]);
-  float L = 0.f, O = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float c = fast_exp2(a.part_ml[(base + p) * 2] - M);
-    L = fmaf(a.part_ml[(base + p) * 2 + 1], c, L);
-    O = fmaf(a.part_acc[(base + p) * D + r], c, O);
+  float* wts = sml;
+  float* ls = sml + a.max_parts;
+
+  // (m, l) of every partition, and this thread's first accumulators, requested together
+  float mloc = -1e30f;
+  for (int p = tid; p < np; p += 256) {
+    const float mp = a.part_ml[(base + p) * 2];
+    wts[p] = mp;
+    ls[p] = a.part_ml[(base + p) * 2 + 1];
+    mloc = fmaxf(mloc, mp);
   }
-  const float o = O / L;
-  if (a.out_bf16)
-    static_cast<uint16_t*>(a.out)[hq * D + r] = f32_to_bf16(o);
-  else
-    static_cast<float*>(a.out)[hq * D + r] = o;
+  mloc = wave_max(mloc);
+  if (lane == 0) red[wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float lsum = 0.f;
+  for (int p = tid; p < np; p += 256) {
+    const float w = fast_exp2(wts[p] - M);
+    wts[p] = w;
+    lsum = fmaf(ls[p], w, lsum);
+  }
+  lsum = wave_sum(lsum);
+  __syncthreads();  // red is reused; wts complete
+  if (lane == 0) red[wave] = lsum;
+  __syncthreads();
+  const float L = (red[0] + red[1]) + (red[2] + red[3]);
+  float O = 0.f;
+#pragma unroll 8
+  for (int p = grp; p < np; p += NG) O = fmaf(a.part_acc[(base + p) * D + r], wts[p], O);
+  part_o[grp][r] = O;
+  __syncthreads();
+  if (grp == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int q2 = 0; q2 < NG; ++q2) t += part_o[q2][r];
+    const float o = t / L;
+    if (a.out_bf16)
+      static_cast<uint16_t*>(a.out)[hq * D + r] = f32_to_bf16(o);
+    else
+      static_cast<float*>(a.out)[hq * D + r] = o;
+  }
 }
 
-template <int D, bool KVB>
-static hipError_t launch_dk(int group, const AttnArgs& a, int grid_parts, hipStream_t s) {
+template <int D, bool KVB, bool FUSED>
+static hipError_t launch_dkf(int group, const AttnArgs& a, int grid_parts, hipStream_t s) {
   const dim3 grid((unsigned)(a.n_kv_heads * grid_parts)), block(256);
   switch (group) {
-    case 1: hipLaunchKernelGGL((k_attn_part<D, KVB, 1>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_attn_part<D, KVB, 2>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_attn_part<D, KVB, 3>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_attn_part<D, KVB, 4>), grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL((k_attn_part<D, KVB, 5>), grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL((k_attn_part<D, KVB, 6>), grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL((k_attn_part<D, KVB, 7>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_attn_part<D, KVB, 8>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_attn<D, KVB, 1, FUSED>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_attn<D, KVB, 2, FUSED>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_attn<D, KVB, 3, FUSED>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_attn<D, KVB, 4, FUSED>), grid, block, 0, s, a); break;
+    case 5: hipLaunchKernelGGL((k_attn<D, KVB, 5, FUSED>), grid, block, 0, s, a); break;
+    case 6: hipLaunchKernelGGL((k_attn<D, KVB, 6, FUSED>), grid, block, 0, s, a); break;
+    case 7: hipLaunchKernelGGL((k_attn<D, KVB, 7, FUSED>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_attn<D, KVB, 8, FUSED>), grid, block, 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attention(int head_dim, bool kv_bf16, int group, const AttnArgs& a,
+hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, const AttnArgs& a,
                             int grid_parts, hipStream_t s) {
-  if (head_dim == 64) return kv_bf16 ? launch_dk<64, true>(group, a, grid_parts, s)
-                                     : launch_dk<64, false>(group, a, grid_parts, s);
-  return kv_bf16 ? launch_dk<128, true>(group, a, grid_parts, s)
-                 : launch_dk<128, false>(group, a, grid_parts, s);
+  if (head_dim == 64) {
+    if (kv_bf16) return fused ? launch_dkf<64, true, true>(group, a, grid_parts, s)
+                              : launch_dkf<64, true, false>(group, a, grid_parts, s);
+    return fused ? launch_dkf<64, false, true>(group, a, grid_parts, s)
+                 : launch_dkf<64, false, false>(group, a, grid_parts, s);
+  }
+  if (kv_bf16) return fused ? launch_dkf<128, true, true>(group, a, grid_parts, s)
+                            : launch_dkf<128, true, false>(group, a, grid_parts, s);
+  return fused ? launch_dkf<128, false, true>(group, a, grid_parts, s)
+               : launch_dkf<128, false, false>(group, a, grid_parts, s);
 }
 
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_q_heads);
+  const dim3 grid((unsigned)a.n_q_heads), block(256);
+  const size_t lds = (size_t)a.max_parts * 2 * sizeof(float);
   if (head_dim == 64)
-    hipLaunchKernelGGL((k_attn_merge<64>), grid, dim3(64), 0, s, a);
+    hipLaunchKernelGGL((k_attn_merge<64>), grid, block, lds, s, a);
   else
-    hipLaunchKernelGGL((k_attn_merge<128>), grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL((k_attn_merge<128>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 

@@ -108,36 +108,47 @@ struct StepDesc {
 };
 
 struct GemvArgs {
-  const void* w;          // [rows x k] (rows = n, or 2n for SwiGLU)
-  const float* scale;     // [rows] for int8 codes
-  const void* x;          // input vector [k] (when gamma == nullptr)
+  const void* w;          // [rows x k] (rows = n, or 2n for SwiGLU: gate rows then up rows)
+  const float* scale;     // [rows] fp32 row scales of int8 codes
+  const void* x;          // input vector [k]; the raw fp32 residual when gamma != nullptr
   int32_t x_bf16;         // x element type
-  int32_t round_h;        // round the normalised input to bf16
-  const float* xn;        // fp32 input to normalise (when gamma != nullptr)
-  const float* gamma;     // RMSNorm gamma [k] or nullptr
+  int32_t round_h;        // round the normalised input to bf16 (16-bit activations)
+  const float* gamma;     // RMSNorm gamma [k], or nullptr for no norm prologue
   float eps;
   int32_t y_bf16;         // output element type for EPI_STORE / EPI_SWIGLU
   void* y;                // output [n]
   float* resid;           // EPI_RESID: resid[n] += W x
-  float* hidden_copy;     // optional: work-group 0 copies xn here (the step's hidden output)
+  float* hidden_copy;     // optional: work-group 0 copies the raw input x here
+  float* part_val;        // optional (EPI_STORE): per-work-group largest rounded output ...
+  int32_t* part_idx;      // ... and its lowest row index (-1 when none)
   int64_t n;              // output rows
   int64_t k;              // input length
+  int32_t split;          // waves sharing one row group along K (set by the launcher)
 };
 
 struct AttnArgs {
+  // fused (model) path: the query heads and the new K/V come from the QKV projection output
+  const float* qkv;           // [(Hq + 2 Hkv) D] fp32
+  const float* q_gamma;       // [D] or nullptr (no Q/K norm)
+  const float* k_gamma;
+  float eps;
+  const float* rope_table;    // [max_pos][D/2][2] (cos, sin)
+  int32_t round_q;            // round the rotated query to bf16 (16-bit activations)
+  // op path: the rotated query heads are given
   const void* q;              // [Hq x D] (bf16 or fp32)
   int32_t q_bf16;
-  const void* k_pool;         // [P][Hkv][16][D] (bf16 or fp32)
-  const void* v_pool;
+  void* k_pool;               // [P][Hkv][16][D] (bf16 or fp32); appended to on the fused path
+  void* v_pool;
   const int32_t* block_table;
+  int32_t bt_len;             // entries that may be read ahead of ctx (all valid page numbers)
   const StepDesc* desc;       // ctx from here when non-null
   int32_t ctx_arg;            // ctx when desc == nullptr
   int32_t n_q_heads, n_kv_heads;
-  int32_t part_fixed, target_wgs;
+  int32_t part_tokens;        // partition length, a multiple of 64
   int32_t max_parts;          // scratch stride (partitions per head)
   float* part_acc;            // [Hq][max_parts][D] unnormalised accumulators
   float* part_ml;             // [Hq][max_parts][2]: running max (log2 units) and denominator
-  void* out;                  // [Hq x D] (when a single partition covers the context)
+  void* out;                  // [Hq x D]
   int32_t out_bf16;
   float qscale;               // log2(e) / sqrt(D)
 };

@@ -13,15 +13,20 @@ namespace qd {
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 
-// Grid cap of the GEMV: enough resident waves per CU to keep many dwordx4 loads in flight.
-constexpr int kGemvMaxWgs = 2048;
-
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s);
+// Number of work-groups (= partial argmax slots) launch_gemv uses for this shape.
+int gemv_partials(int wtype, int epi, int64_t n, int64_t k);
+// Final reduction of per-work-group (value, index) partials to the argmax.
+hipError_t launch_argmax_partials(const float* val, const int32_t* idx, int n, int32_t* out,
+                                  hipStream_t s);
 
-// Split-KV partition kernel over `grid_parts` partitions per KV head (surplus ones exit early).
-hipError_t launch_attention(int head_dim, bool kv_bf16, int group, const AttnArgs& a,
+// Split-KV attention over `grid_parts` partitions per KV head (surplus ones exit early); `fused`
+// adds the Q/K norm + RoPE + K/V append prologue.
+hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, const AttnArgs& a,
                             int grid_parts, hipStream_t s);
+// Exact merge of the partitions (a no-op when the context fits one partition).
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s);
+constexpr int kMaxMergeParts = 8192;  // LDS of the merge: 2 floats per partition
 
 hipError_t launch_rope_append(int head_dim, const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);

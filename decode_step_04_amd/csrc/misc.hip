@@ -167,6 +167,50 @@ hipError_t launch_argmax(const void* x, int x_bf16, int64_t n, int32_t* out, hip
   return hipGetLastError();
 }
 
+// Final step of the LM head's fused argmax: the best of n per-work-group (value, index) partials.
+__global__ __launch_bounds__(1024) void k_argmax_partials(const float* val, const int32_t* idx,
+                                                          int n, int32_t* out) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  float best = -INFINITY;
+  int bi = -1;
+  for (int i = threadIdx.x; i < n; i += 1024)
+    if (better(val[i], idx[i], best, bi)) {
+      best = val[i];
+      bi = idx[i];
+    }
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (better(ov, oi, best, bi)) {
+      best = ov;
+      bi = oi;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float bv = sv[0];
+    int b = si[0];
+    for (int w = 1; w < 16; ++w)
+      if (better(sv[w], si[w], bv, b)) {
+        bv = sv[w];
+        b = si[w];
+      }
+    *out = b;
+  }
+}
+
+hipError_t launch_argmax_partials(const float* val, const int32_t* idx, int n, int32_t* out,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_argmax_partials, dim3(1), dim3(1024), 0, s, val, idx, n, out);
+  return hipGetLastError();
+}
+
 // ---- per-row symmetric int8 quantisation (upload time) -----------------------------------------
 // [ETE], the int8 passage: symmetric, one scale per row.  scale = max|row| / 127 in fp32, code =
 // round-half-even(w / scale) clamped to [-127, 127] (IEEE fp32 division, v_rndne_f32); a zero

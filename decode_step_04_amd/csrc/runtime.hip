@@ -68,12 +68,19 @@ struct Layer {
   void* v_pool = nullptr;
 };
 
-int64_t max_parts_for(const qdec_config& c, int part_fixed) {
-  if (part_fixed > 0) return (c.max_context + part_fixed - 1) / part_fixed;
-  int64_t mx = 1;
-  for (int t = 1; t <= c.max_context; ++t)
-    mx = std::max<int64_t>(mx, n_parts_for(t, part_tokens_for(t, 0, c.n_kv_heads, kTargetWgs)));
-  return mx;
+// Split-KV partition length of a context: the configured one, or the length that gives about
+// kTargetWgs (kv head, partition) work-groups at max_context (a multiple of 64, at least 64).
+int model_part_tokens(const qdec_config& c) {
+  return c.partition_size > 0 ? c.partition_size
+                              : part_tokens_for(c.max_context, 0, c.n_kv_heads, kTargetWgs);
+}
+int64_t model_max_parts(const qdec_config& c) {
+  const int p = model_part_tokens(c);
+  return (c.max_context + p - 1) / p;
+}
+// Device block-table entries: enough for every page a partition may look up ahead of ctx.
+int64_t block_table_entries(const qdec_config& c) {
+  return std::max<int64_t>(c.num_pages, model_max_parts(c) * (model_part_tokens(c) / kPage));
 }
 
 }  // namespace
@@ -81,8 +88,9 @@ int64_t max_parts_for(const qdec_config& c, int part_fixed) {
 struct qdec_ctx {
   qdec_config cfg{};
   int device = 0;
-  int part_fixed = 0;
+  int part_tokens = 64;
   int max_parts = 1;
+  int32_t bt_entries = 0;
   std::vector<void*> allocs;
   int64_t device_bytes = 0;
   Mat embed, lm;
@@ -94,12 +102,14 @@ struct qdec_ctx {
   float* rope = nullptr;
   float* x = nullptr;
   float* qkv = nullptr;
-  void* q = nullptr;
   void* attn = nullptr;
   void* act = nullptr;
   void* logits = nullptr;
   float* part_acc = nullptr;
   float* part_ml = nullptr;
+  float* am_val = nullptr;    // per-work-group partial argmax of the LM head
+  int32_t* am_idx = nullptr;
+  int am_parts = 0;
   StepDesc* desc = nullptr;
   std::vector<uint8_t> uploaded;  // (n_layers + 1) x kNumSlots; row n_layers = global slots
   std::string err;
@@ -138,6 +148,7 @@ struct qdec_ctx {
   }
   uint8_t& slot(int layer, int which) { return uploaded[(size_t)layer * kNumSlots + which]; }
   bool act_bf16() const { return cfg.act_dtype == QDEC_BF16; }
+  bool io_bf16() const { return cfg.io_dtype == QDEC_BF16; }
   bool kv_bf16() const { return cfg.kv_dtype == QDEC_BF16; }
 };
 
@@ -174,18 +185,20 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
     return fail(why, QDEC_E_INVAL, "rope_theta must be finite and above 1");
   auto dt_ok = [](int d) { return d == QDEC_F32 || d == QDEC_BF16 || d == QDEC_I8_ROW; };
-  if (!dt_ok(c->proj_dtype) || !dt_ok(c->lm_head_dtype) || !dt_ok(c->act_dtype) ||
-      !dt_ok(c->kv_dtype))
+  if (!dt_ok(c->proj_dtype) || !dt_ok(c->lm_head_dtype) || !dt_ok(c->io_dtype) ||
+      !dt_ok(c->act_dtype) || !dt_ok(c->kv_dtype))
     return fail(why, QDEC_E_INVAL, "unknown dtype value");
-  if (c->act_dtype == QDEC_F32) {
-    if (c->proj_dtype != QDEC_F32 || c->lm_head_dtype != QDEC_F32 || c->kv_dtype != QDEC_F32)
-      return fail(why, QDEC_E_UNSUPPORTED, "the fp32 path needs fp32 projections, LM head and KV");
-  } else if (c->act_dtype == QDEC_BF16) {
+  if (c->act_dtype == QDEC_I8_ROW || c->io_dtype == QDEC_I8_ROW || c->kv_dtype == QDEC_I8_ROW)
+    return fail(why, QDEC_E_UNSUPPORTED, "io, act and kv dtypes must be F32 or BF16");
+  if (c->io_dtype == QDEC_F32) {
+    if (c->proj_dtype != QDEC_F32 || c->lm_head_dtype != QDEC_F32 || c->kv_dtype != QDEC_F32 ||
+        c->act_dtype != QDEC_F32)
+      return fail(why, QDEC_E_UNSUPPORTED,
+                  "the fp32 path needs fp32 projections, LM head, activations and KV");
+  } else {
     if (c->proj_dtype == QDEC_F32 || c->lm_head_dtype == QDEC_F32 || c->kv_dtype != QDEC_BF16)
       return fail(why, QDEC_E_UNSUPPORTED,
                   "the bf16 path needs bf16 or int8-row projections / LM head and a bf16 KV cache");
-  } else {
-    return fail(why, QDEC_E_UNSUPPORTED, "act_dtype must be F32 or BF16");
   }
   if (c->page_size != kPage)
     return fail(why, QDEC_E_UNSUPPORTED, "page_size %d: only 16 is implemented", c->page_size);
@@ -196,6 +209,9 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if (c->max_context > (1 << 24)) return fail(why, QDEC_E_UNSUPPORTED, "max_context above 2^24");
   if (c->partition_size < 0 || c->partition_size % 64)
     return fail(why, QDEC_E_INVAL, "partition_size must be 0 or a positive multiple of 64");
+  if (model_max_parts(*c) > kMaxMergeParts)
+    return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
+                kMaxMergeParts);
   return QDEC_OK;
 }
 
@@ -213,16 +229,15 @@ static void fill_info(const qdec_config& c, qdec_info* o) {
   o->lm_head_bytes = v * d * elem_size(c.lm_head_dtype) + (c.lm_head_dtype == QDEC_I8_ROW ? v * 4 : 0);
   o->kv_bytes_per_layer_token = 2 * hkv * hd * elem_size(c.kv_dtype);
   o->kv_pool_bytes = L * 2 * (int64_t)c.num_pages * kPage * hkv * hd * elem_size(c.kv_dtype);
-  const int pf = c.partition_size;
-  const int64_t mp = max_parts_for(c, pf);
-  o->partition_tokens = pf > 0 ? pf : part_tokens_for(c.max_context, 0, (int)hkv, kTargetWgs);
+  const int64_t mp = model_max_parts(c);
+  o->partition_tokens = model_part_tokens(c);
   o->max_partitions = (int32_t)mp;
-  const int ae = elem_size(c.act_dtype);
-  const bool lm_alias = c.tied_lm_head && c.lm_head_dtype == c.act_dtype;
-  o->device_bytes = v * d * ae + (lm_alias ? 0 : o->lm_head_bytes) + d * 4 +
+  const int ae = elem_size(c.act_dtype), ie = elem_size(c.io_dtype);
+  const bool lm_alias = c.tied_lm_head && c.lm_head_dtype == c.io_dtype;
+  o->device_bytes = v * d * ie + (lm_alias ? 0 : o->lm_head_bytes) + d * 4 +
                     o->layer_matrix_bytes + o->layer_scale_bytes + L * norms * 4 + o->kv_pool_bytes +
-                    (int64_t)c.num_pages * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
-                    (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ae +
+                    block_table_entries(c) * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
+                    (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ie +
                     hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc);
 }
 
@@ -253,26 +268,25 @@ QDEC_API qdec_status qdec_bytes_model(const qdec_config* c, int32_t context, int
   const int64_t d = c->hidden, hq = c->n_q_heads, hkv = c->n_kv_heads, hd = c->head_dim,
                 f = c->ffn, v = c->vocab, L = c->n_layers, T = context;
   const int64_t we = elem_size(c->proj_dtype), ke = elem_size(c->kv_dtype),
-                ae = elem_size(c->act_dtype), le = elem_size(c->lm_head_dtype);
+                ae = elem_size(c->io_dtype), le = elem_size(c->lm_head_dtype);
   const int64_t sc = c->proj_dtype == QDEC_I8_ROW ? 4 : 0;
   memset(o, 0, sizeof *o);
   o->embed = d * ae;
   o->qkv = L * ((hq + 2 * hkv) * hd * (d * we + sc) + d * 4);
-  o->rope_append = L * ((c->qk_norm ? 2 * hd * 4 : 0) + 2 * hkv * hd * ke);
-  o->attention = L * (T * 2 * hkv * hd * ke);
+  // the attention kernel also normalises/rotates Q and K and appends the new K/V row
+  o->rope_append = 0;
+  o->attention = L * (T * 2 * hkv * hd * ke + (c->qk_norm ? 2 * hd * 4 : 0) + 2 * hkv * hd * ke);
   o->merge = 0;
   o->o_proj = L * (d * (hq * hd * we + sc));
   o->gate_up = L * (2 * f * (d * we + sc) + d * 4);
   o->down = L * (d * (f * we + sc));
   if (with_logits) {
     o->lm_head = v * (d * le + (c->lm_head_dtype == QDEC_I8_ROW ? 4 : 0)) + d * 4 + v * ae;
-    o->argmax = v * ae;
+    o->argmax = 0;  // reduces per-work-group partials written by the LM head
   }
   o->total = o->embed + o->qkv + o->rope_append + o->attention + o->o_proj + o->gate_up + o->down +
              o->lm_head;
-  const int part = c->partition_size > 0 ? c->partition_size
-                                         : part_tokens_for(context, 0, (int)hkv, kTargetWgs);
-  const int64_t np = n_parts_for(context, part);
+  const int64_t np = n_parts_for(context, model_part_tokens(*c));
   o->scratch = np > 1 ? L * hq * np * (hd + 2) * 4 * 2 : 0;
   return QDEC_OK;
 }
@@ -332,11 +346,12 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   qdec_ctx* c = new qdec_ctx();
   c->cfg = *cfg;
   c->device = device;
-  c->part_fixed = cfg->partition_size;
-  c->max_parts = (int)max_parts_for(*cfg, cfg->partition_size);
+  c->part_tokens = model_part_tokens(*cfg);
+  c->max_parts = (int)model_max_parts(*cfg);
+  c->bt_entries = (int32_t)block_table_entries(*cfg);
   const int64_t d = cfg->hidden, hq = cfg->n_q_heads, hkv = cfg->n_kv_heads, hd = cfg->head_dim,
                 f = cfg->ffn, v = cfg->vocab, L = cfg->n_layers;
-  const int ae = elem_size(cfg->act_dtype);
+  const int ae = elem_size(cfg->act_dtype), ie = elem_size(cfg->io_dtype);
   c->uploaded.assign((size_t)(L + 1) * kNumSlots, 0);
 
 #define TRY(x)                  \
@@ -358,8 +373,8 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
     return st;
   };
 
-  TRY(make_mat(c->embed, v, d, cfg->act_dtype, "embedding"));
-  c->lm_alias = cfg->tied_lm_head && cfg->lm_head_dtype == cfg->act_dtype;
+  TRY(make_mat(c->embed, v, d, cfg->io_dtype, "embedding"));
+  c->lm_alias = cfg->tied_lm_head && cfg->lm_head_dtype == cfg->io_dtype;
   if (c->lm_alias)
     c->lm = c->embed;
   else
@@ -383,14 +398,22 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
     TRY(c->hip(hipMemset(ly.k_pool, 0, (size_t)pool_bytes), "hipMemset K pool"));
     TRY(c->hip(hipMemset(ly.v_pool, 0, (size_t)pool_bytes), "hipMemset V pool"));
   }
-  TRY(c->alloc(&c->block_table, (int64_t)cfg->num_pages * 4, "block table"));
+  // zero-filled: every entry is a valid page number, so the attention kernel may read entries
+  // ahead of the context
+  TRY(c->alloc(&c->block_table, (int64_t)c->bt_entries * 4, "block table"));
+  TRY(c->hip(hipMemset(c->block_table, 0, (size_t)c->bt_entries * 4), "hipMemset block table"));
   TRY(c->alloc(&c->rope, (int64_t)cfg->max_context * (hd / 2) * 8, "RoPE table"));
   TRY(c->alloc(&c->x, d * 4, "residual"));
   TRY(c->alloc(&c->qkv, (hq + 2 * hkv) * hd * 4, "qkv"));
-  TRY(c->alloc(&c->q, hq * hd * ae, "q"));
   TRY(c->alloc(&c->attn, hq * hd * ae, "attention output"));
   TRY(c->alloc(&c->act, f * ae, "SwiGLU output"));
-  TRY(c->alloc(&c->logits, v * ae, "logits"));
+  TRY(c->alloc(&c->logits, v * ie, "logits"));
+  c->am_parts = gemv_partials(cfg->lm_head_dtype == QDEC_F32    ? W_F32
+                              : cfg->lm_head_dtype == QDEC_BF16 ? W_BF16
+                                                                : W_I8,
+                              EPI_STORE, v, d);
+  TRY(c->alloc(&c->am_val, (int64_t)c->am_parts * 4, "argmax partials"));
+  TRY(c->alloc(&c->am_idx, (int64_t)c->am_parts * 4, "argmax partials"));
   TRY(c->alloc(&c->part_acc, hq * (int64_t)c->max_parts * hd * 4, "split-KV scratch"));
   TRY(c->alloc(&c->part_ml, hq * (int64_t)c->max_parts * 8, "split-KV scratch"));
   TRY(c->alloc(&c->desc, (int64_t)sizeof(StepDesc), "step descriptor"));
@@ -689,17 +712,15 @@ struct ProfScope {
 };
 
 // Enqueues every kernel of the step after the embedding.  In graph mode the split-KV grid covers
-// max_context and the merge always runs; the kernels take ctx from the device descriptor in both
-// modes, so eager and replayed steps compute the same values.
+// max_context (surplus work-groups exit at once); the kernels take ctx from the device descriptor
+// in both modes, so eager and replayed steps compute the same values.
 static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s,
                                   bool graph) {
   const qdec_config& k = c->cfg;
   const int64_t d = k.hidden, hq = k.n_q_heads, hkv = k.n_kv_heads, hd = k.head_dim, f = k.ffn;
   const bool ab = c->act_bf16();
   const int wt = k.proj_dtype == QDEC_F32 ? W_F32 : k.proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
-  const int ctxlen = pos + 1;
-  const int part = part_tokens_for(ctxlen, c->part_fixed, (int)hkv, kTargetWgs);
-  const int np = n_parts_for(ctxlen, part);
+  const int np = n_parts_for(pos + 1, c->part_tokens);
   const int grid_parts = graph ? c->max_parts : np;
   const int group = (int)(hq / hkv);
   qdec_status rs;
@@ -715,7 +736,7 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
     GemvArgs g{};
     g.w = ly.qkv.data;
     g.scale = ly.qkv.scale;
-    g.xn = c->x;
+    g.x = c->x;
     g.gamma = ly.in_norm;
     g.eps = k.rms_eps;
     g.round_h = ab;
@@ -725,41 +746,29 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
     g.k = d;
     LAUNCH(QDEC_K_QKV, launch_gemv(wt, EPI_STORE, true, g, s));
 
-    RopeAppendArgs r{};
-    r.qkv = c->qkv;
-    r.q_gamma = ly.q_norm;
-    r.k_gamma = ly.k_norm;
-    r.eps = k.rms_eps;
-    r.table = c->rope;
-    r.desc = c->desc;
-    r.q_out = c->q;
-    r.q_bf16 = ab;
-    r.k_pool = ly.k_pool;
-    r.v_pool = ly.v_pool;
-    r.kv_bf16 = c->kv_bf16();
-    r.block_table = c->block_table;
-    r.n_q_heads = (int)hq;
-    r.n_kv_heads = (int)hkv;
-    LAUNCH(QDEC_K_ROPE_APPEND, launch_rope_append((int)hd, r, s));
-
     AttnArgs at{};
-    at.q = c->q;
-    at.q_bf16 = ab;
+    at.qkv = c->qkv;
+    at.q_gamma = ly.q_norm;
+    at.k_gamma = ly.k_norm;
+    at.eps = k.rms_eps;
+    at.rope_table = c->rope;
+    at.round_q = ab;
     at.k_pool = ly.k_pool;
     at.v_pool = ly.v_pool;
     at.block_table = c->block_table;
+    at.bt_len = c->bt_entries;
     at.desc = c->desc;
     at.n_q_heads = (int)hq;
     at.n_kv_heads = (int)hkv;
-    at.part_fixed = c->part_fixed;
-    at.target_wgs = kTargetWgs;
+    at.part_tokens = c->part_tokens;
     at.max_parts = c->max_parts;
     at.part_acc = c->part_acc;
     at.part_ml = c->part_ml;
     at.out = c->attn;
     at.out_bf16 = ab;
     at.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
-    LAUNCH(QDEC_K_ATTENTION, launch_attention((int)hd, c->kv_bf16(), group, at, grid_parts, s));
+    LAUNCH(QDEC_K_ATTENTION,
+           launch_attention((int)hd, c->kv_bf16(), group, true, at, grid_parts, s));
     if (graph || np > 1) LAUNCH(QDEC_K_MERGE, launch_attention_merge((int)hd, at, s));
 
     GemvArgs o{};
@@ -775,7 +784,7 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
     GemvArgs gu{};
     gu.w = ly.gu.data;
     gu.scale = ly.gu.scale;
-    gu.xn = c->x;
+    gu.x = c->x;
     gu.gamma = ly.post_norm;
     gu.eps = k.rms_eps;
     gu.round_h = ab;
@@ -803,17 +812,23 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
     GemvArgs h{};
     h.w = c->lm.data;
     h.scale = c->lm.scale;
-    h.xn = c->x;
+    h.x = c->x;
     h.gamma = c->final_norm;
     h.eps = k.rms_eps;
     h.round_h = ab;
     h.y = lg;
-    h.y_bf16 = ab;
+    h.y_bf16 = c->io_bf16();
     h.hidden_copy = st->hidden_out;
+    if (st->argmax_out) {
+      h.part_val = c->am_val;
+      h.part_idx = c->am_idx;
+    }
     h.n = k.vocab;
     h.k = d;
     LAUNCH(QDEC_K_LM_HEAD, launch_gemv(lt, EPI_STORE, true, h, s));
-    if (st->argmax_out) LAUNCH(QDEC_K_ARGMAX, launch_argmax(lg, ab, k.vocab, st->argmax_out, s));
+    if (st->argmax_out)
+      LAUNCH(QDEC_K_ARGMAX,
+             launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, st->argmax_out, s));
   } else if (st->hidden_out) {
     if ((rs = c->hip(launch_copy(st->hidden_out, c->x, d * 4, s), "hidden copy")) != QDEC_OK)
       return rs;
@@ -825,7 +840,7 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
 static qdec_status enqueue_embed(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s) {
   EmbedArgs e{};
   e.table = c->embed.data;
-  e.table_bf16 = c->act_bf16();
+  e.table_bf16 = c->io_bf16();
   e.emb = st->token_embedding;
   e.token = st->token_id;
   e.x = c->x;
@@ -1092,6 +1107,19 @@ static int op_part(int32_t ctx_len, int32_t n_kv_heads, int32_t partition_size) 
   return part_tokens_for(ctx_len, partition_size, n_kv_heads, kTargetWgs);
 }
 
+// Workspace of the op-level attention with np partitions: accumulators, then (m, l) pairs, the
+// second region 256-byte aligned.
+struct AttnWs {
+  int64_t acc_off, ml_off, bytes;
+};
+static AttnWs attn_ws(int64_t n_q_heads, int64_t np, int64_t head_dim) {
+  AttnWs w;
+  w.acc_off = 0;
+  w.ml_off = (n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
+  w.bytes = w.ml_off + n_q_heads * np * 8;
+  return w;
+}
+
 QDEC_API qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_heads,
                                                  int32_t head_dim, int32_t partition_size,
                                                  size_t* bytes) {
@@ -1101,12 +1129,7 @@ QDEC_API qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_he
   // the automatic size depends on n_kv_heads; take the largest count it can produce (Hkv = 1)
   const int part = partition_size > 0 ? partition_size : op_part(ctx_len, 1, 0);
   const int64_t np = n_parts_for(ctx_len, part);
-  if (np <= 1) {
-    *bytes = 0;
-    return QDEC_OK;
-  }
-  const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
-  *bytes = (size_t)(acc + (int64_t)n_q_heads * np * 8);
+  *bytes = np <= 1 ? 0 : (size_t)attn_ws(n_q_heads, np, head_dim).bytes;
   return QDEC_OK;
 }
 
@@ -1131,36 +1154,36 @@ QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const voi
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(nullptr, QDEC_E_INVAL, "pools must be 16-byte aligned");
   const int part = op_part(ctx_len, n_kv_heads, partition_size);
   const int np = n_parts_for(ctx_len, part);
-  size_t need = 0;
-  if (np > 1) {
-    const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
-    need = (size_t)(acc + (int64_t)n_q_heads * np * 8);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-      return fail(nullptr, QDEC_E_INVAL, "workspace of %zu bytes (256-byte aligned) required", need);
-  }
+  if (np > kMaxMergeParts)
+    return fail(nullptr, QDEC_E_UNSUPPORTED, "more than %d partitions", kMaxMergeParts);
+  const AttnWs ws = attn_ws(n_q_heads, np, head_dim);
+  if (np > 1 && (!workspace || workspace_bytes < (size_t)ws.bytes || !aligned(workspace, 256)))
+    return fail(nullptr, QDEC_E_INVAL, "workspace of %lld bytes (256-byte aligned) required",
+                (long long)ws.bytes);
   AttnArgs a{};
   a.q = q;
   a.q_bf16 = q_dtype == QDEC_BF16;
-  a.k_pool = k_pool;
-  a.v_pool = v_pool;
+  a.k_pool = const_cast<void*>(k_pool);
+  a.v_pool = const_cast<void*>(v_pool);
   a.block_table = block_table;
+  a.bt_len = (ctx_len + kPage - 1) / kPage;  // the caller's table covers exactly the context
   a.desc = nullptr;
   a.ctx_arg = ctx_len;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
-  a.part_fixed = partition_size;
-  a.target_wgs = kTargetWgs;
+  a.part_tokens = part;
   a.max_parts = np;
+  char* wsb = static_cast<char*>(workspace);
   if (np > 1) {
-    a.part_acc = static_cast<float*>(workspace);
-    const int64_t acc = ((int64_t)n_q_heads * np * head_dim * 4 + 255) / 256 * 256;
-    a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
+    a.part_acc = reinterpret_cast<float*>(wsb + ws.acc_off);
+    a.part_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
   }
   a.out = out;
   a.out_bf16 = out_dtype == QDEC_BF16;
   a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_attention(head_dim, kv_dtype == QDEC_BF16, n_q_heads / n_kv_heads, a, np, s);
+  hipError_t e =
+      launch_attention(head_dim, kv_dtype == QDEC_BF16, n_q_heads / n_kv_heads, false, a, np, s);
   if (e == hipSuccess && np > 1) e = launch_attention_merge(head_dim, a, s);
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "attention launch: %s", hipGetErrorString(e));
   return QDEC_OK;

@@ -10,24 +10,30 @@ from . import qdec as Q
 
 
 def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
-               partition_size: int = 0) -> Q.qdec_config:
-    """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights/activations/KV) or 'w8a16'
-    (int8 per-row projections and LM head, bf16 activations and KV)."""
+               partition_size: int = 0, act: str = None) -> Q.qdec_config:
+    """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights, embedding, logits and KV) or 'w8a16'
+    (int8 per-row projections and LM head, bf16 embedding, logits and KV).  act: 'f32' or 'bf16',
+    the precision of activations crossing op boundaries; default f32 for 'bf16' (bf16 as a
+    storage format only) and bf16 for 'w8a16' (16-bit activations)."""
     if path == "fp32":
-        proj = lm = act = kv = Q.F32
+        proj = lm = io = kv = Q.F32
+        act = act or "f32"
     elif path == "bf16":
-        proj = lm = act = kv = Q.BF16
+        proj = lm = io = kv = Q.BF16
+        act = act or "f32"
     elif path == "w8a16":
         proj = lm = Q.I8_ROW
-        act = kv = Q.BF16
+        io = kv = Q.BF16
+        act = act or "bf16"
     else:
         raise ValueError(path)
+    act = Q.F32 if act == "f32" else Q.BF16
     return Q.make_config(
         n_layers=shape["n_layers"], hidden=shape["hidden"], n_q_heads=shape["n_q_heads"],
         n_kv_heads=shape["n_kv_heads"], head_dim=shape["head_dim"], ffn=shape["ffn"],
         vocab=shape["vocab"], tied_lm_head=int(shape["tied"]), qk_norm=int(shape["qk_norm"]),
         rms_eps=shape["eps"], rope_theta=shape["theta"], proj_dtype=proj, lm_head_dtype=lm,
-        act_dtype=act, kv_dtype=kv, page_size=16, num_pages=num_pages, max_context=max_context,
+        io_dtype=io, act_dtype=act, kv_dtype=kv, page_size=16, num_pages=num_pages, max_context=max_context,
         partition_size=partition_size)
 
 

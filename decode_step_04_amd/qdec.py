@@ -37,7 +37,8 @@ class qdec_config(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("vocab", C.c_int32), ("tied_lm_head", C.c_int32), ("qk_norm", C.c_int32),
                 ("rms_eps", C.c_float), ("rope_theta", C.c_float), ("proj_dtype", C.c_int32),
-                ("lm_head_dtype", C.c_int32), ("act_dtype", C.c_int32), ("kv_dtype", C.c_int32),
+                ("lm_head_dtype", C.c_int32), ("io_dtype", C.c_int32), ("act_dtype", C.c_int32),
+                ("kv_dtype", C.c_int32),
                 ("page_size", C.c_int32), ("num_pages", C.c_int32), ("max_context", C.c_int32),
                 ("partition_size", C.c_int32)]
 

@@ -192,3 +192,18 @@ def bf16_to_f32(t) -> np.ndarray:
     import torch
 
     return t.detach().to(torch.float32).cpu().numpy()
+
+
+def host_weights(w: dict) -> dict:
+    """Host copy of a weight dict for the oracle: bf16 tensors become uint16 bit arrays, fp32
+    tensors float32 arrays, lists stay lists."""
+    import torch
+
+    def h(t):
+        if t is None:
+            return None
+        if isinstance(t, np.ndarray):
+            return t
+        return bf16_to_bits(t) if t.dtype == torch.bfloat16 else t.detach().cpu().numpy()
+
+    return {k: ([h(t) for t in v] if isinstance(v, list) else h(v)) for k, v in w.items()}

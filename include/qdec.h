@@ -72,7 +72,13 @@ typedef struct qdec_config {
   float rope_theta;       /* RoPE base, > 1 */
   int32_t proj_dtype;     /* qdec_dtype of the QKV, O, gate-up and down projections */
   int32_t lm_head_dtype;  /* qdec_dtype of the LM head */
-  int32_t act_dtype;      /* QDEC_F32 | QDEC_BF16: embedding table, op-boundary activations, logits */
+  int32_t io_dtype;       /* QDEC_F32 | QDEC_BF16: the embedding table, a caller's token_embedding
+                             and logits_out */
+  int32_t act_dtype;      /* QDEC_F32 | QDEC_BF16: activations that cross an op boundary inside the
+                             step (the normalised GEMV inputs, rotated Q, attention output, SwiGLU
+                             output).  F32 keeps bf16 a storage format only ([ETE], the bf16
+                             passage); BF16 rounds them as in [Qwen3-runtime] §0.1 (the "A16" of
+                             W8A16).  The residual stream is always fp32. */
   int32_t kv_dtype;       /* QDEC_F32 | QDEC_BF16: KV-cache storage */
   int32_t page_size;      /* tokens per KV page; must be 16 */
   int32_t num_pages;      /* physical pages in the pool (each layer has its own pool of this size) */
@@ -81,13 +87,13 @@ typedef struct qdec_config {
 } qdec_config;
 
 /* Supported dtype combinations (checked by qdec_config_validate):
- *   act F32  : proj F32,  lm_head F32,  kv F32          (the fp32 path)
- *   act BF16 : proj BF16 | I8_ROW, lm_head BF16 | I8_ROW, kv BF16   (the bf16 / W8A16 path) */
+ *   io F32  : proj, lm_head, act and kv all F32                                  (the fp32 path)
+ *   io BF16 : proj BF16 | I8_ROW, lm_head BF16 | I8_ROW, act F32 | BF16, kv BF16   (bf16 / W8A16) */
 
 /* Weight slots for qdec_upload / qdec_upload_i8.  Norm gammas are always stored fp32 (small
  * sensitive tensors stay fp32: [ETE], the int8 quantisation passage). */
 typedef enum qdec_weight {
-  QDEC_W_EMBED = 0,      /* [vocab x hidden] in act_dtype; global (layer ignored) */
+  QDEC_W_EMBED = 0,      /* [vocab x hidden] in io_dtype; global (layer ignored) */
   QDEC_W_LM_HEAD = 1,    /* [vocab x hidden] in lm_head_dtype; global.  With tied_lm_head the
                             slot is filled from QDEC_W_EMBED's upload and may not be uploaded. */
   QDEC_W_FINAL_NORM = 2, /* [hidden] fp32; global */
@@ -107,7 +113,7 @@ typedef struct qdec_ctx qdec_ctx; /* opaque, owned by the library */
 /* One decode step ([Qwen3-runtime] §3.2: one new token per step; [ETE] the GPU block pipeline).
  * All pointers are device pointers owned by the caller. */
 typedef struct qdec_step {
-  const void* token_embedding; /* [hidden] act_dtype input row, or NULL to gather EMBED[*token_id] */
+  const void* token_embedding; /* [hidden] io_dtype input row, or NULL to gather EMBED[*token_id] */
   const int32_t* token_id;     /* device int32 token id (read on the device, so it may be the
                                   previous step's argmax_out); required if token_embedding is NULL.
                                   An id outside [0, vocab) yields a zero row and sets the device
@@ -115,7 +121,7 @@ typedef struct qdec_step {
   int32_t pos;                 /* 0-based position of the new token; attention covers 0..pos */
   int32_t reserved;            /* must be 0 */
   float* hidden_out;           /* optional [hidden] fp32: residual stream after the last layer */
-  void* logits_out;            /* optional [vocab] act_dtype logits.  NULL together with
+  void* logits_out;            /* optional [vocab] io_dtype logits.  NULL together with
                                   argmax_out == NULL skips the final norm and LM head (the
                                   prompt-token trim of [ETE]) */
   int32_t* argmax_out;         /* optional device int32: index of the largest logit, the lowest

@@ -231,7 +231,8 @@ def pool_scatter(logical, pos0, block_table, num_pages, page):
 class _ORModel(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn", "vocab", "qk_norm",
-        "embed_type", "proj_type", "lm_type", "act_bf16", "kv_bf16", "max_ctx")] + [
+        "embed_type", "proj_type", "lm_type", "act_bf16", "kv_bf16", "logits_bf16",
+        "max_ctx")] + [
         ("eps", C.c_double), ("theta", C.c_double),
         ("embed", C.c_void_p), ("lm_head", C.c_void_p), ("lm_scale", C.c_void_p),
         ("final_norm", C.c_void_p),
@@ -270,6 +271,7 @@ class Model:
         s.lm_type = _wtype(lm)
         s.act_bf16 = int(cfg["act_bf16"])
         s.kv_bf16 = int(cfg["kv_bf16"])
+        s.logits_bf16 = int(cfg.get("logits_bf16", cfg["kv_bf16"]))
         s.max_ctx = max_ctx
         s.eps, s.theta = float(cfg["eps"]), float(cfg["theta"])
         s.embed = self._hold(weights["embed"])

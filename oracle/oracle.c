@@ -10,9 +10,10 @@
  * 16-bit shift, int8 codes as integers, fp32 as is).  Where the pages fix a narrower precision the
  * oracle applies it at the same place:
  *   - the int8 quantiser computes its scale and codes in fp32 (scale = max|row| / 127);
- *   - on the bf16 path, tensors that cross an op boundary in bf16 ([Qwen3-runtime] §0.1: bf16 in
- *     and out, fp32 inside reductions) are rounded to bf16 there, and the KV cache stores the
- *     rounded values; on the fp32 path the KV cache stores fp32-rounded values.
+ *   - the KV cache stores values rounded to its storage type (bf16 or fp32), and the logits are
+ *     rounded to their output type;
+ *   - when the step keeps bf16 activations at op boundaries ([Qwen3-runtime] §0.1: bf16 in and
+ *     out, fp32 inside reductions), those tensors are rounded to bf16 at the same places.
  *
  * Sources, cited by page title and section:
  *   [Qwen3-runtime]  "从 Qwen3 数学到 CUDA Kernel：0.6B 推理运行时的完整实现与优化" (chengzipai.xyz)
@@ -361,8 +362,9 @@ typedef struct or_model {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   int32_t qk_norm;
   int32_t embed_type, proj_type, lm_type; /* OR_F32 / OR_BF16 / OR_I8 */
-  int32_t act_bf16;                       /* 1: bf16 op-boundary rounding (the bf16 path) */
+  int32_t act_bf16;                       /* 1: bf16 rounding of op-boundary activations */
   int32_t kv_bf16;                        /* 1: the KV cache stores bf16 values, else fp32 */
+  int32_t logits_bf16;                    /* 1: logits are returned as bf16 values, else fp32 */
   int32_t max_ctx;
   double eps, theta;
   const void* embed;
@@ -399,9 +401,11 @@ static double kv_round(const or_model* m, double v) {
  *               x += W_o concat(o_h)
  *               h2 = RMSNorm(x, g_post);  [g|u] = W_gu h2;  a = silu(g) * u;  x += W_down a
  *   hidden = x;  logits = W_lm RMSNorm(x, g_final);  argmax = lowest index of the maximum.
- * Rounding to bf16 (act_bf16) at: each RMSNorm output that feeds a projection, the rotated Q,
- * the attention output, the SwiGLU output and the logits; K/V are stored by kv_round.  On the
- * fp32 path the logits are rounded to fp32 (their output type) before the argmax.
+ * With act_bf16, activations crossing an op boundary are rounded to bf16 ([Qwen3-runtime] §0.1):
+ * each RMSNorm output that feeds a projection, the rotated Q, the attention output and the
+ * SwiGLU output; without it they stay fp64 (bf16 only as a storage format, [ETE]).  K/V are
+ * stored by kv_round.  The logits are rounded to their output type (bf16 or fp32) before the
+ * argmax, so the greedy decision is taken on the values returned.
  * Returns 0, or -1 on a bad argument. */
 int32_t or_decode_step(const or_model* m, int32_t token, const double* emb, int32_t pos,
                        double* hidden_out, double* logits_out, int32_t* argmax_out) {
@@ -484,7 +488,7 @@ int32_t or_decode_step(const or_model* m, int32_t token, const double* emb, int3
     or_rmsnorm(x, m->final_norm, dm, m->eps, h);
     for (int64_t i = 0; i < dm; ++i) h[i] = act_round(m, h[i]);
     or_gemv(m->lm_head, m->lm_type, m->lm_scale, h, v, dm, lg);
-    for (int64_t i = 0; i < v; ++i) lg[i] = m->act_bf16 ? round_bf16(lg[i]) : round_f32(lg[i]);
+    for (int64_t i = 0; i < v; ++i) lg[i] = m->logits_bf16 ? round_bf16(lg[i]) : round_f32(lg[i]);
     if (argmax_out) {
       int32_t best = -1;
       for (int64_t i = 0; i < v; ++i)

@@ -91,8 +91,10 @@ def test_info_reproduces_the_printed_qwen3_numbers():
 def test_bytes_model_components():
     c = cfg(max_context=8192)
     b = Q.qdec_bytes_model(c, 4096, 1)
-    assert b.attention == 28 * 4096 * 4096                      # T keys and values, 28 layers
-    assert b.rope_append == 28 * (2 * 128 * 4 + 4096)            # q/k gammas + one K/V row
+    # T keys and values read, q/k gammas and one appended K/V row per layer (the attention kernel
+    # does the Q/K norm, RoPE and append itself)
+    assert b.attention == 28 * (4096 * 4096 + 2 * 128 * 4 + 4096)
+    assert b.rope_append == 0 and b.merge == 0 and b.argmax == 0
     layer = b.qkv + b.o_proj + b.gate_up + b.down
     assert layer == 840 * MIB + 28 * 2 * 1024 * 4                # matrices + in/post gammas
     assert b.lm_head == 151936 * 1024 * 2 + 1024 * 4 + 151936 * 2
@@ -135,6 +137,7 @@ def test_op_entry_points_validate_before_touching_the_gpu():
 
 def test_attention_workspace_sizes():
     assert Q.qdec_op_attention_workspace(512, 32, 128, 512) == 0           # one partition
+    # accumulators, then (m, l) pairs (256-byte aligned)
     ws = Q.qdec_op_attention_workspace(8192, 32, 128, 512)
     assert ws == 32 * 16 * 128 * 4 + 32 * 16 * 8
     assert Q.qdec_op_attention_workspace(131072, 32, 128, 512) == 32 * 256 * (128 + 2) * 4

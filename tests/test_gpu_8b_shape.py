@@ -1,0 +1,60 @@
+"""The decode step at the 8B-class shape (36 layers, hidden 4096, 32 Q / 8 KV heads, D 128,
+FFN 12288, vocab 151936 untied), bf16, context 8192 with paged KV, all weights and KV resident
+in one GPU's HBM; one step at pos 8191 against the oracle (hidden relative L2 <= 1.5e-2, logits
+max-abs <= 5e-2, greedy id a maximiser of the oracle's logits up to bf16 rounding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_04_amd import loader, synth
+from decode_step_04_amd import qdec as Q
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SHAPE = synth.DENSE_8B
+T = 8192
+
+
+@pytest.mark.timeout(600)
+def test_8b_step_matches_oracle():
+    print("8b setup", flush=True)
+    n_pages = T // 16
+    cfg = loader.config_for(SHAPE, path="bf16", num_pages=n_pages, max_context=T)
+    ctx = Q.qdec_create(cfg, 0)
+    try:
+        w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        loader.upload_weights(ctx, w, DEV)
+        table = synth.block_table(n_pages, n_pages, seed=2)
+        Q.qdec_kv_set_block_table(ctx, table)
+        kv = synth.kv_prefill(SHAPE, T - 1, seed=1, device=DEV)
+        loader.prefill_kv(ctx, kv)
+        tok_id = synth.token_id(SHAPE["vocab"], seed=3)
+        tok = torch.tensor([tok_id], dtype=torch.int32, device=DEV)
+        hidden = torch.empty(SHAPE["hidden"], device=DEV)
+        logits = torch.empty(SHAPE["vocab"], dtype=torch.bfloat16, device=DEV)
+        amax = torch.empty(1, dtype=torch.int32, device=DEV)
+        Q.qdec_decode_step(ctx, Q.make_step(T - 1, token_id=tok, hidden_out=hidden,
+                                            logits_out=logits, argmax_out=amax))
+        torch.cuda.synchronize()
+        gh = hidden.cpu().numpy().astype(np.float64)
+        gl = synth.bf16_to_f32(logits).astype(np.float64)
+        ga = int(amax.item())
+        print("8b oracle", flush=True)
+        hw = synth.host_weights(w)
+        del w
+        om = oracle.Model(dict(SHAPE, act_bf16=0, kv_bf16=1, logits_bf16=1), hw, max_ctx=T)
+        for l, (k, v) in enumerate(kv):
+            om.k_cache[l][: T - 1] = k.float().cpu().numpy()
+            om.v_cache[l][: T - 1] = v.float().cpu().numpy()
+        del kv
+        rh, rl, ra = om.step(T - 1, token=tok_id)
+        rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
+        lmax = np.max(np.abs(gl - rl))
+        print(f"8b hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra}",
+              flush=True)
+        assert rel <= 1.5e-2
+        assert lmax <= 5e-2
+        assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+    finally:
+        Q.qdec_destroy(ctx)

@@ -1,0 +1,177 @@
+"""The decode step at the Qwen3-0.6B shape against the oracle (bf16 and W8A16 paths).
+
+Recipe: random-init weights N(0, 0.02) stored bf16 (seed 0), gammas 1 + N(0, 0.1), KV positions
+0..4094 pre-filled with N(0, 1) bf16 values through a random permutation of the 256 pool pages,
+one token id drawn uniformly; a decode step at pos T-1 for T in 512, 2048, 4096.
+Bar (bf16 / W8A16 path): hidden-state relative L2 <= 1.5e-2 and logits max-abs <= 5e-2; the
+GPU's greedy id must be a maximiser of the oracle's logits up to bf16 rounding; int8 codes and
+scales bit-exact; graph replay bit-identical to the eager step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_04_amd import loader, synth
+from decode_step_04_amd import qdec as Q
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+SHAPE = synth.QWEN3_0P6B
+MAXCTX = 4096
+CONTEXTS = (512, 2048, 4096)
+
+
+class Setup:
+    def __init__(self, path, act):
+        print(f"qwen3-0.6b setup path={path} act={act}", flush=True)
+        self.path = path
+        n_pages = MAXCTX // 16
+        self.cfg = loader.config_for(SHAPE, path=path, num_pages=n_pages, max_context=MAXCTX,
+                                     act=act)
+        self.ctx = Q.qdec_create(self.cfg, 0)
+        self.w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        loader.upload_weights(self.ctx, self.w, DEV)
+        self.table = synth.block_table(n_pages, n_pages, seed=2)
+        Q.qdec_kv_set_block_table(self.ctx, self.table)
+        kv = synth.kv_prefill(SHAPE, MAXCTX - 1, seed=1, device=DEV)
+        loader.prefill_kv(self.ctx, kv)
+        hw = synth.host_weights(self.w)
+        if path == "w8a16":
+            for key in ("qkv", "o", "gate_up", "down"):
+                qs = [oracle.quantize_rows(oracle.bf16_bits_to_f64(b).astype(np.float32))
+                      for b in hw[key]]
+                hw[key] = [q for q, _ in qs]
+                hw[key + "_scale"] = [s for _, s in qs]
+            q, s = oracle.quantize_rows(oracle.bf16_bits_to_f64(hw["embed"]).astype(np.float32))
+            hw["lm_head"], hw["lm_scale"] = q, s
+        self.hw = hw
+        self.om = oracle.Model(dict(SHAPE, act_bf16=int(act == "bf16"), kv_bf16=1, logits_bf16=1),
+                               hw, max_ctx=MAXCTX)
+        for l, (k, v) in enumerate(kv):
+            self.om.k_cache[l][: MAXCTX - 1] = k.float().cpu().numpy()
+            self.om.v_cache[l][: MAXCTX - 1] = v.float().cpu().numpy()
+        del kv
+        self.tok_id = synth.token_id(SHAPE["vocab"], seed=3)
+        self.tok = torch.tensor([self.tok_id], dtype=torch.int32, device=DEV)
+        self.hidden = torch.empty(SHAPE["hidden"], device=DEV)
+        self.logits = torch.empty(SHAPE["vocab"], dtype=torch.bfloat16, device=DEV)
+        self.amax = torch.empty(1, dtype=torch.int32, device=DEV)
+        torch.cuda.synchronize()
+
+    def step(self, pos, graph=False):
+        st = Q.make_step(pos, token_id=self.tok, hidden_out=self.hidden, logits_out=self.logits,
+                         argmax_out=self.amax)
+        if graph:
+            Q.qdec_graph_capture(self.ctx, st)
+            Q.qdec_graph_replay(self.ctx, pos)
+        else:
+            Q.qdec_decode_step(self.ctx, st)
+        torch.cuda.synchronize()
+        return (self.hidden.cpu().numpy().astype(np.float64),
+                synth.bf16_to_f32(self.logits).astype(np.float64), int(self.amax.item()))
+
+    def close(self):
+        Q.qdec_destroy(self.ctx)
+
+
+def _check(got, ref):
+    gh, gl, ga = got
+    rh, rl, ra = ref
+    rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
+    lmax = np.max(np.abs(gl - rl))
+    print(f"hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle {ra}",
+          flush=True)
+    assert rel <= 1.5e-2
+    assert lmax <= 5e-2
+    assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+
+
+_SETUPS = {}
+
+
+def setup(path, act):
+    if (path, act) not in _SETUPS:
+        _SETUPS[(path, act)] = Setup(path, act)
+    return _SETUPS[(path, act)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _close_setups():
+    yield
+    for s in _SETUPS.values():
+        s.close()
+    _SETUPS.clear()
+
+
+# bf16 weights with fp32 activations (bf16 as storage only) at every context; bf16 activations
+# at op boundaries (the 16-bit activation policy) and the int8 per-row weights at both ends.
+CASES = ([("bf16", "f32", T) for T in CONTEXTS] +
+         [("bf16", "bf16", 512), ("bf16", "bf16", 4096), ("w8a16", "bf16", 512),
+          ("w8a16", "bf16", 4096), ("w8a16", "f32", 4096)])
+
+
+@pytest.mark.parametrize("path,act,T", CASES)
+def test_step_matches_oracle(path, act, T):
+    print(f"qwen3-0.6b {path} act={act} T={T}", flush=True)
+    s = setup(path, act)
+    got = s.step(T - 1)
+    ref = s.om.step(T - 1, token=s.tok_id)
+    _check(got, ref)
+
+
+def test_graph_replay_bit_identical():
+    s = setup("bf16", "f32")
+    a = s.step(MAXCTX - 1)
+    b = s.step(MAXCTX - 1, graph=True)
+    c = s.step(MAXCTX - 1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
+    Q.qdec_graph_reset(s.ctx)
+
+
+def test_appended_kv_matches_oracle():
+    """After a step at pos 4095 the K/V rows it appended (read back through the block table)
+    match the oracle's up to one bf16 rounding step, and pre-filled rows are untouched."""
+    s = setup("bf16", "f32")
+    pos = MAXCTX - 1
+    s.step(pos)
+    s.om.step(pos, token=s.tok_id)
+    for layer in (0, 13, 27):
+        k = torch.empty((2, 8, 128), dtype=torch.bfloat16, device=DEV)
+        v = torch.empty_like(k)
+        Q.qdec_kv_read(s.ctx, layer, pos - 1, 2, k, v)
+        torch.cuda.synchronize()
+        kf, vf = k.float().cpu().numpy(), v.float().cpu().numpy()
+        np.testing.assert_array_equal(kf[0], s.om.k_cache[layer][pos - 1])      # pre-filled
+        np.testing.assert_array_equal(vf[0], s.om.v_cache[layer][pos - 1])
+        # one bf16 step of the value, plus an absolute allowance for components near zero (the
+        # fp32-vs-fp64 difference before rounding is ~1e-6 of the row's magnitude)
+        for got, ref in ((kf[1], s.om.k_cache[layer][pos]), (vf[1], s.om.v_cache[layer][pos])):
+            atol = 1e-4 * np.abs(ref).max()
+            assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-7 + atol), layer
+
+
+def test_w8a16_codes_bit_exact():
+    w8 = setup("w8a16", "bf16")
+    for layer in (0, 27):
+        for which, key in ((Q.W_QKV, "qkv"), (Q.W_O, "o"), (Q.W_GATE_UP, "gate_up"),
+                           (Q.W_DOWN, "down")):
+            data, scale = Q.qdec_weight_ptr(w8.ctx, layer, which)
+            ref_q = w8.hw[key][layer]
+            ref_s = w8.hw[key + "_scale"][layer]
+            q = torch.empty(ref_q.shape, dtype=torch.int8, device=DEV)
+            sc = torch.empty(ref_s.shape, dtype=torch.float32, device=DEV)
+            Q.qdec_op_copy(q, data, q.numel())
+            Q.qdec_op_copy(sc, scale, sc.numel() * 4)
+            torch.cuda.synchronize()
+            assert np.array_equal(q.cpu().numpy(), ref_q), (layer, key)
+            assert np.array_equal(sc.cpu().numpy(), ref_s), (layer, key)
+    data, scale = Q.qdec_weight_ptr(w8.ctx, 0, Q.W_LM_HEAD)
+    q = torch.empty(w8.hw["lm_head"].shape, dtype=torch.int8, device=DEV)
+    sc = torch.empty(w8.hw["lm_scale"].shape, dtype=torch.float32, device=DEV)
+    Q.qdec_op_copy(q, data, q.numel())
+    Q.qdec_op_copy(sc, scale, sc.numel() * 4)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), w8.hw["lm_head"])
+    assert np.array_equal(sc.cpu().numpy(), w8.hw["lm_scale"])
