@@ -28,9 +28,8 @@
 //   - Rows, then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With one partition
 //     the normalised output is written directly (the short path of §10.1); otherwise the
 //     unnormalised state goes to scratch for k_attn_merge.
-// k_attn_merge: one work-group per query head.  The (m, l) pairs of all partitions and the
-// accumulators are requested together; M = max m_p, w_p = 2^(m_p - M), out = sum w_p acc_p /
-// sum w_p l_p, reductions through LDS.
+// k_attn_merge: one wave per (query head, 32 dims): M = max m_p, w_p = 2^(m_p - M),
+// out = sum w_p acc_p / sum w_p l_p.
 //
 // Scores are kept in log2 units: q is pre-multiplied by log2(e)/sqrt(D), so exp(s - m) becomes
 // exp2(s' - m') (one v_exp_f32).  The initial running max is -1e30 as in [ETE]; masked tokens
@@ -355,60 +354,46 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 }
 
-// One work-group of 256 threads per query head.  Dynamic LDS: 2 * max_parts floats.
+// One single-wave work-group per (query head, block of 32 dims): lanes 0-31 and 32-63 take the
+// even and odd partitions of 32 consecutive dims.  The accumulator loads do not depend on the
+// weights, so they are all in flight while the (m, l) pairs are reduced.  Dynamic LDS: one
+// weight per partition.
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  extern __shared__ float sml[];  // [max_parts] weights 2^(m_p - M), then [max_parts] l_p
-  __shared__ float red[4];
-  __shared__ float part_o[256 / D][D];
+__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
+  extern __shared__ float wts[];  // [np] weights 2^(m_p - M)
   const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
   const int np = n_parts_for(ctx, a.part_tokens);
   if (np <= 1) return;  // the partition kernel wrote the output itself
   const int hq = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int NG = 256 / D;            // partition groups for the accumulator pass
-  const int r = tid % D, grp = tid / D;
+  const int lane = threadIdx.x;
+  const int dim = blockIdx.y * 32 + (lane & 31);
+  const int half = lane >> 5;
   const int64_t base = (int64_t)hq * a.max_parts;
-  float* wts = sml;
-  float* ls = sml + a.max_parts;
-
-  // (m, l) of every partition, and this thread's first accumulators, requested together
   float mloc = -1e30f;
-  for (int p = tid; p < np; p += 256) {
+  for (int p = lane; p < np; p += 64) {
     const float mp = a.part_ml[(base + p) * 2];
     wts[p] = mp;
-    ls[p] = a.part_ml[(base + p) * 2 + 1];
     mloc = fmaxf(mloc, mp);
   }
-  mloc = wave_max(mloc);
-  if (lane == 0) red[wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float M = wave_max(mloc);
   float lsum = 0.f;
-  for (int p = tid; p < np; p += 256) {
+  for (int p = lane; p < np; p += 64) {
     const float w = fast_exp2(wts[p] - M);
     wts[p] = w;
-    lsum = fmaf(ls[p], w, lsum);
+    lsum = fmaf(a.part_ml[(base + p) * 2 + 1], w, lsum);
   }
-  lsum = wave_sum(lsum);
-  __syncthreads();  // red is reused; wts complete
-  if (lane == 0) red[wave] = lsum;
+  const float L = wave_sum(lsum);
   __syncthreads();
-  const float L = (red[0] + red[1]) + (red[2] + red[3]);
   float O = 0.f;
-#pragma unroll 8
-  for (int p = grp; p < np; p += NG) O = fmaf(a.part_acc[(base + p) * D + r], wts[p], O);
-  part_o[grp][r] = O;
-  __syncthreads();
-  if (grp == 0) {
-    float t = 0.f;
-#pragma unroll
-    for (int q2 = 0; q2 < NG; ++q2) t += part_o[q2][r];
-    const float o = t / L;
+#pragma unroll 16
+  for (int p = half; p < np; p += 2) O = fmaf(a.part_acc[(base + p) * D + dim], wts[p], O);
+  O += __shfl_xor(O, 32);
+  if (half == 0) {
+    const float o = O / L;
     if (a.out_bf16)
-      static_cast<uint16_t*>(a.out)[hq * D + r] = f32_to_bf16(o);
+      static_cast<uint16_t*>(a.out)[hq * D + dim] = f32_to_bf16(o);
     else
-      static_cast<float*>(a.out)[hq * D + r] = o;
+      static_cast<float*>(a.out)[hq * D + dim] = o;
   }
 }
 
@@ -443,8 +428,8 @@ hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, c
 }
 
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_q_heads), block(256);
-  const size_t lds = (size_t)a.max_parts * 2 * sizeof(float);
+  const dim3 grid((unsigned)a.n_q_heads, (unsigned)(head_dim / 32)), block(64);
+  const size_t lds = (size_t)a.max_parts * sizeof(float);
   if (head_dim == 64)
     hipLaunchKernelGGL((k_attn_merge<64>), grid, block, lds, s, a);
   else

@@ -711,126 +711,149 @@ struct ProfScope {
   }
 };
 
-// Enqueues every kernel of the step after the embedding.  In graph mode the split-KV grid covers
-// max_context (surplus work-groups exit at once); the kernels take ctx from the device descriptor
-// in both modes, so eager and replayed steps compute the same values.
-static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s,
-                                  bool graph) {
+// Launches one kernel of the step: class `cls` of layer `l` (the LM head and argmax ignore l).
+// grid_parts is the number of split-KV partitions the attention grid covers.
+static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_t l,
+                               int grid_parts, hipStream_t s) {
   const qdec_config& k = c->cfg;
   const int64_t d = k.hidden, hq = k.n_q_heads, hkv = k.n_kv_heads, hd = k.head_dim, f = k.ffn;
   const bool ab = c->act_bf16();
   const int wt = k.proj_dtype == QDEC_F32 ? W_F32 : k.proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+  const Layer& ly = c->layers[(size_t)l];
+  switch (cls) {
+    case QDEC_K_QKV: {
+      GemvArgs g{};
+      g.w = ly.qkv.data;
+      g.scale = ly.qkv.scale;
+      g.x = c->x;
+      g.gamma = ly.in_norm;
+      g.eps = k.rms_eps;
+      g.round_h = ab;
+      g.y = c->qkv;
+      g.y_bf16 = 0;
+      g.n = (hq + 2 * hkv) * hd;
+      g.k = d;
+      return launch_gemv(wt, EPI_STORE, true, g, s);
+    }
+    case QDEC_K_ATTENTION:
+    case QDEC_K_MERGE: {
+      AttnArgs at{};
+      at.qkv = c->qkv;
+      at.q_gamma = ly.q_norm;
+      at.k_gamma = ly.k_norm;
+      at.eps = k.rms_eps;
+      at.rope_table = c->rope;
+      at.round_q = ab;
+      at.k_pool = ly.k_pool;
+      at.v_pool = ly.v_pool;
+      at.block_table = c->block_table;
+      at.bt_len = c->bt_entries;
+      at.desc = c->desc;
+      at.n_q_heads = (int)hq;
+      at.n_kv_heads = (int)hkv;
+      at.part_tokens = c->part_tokens;
+      at.max_parts = c->max_parts;
+      at.part_acc = c->part_acc;
+      at.part_ml = c->part_ml;
+      at.out = c->attn;
+      at.out_bf16 = ab;
+      at.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+      if (cls == QDEC_K_MERGE) return launch_attention_merge((int)hd, at, s);
+      return launch_attention((int)hd, c->kv_bf16(), (int)(hq / hkv), true, at, grid_parts, s);
+    }
+    case QDEC_K_O_PROJ: {
+      GemvArgs o{};
+      o.w = ly.o.data;
+      o.scale = ly.o.scale;
+      o.x = c->attn;
+      o.x_bf16 = ab;
+      o.resid = c->x;
+      o.n = d;
+      o.k = hq * hd;
+      return launch_gemv(wt, EPI_RESID, false, o, s);
+    }
+    case QDEC_K_GATE_UP: {
+      GemvArgs gu{};
+      gu.w = ly.gu.data;
+      gu.scale = ly.gu.scale;
+      gu.x = c->x;
+      gu.gamma = ly.post_norm;
+      gu.eps = k.rms_eps;
+      gu.round_h = ab;
+      gu.y = c->act;
+      gu.y_bf16 = ab;
+      gu.n = f;
+      gu.k = d;
+      return launch_gemv(wt, EPI_SWIGLU, true, gu, s);
+    }
+    case QDEC_K_DOWN: {
+      GemvArgs dn{};
+      dn.w = ly.down.data;
+      dn.scale = ly.down.scale;
+      dn.x = c->act;
+      dn.x_bf16 = ab;
+      dn.resid = c->x;
+      dn.n = d;
+      dn.k = f;
+      return launch_gemv(wt, EPI_RESID, false, dn, s);
+    }
+    case QDEC_K_LM_HEAD: {
+      const int lt =
+          k.lm_head_dtype == QDEC_F32 ? W_F32 : k.lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+      GemvArgs h{};
+      h.w = c->lm.data;
+      h.scale = c->lm.scale;
+      h.x = c->x;
+      h.gamma = c->final_norm;
+      h.eps = k.rms_eps;
+      h.round_h = ab;
+      h.y = st->logits_out ? st->logits_out : c->logits;
+      h.y_bf16 = c->io_bf16();
+      h.hidden_copy = st->hidden_out;
+      if (st->argmax_out) {
+        h.part_val = c->am_val;
+        h.part_idx = c->am_idx;
+      }
+      h.n = k.vocab;
+      h.k = d;
+      return launch_gemv(lt, EPI_STORE, true, h, s);
+    }
+    case QDEC_K_ARGMAX:
+      return launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, st->argmax_out, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// Enqueues every kernel of the step after the embedding.  In graph mode the split-KV grid covers
+// max_context (surplus work-groups exit at once) and the merge always runs; the kernels take
+// ctx from the device descriptor in both modes, so eager and replayed steps compute the same
+// values.
+static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hipStream_t s,
+                                  bool graph) {
   const int np = n_parts_for(pos + 1, c->part_tokens);
   const int grid_parts = graph ? c->max_parts : np;
-  const int group = (int)(hq / hkv);
   qdec_status rs;
-#define LAUNCH(cls, call)                                   \
-  do {                                                      \
-    ProfScope ps_(c, s, cls, graph);                        \
-    if ((rs = c->hip((call), #cls)) != QDEC_OK) return rs;  \
-    ps_.done();                                             \
+#define LAUNCH(cls, l)                                                                    \
+  do {                                                                                    \
+    ProfScope ps_(c, s, cls, graph);                                                      \
+    if ((rs = c->hip(launch_class(c, st, cls, l, grid_parts, s), #cls)) != QDEC_OK) return rs; \
+    ps_.done();                                                                           \
   } while (0)
-
-  for (int64_t l = 0; l < k.n_layers; ++l) {
-    const Layer& ly = c->layers[(size_t)l];
-    GemvArgs g{};
-    g.w = ly.qkv.data;
-    g.scale = ly.qkv.scale;
-    g.x = c->x;
-    g.gamma = ly.in_norm;
-    g.eps = k.rms_eps;
-    g.round_h = ab;
-    g.y = c->qkv;
-    g.y_bf16 = 0;
-    g.n = (hq + 2 * hkv) * hd;
-    g.k = d;
-    LAUNCH(QDEC_K_QKV, launch_gemv(wt, EPI_STORE, true, g, s));
-
-    AttnArgs at{};
-    at.qkv = c->qkv;
-    at.q_gamma = ly.q_norm;
-    at.k_gamma = ly.k_norm;
-    at.eps = k.rms_eps;
-    at.rope_table = c->rope;
-    at.round_q = ab;
-    at.k_pool = ly.k_pool;
-    at.v_pool = ly.v_pool;
-    at.block_table = c->block_table;
-    at.bt_len = c->bt_entries;
-    at.desc = c->desc;
-    at.n_q_heads = (int)hq;
-    at.n_kv_heads = (int)hkv;
-    at.part_tokens = c->part_tokens;
-    at.max_parts = c->max_parts;
-    at.part_acc = c->part_acc;
-    at.part_ml = c->part_ml;
-    at.out = c->attn;
-    at.out_bf16 = ab;
-    at.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
-    LAUNCH(QDEC_K_ATTENTION,
-           launch_attention((int)hd, c->kv_bf16(), group, true, at, grid_parts, s));
-    if (graph || np > 1) LAUNCH(QDEC_K_MERGE, launch_attention_merge((int)hd, at, s));
-
-    GemvArgs o{};
-    o.w = ly.o.data;
-    o.scale = ly.o.scale;
-    o.x = c->attn;
-    o.x_bf16 = ab;
-    o.resid = c->x;
-    o.n = d;
-    o.k = hq * hd;
-    LAUNCH(QDEC_K_O_PROJ, launch_gemv(wt, EPI_RESID, false, o, s));
-
-    GemvArgs gu{};
-    gu.w = ly.gu.data;
-    gu.scale = ly.gu.scale;
-    gu.x = c->x;
-    gu.gamma = ly.post_norm;
-    gu.eps = k.rms_eps;
-    gu.round_h = ab;
-    gu.y = c->act;
-    gu.y_bf16 = ab;
-    gu.n = f;
-    gu.k = d;
-    LAUNCH(QDEC_K_GATE_UP, launch_gemv(wt, EPI_SWIGLU, true, gu, s));
-
-    GemvArgs dn{};
-    dn.w = ly.down.data;
-    dn.scale = ly.down.scale;
-    dn.x = c->act;
-    dn.x_bf16 = ab;
-    dn.resid = c->x;
-    dn.n = d;
-    dn.k = f;
-    LAUNCH(QDEC_K_DOWN, launch_gemv(wt, EPI_RESID, false, dn, s));
+  for (int64_t l = 0; l < c->cfg.n_layers; ++l) {
+    LAUNCH(QDEC_K_QKV, l);
+    LAUNCH(QDEC_K_ATTENTION, l);
+    if (graph || np > 1) LAUNCH(QDEC_K_MERGE, l);
+    LAUNCH(QDEC_K_O_PROJ, l);
+    LAUNCH(QDEC_K_GATE_UP, l);
+    LAUNCH(QDEC_K_DOWN, l);
   }
-
-  const bool want_logits = st->logits_out || st->argmax_out;
-  if (want_logits) {
-    void* lg = st->logits_out ? st->logits_out : c->logits;
-    const int lt = k.lm_head_dtype == QDEC_F32 ? W_F32 : k.lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
-    GemvArgs h{};
-    h.w = c->lm.data;
-    h.scale = c->lm.scale;
-    h.x = c->x;
-    h.gamma = c->final_norm;
-    h.eps = k.rms_eps;
-    h.round_h = ab;
-    h.y = lg;
-    h.y_bf16 = c->io_bf16();
-    h.hidden_copy = st->hidden_out;
-    if (st->argmax_out) {
-      h.part_val = c->am_val;
-      h.part_idx = c->am_idx;
-    }
-    h.n = k.vocab;
-    h.k = d;
-    LAUNCH(QDEC_K_LM_HEAD, launch_gemv(lt, EPI_STORE, true, h, s));
-    if (st->argmax_out)
-      LAUNCH(QDEC_K_ARGMAX,
-             launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, st->argmax_out, s));
+  if (st->logits_out || st->argmax_out) {
+    LAUNCH(QDEC_K_LM_HEAD, 0);
+    if (st->argmax_out) LAUNCH(QDEC_K_ARGMAX, 0);
   } else if (st->hidden_out) {
-    if ((rs = c->hip(launch_copy(st->hidden_out, c->x, d * 4, s), "hidden copy")) != QDEC_OK)
+    if ((rs = c->hip(launch_copy(st->hidden_out, c->x, c->cfg.hidden * 4, s), "hidden copy")) !=
+        QDEC_OK)
       return rs;
   }
 #undef LAUNCH
@@ -996,6 +1019,31 @@ QDEC_API qdec_status qdec_profile_collect(qdec_ctx* c, double* ms, int64_t* laun
   for (int k = 0; k < QDEC_K_COUNT; ++k) {
     if (ms) ms[k] = c->prof_ms[k];
     if (launches) launches[k] = c->prof_n[k];
+  }
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_profile_kernel(qdec_ctx* c, int32_t kclass, int32_t layer, int32_t reps,
+                                         const qdec_step* st, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (kclass < QDEC_K_QKV || kclass > QDEC_K_ARGMAX)
+    return fail(&c->err, QDEC_E_INVAL, "kernel class %d cannot be replayed alone", kclass);
+  if (layer < -1 || layer >= c->cfg.n_layers || reps < 1)
+    return fail(&c->err, QDEC_E_INVAL, "bad layer or repetition count");
+  qdec_status r = check_step(c, st, true);
+  if (r != QDEC_OK) return r;
+  if ((kclass == QDEC_K_LM_HEAD || kclass == QDEC_K_ARGMAX) && !st->argmax_out && !st->logits_out)
+    return fail(&c->err, QDEC_E_INVAL, "the LM head needs logits_out or argmax_out");
+  if (kclass == QDEC_K_ARGMAX && !st->argmax_out)
+    return fail(&c->err, QDEC_E_INVAL, "argmax needs argmax_out");
+  if (kclass == QDEC_K_ROPE_APPEND)
+    return fail(&c->err, QDEC_E_INVAL, "Q/K norm, RoPE and append run inside the attention kernel");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  const int np = n_parts_for(st->pos + 1, c->part_tokens);
+  for (int i = 0; i < reps; ++i) {
+    const int l = layer >= 0 ? layer : i % c->cfg.n_layers;
+    if ((r = c->hip(launch_class(c, st, kclass, l, np, s), "profiled kernel")) != QDEC_OK) return r;
   }
   return QDEC_OK;
 }

@@ -86,6 +86,7 @@ _SIGS = {
     "qdec_device_error": [_P, C.POINTER(_I32), _P],
     "qdec_profile_enable": [_P, _I32],
     "qdec_profile_collect": [_P, C.POINTER(C.c_double), C.POINTER(_I64)],
+    "qdec_profile_kernel": [_P, _I32, _I32, _I32, C.POINTER(qdec_step), _P],
     "qdec_op_gemv": [_P, _I32, _P, _P, _I32, _P, _I32, _I64, _I64, _P],
     "qdec_op_quantize_rows": [_P, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
@@ -285,6 +286,10 @@ def qdec_profile_collect(ctx):
     n = (C.c_int64 * K_COUNT)()
     _call("qdec_profile_collect", ctx, ms, n, ctx=ctx)
     return {K_NAMES[i]: (ms[i], n[i]) for i in range(K_COUNT)}
+
+
+def qdec_profile_kernel(ctx, kclass, layer, reps, step: qdec_step, stream=None):
+    _call("qdec_profile_kernel", ctx, kclass, layer, reps, C.byref(step), _p(stream), ctx=ctx)
 
 
 # ---- op-level entry points ------------------------------------------------------------------------------

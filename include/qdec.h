@@ -287,6 +287,19 @@ qdec_status qdec_profile_enable(qdec_ctx* ctx, int32_t enable);
  * for each class k < QDEC_K_COUNT (either pointer may be NULL). */
 qdec_status qdec_profile_collect(qdec_ctx* ctx, double* ms, int64_t* launches);
 
+/* Enqueues `reps` launches of one kernel class of the step (QDEC_K_QKV .. QDEC_K_ARGMAX, not
+ * QDEC_K_EMBED or QDEC_K_ROPE_APPEND) exactly as qdec_decode_step launches it for `layer` with
+ * the buffers and pos of `step` (same arguments, grid and data; the kernels read pos from the
+ * step descriptor the last embedding kernel wrote, so run a step at the same pos first).
+ * layer = -1 cycles through the layers (launch i uses layer i % n_layers), so consecutive
+ * launches read different weights and KV pools, as in a step, instead of finding the previous
+ * launch's data in the caches.  Meant for timing one kernel in isolation, for example inside a
+ * captured graph.  Side effects are those of repeating the kernel: O and down projections add
+ * into the residual stream on every launch, and the attention kernel re-appends the K/V row of
+ * pos.  QDEC_E_INVAL for a bad class, layer < -1, layer >= n_layers or reps < 1. */
+qdec_status qdec_profile_kernel(qdec_ctx* ctx, int32_t kclass, int32_t layer, int32_t reps,
+                                const qdec_step* step, void* stream);
+
 /* ---- op-level entry points on caller-owned device buffers ---------------------------------- */
 
 /* y = W x for one row-major matrix ([Qwen3-runtime] §4.1: M = 1 is a GEMV; §13.1 W8A16).
