@@ -13,7 +13,6 @@ the roofline of the dominant kernel (event-timed live, per launch), per-kernel t
 check of the timed step against the CPU oracle, and the oracle's own rate on the host CPU.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -24,11 +23,6 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs peak (Qwen3-0.6B shape, 4K ctx)"
-KERNEL_SOURCES = {  # kernel class -> source file whose change invalidates stored counters
-    "qkv": "gemv.hip", "o_proj": "gemv.hip", "gate_up": "gemv.hip", "down": "gemv.hip",
-    "lm_head": "gemv.hip", "attention": "attention.hip", "merge": "attention.hip",
-    "rope_append": "misc.hip", "embed": "misc.hip", "argmax": "misc.hip",
-}
 
 
 def parse():
@@ -42,18 +36,17 @@ def parse():
                    help="activation precision at op boundaries (default f32 for bf16 weights, "
                         "bf16 for w8a16)")
     p.add_argument("--ctx", type=int, default=None, help="context T (default 4096 / 8192 for 8b)")
+    p.add_argument("--partition", type=int, default=0,
+                   help="split-KV partition length in tokens (multiple of 16; 0 = automatic)")
     p.add_argument("--profile-steps", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall-clock budget of the CPU-oracle baseline (0 disables it)")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run the library's copy kernel on 1 GiB (counter calibration)")
+    p.add_argument("--eager-only", type=int, default=0, metavar="N",
+                   help="only set up the workload and run N eager steps (for counter passes)")
     return p.parse_args()
-
-
-def sha_of(fname):
-    with open(os.path.join(ROOT, "decode_step_04_amd", "csrc", fname), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def load_traffic(kclass, workload):
@@ -64,8 +57,11 @@ def load_traffic(kclass, workload):
         return None
     with open(path) as f:
         tab = json.load(f)
+    from decode_step_04_amd import profiling
+
     ent = tab.get(workload, {}).get(kclass)
-    if not ent or ent.get("source_sha") != sha_of(KERNEL_SOURCES[kclass]):
+    if not ent or kclass not in profiling.KERNEL_SOURCES or \
+            ent.get("source_sha") != profiling.source_sha(kclass):
         return None
     return ent["bytes_per_launch"]
 
@@ -111,9 +107,10 @@ def main():
     dev = "cuda"
     n_pages = (T + 15) // 16
     cfg = loader.config_for(shape, path=args.path, num_pages=n_pages, max_context=T,
-                            act=args.act)
+                            partition_size=args.partition, act=args.act)
     act_name = "bf16" if cfg.act_dtype == Q.BF16 else "f32"
     ctx = Q.qdec_create(cfg, 0)
+    part_tokens = Q.qdec_info_get(ctx).partition_tokens
     w = synth.bf16_model(shape, seed=0, device=dev)
     loader.upload_weights(ctx, w, dev)
     table = synth.block_table(n_pages, n_pages, seed=2)
@@ -128,6 +125,13 @@ def main():
     pos = T - 1
     step = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax)
     torch.cuda.synchronize()
+    if args.eager_only:
+        for _ in range(args.eager_only):
+            Q.qdec_decode_step(ctx, step)
+        torch.cuda.synchronize()
+        Q.qdec_destroy(ctx)
+        print(json.dumps({"eager_steps": args.eager_only, "argmax": int(amax.item())}))
+        return
 
     # eager warm-up, then capture the step into a graph
     for _ in range(3):
@@ -266,7 +270,8 @@ def main():
                                "weights, bf16 KV, graph replay",
                    "context": T, "batch": 1, "weights": args.path, "kv_cache": "bf16",
                    "activations": act_name,
-                   "page_size": 16, "block_table": "random permutation",
+                   "page_size": 16, "partition_tokens": part_tokens,
+                   "block_table": "random permutation",
                    "parallelism": "single GPU"},
         "hbm_gbps": round(bm.total / graph_s / 1e9, 1),
         "hbm_frac": round(bm.total / graph_s / 1e9 / PEAK_HBM_GBPS, 4),
