@@ -3,9 +3,15 @@
 Recipe: random-init weights N(0, 0.02) stored bf16 (seed 0), gammas 1 + N(0, 0.1), KV positions
 0..4094 pre-filled with N(0, 1) bf16 values through a random permutation of the 256 pool pages,
 one token id drawn uniformly; a decode step at pos T-1 for T in 512, 2048, 4096.
-Bar (bf16 / W8A16 path): hidden-state relative L2 <= 1.5e-2 and logits max-abs <= 5e-2; the
-GPU's greedy id must be a maximiser of the oracle's logits up to bf16 rounding; int8 codes and
-scales bit-exact; graph replay bit-identical to the eager step.
+Bar with fp32 activations (bf16 and int8 as storage formats only): hidden-state relative L2
+<= 1e-4 (fp32 accumulation against fp64, ~1e-6 measured) and every logit within one bf16 spacing
+of the oracle's (2^-7 |logit|, plus 1e-5 of the largest logit for values near zero), since both
+sides round the same near-identical fp32 value to bf16.  Bar with bf16 activations at op
+boundaries: hidden relative L2 <= 1.5e-2 and logits max-abs <= 5e-2 (each bf16 rounding of an
+activation that differs by d before rounding leaves a difference of order sqrt(d * ulp), so the
+two sides drift apart by ~1e-2 however closely their arithmetic agrees).  In both cases the GPU's
+greedy id must be a maximiser of the oracle's logits up to bf16 rounding; int8 codes and scales
+bit-exact; graph replay bit-identical to the eager step.
 """
 import numpy as np
 import pytest
@@ -75,15 +81,19 @@ class Setup:
         Q.qdec_destroy(self.ctx)
 
 
-def _check(got, ref):
+def _check(got, ref, act):
     gh, gl, ga = got
     rh, rl, ra = ref
     rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
     lmax = np.max(np.abs(gl - rl))
     print(f"hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle {ra}",
           flush=True)
-    assert rel <= 1.5e-2
-    assert lmax <= 5e-2
+    if act == "f32":
+        assert rel <= 1e-4
+        assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max())
+    else:
+        assert rel <= 1.5e-2
+        assert lmax <= 5e-2
     assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
 
 
@@ -117,7 +127,7 @@ def test_step_matches_oracle(path, act, T):
     s = setup(path, act)
     got = s.step(T - 1)
     ref = s.om.step(T - 1, token=s.tok_id)
-    _check(got, ref)
+    _check(got, ref, act)
 
 
 def test_graph_replay_bit_identical():
