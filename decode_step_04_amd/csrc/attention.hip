@@ -72,22 +72,41 @@ __device__ __forceinline__ void widen16(const uint4 w, float (&f)[EPL]) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Per-head RMSNorm (gamma may be null) and rotate-half RoPE of one D-vector by one wave; lane l
-// holds the pair (x0, x1) = (v[l], v[l + D/2]) (zeros for l >= D/2) and gets the rotated pair.
+// Per-head RMSNorm (when `norm`) and rotate-half RoPE of one D-vector by one wave; lane l holds
+// the pair (x0, x1) = (v[l], v[l + D/2]) and its gammas (g0, g1) (zeros for l >= D/2) and gets
+// the rotated pair.
+// Branch-free, so that the compiler keeps the gamma loads where they are issued.
 template <int D>
-__device__ __forceinline__ void norm_rope(float x0, float x1, const float* gamma, float eps,
-                                          float2 cs, int lane, float& y0, float& y1) {
-  constexpr int HALF = D / 2;
-  if (gamma != nullptr) {
-    const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
-    const float rinv = 1.0f / sqrtf(ss / (float)D + eps);
-    if (lane < HALF) {
-      x0 = x0 * rinv * gamma[lane];
-      x1 = x1 * rinv * gamma[lane + HALF];
-    }
-  }
+__device__ __forceinline__ void norm_rope(float x0, float x1, bool norm, float g0, float g1,
+                                          float eps, float2 cs, float& y0, float& y1) {
+  const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+  const float rinv = norm ? __builtin_amdgcn_rsqf(ss / (float)D + eps) : 1.0f;
+  x0 = norm ? x0 * rinv * g0 : x0;
+  x1 = norm ? x1 * rinv * g1 : x1;
   y0 = x0 * cs.x - x1 * cs.y;
   y1 = x1 * cs.x + x0 * cs.y;
+}
+
+// Merges the (m, l, acc) states of the lane pairs (l, l ^ OFF): M = max, each side rescaled by
+// 2^(m - M).  Both lanes of a pair end with the same merged state.
+template <int OFF, int G, int EPL>
+__device__ __forceinline__ void combine_rows(float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float ma, mb, la, lb;
+    lane_pair<OFF>(m[h], ma, mb);
+    lane_pair<OFF>(l[h], la, lb);
+    const float mx = fmaxf(ma, mb);
+    const float ca = fast_exp2(ma - mx), cb = fast_exp2(mb - mx);
+    l[h] = fmaf(la, ca, lb * cb);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float aa, ab;
+      lane_pair<OFF>(acc[h][e], aa, ab);
+      acc[h][e] = fmaf(aa, ca, ab * cb);
+    }
+    m[h] = mx;
+  }
 }
 
 template <int D, bool KVB, int G, bool FUSED>
@@ -110,54 +129,84 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int ppp = part / kPage;                  // pages per partition
   const int pg_first = pi * ppp;
 
-  // ---- independent loads: block-table entries, ctx, the QKV rows of the prologue ----
+  // ---- independent loads: block-table entries, ctx, the QKV rows of the prologue.  Every load
+  //      of the kernel is issued unconditionally (an unused one reads a valid clamped address and
+  //      its value is discarded): loads complete in order, and with no load under a branch each
+  //      wait the compiler inserts covers exactly the loads its consumer needs ----
   int phys[NPH];
   const int npw = (ppp + 3 - wave) / 4;          // pages of this wave in a full partition
 #pragma unroll
   for (int j = 0; j < NPH; ++j) {
     const int idx = pg_first + wave + 4 * j;
-    phys[j] = (j < npw && idx < a.bt_len) ? a.block_table[idx] : 0;
+    const bool ok = j < npw && idx < a.bt_len;   // bt_len >= 1: entry 0 always exists
+    const int v = a.block_table[ok ? idx : 0];
+    phys[j] = ok ? v : 0;
   }
-  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
-  float qx0[2] = {0.f, 0.f}, qx1[2] = {0.f, 0.f};  // this wave's query heads (h = wave, wave+4)
+  constexpr int QP = (G * D + 255) / 256;        // op path: query values per thread
+  float qx0[2], qx1[2];                          // fused path: this wave's query heads (wave, wave+4)
   float kx0 = 0.f, kx1 = 0.f, vx0 = 0.f, vx1 = 0.f;
+  float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;  // Q/K-norm gammas of this lane's pair
+  float qop[QP];
+  const bool qk_norm = a.q_gamma != nullptr;
+  const int hl = lane & (HALF - 1);              // lanes >= D/2 read lane - D/2, then zero it
+  const bool lo_half = lane < HALF;
+  float2 cs = make_float2(1.f, 0.f);              // (cos, sin) of this lane's pair at pos
   if constexpr (FUSED) {
-    if (lane < HALF) {
+    cs = reinterpret_cast<const float2*>(a.rope_step)[hl];
+    const float* gqs = qk_norm ? a.q_gamma : a.qkv;
+    const float* gks = qk_norm ? a.k_gamma : a.qkv;
+    gq0 = gqs[hl];
+    gq1 = gqs[hl + HALF];
+    gk0 = gks[hl];
+    gk1 = gks[hl + HALF];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int h = wave + 4 * t;
-        if (h < G) {
-          const float* src = a.qkv + (int64_t)(g * G + h) * D;
-          qx0[t] = src[lane];
-          qx1[t] = src[lane + HALF];
-        }
-      }
-      if (wave == 3) {
-        const float* ks = a.qkv + (int64_t)(a.n_q_heads + g) * D;
-        const float* vs = a.qkv + (int64_t)(a.n_q_heads + hkv + g) * D;
-        kx0 = ks[lane];
-        kx1 = ks[lane + HALF];
-        vx0 = vs[lane];
-        vx1 = vs[lane + HALF];
-      }
+    for (int t = 0; t < 2; ++t) {
+      const int h = wave + 4 * t;
+      const float* src = a.qkv + (int64_t)(g * G + (h < G ? h : 0)) * D;
+      qx0[t] = src[hl];
+      qx1[t] = src[hl + HALF];
+    }
+    const float* ks = a.qkv + (int64_t)(a.n_q_heads + g) * D;
+    const float* vs = a.qkv + (int64_t)(a.n_q_heads + hkv + g) * D;
+    kx0 = ks[hl];
+    kx1 = ks[hl + HALF];
+    vx0 = vs[hl];
+    vx1 = vs[hl + HALF];
+  } else {
+#pragma unroll
+    for (int t = 0; t < QP; ++t) {
+      const int i = threadIdx.x + 256 * t;
+      const int idx = g * G * D + (i < G * D ? i : 0);
+      qop[t] = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[idx])
+                        : static_cast<const float*>(a.q)[idx];
     }
   }
+  // the context length last: scalar loads are waited for all at once, so the loads above are
+  // issued before the wait for this one
+  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
   const int pos = ctx - 1;
   const int np = n_parts_for(ctx, part);
-  if (pi >= np) return;
+  // Surplus partitions (a graph captured for a longer context) run through with empty ranges
+  // and store nothing; returning early instead would let the compiler move the loads above
+  // below that branch, behind the context load.
+  const bool live = pi < np;
   const int tok0 = pi * part;
   const int tok1 = min(ctx, tok0 + part);
   const int pg1 = (tok1 + kPage - 1) / kPage;    // one past the last page of the partition
   const bool has_new = FUSED && (pos >= tok0) && (pos < tok1);
 
-  // ---- first page tile of this wave, requested before the prologue ----
+  // ---- the page of the new token, then this wave's first page tile (page 0's when the wave has
+  //      none; those values are never used) ----
+  int64_t phys_new = 0;
+  if constexpr (FUSED) phys_new = a.block_table[pos / kPage];
   const int64_t tile_bytes = (int64_t)kPage * D * ELEM;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   uint4 kw[NI], vw[NI];
   int pg = pg_first + wave;
-  if (pg < pg1) {
-    const int64_t tile = ((int64_t)phys[0] * hkv + g) * tile_bytes;
+  {
+    // a surplus partition reads page 0 of head 0 (cached after the first), not HBM
+    const int64_t tile = live ? ((int64_t)phys[0] * hkv + g) * tile_bytes : 0;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
       kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
@@ -165,57 +214,59 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int i = 0; i < NI; ++i)
       vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
   }
+  if (!lo_half) {
+    qx0[0] = qx1[0] = qx0[1] = qx1[1] = 0.f;
+    kx0 = kx1 = vx0 = vx1 = 0.f;
+    gq0 = gq1 = gk0 = gk1 = 0.f;
+    cs = make_float2(1.f, 0.f);
+  }
 
-  // ---- prologue: query heads (and the new K/V) into LDS ----
+  // ---- prologue: query heads (and the new K/V) into LDS.  Every wave computes every norm and
+  //      rotation (cheap) and stores only what it owns: with the values used unconditionally the
+  //      compiler keeps their loads ahead of the page loads, instead of moving them into the
+  //      branch that would use them ----
   if constexpr (FUSED) {
-    const float2 cs = (lane < HALF)
-                          ? reinterpret_cast<const float2*>(a.rope_table)[(int64_t)pos * HALF + lane]
-                          : make_float2(1.f, 0.f);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int h = wave + 4 * t;
-      if (h < G) {
-        float y0, y1;
-        norm_rope<D>(qx0[t], qx1[t], a.q_gamma, a.eps, cs, lane, y0, y1);
-        if (lane < HALF) {
-          if (a.round_q) {
-            y0 = round_bf16(y0);
-            y1 = round_bf16(y1);
-          }
-          sq[h][lane] = y0 * a.qscale;
-          sq[h][lane + HALF] = y1 * a.qscale;
-        }
+      float y0, y1;
+      norm_rope<D>(qx0[t], qx1[t], qk_norm, gq0, gq1, a.eps, cs, y0, y1);
+      if (a.round_q) {
+        y0 = round_bf16(y0);
+        y1 = round_bf16(y1);
+      }
+      if (h < G && lane < HALF) {
+        sq[h][lane] = y0 * a.qscale;
+        sq[h][lane + HALF] = y1 * a.qscale;
       }
     }
-    if (has_new && wave == 3) {
-      float y0, y1;
-      norm_rope<D>(kx0, kx1, a.k_gamma, a.eps, cs, lane, y0, y1);
-      if (lane < HALF) {
-        float v0 = vx0, v1 = vx1;
-        const int64_t phys_new = a.block_table[pos / kPage];
-        const int64_t off = ((phys_new * hkv + g) * kPage + pos % kPage) * D + lane;
-        if constexpr (KVB) {
-          y0 = round_bf16(y0); y1 = round_bf16(y1); v0 = round_bf16(v0); v1 = round_bf16(v1);
-          uint16_t* kp = static_cast<uint16_t*>(a.k_pool);
-          uint16_t* vp = static_cast<uint16_t*>(a.v_pool);
-          kp[off] = f32_to_bf16(y0); kp[off + HALF] = f32_to_bf16(y1);
-          vp[off] = f32_to_bf16(v0); vp[off + HALF] = f32_to_bf16(v1);
-        } else {
-          float* kp = static_cast<float*>(a.k_pool);
-          float* vp = static_cast<float*>(a.v_pool);
-          kp[off] = y0; kp[off + HALF] = y1;
-          vp[off] = v0; vp[off + HALF] = v1;
-        }
-        skv[0][lane] = y0; skv[0][lane + HALF] = y1;
-        skv[1][lane] = v0; skv[1][lane + HALF] = v1;
+    float y0, y1;
+    norm_rope<D>(kx0, kx1, qk_norm, gk0, gk1, a.eps, cs, y0, y1);
+    float v0 = vx0, v1 = vx1;
+    if constexpr (KVB) {
+      y0 = round_bf16(y0); y1 = round_bf16(y1); v0 = round_bf16(v0); v1 = round_bf16(v1);
+    }
+    if (has_new && wave == 3 && lane < HALF) {
+      const int64_t off = ((phys_new * hkv + g) * kPage + pos % kPage) * D + lane;
+      if constexpr (KVB) {
+        uint16_t* kp = static_cast<uint16_t*>(a.k_pool);
+        uint16_t* vp = static_cast<uint16_t*>(a.v_pool);
+        kp[off] = f32_to_bf16(y0); kp[off + HALF] = f32_to_bf16(y1);
+        vp[off] = f32_to_bf16(v0); vp[off + HALF] = f32_to_bf16(v1);
+      } else {
+        float* kp = static_cast<float*>(a.k_pool);
+        float* vp = static_cast<float*>(a.v_pool);
+        kp[off] = y0; kp[off + HALF] = y1;
+        vp[off] = v0; vp[off + HALF] = v1;
       }
+      skv[0][lane] = y0; skv[0][lane + HALF] = y1;
+      skv[1][lane] = v0; skv[1][lane + HALF] = v1;
     }
   } else {
-    for (int i = threadIdx.x; i < G * D; i += 256) {
-      const int idx = g * G * D + i;
-      const float v = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[idx])
-                               : static_cast<const float*>(a.q)[idx];
-      sq[i / D][i % D] = v * a.qscale;
+#pragma unroll
+    for (int t = 0; t < QP; ++t) {
+      const int i = threadIdx.x + 256 * t;
+      if (i < G * D) sq[i / D][i % D] = qop[t] * a.qscale;
     }
   }
   __syncthreads();
@@ -249,25 +300,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       for (int i = 0; i < NI; ++i)
         vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
     }
+    // scores from K first; V is still arriving (loads complete in order)
     float s[G][NI];
-    float kf[NI][EPL], vf[NI][EPL];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      widen16<KVB, EPL>(kw[i], kf[i]);
-      widen16<KVB, EPL>(vw[i], vf[i]);
+      float kf[EPL];
+      widen16<KVB, EPL>(kw[i], kf);
       const int tok = pg * kPage + i * TPI + trow;
       if (has_new && tok == pos) {  // the appended slot: use the values just computed
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          kf[i][e] = skv[0][dsub + e];
-          vf[i][e] = skv[1][dsub + e];
-        }
+        for (int e = 0; e < EPL; ++e) kf[e] = skv[0][dsub + e];
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float p = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[i][e], p);
+        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
         p = lanes_sum<LPT>(p);
         s[h][i] = (tok < tok1) ? p : -INFINITY;
       }
@@ -283,33 +331,31 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const float p = fast_exp2(s[h][i] - mx);
-        l[h] += p;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(p, vf[i][e], acc[h][e]);
+        s[h][i] = fast_exp2(s[h][i] - mx);
+        l[h] += s[h][i];
       }
       m[h] = mx;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float vf[EPL];
+      widen16<KVB, EPL>(vw[i], vf);
+      const int tok = pg * kPage + i * TPI + trow;
+      if (has_new && tok == pos) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = skv[1][dsub + e];
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[h][i], vf[e], acc[h][e]);
     }
   }
 
   // combine the token rows of the wave (lanes with equal dims), exact rescaling
-#pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float mx = fmaxf(m[h], mo);
-      const float ca = fast_exp2(m[h] - mx), cb = fast_exp2(mo - mx);
-      l[h] = l[h] * ca + lo * cb;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float ao = __shfl_xor(acc[h][e], off);
-        acc[h][e] = acc[h][e] * ca + ao * cb;
-      }
-      m[h] = mx;
-    }
-  }
+  if constexpr (LPT <= 8) combine_rows<8, G, EPL>(m, l, acc);
+  if constexpr (LPT <= 16) combine_rows<16, G, EPL>(m, l, acc);
+  combine_rows<32, G, EPL>(m, l, acc);
   if (trow == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -337,7 +383,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       O = fmaf(sm_acc[w][h][r], c, O);
     }
     const int hq = g * G + h;
-    if (np == 1) {
+    if (!live) {
+      // nothing to store
+    } else if (np == 1) {
       const float o = O / L;
       if (a.out_bf16)
         static_cast<uint16_t*>(a.out)[hq * D + r] = f32_to_bf16(o);
@@ -355,38 +403,56 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 }
 
 // One single-wave work-group per (query head, block of 32 dims): lanes 0-31 and 32-63 take the
-// even and odd partitions of 32 consecutive dims.  The accumulator loads do not depend on the
-// weights, so they are all in flight while the (m, l) pairs are reduced.  Dynamic LDS: one
-// weight per partition.
+// even and odd partitions of 32 consecutive dims.  The (m, l) pairs of the first 64 partitions
+// and their accumulators are requested before the context length is known (every address below
+// max_parts is valid scratch; entries at or past the step's partition count hold stale values
+// and are never combined), so the merge costs one memory round trip after launch.  Dynamic LDS:
+// one weight per partition.
 template <int D>
 __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
+  constexpr int PF = 32;  // prefetched accumulators per lane (64 partitions)
   extern __shared__ float wts[];  // [np] weights 2^(m_p - M)
-  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
-  const int np = n_parts_for(ctx, a.part_tokens);
-  if (np <= 1) return;  // the partition kernel wrote the output itself
   const int hq = blockIdx.x;
   const int lane = threadIdx.x;
   const int dim = blockIdx.y * 32 + (lane & 31);
   const int half = lane >> 5;
-  const int64_t base = (int64_t)hq * a.max_parts;
-  float mloc = -1e30f;
-  for (int p = lane; p < np; p += 64) {
-    const float mp = a.part_ml[(base + p) * 2];
-    wts[p] = mp;
-    mloc = fmaxf(mloc, mp);
+  const int maxp = a.max_parts;
+  const int64_t base = (int64_t)hq * maxp;
+  const int pl = lane < maxp ? lane : 0;
+  const float m0 = a.part_ml[(base + pl) * 2];
+  const float l0 = a.part_ml[(base + pl) * 2 + 1];
+  float pre[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int p = half + 2 * i;
+    pre[i] = a.part_acc[(base + (p < maxp ? p : 0)) * D + dim];
   }
+  const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
+  const int np = n_parts_for(ctx, a.part_tokens);
+  if (np <= 1) return;  // the partition kernel wrote the output itself
+  float mloc = lane < np ? m0 : -1e30f;
+  for (int p = lane + 64; p < np; p += 64) mloc = fmaxf(mloc, a.part_ml[(base + p) * 2]);
   const float M = wave_max(mloc);
   float lsum = 0.f;
-  for (int p = lane; p < np; p += 64) {
-    const float w = fast_exp2(wts[p] - M);
+  if (lane < np) {
+    const float w = fast_exp2(m0 - M);
+    wts[lane] = w;
+    lsum = l0 * w;
+  }
+  for (int p = lane + 64; p < np; p += 64) {
+    const float w = fast_exp2(a.part_ml[(base + p) * 2] - M);
     wts[p] = w;
     lsum = fmaf(a.part_ml[(base + p) * 2 + 1], w, lsum);
   }
   const float L = wave_sum(lsum);
   __syncthreads();
   float O = 0.f;
-#pragma unroll 16
-  for (int p = half; p < np; p += 2) O = fmaf(a.part_acc[(base + p) * D + dim], wts[p], O);
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int p = half + 2 * i;
+    if (p < np) O = fmaf(pre[i], wts[p], O);
+  }
+  for (int p = half + 2 * PF; p < np; p += 2) O = fmaf(a.part_acc[(base + p) * D + dim], wts[p], O);
   O += __shfl_xor(O, 32);
   if (half == 0) {
     const float o = O / L;

@@ -22,12 +22,12 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.  Branch-free.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
+  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
+  return (uint16_t)((nan ? (u | 0x00400000u) : r) >> 16);
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
@@ -82,6 +82,33 @@ __device__ __forceinline__ float wave_max(float v) {
                fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
+// The two values of the lane pair (l, l ^ OFF), OFF = 8, 16 or 32: `lo` from the lane with bit
+// OFF clear, `hi` from the lane with it set, identical on both lanes of the pair.  OFF = 8 uses
+// a DPP rotation by 8 inside each 16-lane row; 16 and 32 use the gfx950 lane-swap instructions
+// (v_permlane16_swap exchanges odd rows of its first operand with even rows of its second,
+// v_permlane32_swap the upper half of the first with the lower half of the second), so no
+// exchange goes through LDS.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
+  static_assert(OFF == 8 || OFF == 16 || OFF == 32, "pair distance");
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (OFF == 8) {
+    const float o = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+    const bool upper = (__lane_id() & 8) != 0;
+    lo = upper ? o : v;
+    hi = upper ? v : o;
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  }
+}
+
 // ---- split-KV partition sizing (shared by the host launcher and the kernels) -----------------
 // Fixed partitions when part_fixed > 0; otherwise the partition length grows with the context
 // so that Hkv * n_part stays near target_wgs work-groups, with a floor of 64 tokens.
@@ -133,6 +160,7 @@ struct AttnArgs {
   const float* k_gamma;
   float eps;
   const float* rope_table;    // [max_pos][D/2][2] (cos, sin)
+  const float* rope_step;     // [D/2][2]: the row of rope_table at this step's pos
   int32_t round_q;            // round the rotated query to bf16 (16-bit activations)
   // op path: the rotated query heads are given
   const void* q;              // [Hq x D] (bf16 or fp32)
@@ -177,6 +205,9 @@ struct EmbedArgs {
   const int32_t* token;       // device token id
   float* x;                   // [d] fp32 residual stream
   StepDesc* desc;             // written: pos, ctx (nullable)
+  const float* rope_table;    // [max_pos][half][2] (nullable)
+  float* rope_step;           // written: row pos of rope_table (the attention kernel reads it
+  int32_t rope_half;          // without waiting for the descriptor)
   int32_t pos;
   int32_t vocab;
   int32_t d;

@@ -9,20 +9,22 @@
 //
 // k_gemv: a work-group of 4 waves handles 4/SPLIT row groups per round; a row group is R output
 // rows (R gate + R up rows for SwiGLU, [Qwen3-runtime] §2.7) split along K over SPLIT waves.
-//   1. Every wave first issues the 16-byte loads of its rows' K-slice for the first round (lane l
-//      reads elements kslice + c*64*VEC + l*VEC .. +VEC of each row: one wave-wide load is a
-//      contiguous 1 KiB of a row), so HBM latency overlaps everything below.
-//   2. The work-group stages the input vector once in LDS (x * gamma when the RMSNorm prologue of
-//      [Qwen3-runtime] §2.1 is fused, with the sum of squares reduced on the way).  The LDS layout
-//      is interleaved per wave slice so that each lane's later 16-byte LDS reads are consecutive
-//      across the wave.
-//   3. Each wave copies its slice into registers (times rsqrt(mean + eps), rounded to bf16 when
-//      activations are 16-bit).
-//   4. Rounds: FMAs over the registers, a DPP + readlane reduction per row, a reduction over the
-//      SPLIT waves through LDS, and the epilogue: store (fp32 / bf16), residual add into the fp32
-//      stream, or silu(gate) * up.  With several rounds per work-group (the LM head), the next
-//      round's rows are requested before the current one is reduced, and the work-group keeps
-//      the running (max, lowest index) of its rounded outputs for the greedy argmax.
+//   1. Every wave first requests what does not depend on the weights: its K-slice of the input
+//      vector (and of gamma when the RMSNorm prologue of [Qwen3-runtime] §2.1 is fused) and the
+//      epilogue operands of its rows (residual values, int8 row scales).  Then it issues the
+//      16-byte loads of its rows' K-slice for the first round (lane l reads elements
+//      kslice + c*64*VEC + l*VEC .. +VEC of each row: one wave-wide load is a contiguous 1 KiB of
+//      a row).  Loads complete in order, so the input is ready -- and normalised, with the sum
+//      of squares reduced over the wave (and across the SPLIT waves of a group through LDS) --
+//      while the weights are still in flight.  Every load is unconditional (rows past the end
+//      are clamped to the last row, chunks past the slice to its start, results discarded), so
+//      each compiler-inserted wait covers exactly what its consumer needs.
+//   2. Rounds: FMAs over the registers, a DPP + readlane reduction per row, a reduction over the
+//      SPLIT waves through LDS, and the epilogue on lane r of row r: store (fp32 / bf16), the
+//      residual add (from the prefetched residual value), or silu(gate) * up.  With several
+//      rounds per work-group (the LM head), the next round's rows are requested before the
+//      current one is reduced, and each lane keeps the running (max, lowest index) of its rows'
+//      rounded outputs for the greedy argmax.
 #include "common.h"
 #include "launch.h"
 
@@ -80,29 +82,46 @@ __device__ __forceinline__ float dot16(uint4 w, const float* __restrict__ x, flo
   return acc;
 }
 
-// 4 consecutive input values starting at element k (fp32 or bf16 source), k % 4 == 0.
-__device__ __forceinline__ float4 load4(const void* x, int x_bf16, int64_t k) {
-  if (x_bf16) {
-    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + k);
-    return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-  }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(x) + k);
-}
-
 __device__ __forceinline__ bool argmax_better(float vb, int ib, float va, int ia) {
   if (ib < 0) return false;
   if (ia < 0) return true;
   return vb > va || (vb == va && ib < ia);
 }
 
-template <int WT, int EPI, bool NORM, int R, int MAXCH, bool PIPE>
+// VEC consecutive input values at element k (fp32, or bf16 when XB).
+template <bool XB, int VEC>
+__device__ __forceinline__ void load_vec(const void* x, int64_t k, float (&v)[VEC]) {
+  if constexpr (XB) {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + k;
+    if constexpr (VEC == 4) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p);
+      v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    } else {
+#pragma unroll
+      for (int j = 0; j < VEC / 8; ++j) {
+        const uint4 u = *reinterpret_cast<const uint4*>(p + 8 * j);
+        v[8 * j + 0] = bf16_lo(u.x); v[8 * j + 1] = bf16_hi(u.x);
+        v[8 * j + 2] = bf16_lo(u.y); v[8 * j + 3] = bf16_hi(u.y);
+        v[8 * j + 4] = bf16_lo(u.z); v[8 * j + 5] = bf16_hi(u.z);
+        v[8 * j + 6] = bf16_lo(u.w); v[8 * j + 7] = bf16_hi(u.w);
+      }
+    }
+  } else {
+    const float* p = static_cast<const float*>(x) + k;
+#pragma unroll
+    for (int j = 0; j < VEC / 4; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(p + 4 * j);
+      v[4 * j + 0] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+    }
+  }
+}
+
+template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = WTraits<WT>::VEC;
   constexpr int ELEM = WTraits<WT>::ELEM;
   constexpr int CH = kWave * VEC;                  // elements per wave-wide load
-  constexpr int NP = VEC / 4;                      // float4 pieces per lane per chunk
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * R : R;
-  extern __shared__ float4 xs4[];                  // interleaved input, see below
   __shared__ float red_ss[4];
   __shared__ float red_acc[4][NR];
   __shared__ float red_bv[4];
@@ -116,7 +135,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int K = (int)a.k;
   const int KW = K / split;                        // elements per slice
   const int kbase = sub * KW;
-  const int slice_f4 = ((KW + CH - 1) / CH) * CH / 4;  // LDS float4s per slice (whole chunks)
   const int64_t n = a.n;
   const int64_t ngroups = (n + R - 1) / R;
   const char* __restrict__ wbase = static_cast<const char*>(a.w);
@@ -130,103 +148,115 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
       const int kk = c * CH + lane * VEC;
-      if (kk < KW) {
+      const int kc = kbase + (kk < KW ? kk : 0);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t row = row_of(gg, r);
-          dst[r][c] = *reinterpret_cast<const uint4*>(wbase + row * row_bytes +
-                                                      (int64_t)(kbase + kk) * ELEM);
-          if constexpr (EPI == EPI_SWIGLU)
-            dst[R + r][c] = *reinterpret_cast<const uint4*>(wbase + (row + n) * row_bytes +
-                                                            (int64_t)(kbase + kk) * ELEM);
-        }
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = row_of(gg, r);
+        dst[r][c] = *reinterpret_cast<const uint4*>(wbase + row * row_bytes + (int64_t)kc * ELEM);
+        if constexpr (EPI == EPI_SWIGLU)
+          dst[R + r][c] = *reinterpret_cast<const uint4*>(wbase + (row + n) * row_bytes +
+                                                          (int64_t)kc * ELEM);
       }
     }
   };
-
-  // 1. first round's weights
-  const int64_t round0 = blockIdx.x;
-  int64_t g = round0 * gpw + grp;
-  uint4 wv[NR][MAXCH];
-  if (g < ngroups) load_rows(g, wv);
-
-  // 2. stage the input (x * gamma with the norm prologue) once per work-group.  Element k of
-  //    slice s, chunk c, lane l, piece j (k = s*KW + c*CH + l*VEC + 4j + t) lives in float4
-  //    s*slice_f4 + (c*NP + j)*64 + l, component t.
-  float ss = 0.f;
-  for (int q4 = tid; q4 < K / 4; q4 += 256) {
-    const int k = q4 * 4;
-    float4 v = load4(a.x, a.x_bf16, k);
-    if constexpr (NORM) {
-      ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
-      if (a.hidden_copy != nullptr && blockIdx.x == 0)
-        *reinterpret_cast<float4*>(a.hidden_copy + k) = v;
-      const float4 gm = *reinterpret_cast<const float4*>(a.gamma + k);
-      v.x *= gm.x; v.y *= gm.y; v.z *= gm.z; v.w *= gm.w;
+  // epilogue operands of lane r's row in group gg (lanes >= R read row 0 of the group)
+  auto load_epi = [&](int64_t gg, float& res, float& s1, float& s2) {
+    const int64_t row = row_of(gg, lane < R ? lane : 0);
+    if constexpr (EPI == EPI_RESID) res = a.resid[row];
+    if constexpr (WT == W_I8) {
+      s1 = a.scale[row];
+      if constexpr (EPI == EPI_SWIGLU) s2 = a.scale[row + n];
     }
-    const int s = k / KW, rem = k - s * KW;
-    const int c = rem / CH, r2 = rem - c * CH;
-    const int l = r2 / VEC, j = (r2 - l * VEC) / 4;
-    xs4[s * slice_f4 + (c * NP + j) * kWave + l] = v;
-  }
-  float rinv = 1.f;
-  if constexpr (NORM) {
-    ss = wave_sum(ss);
-    if (lane == 0) red_ss[wave] = ss;
-  }
-  __syncthreads();
-  if constexpr (NORM) {
-    const float tot = (red_ss[0] + red_ss[1]) + (red_ss[2] + red_ss[3]);
-    rinv = 1.0f / sqrtf(tot / (float)K + a.eps);
-  }
+  };
 
-  // 3. this wave's slice into registers
+  // 1. input slice (+ gamma), epilogue operands, then the first round's weights
   float xv[MAXCH][VEC];
+  float gv[NORM ? MAXCH : 1][VEC];
 #pragma unroll
   for (int c = 0; c < MAXCH; ++c) {
     const int kk = c * CH + lane * VEC;
+    const int64_t kc = kbase + (kk < KW ? kk : 0);
+    load_vec<XB, VEC>(a.x, kc, xv[c]);
+    if constexpr (NORM) load_vec<false, VEC>(a.gamma, kc, gv[c]);
+  }
+  const int64_t round0 = blockIdx.x;
+  int64_t g = round0 * gpw + grp;
+  float ep_res = 0.f, ep_s1 = 1.f, ep_s2 = 1.f;
+  load_epi(g, ep_res, ep_s1, ep_s2);
+  uint4 wv[NR][MAXCH];
+  load_rows(g, wv);
+
+  // 2. the input while the weights arrive: zero the chunks past the slice, copy the raw input
+  //    (work-group 0), normalise
 #pragma unroll
-    for (int j = 0; j < NP; ++j) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (kk < KW) v = xs4[sub * slice_f4 + (c * NP + j) * kWave + lane];
-      if constexpr (NORM) {
-        v.x *= rinv; v.y *= rinv; v.z *= rinv; v.w *= rinv;
-        if (a.round_h) {
-          v.x = round_bf16(v.x); v.y = round_bf16(v.y);
-          v.z = round_bf16(v.z); v.w = round_bf16(v.w);
+  for (int c = 0; c < MAXCH; ++c) {
+    const int kk = c * CH + lane * VEC;
+    if (kk >= KW) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) xv[c][e] = 0.f;
+    }
+  }
+  if constexpr (NORM) {
+    if (a.hidden_copy != nullptr && blockIdx.x == 0 && grp == 0) {
+#pragma unroll
+      for (int c = 0; c < MAXCH; ++c) {
+        const int kk = c * CH + lane * VEC;
+        if (kk < KW) {
+#pragma unroll
+          for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4*>(a.hidden_copy + kbase + kk + e) =
+                make_float4(xv[c][e], xv[c][e + 1], xv[c][e + 2], xv[c][e + 3]);
         }
       }
-      xv[c][4 * j + 0] = v.x; xv[c][4 * j + 1] = v.y;
-      xv[c][4 * j + 2] = v.z; xv[c][4 * j + 3] = v.w;
     }
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss = fmaf(xv[c][e], xv[c][e], ss);
+    ss = wave_sum(ss);
+    if (split > 1) {
+      if (lane == 0) red_ss[wave] = ss;
+      __syncthreads();
+      float t = 0.f;
+      for (int s2 = 0; s2 < split; ++s2) t += red_ss[grp * split + s2];
+      ss = t;
+    }
+    const float rinv = 1.0f / sqrtf(ss / (float)K + a.eps);
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        float v = xv[c][e] * gv[c][e] * rinv;
+        if (a.round_h) v = round_bf16(v);
+        xv[c][e] = v;
+      }
   }
 
   float best_v = -INFINITY;
   int best_i = -1;
   const bool want_argmax = a.part_val != nullptr;
 
-  // 4. rounds
+  // 3. rounds
   for (int64_t rnd = round0; rnd * gpw < ngroups; rnd += gridDim.x) {
     g = rnd * gpw + grp;
     const bool active = g < ngroups;
     uint4 wn[NR][MAXCH];
+    float nres = 0.f, ns1 = 1.f, ns2 = 1.f;
     if constexpr (PIPE) {
       const int64_t gn = (rnd + gridDim.x) * gpw + grp;
-      if (gn < ngroups) load_rows(gn, wn);
+      if (gn < ngroups) {
+        load_epi(gn, nres, ns1, ns2);
+        load_rows(gn, wn);
+      }
     }
     float acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-    if (active) {
 #pragma unroll
-      for (int c = 0; c < MAXCH; ++c) {
-        const int kk = c * CH + lane * VEC;
-        if (kk < KW) {
+    for (int c = 0; c < MAXCH; ++c)
 #pragma unroll
-          for (int r = 0; r < NR; ++r) acc[r] = dot16<WT>(wv[r][c], xv[c], acc[r]);
-        }
-      }
-    }
+      for (int r = 0; r < NR; ++r) acc[r] = dot16<WT>(wv[r][c], xv[c], acc[r]);
     float tot[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) tot[r] = wave_sum(acc[r]);
@@ -243,40 +273,40 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
       __syncthreads();  // red_acc is reused next round
     }
-    if (active && sub == 0) {
-      if constexpr (WT == W_I8) {
+    // lane r takes row r of the group
+    float vg = tot[0], vu = 0.f;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          tot[r] *= a.scale[row_of(g, r)];
-          if constexpr (EPI == EPI_SWIGLU) tot[R + r] *= a.scale[row_of(g, r) + n];
-        }
+    for (int r = 1; r < R; ++r)
+      if (lane == r) vg = tot[r];
+    if constexpr (EPI == EPI_SWIGLU) {
+      vu = tot[R];
+#pragma unroll
+      for (int r = 1; r < R; ++r)
+        if (lane == r) vu = tot[R + r];
+    }
+    const int64_t row = g * R + lane;
+    if (active && sub == 0 && lane < R && row < n) {
+      float v = vg;
+      if constexpr (WT == W_I8) v *= ep_s1;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const float u = (WT == W_I8) ? vu * ep_s2 : vu;
+        v = v / (1.0f + expf(-v)) * u;
       }
-      float outv = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float v = tot[r];
-        if constexpr (EPI == EPI_SWIGLU) v = tot[r] / (1.0f + expf(-tot[r])) * tot[R + r];
-        if (lane == r) outv = v;
+      if constexpr (EPI == EPI_RESID) {
+        a.resid[row] = ep_res + v;
+      } else {
+        if (a.y_bf16)
+          static_cast<uint16_t*>(a.y)[row] = f32_to_bf16(v);
+        else
+          static_cast<float*>(a.y)[row] = v;
         if constexpr (EPI == EPI_STORE) {
           if (want_argmax) {
-            const int64_t row = g * R + r;
             const float rv = a.y_bf16 ? round_bf16(v) : v;
-            if (row < n && rv == rv && (best_i < 0 || rv > best_v)) {
+            if (rv == rv && (best_i < 0 || rv > best_v)) {  // rows rise with the rounds
               best_v = rv;
               best_i = (int)row;
             }
           }
-        }
-      }
-      const int64_t row = g * R + lane;
-      if (lane < R && row < n) {
-        if constexpr (EPI == EPI_RESID) {
-          a.resid[row] += outv;
-        } else {
-          if (a.y_bf16)
-            static_cast<uint16_t*>(a.y)[row] = f32_to_bf16(outv);
-          else
-            static_cast<float*>(a.y)[row] = outv;
         }
       }
     }
@@ -285,11 +315,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int c = 0; c < MAXCH; ++c) wv[r][c] = wn[r][c];
+      ep_res = nres;
+      ep_s1 = ns1;
+      ep_s2 = ns2;
     }
   }
 
   if constexpr (EPI == EPI_STORE) {
     if (want_argmax) {  // a kernel argument: uniform over the work-group
+      // (max, lowest index) over the lanes of the wave, then over the waves
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const float ov = __shfl_xor(best_v, off);
+        const int oi = __shfl_xor(best_i, off);
+        if (argmax_better(ov, oi, best_v, best_i)) {
+          best_v = ov;
+          best_i = oi;
+        }
+      }
       if (lane == 0) {
         red_bv[wave] = best_v;
         red_bi[wave] = best_i;
@@ -323,7 +366,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 struct GemvPlan {
   int split, maxch, r;
   unsigned wgs;
-  size_t lds;
+  bool ok;  // every slice fits in 8 wave-wide chunks (the register-resident input)
 };
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
@@ -338,6 +381,7 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   GemvPlan p{};
   p.split = split;
   const int c = chunks(split);
+  p.ok = c <= 8 && k % vec == 0;
   p.maxch = c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
   // loads per lane in flight: 16, or 8 when the next round is prefetched (two sets of registers)
   const int budget = epi == EPI_STORE ? 8 : 16;
@@ -354,51 +398,57 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   int64_t wgs = (groups + gpw - 1) / gpw;
   if (epi == EPI_STORE && wgs > 1024) wgs = 1024;
   p.wgs = (unsigned)(wgs < 1 ? 1 : wgs);
-  const int64_t slice_f4 = ((k / split + ch - 1) / ch) * ch / 4;
-  p.lds = (size_t)(split * slice_f4 * 16);
   return p;
 }
 
-template <int WT, int EPI, bool NORM, int R, int MAXCH>
+template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH>
 static hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   constexpr bool PIPE = EPI == EPI_STORE;
   constexpr int loads = (EPI == EPI_SWIGLU ? 2 : 1) * R * MAXCH;
   if constexpr (loads > (PIPE ? 8 : 16)) {
     return hipErrorInvalidConfiguration;  // never planned: over the register budget
   } else {
-    hipLaunchKernelGGL((k_gemv<WT, EPI, NORM, R, MAXCH, PIPE>), dim3(p.wgs), dim3(256), p.lds, s,
+    hipLaunchKernelGGL((k_gemv<WT, EPI, NORM, XB, R, MAXCH, PIPE>), dim3(p.wgs), dim3(256), 0, s,
                        a);
     return hipGetLastError();
   }
 }
 
-template <int WT, int EPI, bool NORM, int R>
+template <int WT, int EPI, bool NORM, bool XB, int R>
 static hipError_t go_ch(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   switch (p.maxch) {
-    case 1: return go<WT, EPI, NORM, R, 1>(a, p, s);
-    case 2: return go<WT, EPI, NORM, R, 2>(a, p, s);
-    case 4: return go<WT, EPI, NORM, R, 4>(a, p, s);
-    default: return go<WT, EPI, NORM, R, 8>(a, p, s);
+    case 1: return go<WT, EPI, NORM, XB, R, 1>(a, p, s);
+    case 2: return go<WT, EPI, NORM, XB, R, 2>(a, p, s);
+    case 4: return go<WT, EPI, NORM, XB, R, 4>(a, p, s);
+    default: return go<WT, EPI, NORM, XB, R, 8>(a, p, s);
   }
 }
 
-template <int WT, int EPI, bool NORM>
+template <int WT, int EPI, bool NORM, bool XB>
 static hipError_t go_r(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   switch (p.r) {
-    case 4: return go_ch<WT, EPI, NORM, 4>(a, p, s);
-    case 2: return go_ch<WT, EPI, NORM, 2>(a, p, s);
-    default: return go_ch<WT, EPI, NORM, 1>(a, p, s);
+    case 4: return go_ch<WT, EPI, NORM, XB, 4>(a, p, s);
+    case 2: return go_ch<WT, EPI, NORM, XB, 2>(a, p, s);
+    default: return go_ch<WT, EPI, NORM, XB, 1>(a, p, s);
   }
 }
 
+// The norm prologue reads the fp32 residual stream; other inputs are fp32 or bf16.
 template <int WT>
 static hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
   const GemvPlan p = plan_gemv(WT, epi, a.n, a.k);
+  if (!p.ok) return hipErrorInvalidValue;
   a.split = p.split;
-  if (epi == EPI_STORE)
-    return norm ? go_r<WT, EPI_STORE, true>(a, p, s) : go_r<WT, EPI_STORE, false>(a, p, s);
-  if (epi == EPI_RESID) return go_r<WT, EPI_RESID, false>(a, p, s);
-  return go_r<WT, EPI_SWIGLU, true>(a, p, s);
+  const bool xb = a.x_bf16 != 0;
+  if (norm && xb) return hipErrorInvalidValue;
+  if (epi == EPI_STORE) {
+    if (norm) return go_r<WT, EPI_STORE, true, false>(a, p, s);
+    return xb ? go_r<WT, EPI_STORE, false, true>(a, p, s) : go_r<WT, EPI_STORE, false, false>(a, p, s);
+  }
+  if (epi == EPI_RESID)
+    return xb ? go_r<WT, EPI_RESID, false, true>(a, p, s) : go_r<WT, EPI_RESID, false, false>(a, p, s);
+  if (!norm) return hipErrorInvalidValue;
+  return go_r<WT, EPI_SWIGLU, true, false>(a, p, s);
 }
 
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s) {
@@ -412,6 +462,10 @@ hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStre
 
 int gemv_partials(int wtype, int epi, int64_t n, int64_t k) {
   return (int)plan_gemv(wtype, epi, n, k).wgs;
+}
+
+bool gemv_supported(int wtype, int epi, int64_t n, int64_t k) {
+  return n >= 1 && k >= 1 && plan_gemv(wtype, epi, n, k).ok;
 }
 
 }  // namespace qd

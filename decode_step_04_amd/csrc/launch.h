@@ -16,6 +16,9 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s);
 // Number of work-groups (= partial argmax slots) launch_gemv uses for this shape.
 int gemv_partials(int wtype, int epi, int64_t n, int64_t k);
+// Whether launch_gemv handles this shape: k a multiple of the 16-byte vector and each wave's
+// K-slice within 8 wave-wide loads (k <= 8192 fp32, 16384 bf16, 32768 int8 weights).
+bool gemv_supported(int wtype, int epi, int64_t n, int64_t k);
 // Final reduction of per-work-group (value, index) partials to the argmax.
 hipError_t launch_argmax_partials(const float* val, const int32_t* idx, int n, int32_t* out,
                                   hipStream_t s);

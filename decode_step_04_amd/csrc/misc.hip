@@ -97,6 +97,10 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
     a.desc->ctx = a.pos + 1;
     if (bad) a.desc->error = 1;
   }
+  if (a.rope_step != nullptr)
+    for (int i = tid; i < a.rope_half; i += 256)
+      reinterpret_cast<float2*>(a.rope_step)[i] =
+          reinterpret_cast<const float2*>(a.rope_table)[(int64_t)a.pos * a.rope_half + i];
   const void* src = a.emb ? a.emb : a.table;
   const int64_t base = a.emb ? 0 : (int64_t)tok * a.d;
   for (int i = tid; i < a.d; i += 256) {

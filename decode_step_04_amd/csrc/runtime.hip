@@ -100,6 +100,7 @@ struct qdec_ctx {
   int32_t* block_table = nullptr;
   int32_t n_logical = 0;
   float* rope = nullptr;
+  float* rope_step = nullptr;  // [D/2] (cos, sin) of the current step's pos
   float* x = nullptr;
   float* qkv = nullptr;
   void* attn = nullptr;
@@ -166,7 +167,7 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
     return fail(why, QDEC_E_UNSUPPORTED, "hidden (%d) and ffn (%d) must be multiples of 64",
                 c->hidden, c->ffn);
   if (c->hidden > 16384 || c->ffn > 16384)
-    return fail(why, QDEC_E_UNSUPPORTED, "hidden and ffn are limited to 16384 (LDS staging)");
+    return fail(why, QDEC_E_UNSUPPORTED, "hidden and ffn are limited to 16384");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(why, QDEC_E_UNSUPPORTED, "head_dim %d: only 64 and 128 are implemented",
                 c->head_dim);
@@ -212,6 +213,19 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if (model_max_parts(*c) > kMaxMergeParts)
     return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
                 kMaxMergeParts);
+  {
+    const int wp = c->proj_dtype == QDEC_F32 ? W_F32 : c->proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+    const int wl = c->lm_head_dtype == QDEC_F32 ? W_F32
+                   : c->lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+    const int64_t d = c->hidden, f = c->ffn, qd = (int64_t)c->n_q_heads * c->head_dim,
+                  nqkv = (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
+    if (!gemv_supported(wp, EPI_STORE, nqkv, d) || !gemv_supported(wp, EPI_RESID, d, qd) ||
+        !gemv_supported(wp, EPI_SWIGLU, f, d) || !gemv_supported(wp, EPI_RESID, d, f) ||
+        !gemv_supported(wl, EPI_STORE, c->vocab, d))
+      return fail(why, QDEC_E_UNSUPPORTED,
+                  "a projection's input length exceeds what the GEMV keeps in registers "
+                  "(8192 fp32, 16384 bf16, 32768 int8 values)");
+  }
   return QDEC_OK;
 }
 
@@ -403,6 +417,7 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   TRY(c->alloc(&c->block_table, (int64_t)c->bt_entries * 4, "block table"));
   TRY(c->hip(hipMemset(c->block_table, 0, (size_t)c->bt_entries * 4), "hipMemset block table"));
   TRY(c->alloc(&c->rope, (int64_t)cfg->max_context * (hd / 2) * 8, "RoPE table"));
+  TRY(c->alloc(&c->rope_step, (hd / 2) * 8, "RoPE row of the step"));
   TRY(c->alloc(&c->x, d * 4, "residual"));
   TRY(c->alloc(&c->qkv, (hq + 2 * hkv) * hd * 4, "qkv"));
   TRY(c->alloc(&c->attn, hq * hd * ae, "attention output"));
@@ -743,6 +758,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       at.k_gamma = ly.k_norm;
       at.eps = k.rms_eps;
       at.rope_table = c->rope;
+      at.rope_step = c->rope_step;
       at.round_q = ab;
       at.k_pool = ly.k_pool;
       at.v_pool = ly.v_pool;
@@ -868,6 +884,9 @@ static qdec_status enqueue_embed(qdec_ctx* c, const qdec_step* st, int pos, hipS
   e.token = st->token_id;
   e.x = c->x;
   e.desc = c->desc;
+  e.rope_table = c->rope;
+  e.rope_step = c->rope_step;
+  e.rope_half = c->cfg.head_dim / 2;
   e.pos = pos;
   e.vocab = c->cfg.vocab;
   e.d = c->cfg.hidden;
@@ -1064,10 +1083,13 @@ QDEC_API qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w
   if ((x_dtype != QDEC_F32 && x_dtype != QDEC_BF16) || (y_dtype != QDEC_F32 && y_dtype != QDEC_BF16))
     return fail(nullptr, QDEC_E_INVAL, "x/y dtype must be F32 or BF16");
   if (n < 1 || k < 1) return fail(nullptr, QDEC_E_INVAL, "n and k must be positive");
-  if (k > 16384) return fail(nullptr, QDEC_E_UNSUPPORTED, "k above 16384 (LDS staging)");
   if ((k * elem_size(w_dtype)) % 16) return fail(nullptr, QDEC_E_INVAL, "rows must be 16-byte multiples");
-  if (!aligned(w, 16) || !aligned(x, 4) || !aligned(y, 4) || (w_scale && !aligned(w_scale, 4)))
-    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer");
+  if (!gemv_supported(wt_of(w_dtype), EPI_STORE, n, k))
+    return fail(nullptr, QDEC_E_UNSUPPORTED,
+                "k = %lld exceeds what the GEMV keeps in registers (8192 fp32, 16384 bf16, "
+                "32768 int8 values)", (long long)k);
+  if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || (w_scale && !aligned(w_scale, 4)))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer (w and x 16-byte, y 4-byte)");
   GemvArgs a{};
   a.w = w;
   a.scale = w_scale;

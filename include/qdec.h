@@ -305,8 +305,10 @@ qdec_status qdec_profile_kernel(qdec_ctx* ctx, int32_t kclass, int32_t layer, in
 /* y = W x for one row-major matrix ([Qwen3-runtime] §4.1: M = 1 is a GEMV; §13.1 W8A16).
  * w: [n x k] of w_dtype (F32, BF16, or I8_ROW codes with w_scale = [n] fp32 row scales; w_scale
  * must be NULL otherwise).  x: [k] of x_dtype (F32 | BF16).  y: [n] of y_dtype (F32 | BF16, the
- * fp32 sum rounded to nearest even).  k must be a multiple of 16 / elem_size(w) and every
- * pointer 16-byte aligned. */
+ * fp32 sum rounded to nearest even).  k must be a multiple of 16 / elem_size(w) and at most
+ * 8192 (F32 weights), 16384 (BF16) or 32768 (I8_ROW): the kernel keeps each wave's slice of x
+ * in registers (QDEC_E_UNSUPPORTED beyond).  w and x 16-byte aligned, y and w_scale 4-byte
+ * aligned (QDEC_E_INVAL otherwise). */
 qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale, const void* x,
                          int32_t x_dtype, void* y, int32_t y_dtype, int64_t n, int64_t k,
                          void* stream);
