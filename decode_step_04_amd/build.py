@@ -15,7 +15,14 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqdec.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["gemv.hip", "attention.hip", "misc.hip", "runtime.hip"]
+# (source, object, extra flags): gemv.hip is built once per weight type and once for its
+# dispatcher, in parallel
+SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
+           ("gemv.hip", "gemv_bf16", ["-DQD_GEMV_PART=1"]),
+           ("gemv.hip", "gemv_i8", ["-DQD_GEMV_PART=2"]),
+           ("gemv.hip", "gemv_dispatch", ["-DQD_GEMV_PART=-1"]),
+           ("attention.hip", "attention", []), ("misc.hip", "misc", []),
+           ("runtime.hip", "runtime", [])]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-rdc",
@@ -25,9 +32,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry, verbose: bool) -> str:
+    src, name, extra = entry
+    obj = os.path.join(OUT_DIR, name + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

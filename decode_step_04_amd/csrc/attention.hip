@@ -28,7 +28,7 @@
 //   - Rows, then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With one partition
 //     the normalised output is written directly (the short path of §10.1); otherwise the
 //     unnormalised state goes to scratch for k_attn_merge.
-// k_attn_merge: one wave per (query head, 32 dims): M = max m_p, w_p = 2^(m_p - M),
+// k_attn_merge: one work-group per (query head, 32 dims): M = max m_p, w_p = 2^(m_p - M),
 // out = sum w_p acc_p / sum w_p l_p.
 //
 // Scores are kept in log2 units: q is pre-multiplied by log2(e)/sqrt(D), so exp(s - m) becomes
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   using Gm = Geo<D, KVB>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPI = Gm::TPI, NI = Gm::NI, ELEM = Gm::ELEM;
   constexpr int HALF = D / 2;
-  constexpr int NPH = 4;            // block-table entries per wave read ahead of ctx
+  constexpr int NPH = kMaxPartTokens / kPage / 4;  // block-table entries per wave, read ahead
   __shared__ float sq[G][D];        // scaled query heads
   __shared__ float skv[2][D];       // K and V of the new token (as stored)
   __shared__ float sm_acc[4][G][D];
@@ -202,18 +202,26 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int64_t tile_bytes = (int64_t)kPage * D * ELEM;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
-  uint4 kw[NI], vw[NI];
+  // pages are requested one ahead of the one being computed, in two alternating register sets
+  // (separate arrays: indexing one array by set would make the compiler move registers)
+  uint4 k0[NI], v0[NI], k1[NI], v1[NI];
+  int t0, t1;  // physical page of each set
   int pg = pg_first + wave;
-  {
-    // a surplus partition reads page 0 of head 0 (cached after the first), not HBM
-    const int64_t tile = live ? ((int64_t)phys[0] * hkv + g) * tile_bytes : 0;
+  const int gh = live ? g : 0;
+  // The address is computed from a page number chosen by a select (not a select of two
+  // addresses), so the compiler cannot fold a re-request into a copy of another set's registers.
+  auto request = [&](uint4 (&kd)[NI], uint4 (&vd)[NI], int& td, int ph) {
+    td = ph;
+    const int64_t tile = ((int64_t)ph * hkv + gh) * tile_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
+      kd[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
-  }
+      vd[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
+  };
+  // a surplus partition reads page 0 of head 0 (cached after the first), not HBM
+  request(k0, v0, t0, live ? phys[0] : 0);
   if (!lo_half) {
     qx0[0] = qx1[0] = qx0[1] = qx1[1] = 0.f;
     kx0 = kx1 = vx0 = vx1 = 0.f;
@@ -287,25 +295,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
 
-  for (int j = 0; pg < pg1; pg += 4, ++j) {
-    if (j > 0) {
-      // select chain instead of phys[j]: a runtime index would put the array in scratch memory
-      const int64_t ph = j == 1 ? phys[1] : j == 2 ? phys[2] : j == 3 ? phys[3]
-                                                                      : a.block_table[pg];
-      const int64_t tile = (ph * hkv + g) * tile_bytes;
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        kw[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        vw[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
-    }
+  // One page per step: request the wave's next page (on the last page the current one again,
+  // served by the caches, so that no load sits under a branch), then compute the current one.
+  // The two register sets alternate between the steps; copying an in-flight load's registers
+  // would make the compiler wait for it.
+  auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
+                       uint4 (&nv)[NI], int& tn, int ph1) {
+    request(nk, nv, tn, (pg + 4 < pg1) ? ph1 : tc);
     // scores from K first; V is still arriving (loads complete in order)
     float s[G][NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float kf[EPL];
-      widen16<KVB, EPL>(kw[i], kf);
+      widen16<KVB, EPL>(ck[i], kf);
       const int tok = pg * kPage + i * TPI + trow;
       if (has_new && tok == pos) {  // the appended slot: use the values just computed
 #pragma unroll
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       float vf[EPL];
-      widen16<KVB, EPL>(vw[i], vf);
+      widen16<KVB, EPL>(cv[i], vf);
       const int tok = pg * kPage + i * TPI + trow;
       if (has_new && tok == pos) {
 #pragma unroll
@@ -350,6 +352,19 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[h][i], vf[e], acc[h][e]);
     }
+    pg += 4;
+  };
+  // Fully unrolled over the at most NPH pages of the wave: every step's code follows the
+  // previous one's with no loop back-edge, so each wait counts exactly the loads in flight (a
+  // loop makes the compiler drain all loads before entering it).
+#pragma unroll
+  for (int jj = 0; jj < NPH; ++jj) {
+    if (pg >= pg1) break;
+    const int ph1 = jj + 1 < NPH ? phys[jj + 1 < NPH ? jj + 1 : 0] : 0;
+    if (jj % 2 == 0)
+      page_step(k0, v0, t0, k1, v1, t1, ph1);
+    else
+      page_step(k1, v1, t1, k0, v0, t0, ph1);
   }
 
   // combine the token rows of the wave (lanes with equal dims), exact rescaling
@@ -402,60 +417,84 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 }
 
-// One single-wave work-group per (query head, block of 32 dims): lanes 0-31 and 32-63 take the
-// even and odd partitions of 32 consecutive dims.  The (m, l) pairs of the first 64 partitions
-// and their accumulators are requested before the context length is known (every address below
-// max_parts is valid scratch; entries at or past the step's partition count hold stale values
-// and are never combined), so the merge costs one memory round trip after launch.  Dynamic LDS:
-// one weight per partition.
+// One 256-thread work-group per (query head, block of 32 dims); thread t works on dim t % 32
+// and the partitions p = t / 32 (mod 8).  The (m, l) pairs of the first 256 partitions and the
+// accumulators of the first 128 are requested before the context length is known (every address
+// below max_parts is valid scratch; entries at or past the step's partition count hold stale
+// values and are never combined), so the merge costs one memory round trip after launch.
+// Dynamic LDS: one weight per partition.
 template <int D>
-__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-  constexpr int PF = 32;  // prefetched accumulators per lane (64 partitions)
-  extern __shared__ float wts[];  // [np] weights 2^(m_p - M)
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+  constexpr int PF = 16;            // prefetched accumulators per thread (128 partitions)
+  extern __shared__ float wts[];    // [np] weights 2^(m_p - M)
+  __shared__ float red[8][32];
+  __shared__ float red_w[2][4];
   const int hq = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int dim = blockIdx.y * 32 + (lane & 31);
-  const int half = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int dim = blockIdx.y * 32 + (t & 31);
+  const int grp = t >> 5;
   const int maxp = a.max_parts;
   const int64_t base = (int64_t)hq * maxp;
-  const int pl = lane < maxp ? lane : 0;
-  const float m0 = a.part_ml[(base + pl) * 2];
-  const float l0 = a.part_ml[(base + pl) * 2 + 1];
+  const int pm = t < maxp ? t : 0;
+  const float m0 = a.part_ml[(base + pm) * 2];
+  const float l0 = a.part_ml[(base + pm) * 2 + 1];
   float pre[PF];
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
-    const int p = half + 2 * i;
+    const int p = grp + 8 * i;
     pre[i] = a.part_acc[(base + (p < maxp ? p : 0)) * D + dim];
   }
   const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
   const int np = n_parts_for(ctx, a.part_tokens);
-  if (np <= 1) return;  // the partition kernel wrote the output itself
-  float mloc = lane < np ? m0 : -1e30f;
-  for (int p = lane + 64; p < np; p += 64) mloc = fmaxf(mloc, a.part_ml[(base + p) * 2]);
-  const float M = wave_max(mloc);
+  if (np <= 1) return;  // the partition kernel wrote the output itself (uniform exit)
+  // M = max over partitions
+  float mloc = t < np ? m0 : -1e30f;
+  for (int p = t + 256; p < np; p += 256) mloc = fmaxf(mloc, a.part_ml[(base + p) * 2]);
+  mloc = wave_max(mloc);
+  if (lane == 0) red_w[0][wave] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_w[0][0], red_w[0][1]), fmaxf(red_w[0][2], red_w[0][3]));
+  // weights and L = sum w_p l_p
   float lsum = 0.f;
-  if (lane < np) {
+  if (t < np) {
     const float w = fast_exp2(m0 - M);
-    wts[lane] = w;
+    wts[t] = w;
     lsum = l0 * w;
   }
-  for (int p = lane + 64; p < np; p += 64) {
+  for (int p = t + 256; p < np; p += 256) {
     const float w = fast_exp2(a.part_ml[(base + p) * 2] - M);
     wts[p] = w;
     lsum = fmaf(a.part_ml[(base + p) * 2 + 1], w, lsum);
   }
-  const float L = wave_sum(lsum);
+  lsum = wave_sum(lsum);
+  if (lane == 0) red_w[1][wave] = lsum;
   __syncthreads();
+  const float L = (red_w[1][0] + red_w[1][1]) + (red_w[1][2] + red_w[1][3]);
+  // O = sum w_p acc_p over this thread's partitions, then over the 8 groups
   float O = 0.f;
 #pragma unroll
   for (int i = 0; i < PF; ++i) {
-    const int p = half + 2 * i;
+    const int p = grp + 8 * i;
     if (p < np) O = fmaf(pre[i], wts[p], O);
   }
-  for (int p = half + 2 * PF; p < np; p += 2) O = fmaf(a.part_acc[(base + p) * D + dim], wts[p], O);
-  O += __shfl_xor(O, 32);
-  if (half == 0) {
-    const float o = O / L;
+  for (int p0 = grp + 8 * PF; p0 < np; p0 += 8 * 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = p0 + 8 * j;
+      v[j] = a.part_acc[(base + (p < np ? p : 0)) * D + dim];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (p0 + 8 * j < np) O = fmaf(v[j], wts[p0 + 8 * j], O);
+  }
+  red[grp][t & 31] = O;
+  __syncthreads();
+  if (t < 32) {
+    float tot = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tot += red[j][t];
+    const float o = tot / L;
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[hq * D + dim] = f32_to_bf16(o);
     else
@@ -494,7 +533,7 @@ hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, c
 }
 
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_q_heads, (unsigned)(head_dim / 32)), block(64);
+  const dim3 grid((unsigned)a.n_q_heads, (unsigned)(head_dim / 32)), block(256);
   const size_t lds = (size_t)a.max_parts * sizeof(float);
   if (head_dim == 64)
     hipLaunchKernelGGL((k_attn_merge<64>), grid, block, lds, s, a);

@@ -111,13 +111,17 @@ __device__ __forceinline__ void lane_pair(float v, float& lo, float& hi) {
 
 // ---- split-KV partition sizing (shared by the host launcher and the kernels) -----------------
 // Fixed partitions when part_fixed > 0; otherwise the partition length grows with the context
-// so that Hkv * n_part stays near target_wgs work-groups, with a floor of 64 tokens.
+// so that Hkv * n_part stays near target_wgs work-groups, between 64 and kMaxPartTokens tokens.
+// Partitions are at most kMaxPartTokens long (the attention kernel reads a partition's
+// block-table entries ahead, 8 pages per wave).
+constexpr int kMaxPartTokens = 512;
 __host__ __device__ inline int part_tokens_for(int ctx, int part_fixed, int n_kv_heads,
                                                int target_wgs) {
   if (part_fixed > 0) return part_fixed;
   long long want = ((long long)ctx * n_kv_heads + target_wgs - 1) / target_wgs;
   int p = (int)(((want + 63) / 64) * 64);
-  return p < 64 ? 64 : p;
+  p = p < 64 ? 64 : p;
+  return p > kMaxPartTokens ? kMaxPartTokens : p;
 }
 __host__ __device__ inline int n_parts_for(int ctx, int part_tokens) {
   return (ctx + part_tokens - 1) / part_tokens;

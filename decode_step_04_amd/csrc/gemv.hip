@@ -28,6 +28,10 @@
 #include "common.h"
 #include "launch.h"
 
+#ifndef QD_GEMV_PART
+#error "compile with -DQD_GEMV_PART=<weight type> or -1 (dispatcher)"
+#endif
+
 namespace qd {
 
 template <int WT>
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     if constexpr (NORM) load_vec<false, VEC>(a.gamma, kc, gv[c]);
   }
   const int64_t round0 = blockIdx.x;
-  int64_t g = round0 * gpw + grp;
+  const int64_t g = round0 * gpw + grp;
   float ep_res = 0.f, ep_s1 = 1.f, ep_s2 = 1.f;
   load_epi(g, ep_res, ep_s1, ep_s2);
   uint4 wv[NR][MAXCH];
@@ -237,26 +241,29 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   int best_i = -1;
   const bool want_argmax = a.part_val != nullptr;
 
-  // 3. rounds
-  for (int64_t rnd = round0; rnd * gpw < ngroups; rnd += gridDim.x) {
-    g = rnd * gpw + grp;
-    const bool active = g < ngroups;
-    uint4 wn[NR][MAXCH];
-    float nres = 0.f, ns1 = 1.f, ns2 = 1.f;
+  // 3. rounds.  A round computes the rows of group g from the weights `cw` (with the epilogue
+  //    operands c_*) and, when the launch has several rounds (PIPE), first requests the next
+  //    round's rows into `nw` -- the last round requests its own rows again (cached), so that no
+  //    load sits under a branch.  Two register sets alternate between rounds: copying registers
+  //    of an in-flight load would make the compiler wait for it.
+  auto do_round = [&](const uint4 (&cw)[NR][MAXCH], float c_res, float c_s1, float c_s2,
+                      uint4 (&nw)[NR][MAXCH], float& n_res, float& n_s1, float& n_s2,
+                      int64_t rnd) {
+    const int64_t gg = rnd * gpw + grp;
     if constexpr (PIPE) {
       const int64_t gn = (rnd + gridDim.x) * gpw + grp;
-      if (gn < ngroups) {
-        load_epi(gn, nres, ns1, ns2);
-        load_rows(gn, wn);
-      }
+      const int64_t gl = gn < ngroups ? gn : gg;
+      load_epi(gl, n_res, n_s1, n_s2);
+      load_rows(gl, nw);
     }
+    const bool active = gg < ngroups;
     float acc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r] = 0.f;
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = dot16<WT>(wv[r][c], xv[c], acc[r]);
+      for (int r = 0; r < NR; ++r) acc[r] = dot16<WT>(cw[r][c], xv[c], acc[r]);
     float tot[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) tot[r] = wave_sum(acc[r]);
@@ -284,16 +291,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       for (int r = 1; r < R; ++r)
         if (lane == r) vu = tot[R + r];
     }
-    const int64_t row = g * R + lane;
+    const int64_t row = gg * R + lane;
     if (active && sub == 0 && lane < R && row < n) {
       float v = vg;
-      if constexpr (WT == W_I8) v *= ep_s1;
+      if constexpr (WT == W_I8) v *= c_s1;
       if constexpr (EPI == EPI_SWIGLU) {
-        const float u = (WT == W_I8) ? vu * ep_s2 : vu;
+        const float u = (WT == W_I8) ? vu * c_s2 : vu;
         v = v / (1.0f + expf(-v)) * u;
       }
       if constexpr (EPI == EPI_RESID) {
-        a.resid[row] = ep_res + v;
+        a.resid[row] = c_res + v;
       } else {
         if (a.y_bf16)
           static_cast<uint16_t*>(a.y)[row] = f32_to_bf16(v);
@@ -310,15 +317,22 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         }
       }
     }
-    if constexpr (PIPE) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int c = 0; c < MAXCH; ++c) wv[r][c] = wn[r][c];
-      ep_res = nres;
-      ep_s1 = ns1;
-      ep_s2 = ns2;
+  };
+  if constexpr (PIPE) {
+    uint4 wb[NR][MAXCH];
+    float rb = 0.f, s1b = 1.f, s2b = 1.f;
+    for (int64_t rnd = round0;;) {
+      do_round(wv, ep_res, ep_s1, ep_s2, wb, rb, s1b, s2b, rnd);
+      rnd += gridDim.x;
+      if (rnd * gpw >= ngroups) break;
+      do_round(wb, rb, s1b, s2b, wv, ep_res, ep_s1, ep_s2, rnd);
+      rnd += gridDim.x;
+      if (rnd * gpw >= ngroups) break;
     }
+  } else {
+    // one round: the grid covers every group
+    float d0, d1, d2;
+    do_round(wv, ep_res, ep_s1, ep_s2, wv, d0, d1, d2, round0);
   }
 
   if constexpr (EPI == EPI_STORE) {
@@ -356,54 +370,69 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 // ---- launch planning ------------------------------------------------------------------------------
 
 // How a projection of n output rows and input length k is launched:
-//   split: K is split over 2 or 4 waves when one wave's slice would need more than 8 wave-wide
-//          loads per row (register budget), or when even one row per wave leaves fewer than 1024
-//          waves (4 per CU) -- slices stay whole multiples of the 16-byte vector;
-//   R:     rows per wave, the largest of 4, 2, 1 that keeps at least 1024 waves and at most 16
-//          loads per lane in flight (8 when the next round is prefetched);
-//   wgs:   enough work-groups for one round, capped at 1024 for the store epilogue (the LM
-//          head), which then runs several rounds with the next one prefetched.
+//   split: K is split over 4, 2 or 1 waves of a work-group: the largest split that leaves every
+//          wave at least two wave-wide loads per row (and whole 16-byte vectors).  Each wave
+//          reads its slice of x (and gamma) from L1/L2 into registers, so the input traffic per
+//          weight byte is 1 / (R * rows per pair) whatever the split, and a larger split lets R
+//          grow within the register budget;
+//   R:     rows per wave, the largest of 4, 2, 1 that keeps at most 16 loads per lane in flight
+//          (8 when the next round is prefetched) and at least 1024 waves in the grid;
+//   wgs:   enough work-groups for one round, up to 4096; beyond that 1024 work-groups (4096
+//          waves, all resident) each run several rounds with the next one requested ahead
+//          (PIPE), R re-chosen for two sets of 8 loads.
 struct GemvPlan {
   int split, maxch, r;
+  bool pipe;  // several rounds per work-group, the next round's rows requested ahead
   unsigned wgs;
-  bool ok;  // every slice fits in 8 wave-wide chunks (the register-resident input)
+  bool ok;    // every slice fits in 8 wave-wide chunks (the register-resident input)
 };
+
+// A single-round launch takes up to kMaxOneRoundWgs work-groups (the hardware schedules those
+// beyond the resident ones as others finish); larger matrices (the LM head) run kPipeWgs
+// work-groups of several rounds each, every round requesting the next one's rows ahead.
+constexpr int64_t kMaxOneRoundWgs = 4096;
+constexpr int64_t kPipeWgs = 1024;
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int vec = wtype == W_F32 ? 4 : wtype == W_BF16 ? 8 : 16;
   const int64_t ch = 64 * vec;
   const int pairs = epi == EPI_SWIGLU ? 2 : 1;
-  int split = 1;
   auto chunks = [&](int s) { return (int)((k / s + ch - 1) / ch); };
-  auto can = [&](int s) { return s <= 4 && k % ((int64_t)s * vec) == 0; };
-  while (can(split * 2) && chunks(split) > 8) split *= 2;
-  while (can(split * 2) && n * split < 1024 && k / (split * 2) >= ch) split *= 2;
+  auto fits = [&](int s) { return k % ((int64_t)s * vec) == 0; };
+  int split = 1;
+  for (int s : {4, 2})
+    if (fits(s) && k / s >= 2 * ch) {
+      split = s;
+      break;
+    }
+  // a slice longer than 8 chunks does not fit in registers: split further when possible
+  while (chunks(split) > 8 && split < 4 && fits(split * 2)) split *= 2;
   GemvPlan p{};
   p.split = split;
   const int c = chunks(split);
   p.ok = c <= 8 && k % vec == 0;
-  p.maxch = c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
-  // loads per lane in flight: 16, or 8 when the next round is prefetched (two sets of registers)
-  const int budget = epi == EPI_STORE ? 8 : 16;
-  int r = 1;
-  for (int cand : {4, 2}) {
-    if (cand * pairs * p.maxch <= budget && ((n + cand - 1) / cand) * split >= 1024) {
-      r = cand;
-      break;
-    }
-  }
-  p.r = r;
-  const int64_t groups = (n + r - 1) / r;
+  p.maxch = c <= 4 ? (c <= 1 ? 1 : c) : c <= 6 ? 6 : 8;
   const int gpw = 4 / split;
-  int64_t wgs = (groups + gpw - 1) / gpw;
-  if (epi == EPI_STORE && wgs > 1024) wgs = 1024;
+  // loads per lane in flight: 16, or 8 per set when the next round is requested ahead
+  auto pick_r = [&](int budget) {
+    for (int cand : {4, 2})
+      if (cand * pairs * p.maxch <= budget && ((n + cand - 1) / cand) * split >= 1024) return cand;
+    return 1;
+  };
+  p.r = pick_r(16);
+  int64_t wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
+  p.pipe = wgs > kMaxOneRoundWgs;
+  if (p.pipe) {
+    p.r = pick_r(8);
+    wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
+    if (wgs > kPipeWgs) wgs = kPipeWgs;
+  }
   p.wgs = (unsigned)(wgs < 1 ? 1 : wgs);
   return p;
 }
 
-template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH>
+template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
 static hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
-  constexpr bool PIPE = EPI == EPI_STORE;
   constexpr int loads = (EPI == EPI_SWIGLU ? 2 : 1) * R * MAXCH;
   if constexpr (loads > (PIPE ? 8 : 16)) {
     return hipErrorInvalidConfiguration;  // never planned: over the register budget
@@ -414,13 +443,21 @@ static hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   }
 }
 
+template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH>
+static hipError_t go_p(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
+  return p.pipe ? go<WT, EPI, NORM, XB, R, MAXCH, true>(a, p, s)
+                : go<WT, EPI, NORM, XB, R, MAXCH, false>(a, p, s);
+}
+
 template <int WT, int EPI, bool NORM, bool XB, int R>
 static hipError_t go_ch(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   switch (p.maxch) {
-    case 1: return go<WT, EPI, NORM, XB, R, 1>(a, p, s);
-    case 2: return go<WT, EPI, NORM, XB, R, 2>(a, p, s);
-    case 4: return go<WT, EPI, NORM, XB, R, 4>(a, p, s);
-    default: return go<WT, EPI, NORM, XB, R, 8>(a, p, s);
+    case 1: return go_p<WT, EPI, NORM, XB, R, 1>(a, p, s);
+    case 2: return go_p<WT, EPI, NORM, XB, R, 2>(a, p, s);
+    case 3: return go_p<WT, EPI, NORM, XB, R, 3>(a, p, s);
+    case 4: return go_p<WT, EPI, NORM, XB, R, 4>(a, p, s);
+    case 6: return go_p<WT, EPI, NORM, XB, R, 6>(a, p, s);
+    default: return go_p<WT, EPI, NORM, XB, R, 8>(a, p, s);
   }
 }
 
@@ -433,9 +470,16 @@ static hipError_t go_r(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   }
 }
 
+// This file is compiled once per weight type (QD_GEMV_PART = W_F32, W_BF16, W_I8: the kernels
+// of that type) and once with QD_GEMV_PART = -1 (the dispatcher), so that the builds run in
+// parallel.
+template <int WT>
+hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s);
+
+#if QD_GEMV_PART >= 0
 // The norm prologue reads the fp32 residual stream; other inputs are fp32 or bf16.
 template <int WT>
-static hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
+hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
   const GemvPlan p = plan_gemv(WT, epi, a.n, a.k);
   if (!p.ok) return hipErrorInvalidValue;
   a.split = p.split;
@@ -450,7 +494,8 @@ static hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
   if (!norm) return hipErrorInvalidValue;
   return go_r<WT, EPI_SWIGLU, true, false>(a, p, s);
 }
-
+template hipError_t launch_wt<QD_GEMV_PART>(int, bool, GemvArgs, hipStream_t);
+#else
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   switch (wtype) {
@@ -467,5 +512,6 @@ int gemv_partials(int wtype, int epi, int64_t n, int64_t k) {
 bool gemv_supported(int wtype, int epi, int64_t n, int64_t k) {
   return n >= 1 && k >= 1 && plan_gemv(wtype, epi, n, k).ok;
 }
+#endif
 
 }  // namespace qd

@@ -31,7 +31,12 @@ namespace {
 
 thread_local std::string g_err;  // last error of context-free calls on this thread
 
-constexpr int kTargetWgs = 1024;  // split-KV work-groups aimed for when partitions are automatic
+// Split-KV work-groups aimed for when partitions are automatic: one per CU.  Each wave then
+// streams several pages with the next one requested ahead, which measured faster than one page
+// per wave on four times as many work-groups (less per-wave prologue and combine work, fewer
+// partitions to merge).
+inline int target_wgs(int /*n_q_heads*/, int /*n_kv_heads*/) { return 256; }
+constexpr int kMaxTargetWgs = 256;
 constexpr int kNumSlots = 11;
 
 qdec_status fail(std::string* dst, qdec_status s, const char* fmt, ...) {
@@ -69,10 +74,11 @@ struct Layer {
 };
 
 // Split-KV partition length of a context: the configured one, or the length that gives about
-// kTargetWgs (kv head, partition) work-groups at max_context (a multiple of 64, at least 64).
+// target_wgs (kv head, partition) work-groups at max_context (a multiple of 64, at least 64).
 int model_part_tokens(const qdec_config& c) {
-  return c.partition_size > 0 ? c.partition_size
-                              : part_tokens_for(c.max_context, 0, c.n_kv_heads, kTargetWgs);
+  return c.partition_size > 0
+             ? c.partition_size
+             : part_tokens_for(c.max_context, 0, c.n_kv_heads, target_wgs(c.n_q_heads, c.n_kv_heads));
 }
 int64_t model_max_parts(const qdec_config& c) {
   const int p = model_part_tokens(c);
@@ -208,8 +214,9 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if ((int64_t)c->num_pages * kPage < c->max_context)
     return fail(why, QDEC_E_INVAL, "max_context %d exceeds num_pages * page_size", c->max_context);
   if (c->max_context > (1 << 24)) return fail(why, QDEC_E_UNSUPPORTED, "max_context above 2^24");
-  if (c->partition_size < 0 || c->partition_size % 64)
-    return fail(why, QDEC_E_INVAL, "partition_size must be 0 or a positive multiple of 64");
+  if (c->partition_size < 0 || c->partition_size % 64 || c->partition_size > kMaxPartTokens)
+    return fail(why, QDEC_E_INVAL, "partition_size must be 0 or a multiple of 64 up to %d",
+                kMaxPartTokens);
   if (model_max_parts(*c) > kMaxMergeParts)
     return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
                 kMaxMergeParts);
@@ -1173,8 +1180,8 @@ QDEC_API qdec_status qdec_op_qk_norm_rope_append(
   return QDEC_OK;
 }
 
-static int op_part(int32_t ctx_len, int32_t n_kv_heads, int32_t partition_size) {
-  return part_tokens_for(ctx_len, partition_size, n_kv_heads, kTargetWgs);
+static int op_part(int32_t ctx_len, int32_t n_q_heads, int32_t n_kv_heads, int32_t partition_size) {
+  return part_tokens_for(ctx_len, partition_size, n_kv_heads, target_wgs(n_q_heads, n_kv_heads));
 }
 
 // Workspace of the op-level attention with np partitions: accumulators, then (m, l) pairs, the
@@ -1194,10 +1201,12 @@ QDEC_API qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_he
                                                  int32_t head_dim, int32_t partition_size,
                                                  size_t* bytes) {
   if (!bytes) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
-  if (ctx_len < 1 || n_q_heads < 1 || head_dim < 1 || partition_size < 0 || partition_size % 64)
+  if (ctx_len < 1 || n_q_heads < 1 || head_dim < 1 || partition_size < 0 || partition_size % 64 ||
+      partition_size > kMaxPartTokens)
     return fail(nullptr, QDEC_E_INVAL, "bad sizes");
   // the automatic size depends on n_kv_heads; take the largest count it can produce (Hkv = 1)
-  const int part = partition_size > 0 ? partition_size : op_part(ctx_len, 1, 0);
+  const int part = partition_size > 0 ? partition_size
+                                      : part_tokens_for(ctx_len, 0, 1, kMaxTargetWgs);
   const int64_t np = n_parts_for(ctx_len, part);
   *bytes = np <= 1 ? 0 : (size_t)attn_ws(n_q_heads, np, head_dim).bytes;
   return QDEC_OK;
@@ -1216,13 +1225,14 @@ QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const voi
   if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8)
     return fail(nullptr, QDEC_E_INVAL, "bad head counts");
   if (ctx_len < 1) return fail(nullptr, QDEC_E_INVAL, "ctx_len must be positive");
-  if (partition_size < 0 || partition_size % 64)
-    return fail(nullptr, QDEC_E_INVAL, "partition_size must be 0 or a multiple of 64");
+  if (partition_size < 0 || partition_size % 64 || partition_size > kMaxPartTokens)
+    return fail(nullptr, QDEC_E_INVAL, "partition_size must be 0 or a multiple of 64 up to %d",
+                kMaxPartTokens);
   if ((q_dtype != QDEC_F32 && q_dtype != QDEC_BF16) || (kv_dtype != QDEC_F32 && kv_dtype != QDEC_BF16) ||
       (out_dtype != QDEC_F32 && out_dtype != QDEC_BF16))
     return fail(nullptr, QDEC_E_INVAL, "bad dtype");
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(nullptr, QDEC_E_INVAL, "pools must be 16-byte aligned");
-  const int part = op_part(ctx_len, n_kv_heads, partition_size);
+  const int part = op_part(ctx_len, n_q_heads, n_kv_heads, partition_size);
   const int np = n_parts_for(ctx_len, part);
   if (np > kMaxMergeParts)
     return fail(nullptr, QDEC_E_UNSUPPORTED, "more than %d partitions", kMaxMergeParts);

@@ -13,8 +13,9 @@ def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
                partition_size: int = 0, act: str = None) -> Q.qdec_config:
     """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights, embedding, logits and KV) or 'w8a16'
     (int8 per-row projections and LM head, bf16 embedding, logits and KV).  act: 'f32' or 'bf16',
-    the precision of activations crossing op boundaries; default f32 for 'bf16' (bf16 as a
-    storage format only) and bf16 for 'w8a16' (16-bit activations)."""
+    the precision of activations crossing op boundaries; default 'f32' for every path (the weight
+    and cache formats are storage formats; activations are a few KiB per step, so their precision
+    costs no bandwidth), 'bf16' rounds them to 16 bits at every op boundary."""
     if path == "fp32":
         proj = lm = io = kv = Q.F32
         act = act or "f32"
@@ -24,7 +25,7 @@ def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
     elif path == "w8a16":
         proj = lm = Q.I8_ROW
         io = kv = Q.BF16
-        act = act or "bf16"
+        act = act or "f32"
     else:
         raise ValueError(path)
     act = Q.F32 if act == "f32" else Q.BF16

@@ -83,7 +83,8 @@ typedef struct qdec_config {
   int32_t page_size;      /* tokens per KV page; must be 16 */
   int32_t num_pages;      /* physical pages in the pool (each layer has its own pool of this size) */
   int32_t max_context;    /* positions 0 .. max_context-1 may be decoded; <= num_pages*page_size */
-  int32_t partition_size; /* split-KV partition length in tokens (multiple of 64), 0 = automatic */
+  int32_t partition_size; /* split-KV partition length in tokens (multiple of 64, at most 512),
+                           * 0 = automatic (about one GPU-full of work-groups at max_context) */
 } qdec_config;
 
 /* Supported dtype combinations (checked by qdec_config_validate):
@@ -347,7 +348,7 @@ qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_heads, int3
 /* Causal GQA decode attention of one query per head over positions 0..ctx_len-1
  * ([Qwen3-runtime] §2.5-2.6, §9.1, §10.1-10.2): q [Hq x D] of q_dtype; k_pool/v_pool one layer's
  * pools of kv_dtype (layout above); query head h reads kv head h / (Hq/Hkv); scores scaled by
- * 1/sqrt(D); each partition of partition_size tokens (multiple of 64; 0 = automatic) keeps an
+ * 1/sqrt(D); each partition of partition_size tokens (multiple of 64 up to 512; 0 = automatic) keeps an
  * fp32 online-softmax state (m, l, acc) and the partitions are merged exactly.  out [Hq x D] of
  * out_dtype.  workspace: device buffer of at least qdec_op_attention_workspace() bytes, 256-byte
  * aligned (may be NULL when that size is 0). */

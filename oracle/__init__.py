@@ -51,6 +51,8 @@ def lib():
             "or_pool_scatter": (None, [_P, _I32, _I32, _I32, _P, _I32, _I32, _I32, _P]),
             "or_decode_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P]),
             "or_argmax": (_I64, [_P, _I64]),
+            "or_set_fp32": (None, [_I32]),
+            "or_get_fp32": (_I32, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(_lib, name)
@@ -61,6 +63,22 @@ def lib():
 
 def _ptr(a):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+class fp32_arithmetic:
+    """Context manager: inside it every oracle function computes in plain sequential fp32 (each
+    partial sum, unfused product and function value rounded to fp32) instead of fp64.  Used only
+    to measure a plain fp32 implementation's distance from the fp64 result; the parity
+    reference is always the default fp64 mode."""
+
+    def __enter__(self):
+        self._prev = lib().or_get_fp32()
+        lib().or_set_fp32(1)
+        return self
+
+    def __exit__(self, *exc):
+        lib().or_set_fp32(self._prev)
+        return False
 
 
 def _f64(a):

@@ -72,6 +72,18 @@ static uint16_t bf16_bits_of(double rounded) {
 
 static double round_f32(double v) { return (double)(float)v; }
 
+/* Arithmetic mode.  0 (the default, and the reference every test compares against): every sum,
+ * product and function in fp64.  1: plain fp32 -- every partial sum, every product that is not
+ * fused into a sum, and every function value rounded to fp32, in the sequential order the loops
+ * below state, as a straightforward fp32 implementation computes them.  The fp32 mode measures
+ * how far a correct fp32 implementation of the same method lands from the fp64 result; with
+ * 16-bit activations that distance is the method's own sensitivity to fp32 rounding, which the
+ * tests use to bound the GPU's distance. */
+static int g_fp32 = 0;
+void or_set_fp32(int32_t on) { g_fp32 = on != 0; }
+int32_t or_get_fp32(void) { return g_fp32; }
+static double F(double v) { return g_fp32 ? round_f32(v) : v; }
+
 void or_round_bf16(const double* in, double* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = round_bf16(in[i]);
 }
@@ -122,13 +134,13 @@ int64_t or_kv_bytes_per_layer_token(int64_t hkv, int64_t d, int64_t elem) {
 /* RMSNorm without mean subtraction ([Qwen3-runtime] §2.1): y = x / sqrt(mean(x^2) + eps) * gamma. */
 void or_rmsnorm(const double* x, const float* gamma, int64_t n, double eps, double* y) {
   double ss = 0.0;
-  for (int64_t i = 0; i < n; ++i) ss += x[i] * x[i];
-  double inv = 1.0 / sqrt(ss / (double)n + eps);
-  for (int64_t i = 0; i < n; ++i) y[i] = x[i] * inv * (double)gamma[i];
+  for (int64_t i = 0; i < n; ++i) ss = F(ss + x[i] * x[i]);
+  double inv = F(1.0 / F(sqrt(F(F(ss / (double)n) + eps))));
+  for (int64_t i = 0; i < n; ++i) y[i] = F(F(x[i] * inv) * (double)gamma[i]);
 }
 
 /* SiLU ([Qwen3-runtime] §2.7): silu(z) = z * sigmoid(z). */
-static double silu(double z) { return z / (1.0 + exp(-z)); }
+static double silu(double z) { return F(z / F(1.0 + F(exp(-z)))); }
 
 void or_silu(const double* z, double* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = silu(z[i]);
@@ -142,10 +154,10 @@ void or_rope(double* v, int32_t d, int64_t pos, double base) {
   int32_t h = d / 2;
   for (int32_t i = 0; i < h; ++i) {
     double ang = (double)pos * pow(base, -2.0 * (double)i / (double)d);
-    double c = cos(ang), s = sin(ang);
+    double c = F(cos(ang)), s = F(sin(ang));
     double a = v[i], b = v[i + h];
-    v[i] = a * c - b * s;
-    v[i + h] = b * c + a * s;
+    v[i] = F(a * c - F(b * s));
+    v[i + h] = F(b * c + F(a * s));
   }
 }
 
@@ -164,7 +176,7 @@ void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
       double s = 0.0;
-      for (int64_t c = 0; c < k; ++c) s += (double)W[r * k + c] * x[c];
+      for (int64_t c = 0; c < k; ++c) s = F(s + (double)W[r * k + c] * x[c]);
       y[r] = s;
     }
   } else if (wt == OR_BF16) {
@@ -172,7 +184,7 @@ void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
       double s = 0.0;
-      for (int64_t c = 0; c < k; ++c) s += bf16_bits_to_double(W[r * k + c]) * x[c];
+      for (int64_t c = 0; c < k; ++c) s = F(s + bf16_bits_to_double(W[r * k + c]) * x[c]);
       y[r] = s;
     }
   } else {
@@ -180,8 +192,8 @@ void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
       double s = 0.0;
-      for (int64_t c = 0; c < k; ++c) s += (double)W[r * k + c] * x[c];
-      y[r] = s * (double)scale[r];
+      for (int64_t c = 0; c < k; ++c) s = F(s + (double)W[r * k + c] * x[c]);
+      y[r] = F(s * (double)scale[r]);
     }
   }
 }
@@ -233,20 +245,20 @@ void or_attention(const double* q, const float* K, const float* V, int64_t t, in
     for (int64_t j = 0; j < t; ++j) {
       const float* kj = K + (j * hkv + g) * d;
       double dot = 0.0;
-      for (int32_t r = 0; r < d; ++r) dot += qh[r] * (double)kj[r];
-      s[j] = dot / rs;
+      for (int32_t r = 0; r < d; ++r) dot = F(dot + qh[r] * (double)kj[r]);
+      s[j] = F(dot / F(rs));
       if (s[j] > mx) mx = s[j];
     }
     double* o = out + (int64_t)h * d;
     for (int32_t r = 0; r < d; ++r) o[r] = 0.0;
     double den = 0.0;
     for (int64_t j = 0; j < t; ++j) {
-      double w = exp(s[j] - mx);
-      den += w;
+      double w = F(exp(F(s[j] - mx)));
+      den = F(den + w);
       const float* vj = V + (j * hkv + g) * d;
-      for (int32_t r = 0; r < d; ++r) o[r] += w * (double)vj[r];
+      for (int32_t r = 0; r < d; ++r) o[r] = F(o[r] + w * (double)vj[r]);
     }
-    for (int32_t r = 0; r < d; ++r) o[r] /= den;
+    for (int32_t r = 0; r < d; ++r) o[r] = F(o[r] / den);
     free(s);
   }
 }
@@ -468,16 +480,16 @@ int32_t or_decode_step(const or_model* m, int32_t token, const double* emb, int3
     or_attention(q, kc, vc, (int64_t)pos + 1, (int32_t)hq, (int32_t)hkv, (int32_t)d, att);
     for (int64_t i = 0; i < qw; ++i) att[i] = act_round(m, att[i]);
     or_gemv(m->o[l], m->proj_type, m->o_scale ? m->o_scale[l] : NULL, att, dm, qw, y);
-    for (int64_t i = 0; i < dm; ++i) x[i] += y[i];
+    for (int64_t i = 0; i < dm; ++i) x[i] = F(x[i] + y[i]);
 
     /* MLP block */
     or_rmsnorm(x, m->post_norm[l], dm, m->eps, h);
     for (int64_t i = 0; i < dm; ++i) h[i] = act_round(m, h[i]);
     or_gemv(m->gate_up[l], m->proj_type, m->gate_up_scale ? m->gate_up_scale[l] : NULL, h, 2 * f,
             dm, y);
-    for (int64_t i = 0; i < f; ++i) a[i] = act_round(m, silu(y[i]) * y[f + i]);
+    for (int64_t i = 0; i < f; ++i) a[i] = act_round(m, F(silu(y[i]) * y[f + i]));
     or_gemv(m->down[l], m->proj_type, m->down_scale ? m->down_scale[l] : NULL, a, dm, f, y);
-    for (int64_t i = 0; i < dm; ++i) x[i] += y[i];
+    for (int64_t i = 0; i < dm; ++i) x[i] = F(x[i] + y[i]);
   }
 
   if (hidden_out)

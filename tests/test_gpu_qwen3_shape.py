@@ -7,9 +7,12 @@ Bar with fp32 activations (bf16 and int8 as storage formats only): hidden-state 
 <= 1e-4 (fp32 accumulation against fp64, ~1e-6 measured) and every logit within one bf16 spacing
 of the oracle's (2^-7 |logit|, plus 1e-5 of the largest logit for values near zero), since both
 sides round the same near-identical fp32 value to bf16.  Bar with bf16 activations at op
-boundaries: hidden relative L2 <= 1.5e-2 and logits max-abs <= 5e-2 (each bf16 rounding of an
-activation that differs by d before rounding leaves a difference of order sqrt(d * ulp), so the
-two sides drift apart by ~1e-2 however closely their arithmetic agrees).  In both cases the GPU's
+boundaries: hidden relative L2 <= max(1.5e-2, 2 d32) and logits max-abs <= max(5e-2, 2 l32), where
+d32 and l32 are the distances of the oracle's own plain-fp32 arithmetic mode from its fp64 result
+on the same inputs.  Each bf16 rounding of an activation that differs by a tiny amount before
+rounding flips with some probability and the flips compound over the layers, so even a plain
+fp32 implementation of the method lands ~1.5e-2 away at this shape (measured 0.9e-2 at T=512,
+1.3-1.5e-2 at T=4096); the GPU must be no further than twice that.  In every case the GPU's
 greedy id must be a maximiser of the oracle's logits up to bf16 rounding; int8 codes and scales
 bit-exact; graph replay bit-identical to the eager step.
 """
@@ -81,7 +84,7 @@ class Setup:
         Q.qdec_destroy(self.ctx)
 
 
-def _check(got, ref, act):
+def _check(got, ref, act, ref32=None):
     gh, gl, ga = got
     rh, rl, ra = ref
     rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
@@ -92,8 +95,11 @@ def _check(got, ref, act):
         assert rel <= 1e-4
         assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max())
     else:
-        assert rel <= 1.5e-2
-        assert lmax <= 5e-2
+        d32 = np.linalg.norm(ref32[0] - rh) / np.linalg.norm(rh)
+        l32 = np.max(np.abs(ref32[1] - rl))
+        print(f"  plain-fp32 oracle: hidden rel-L2 {d32:.3e}  logits max-abs {l32:.3e}", flush=True)
+        assert rel <= max(1.5e-2, 2 * d32)
+        assert lmax <= max(5e-2, 2 * l32)
     assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
 
 
@@ -126,8 +132,12 @@ def test_step_matches_oracle(path, act, T):
     print(f"qwen3-0.6b {path} act={act} T={T}", flush=True)
     s = setup(path, act)
     got = s.step(T - 1)
+    ref32 = None
+    if act == "bf16":
+        with oracle.fp32_arithmetic():
+            ref32 = s.om.step(T - 1, token=s.tok_id)
     ref = s.om.step(T - 1, token=s.tok_id)
-    _check(got, ref, act)
+    _check(got, ref, act, ref32)
 
 
 def test_graph_replay_bit_identical():

@@ -440,3 +440,94 @@ def test_step_rejects_bad_arguments():
         om.step(64, token=1)
     with pytest.raises(ValueError):
         om.step(0, token=512)
+
+
+# ---- the plain-fp32 arithmetic mode (used to measure a plain fp32 implementation's distance) ---------
+# Each pin restates, in numpy float32 steps, the sequential fp32 computation the mode promises:
+# every fused multiply-add rounded once (products of fp32/bf16 values are exact in fp64), every
+# function value and quotient rounded to fp32.
+
+def _f32(v):
+    return float(np.float32(v))
+
+
+def test_fp32_mode_gemv_is_sequential_fp32_fma():
+    rng = np.random.default_rng(21)
+    n, k = 5, 37
+    x = rng.standard_normal(k).astype(np.float32)
+    w32 = (rng.standard_normal((n, k)) * 0.1).astype(np.float32)
+    wbf = oracle.to_bf16_bits(w32.astype(np.float64))
+    q, sc = oracle.quantize_rows(w32)
+    with oracle.fp32_arithmetic():
+        got = {"f32": oracle.gemv(w32, x), "bf16": oracle.gemv(wbf, x), "i8": oracle.gemv(q, x, sc)}
+    wb = oracle.bf16_bits_to_f64(wbf)
+    for name, W, scale in (("f32", w32.astype(np.float64), None), ("bf16", wb, None),
+                           ("i8", q.astype(np.float64), sc)):
+        for r in range(n):
+            s = 0.0
+            for c in range(k):
+                s = _f32(s + W[r, c] * float(x[c]))
+            if scale is not None:
+                s = _f32(s * float(scale[r]))
+            assert got[name][r] == s, (name, r)
+    # and it is not the fp64 result (the mode is on), only close to it
+    ref = oracle.gemv(wbf, x)
+    assert not np.array_equal(got["bf16"], ref)
+    np.testing.assert_allclose(got["bf16"], ref, rtol=0, atol=1e-5)
+
+
+def test_fp32_mode_rmsnorm_silu_rope_steps():
+    rng = np.random.default_rng(22)
+    n = 48
+    x = rng.standard_normal(n).astype(np.float32).astype(np.float64)
+    g = (1 + 0.1 * rng.standard_normal(n)).astype(np.float32)
+    eps = 1e-6
+    with oracle.fp32_arithmetic():
+        y = oracle.rmsnorm(x, g, eps)
+        z = oracle.silu(x)
+        v = x.copy()
+        oracle_rope_in = v[:16].copy()
+        r = oracle.rope(oracle_rope_in, 7, 1e6)
+    ss = 0.0
+    for t in x:
+        ss = _f32(ss + t * t)
+    inv = _f32(1.0 / _f32(np.sqrt(_f32(_f32(ss / n) + eps))))
+    np.testing.assert_array_equal(y, [_f32(_f32(t * inv) * float(gi)) for t, gi in zip(x, g)])
+    np.testing.assert_array_equal(z, [_f32(t / _f32(1.0 + _f32(np.exp(-t)))) for t in x])
+    h = 8
+    want = oracle_rope_in.copy()
+    src = v[:16]
+    for i in range(h):
+        ang = 7 * 1e6 ** (-2.0 * i / 16)
+        c, s_ = _f32(np.cos(ang)), _f32(np.sin(ang))
+        a, b = src[i], src[i + h]
+        want[i] = _f32(a * c - _f32(b * s_))
+        want[i + h] = _f32(b * c + _f32(a * s_))
+    np.testing.assert_array_equal(r, want)
+
+
+def test_fp32_mode_attention_steps():
+    rng = np.random.default_rng(23)
+    hq, hkv, d, t = 2, 1, 8, 5
+    q = rng.standard_normal((hq, d)).astype(np.float32).astype(np.float64)
+    K = rng.standard_normal((t, hkv, d)).astype(np.float32)
+    V = rng.standard_normal((t, hkv, d)).astype(np.float32)
+    with oracle.fp32_arithmetic():
+        got = oracle.attention(q, K, V)
+    rs = _f32(np.sqrt(d))
+    for h in range(hq):
+        s = []
+        for j in range(t):
+            dot = 0.0
+            for r in range(d):
+                dot = _f32(dot + q[h, r] * float(K[j, 0, r]))
+            s.append(_f32(dot / rs))
+        mx = max(s)
+        o = [0.0] * d
+        den = 0.0
+        for j in range(t):
+            w = _f32(np.exp(_f32(s[j] - mx)))
+            den = _f32(den + w)
+            for r in range(d):
+                o[r] = _f32(o[r] + w * float(V[j, 0, r]))
+        np.testing.assert_array_equal(got[h], [_f32(v / den) for v in o])
