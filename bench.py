@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run the library's copy kernel on 1 GiB (counter calibration)")
+    p.add_argument("--no-ops", action="store_true",
+                   help="skip the op-level workloads (attention stress, W8A16 GEMV, copy)")
     p.add_argument("--eager-only", type=int, default=0, metavar="N",
                    help="only set up the workload and run N eager steps (for counter passes)")
     return p.parse_args()
@@ -83,6 +85,103 @@ def copy_calibration():
     dt = (time.perf_counter() - t0) / 20
     print(json.dumps({"copy_bytes_each_way": n, "copy_ms": dt * 1e3,
                       "copy_gbps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def ops_bench():
+    """Op-level workloads timed in HIP graphs, each launch reading a different copy of its data so
+    that nothing is served by the 256 MB Infinity Cache: split-KV attention (32 Q / 8 KV heads,
+    D 128, bf16 K/V, contexts 8K / 32K / 128K, partitions of 512 tokens and automatic), the W8A16
+    GEMV at 130560x1536 and 151936x1024 (int8 codes, fp32 row scales, bf16 x and y) next to the
+    bf16 GEMV of the same shapes, and the copy kernel on 1 GiB (read + write)."""
+    import math
+
+    import torch
+
+    from decode_step_04_amd import synth
+    from decode_step_04_amd import qdec as Q
+
+    dev = "cuda"
+    s = torch.cuda.Stream()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+
+    def per_launch_us(enqueue, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            enqueue(0)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=s):
+                for i in range(reps):
+                    enqueue(i)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(3):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (3 * reps)
+        del g
+        return us
+
+    out = {"attention": [], "gemv": []}
+    hq, hkv, d = 32, 8, 128
+    for T in (8192, 32768, 131072):
+        kv_bytes = T * hkv * d * 2 * 2
+        copies = max(2, min(32, math.ceil((1 << 30) / kv_bytes)))
+        n_pages = T // 16
+        pools = [(torch.randn((n_pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16),
+                  torch.randn((n_pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+                 for _ in range(copies)]
+        q = synth.attention_stress(min(T, 8192), device=dev)[0]
+        bt = torch.from_numpy(synth.block_table(n_pages, n_pages, seed=12)).to(dev)
+        att = torch.empty((hq, d), device=dev)
+        for part in (512, 0):
+            ws_bytes = Q.qdec_op_attention_workspace(T, hq, d, part)
+            ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+            def enq(i, part=part, ws=ws, ws_bytes=ws_bytes):
+                kp, vp = pools[i % copies]
+                Q.qdec_op_attention(q, Q.F32, kp, vp, Q.BF16, bt, T, hq, hkv, d, part, ws,
+                                    ws_bytes, att, Q.F32, stream=s.cuda_stream)
+
+            us = per_launch_us(enq, 4 * copies if copies < 16 else copies)
+            out["attention"].append({"context": T, "partition": part or "auto", "us": round(us, 2),
+                                     "bytes": kv_bytes, "gbps": round(kv_bytes / us / 1e3, 1)})
+        del pools
+        torch.cuda.empty_cache()
+    for n, k in synth.GEMV_SHAPES:
+        for wt in ("w8a16", "bf16"):
+            wb = n * k * (1 if wt == "w8a16" else 2)
+            copies = max(2, math.ceil((1 << 30) / wb))
+            if wt == "w8a16":
+                ws = [(torch.randint(-127, 128, (n, k), generator=gen, device=dev,
+                                     dtype=torch.int8),
+                       torch.rand((n,), generator=gen, device=dev) * 1e-3) for _ in range(copies)]
+                nbytes = n * k + 4 * n + 2 * k + 2 * n
+            else:
+                ws = [(torch.randn((n, k), generator=gen, device=dev).mul_(0.02).to(torch.bfloat16),
+                       None) for _ in range(copies)]
+                nbytes = 2 * n * k + 2 * k + 2 * n
+            x = torch.randn((k,), generator=gen, device=dev).to(torch.bfloat16)
+            y = torch.empty((n,), dtype=torch.bfloat16, device=dev)
+
+            def enq(i, ws=ws, wt=wt):
+                w, sc = ws[i % copies]
+                Q.qdec_op_gemv(w, Q.I8_ROW if wt == "w8a16" else Q.BF16, sc, x, Q.BF16, y, Q.BF16,
+                               n, k, stream=s.cuda_stream)
+
+            us = per_launch_us(enq, 2 * copies)
+            out["gemv"].append({"shape": [n, k], "weights": wt, "us": round(us, 2),
+                                "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1)})
+            del ws
+            torch.cuda.empty_cache()
+    nb = 1 << 30
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    b = torch.empty(nb, dtype=torch.uint8, device=dev)
+    us = per_launch_us(lambda i: Q.qdec_op_copy(b, a, nb, stream=s.cuda_stream), 4)
+    out["copy_1gib"] = {"us": round(us, 1), "gbps_read_plus_write": round(2 * nb / us / 1e3, 1)}
+    return out
 
 
 def main():
@@ -237,10 +336,8 @@ def main():
             om.k_cache[l][: T - 1] = k.float().cpu().numpy()
             om.v_cache[l][: T - 1] = v.float().cpu().numpy()
         del kv
-        ref32 = None
-        if act_name == "bf16":  # the plain-fp32 oracle's distance bounds the 16-bit-activation drift
-            with oracle.fp32_arithmetic():
-                ref32 = om.step(pos, token=tok_id)
+        with oracle.fp32_arithmetic():  # the plain-fp32 oracle's distance bounds the drift
+            ref32 = om.step(pos, token=tok_id)
         t0 = time.perf_counter()
         oh, ol, oa = om.step(pos, token=tok_id)
         first = time.perf_counter() - t0
@@ -248,18 +345,20 @@ def main():
         parity = {"hidden_rel_l2": rel, "logits_max_abs": float(np.max(np.abs(g_logits - ol))),
                   "argmax_gpu": g_arg, "argmax_oracle": oa,
                   "argmax_valid": bool(ol[g_arg] >= ol.max() - 2 * 2.0**-8 * abs(ol.max())),
-                  "bar": "fp32 activations: hidden rel-L2 <= 1e-4 and each logit within one "
-                         "bf16 spacing; bf16 activations: rel-L2 <= max(1.5e-2, 2 d32), logits "
-                         "max-abs <= max(5e-2, 2 l32), d32/l32 = the plain-fp32 oracle's distance"}
+                  "bar": "d32/l32 = the plain-fp32 oracle's distance; fp32 activations: hidden "
+                         "rel-L2 <= max(1e-4, 4 d32), each logit within one bf16 spacing + 4 l32; "
+                         "bf16 activations: rel-L2 <= max(1.5e-2, 2 d32), logits max-abs <= "
+                         "max(5e-2, 2 l32)"}
+        d32 = float(np.linalg.norm(ref32[0] - oh) / np.linalg.norm(oh))
+        l32 = float(np.max(np.abs(ref32[1] - ol)))
+        parity["fp32_oracle_hidden_rel_l2"] = d32
+        parity["fp32_oracle_logits_max_abs"] = l32
         if act_name == "f32":
-            parity["ok"] = rel <= 1e-4 and bool(np.all(
-                np.abs(g_logits - ol) <= 2.0**-7 * np.abs(ol) + 1e-5 * np.abs(ol).max()))
+            parity["ok"] = rel <= max(1e-4, 4 * d32) and bool(np.all(
+                np.abs(g_logits - ol) <= 2.0**-7 * np.abs(ol) + 1e-5 * np.abs(ol).max() + 4 * l32))
         else:
-            d32 = float(np.linalg.norm(ref32[0] - oh) / np.linalg.norm(oh))
-            l32 = float(np.max(np.abs(ref32[1] - ol)))
-            parity["fp32_oracle_hidden_rel_l2"] = d32
-            parity["fp32_oracle_logits_max_abs"] = l32
-            parity["ok"] = rel <= max(1.5e-2, 2 * d32) and parity["logits_max_abs"] <= max(5e-2, 2 * l32)
+            parity["ok"] = rel <= max(1.5e-2, 2 * d32) and \
+                parity["logits_max_abs"] <= max(5e-2, 2 * l32)
         if args.cpu_seconds > 0:
             n, spent = 1, first
             while spent < args.cpu_seconds and n < 5000:
@@ -274,6 +373,9 @@ def main():
                              f"position) on {threads} OpenMP threads, {spent:.1f} s"}
 
     Q.qdec_destroy(ctx)
+    del w
+    torch.cuda.empty_cache()
+    ops = None if args.no_ops else ops_bench()
     tok_s = 1.0 / graph_s
     out = {
         "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
@@ -295,6 +397,7 @@ def main():
         "kernels": kernels,
         "parity": parity,
         "cpu_baseline": cpu,
+        "ops": ops,
     }
     print(json.dumps(out))
 

@@ -52,11 +52,13 @@ struct WTraits<W_I8> {
   static constexpr int ELEM = 1;
 };
 
-__device__ __forceinline__ float i8_at(uint32_t w, int b) {
-  return (float)(int32_t)(int8_t)(uint8_t)(w >> (8 * b));
-}
+// An int8 code q read as the unsigned byte u = q ^ 0x80 = q + 128: one conversion instruction per
+// element (v_cvt_f32_ubyte0..3); the dot product then over-counts 128 * sum(x), which the caller
+// subtracts once per row.
+__device__ __forceinline__ float u8_at(uint32_t u, int b) { return (float)((u >> (8 * b)) & 0xFFu); }
 
-// acc + sum over the VEC elements of one 16-byte weight vector times VEC fp32 values.
+// acc + sum over the VEC elements of one 16-byte weight vector times VEC fp32 values (for int8:
+// the codes plus 128, see u8_at).
 template <int WT>
 __device__ __forceinline__ float dot16(uint4 w, const float* __restrict__ x, float acc) {
   if constexpr (WT == W_F32) {
@@ -74,13 +76,14 @@ __device__ __forceinline__ float dot16(uint4 w, const float* __restrict__ x, flo
     acc = fmaf(bf16_lo(w.w), x[6], acc);
     acc = fmaf(bf16_hi(w.w), x[7], acc);
   } else {
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t ws[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
+                            w.w ^ 0x80808080u};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc = fmaf(i8_at(ws[j], 0), x[4 * j + 0], acc);
-      acc = fmaf(i8_at(ws[j], 1), x[4 * j + 1], acc);
-      acc = fmaf(i8_at(ws[j], 2), x[4 * j + 2], acc);
-      acc = fmaf(i8_at(ws[j], 3), x[4 * j + 3], acc);
+      acc = fmaf(u8_at(ws[j], 0), x[4 * j + 0], acc);
+      acc = fmaf(u8_at(ws[j], 1), x[4 * j + 1], acc);
+      acc = fmaf(u8_at(ws[j], 2), x[4 * j + 2], acc);
+      acc = fmaf(u8_at(ws[j], 3), x[4 * j + 3], acc);
     }
   }
   return acc;
@@ -237,6 +240,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
   }
 
+  // int8: each row's sum over the lane's elements exceeds the true one by 128 * sum(x) (u8_at)
+  float x_corr = 0.f;
+  if constexpr (WT == W_I8) {
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x_corr += xv[c][e];
+    x_corr *= -128.f;
+  }
+
   float best_v = -INFINITY;
   int best_i = -1;
   const bool want_argmax = a.part_val != nullptr;
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     const bool active = gg < ngroups;
     float acc[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+    for (int r = 0; r < NR; ++r) acc[r] = x_corr;
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c)
 #pragma unroll
@@ -440,8 +453,10 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int64_t wbytes = n * pairs * k * (vec == 4 ? 4 : vec == 8 ? 2 : 1);
   int64_t wgs;
   if (wbytes > kStreamBytes) {
-    p.pipe = kStreamPipe;
     p.r = pick_r(kStreamLoads);
+    // fewer than kStreamLoads loads per round (short int8 rows): request the next round ahead
+    // so that a wave still keeps about that many in flight
+    p.pipe = kStreamPipe || p.r * pairs * p.maxch < kStreamLoads;
     wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
     if (wgs > kStreamWgs) wgs = kStreamWgs;
   } else {

@@ -1,8 +1,10 @@
 """The decode step at the 8B-class shape (36 layers, hidden 4096, 32 Q / 8 KV heads, D 128,
 FFN 12288, vocab 151936 untied), bf16, context 8192 with paged KV, all weights and KV resident
-in one GPU's HBM, fp32 activations; one step at pos 8191 against the oracle: hidden relative L2
-<= 1e-4, every logit within one bf16 spacing of the oracle's (2^-7 |logit| plus 1e-5 of the
-largest), greedy id a maximiser of the oracle's logits up to bf16 rounding."""
+in one GPU's HBM, fp32 activations; one step at pos 8191 against the oracle with the bar of the
+Qwen3-shape test: hidden relative L2 <= max(1e-4, 4 d32), every logit within one bf16 spacing
+(2^-7 |logit| plus 1e-5 of the largest) plus 4 l32, where d32 / l32 are the plain-fp32 oracle
+mode's distances from the fp64 result; greedy id a maximiser of the oracle's logits up to bf16
+rounding."""
 import numpy as np
 import pytest
 import torch
@@ -49,13 +51,17 @@ def test_8b_step_matches_oracle():
             om.k_cache[l][: T - 1] = k.float().cpu().numpy()
             om.v_cache[l][: T - 1] = v.float().cpu().numpy()
         del kv
+        with oracle.fp32_arithmetic():
+            r32 = om.step(T - 1, token=tok_id)
         rh, rl, ra = om.step(T - 1, token=tok_id)
         rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
         lmax = np.max(np.abs(gl - rl))
-        print(f"8b hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra}",
-              flush=True)
-        assert rel <= 1e-4
-        assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max())
+        d32 = np.linalg.norm(r32[0] - rh) / np.linalg.norm(rh)
+        l32 = np.max(np.abs(r32[1] - rl))
+        print(f"8b hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra} "
+              f"(plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
+        assert rel <= max(1e-4, 4 * d32)
+        assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max() + 4 * l32)
         assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
     finally:
         Q.qdec_destroy(ctx)

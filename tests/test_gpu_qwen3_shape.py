@@ -3,18 +3,21 @@
 Recipe: random-init weights N(0, 0.02) stored bf16 (seed 0), gammas 1 + N(0, 0.1), KV positions
 0..4094 pre-filled with N(0, 1) bf16 values through a random permutation of the 256 pool pages,
 one token id drawn uniformly; a decode step at pos T-1 for T in 512, 2048, 4096.
-Bar with fp32 activations (bf16 and int8 as storage formats only): hidden-state relative L2
-<= 1e-4 (fp32 accumulation against fp64, ~1e-6 measured) and every logit within one bf16 spacing
-of the oracle's (2^-7 |logit|, plus 1e-5 of the largest logit for values near zero), since both
-sides round the same near-identical fp32 value to bf16.  Bar with bf16 activations at op
-boundaries: hidden relative L2 <= max(1.5e-2, 2 d32) and logits max-abs <= max(5e-2, 2 l32), where
-d32 and l32 are the distances of the oracle's own plain-fp32 arithmetic mode from its fp64 result
-on the same inputs.  Each bf16 rounding of an activation that differs by a tiny amount before
-rounding flips with some probability and the flips compound over the layers, so even a plain
-fp32 implementation of the method lands ~1.5e-2 away at this shape (measured 0.9e-2 at T=512,
-1.3-1.5e-2 at T=4096); the GPU must be no further than twice that.  In every case the GPU's
-greedy id must be a maximiser of the oracle's logits up to bf16 rounding; int8 codes and scales
-bit-exact; graph replay bit-identical to the eager step.
+Bar, derived from the arithmetic: d32 and l32 are the distances (hidden relative L2, logits
+max-abs) of the oracle's own plain-fp32 arithmetic mode from its fp64 result on the same inputs,
+i.e. how far a correct fp32 implementation of the method lands.  Wherever the step rounds to bf16
+(the appended K/V row always, activations at op boundaries with 16-bit activations), values that
+differ by a tiny amount before rounding flip with some probability and the flips compound over
+the layers, so the GPU's distance and d32 are two samples of the same process:
+  - fp32 activations: hidden relative L2 <= max(1e-4, 4 d32) and every logit within one bf16
+    spacing of the oracle's (2^-7 |logit| plus 1e-5 of the largest) plus 4 l32.  Long contexts
+    measure ~2e-6 (d32 ~1e-5); at pos 0-1 the appended V row is most of the attention output,
+    only a handful of roundings flip, and single samples differ by up to 3x (d32 0.5-1.6e-3);
+  - bf16 activations: hidden relative L2 <= max(1.5e-2, 2 d32) and logits max-abs
+    <= max(5e-2, 2 l32): thousands of flips, so samples agree more closely (a plain fp32
+    implementation lands 0.9-1.7e-2 away at this shape, the GPU 0.4-1.6e-2).
+In every case the GPU's greedy id must be a maximiser of the oracle's logits up to bf16 rounding;
+int8 codes and scales bit-exact; graph replay bit-identical to the eager step.
 """
 import numpy as np
 import pytest
@@ -84,23 +87,30 @@ class Setup:
         Q.qdec_destroy(self.ctx)
 
 
-def _check(got, ref, act, ref32=None):
+def _check(got, ref, act, ref32):
     gh, gl, ga = got
     rh, rl, ra = ref
     rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
     lmax = np.max(np.abs(gl - rl))
-    print(f"hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle {ra}",
-          flush=True)
+    d32 = np.linalg.norm(ref32[0] - rh) / np.linalg.norm(rh)
+    l32 = np.max(np.abs(ref32[1] - rl))
+    print(f"hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle {ra}  "
+          f"(plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
     if act == "f32":
-        assert rel <= 1e-4
-        assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max())
+        assert rel <= max(1e-4, 4 * d32)
+        assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max() + 4 * l32)
     else:
-        d32 = np.linalg.norm(ref32[0] - rh) / np.linalg.norm(rh)
-        l32 = np.max(np.abs(ref32[1] - rl))
-        print(f"  plain-fp32 oracle: hidden rel-L2 {d32:.3e}  logits max-abs {l32:.3e}", flush=True)
         assert rel <= max(1.5e-2, 2 * d32)
         assert lmax <= max(5e-2, 2 * l32)
     assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+
+
+def _oracle_pair(om, pos, tok_id):
+    """(plain-fp32 oracle result, fp64 oracle result) of the step at pos; the fp64 one last, so
+    the oracle's cache holds its K/V row for pos afterwards."""
+    with oracle.fp32_arithmetic():
+        r32 = om.step(pos, token=tok_id)
+    return r32, om.step(pos, token=tok_id)
 
 
 _SETUPS = {}
@@ -132,11 +142,7 @@ def test_step_matches_oracle(path, act, T):
     print(f"qwen3-0.6b {path} act={act} T={T}", flush=True)
     s = setup(path, act)
     got = s.step(T - 1)
-    ref32 = None
-    if act == "bf16":
-        with oracle.fp32_arithmetic():
-            ref32 = s.om.step(T - 1, token=s.tok_id)
-    ref = s.om.step(T - 1, token=s.tok_id)
+    ref32, ref = _oracle_pair(s.om, T - 1, s.tok_id)
     _check(got, ref, act, ref32)
 
 
@@ -195,3 +201,32 @@ def test_w8a16_codes_bit_exact():
     torch.cuda.synchronize()
     assert np.array_equal(q.cpu().numpy(), w8.hw["lm_head"])
     assert np.array_equal(sc.cpu().numpy(), w8.hw["lm_scale"])
+
+
+def test_graph_replay_at_many_positions():
+    """One graph captured for the full 4096-token context (32 partitions of 128 tokens per head)
+    and replayed at positions that start, end and straddle pages and partitions: every replay is
+    bit-identical to the eager step at that position (surplus partitions contribute nothing) and
+    matches the oracle to the fp32-activation bar.  A fresh context, and positions in decreasing
+    order: a step at pos appends its own K/V row at pos on each side, so visiting a smaller
+    position afterwards never reads a row the two sides computed separately."""
+    s = Setup("bf16", "f32")
+    try:
+        info = Q.qdec_info_get(s.ctx)
+        assert info.partition_tokens == 128 and info.max_partitions == 32
+        st = Q.make_step(MAXCTX - 1, token_id=s.tok, hidden_out=s.hidden, logits_out=s.logits,
+                         argmax_out=s.amax)
+        Q.qdec_graph_capture(s.ctx, st)
+        for pos in (2047, 255, 129, 128, 127, 17, 16, 15, 1, 0):
+            print(f"qwen3-0.6b graph replay pos={pos}", flush=True)
+            Q.qdec_graph_replay(s.ctx, pos)
+            torch.cuda.synchronize()
+            g = (s.hidden.cpu().numpy().astype(np.float64),
+                 synth.bf16_to_f32(s.logits).astype(np.float64), int(s.amax.item()))
+            e = s.step(pos)
+            assert np.array_equal(g[0], e[0]) and np.array_equal(g[1], e[1]) and g[2] == e[2], pos
+            ref32, ref = _oracle_pair(s.om, pos, s.tok_id)
+            _check(e, ref, "f32", ref32)
+        Q.qdec_graph_reset(s.ctx)
+    finally:
+        s.close()
