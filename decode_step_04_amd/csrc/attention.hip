@@ -417,88 +417,102 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
 }
 
-// One 256-thread work-group per (query head, block of 32 dims); thread t works on dim t % 32
-// and the partitions p = t / 32 (mod 8).  The (m, l) pairs of the first 256 partitions and the
-// accumulators of the first 128 are requested before the context length is known (every address
-// below max_parts is valid scratch; entries at or past the step's partition count hold stale
-// values and are never combined), so the merge costs one memory round trip after launch.
-// Dynamic LDS: one weight per partition.
-template <int D>
-__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
-  constexpr int PF = 16;            // prefetched accumulators per thread (128 partitions)
-  extern __shared__ float wts[];    // [np] weights 2^(m_p - M)
-  __shared__ float red[8][32];
-  __shared__ float red_w[2][4];
+// One work-group of NW waves per (query head, 64 dims); lane l of every wave owns dim l of the
+// block.  NW = 1 when the scratch holds at most CH partitions per head, else 4.
+// Partitions are folded in chunks of CH: lane j < CH holds the (m, l) pair of partition p0 + j,
+// so the chunk maximum and the denominator are wave reductions, and every lane reads the weights
+// from the lanes that hold them.  Wave w takes the chunks w, w + 4, ...; its first chunk is
+// requested before the context length is known (every slot below max_parts is valid scratch;
+// slots at or past the step's partition count hold stale bits and are masked by selects), so a
+// merge of up to CH partitions is one memory round trip after launch, done by wave 0 alone with
+// no LDS and no barrier.  Longer merges (NW = 4) request each chunk of a wave while folding the one
+// before, in two alternating register sets, and combine the four waves' states through LDS.  The
+// running sums are rescaled to each chunk's maximum (exact up to rounding).
+constexpr int kMergeChunk = 32;
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_attn_merge(AttnArgs a) {
+  constexpr int CH = kMergeChunk;
+  __shared__ float s_m[NW], s_l[NW], s_o[NW][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hq = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int dim = blockIdx.y * 32 + (t & 31);
-  const int grp = t >> 5;
+  const int dim = blockIdx.y * 64 + lane;
   const int maxp = a.max_parts;
   const int64_t base = (int64_t)hq * maxp;
-  const int pm = t < maxp ? t : 0;
-  const float m0 = a.part_ml[(base + pm) * 2];
-  const float l0 = a.part_ml[(base + pm) * 2 + 1];
-  float pre[PF];
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + base;
+  const float* acc = a.part_acc + base * D + dim;
+  // In the chunk loop an empty asm with a memory clobber keeps the compiler from moving a chunk's
+  // loads down to their use in the following fold, which would serialise the chunks; it emits no
+  // instruction.
+  auto request = [&](float2& mv, float (&pv)[CH], int p0, int last) {
+    mv = ml[min(p0 + (lane & (CH - 1)), last)];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int p = grp + 8 * i;
-    pre[i] = a.part_acc[(base + (p < maxp ? p : 0)) * D + dim];
-  }
+    for (int j = 0; j < CH; ++j) pv[j] = acc[(int64_t)min(p0 + j, last) * D];
+    if constexpr (NW > 1) asm volatile("" ::: "memory");
+  };
+  float2 mlA, mlB;
+  float pA[CH], pB[CH];
+  request(mlA, pA, wave * CH, maxp - 1);
   const int ctx = a.desc ? a.desc->ctx : a.ctx_arg;
   const int np = n_parts_for(ctx, a.part_tokens);
-  if (np <= 1) return;  // the partition kernel wrote the output itself (uniform exit)
-  // M = max over partitions
-  float mloc = t < np ? m0 : -1e30f;
-  for (int p = t + 256; p < np; p += 256) mloc = fmaxf(mloc, a.part_ml[(base + p) * 2]);
-  mloc = wave_max(mloc);
-  if (lane == 0) red_w[0][wave] = mloc;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_w[0][0], red_w[0][1]), fmaxf(red_w[0][2], red_w[0][3]));
-  // weights and L = sum w_p l_p
-  float lsum = 0.f;
-  if (t < np) {
-    const float w = fast_exp2(m0 - M);
-    wts[t] = w;
-    lsum = l0 * w;
-  }
-  for (int p = t + 256; p < np; p += 256) {
-    const float w = fast_exp2(a.part_ml[(base + p) * 2] - M);
-    wts[p] = w;
-    lsum = fmaf(a.part_ml[(base + p) * 2 + 1], w, lsum);
-  }
-  lsum = wave_sum(lsum);
-  if (lane == 0) red_w[1][wave] = lsum;
-  __syncthreads();
-  const float L = (red_w[1][0] + red_w[1][1]) + (red_w[1][2] + red_w[1][3]);
-  // O = sum w_p acc_p over this thread's partitions, then over the 8 groups
-  float O = 0.f;
+  float M = -1e30f, L = 0.f, O = 0.f;
+  auto fold = [&](const float2& mv, const float (&pv)[CH], int p0) {
+    const bool ok = lane < CH && p0 + lane < np;
+    const float mx = fmaxf(M, wave_max(ok ? mv.x : -1e30f));
+    const float w = ok ? fast_exp2(mv.x - mx) : 0.f;
+    const float c = fast_exp2(M - mx);
+    L = fmaf(L, c, wave_sum(ok ? w * mv.y : 0.f));
+    O *= c;
 #pragma unroll
-  for (int i = 0; i < PF; ++i) {
-    const int p = grp + 8 * i;
-    if (p < np) O = fmaf(pre[i], wts[p], O);
-  }
-  for (int p0 = grp + 8 * PF; p0 < np; p0 += 8 * 4) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = p0 + 8 * j;
-      v[j] = a.part_acc[(base + (p < np ? p : 0)) * D + dim];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (p0 + 8 * j < np) O = fmaf(v[j], wts[p0 + 8 * j], O);
-  }
-  red[grp][t & 31] = O;
-  __syncthreads();
-  if (t < 32) {
-    float tot = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tot += red[j][t];
-    const float o = tot / L;
+    for (int j = 0; j < CH; ++j) O = fmaf(lane_value(w, j), p0 + j < np ? pv[j] : 0.f, O);
+    M = mx;
+  };
+  auto store = [&](float o) {
     if (a.out_bf16)
       static_cast<uint16_t*>(a.out)[hq * D + dim] = f32_to_bf16(o);
     else
       static_cast<float*>(a.out)[hq * D + dim] = o;
+  };
+  if (NW == 1 || np <= CH) {  // uniform; with one partition the partition kernel wrote the output
+    if (wave == 0 && np > 1) {
+      fold(mlA, pA, 0);
+      store(O / L);
+    }
+    return;
+  }
+  constexpr int STEP = NW * CH;
+  int p0 = wave * CH;
+  if (p0 < np) {  // wave-uniform
+    request(mlB, pB, p0 + STEP, np - 1);
+    fold(mlA, pA, p0);
+    for (p0 += STEP; p0 < np;) {
+      request(mlA, pA, p0 + STEP, np - 1);
+      fold(mlB, pB, p0);
+      p0 += STEP;
+      if (p0 >= np) break;
+      request(mlB, pB, p0 + STEP, np - 1);
+      fold(mlA, pA, p0);
+      p0 += STEP;
+    }
+  }
+  if (lane == 0) {
+    s_m[wave] = M;
+    s_l[wave] = L;
+  }
+  s_o[wave][lane] = O;
+  __syncthreads();
+  if (wave == 0) {
+    float mx = s_m[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) mx = fmaxf(mx, s_m[w]);
+    float lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float c = fast_exp2(s_m[w] - mx);  // 0 for a wave that had no partition
+      lt = fmaf(s_l[w], c, lt);
+      ot = fmaf(s_o[w][lane], c, ot);
+    }
+    store(ot / lt);
   }
 }
 
@@ -533,12 +547,19 @@ hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, c
 }
 
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_q_heads, (unsigned)(head_dim / 32)), block(256);
-  const size_t lds = (size_t)a.max_parts * sizeof(float);
-  if (head_dim == 64)
-    hipLaunchKernelGGL((k_attn_merge<64>), grid, block, lds, s, a);
-  else
-    hipLaunchKernelGGL((k_attn_merge<128>), grid, block, lds, s, a);
+  const dim3 grid((unsigned)a.n_q_heads, (unsigned)(head_dim / 64));
+  const bool one = a.max_parts <= kMergeChunk;  // every possible partition fits one chunk
+  if (head_dim == 64) {
+    if (one)
+      hipLaunchKernelGGL((k_attn_merge<64, 1>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_merge<64, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    if (one)
+      hipLaunchKernelGGL((k_attn_merge<128, 1>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_attn_merge<128, 4>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

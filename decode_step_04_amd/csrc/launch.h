@@ -29,7 +29,7 @@ hipError_t launch_attention(int head_dim, bool kv_bf16, int group, bool fused, c
                             int grid_parts, hipStream_t s);
 // Exact merge of the partitions (a no-op when the context fits one partition).
 hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s);
-constexpr int kMaxMergeParts = 8192;  // LDS of the merge: one float per partition
+constexpr int kMaxMergeParts = 8192;  // partitions per head the split-KV scratch layout allows
 
 hipError_t launch_rope_append(int head_dim, const RopeAppendArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
