@@ -109,17 +109,22 @@ __device__ __forceinline__ void combine_rows(float (&m)[G], float (&l)[G], float
   }
 }
 
+constexpr int kAttnWaves = 4;  // waves per work-group of k_attn (8 measured slower at both shapes)
+constexpr int kAttnThreads = kAttnWaves * kWave;
+
 template <int D, bool KVB, int G, bool FUSED>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   using Gm = Geo<D, KVB>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPI = Gm::TPI, NI = Gm::NI, ELEM = Gm::ELEM;
   constexpr int HALF = D / 2;
-  constexpr int NPH = kMaxPartTokens / kPage / 4;  // block-table entries per wave, read ahead
+  constexpr int NW = kAttnWaves, NT = kAttnThreads;
+  constexpr int NPH = kMaxPartTokens / kPage / NW;  // block-table entries per wave, read ahead
+  constexpr int QT = (G + NW - 1) / NW;             // query heads per wave in the prologue
   __shared__ float sq[G][D];        // scaled query heads
   __shared__ float skv[2][D];       // K and V of the new token (as stored)
-  __shared__ float sm_acc[4][G][D];
-  __shared__ float sm_m[4][G];
-  __shared__ float sm_l[4][G];
+  __shared__ float sm_acc[NW][G][D];
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hkv = a.n_kv_heads;
@@ -134,16 +139,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   //      its value is discarded): loads complete in order, and with no load under a branch each
   //      wait the compiler inserts covers exactly the loads its consumer needs ----
   int phys[NPH];
-  const int npw = (ppp + 3 - wave) / 4;          // pages of this wave in a full partition
+  const int npw = (ppp + NW - 1 - wave) / NW;    // pages of this wave in a full partition
 #pragma unroll
   for (int j = 0; j < NPH; ++j) {
-    const int idx = pg_first + wave + 4 * j;
+    const int idx = pg_first + wave + NW * j;
     const bool ok = j < npw && idx < a.bt_len;   // bt_len >= 1: entry 0 always exists
     const int v = a.block_table[ok ? idx : 0];
     phys[j] = ok ? v : 0;
   }
-  constexpr int QP = (G * D + 255) / 256;        // op path: query values per thread
-  float qx0[2], qx1[2];                          // fused path: this wave's query heads (wave, wave+4)
+  constexpr int QP = (G * D + NT - 1) / NT;      // op path: query values per thread
+  float qx0[QT], qx1[QT];                        // fused path: this wave's query heads wave + NW t
   float kx0 = 0.f, kx1 = 0.f, vx0 = 0.f, vx1 = 0.f;
   float gq0 = 0.f, gq1 = 0.f, gk0 = 0.f, gk1 = 0.f;  // Q/K-norm gammas of this lane's pair
   float qop[QP];
@@ -160,8 +165,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     gk0 = gks[hl];
     gk1 = gks[hl + HALF];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int h = wave + 4 * t;
+    for (int t = 0; t < QT; ++t) {
+      const int h = wave + NW * t;
       const float* src = a.qkv + (int64_t)(g * G + (h < G ? h : 0)) * D;
       qx0[t] = src[hl];
       qx1[t] = src[hl + HALF];
@@ -175,7 +180,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   } else {
 #pragma unroll
     for (int t = 0; t < QP; ++t) {
-      const int i = threadIdx.x + 256 * t;
+      const int i = threadIdx.x + NT * t;
       const int idx = g * G * D + (i < G * D ? i : 0);
       qop[t] = a.q_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.q)[idx])
                         : static_cast<const float*>(a.q)[idx];
@@ -223,7 +228,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   // a surplus partition reads page 0 of head 0 (cached after the first), not HBM
   request(k0, v0, t0, live ? phys[0] : 0);
   if (!lo_half) {
-    qx0[0] = qx1[0] = qx0[1] = qx1[1] = 0.f;
+#pragma unroll
+    for (int t = 0; t < QT; ++t) qx0[t] = qx1[t] = 0.f;
     kx0 = kx1 = vx0 = vx1 = 0.f;
     gq0 = gq1 = gk0 = gk1 = 0.f;
     cs = make_float2(1.f, 0.f);
@@ -235,8 +241,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   //      branch that would use them ----
   if constexpr (FUSED) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int h = wave + 4 * t;
+    for (int t = 0; t < QT; ++t) {
+      const int h = wave + NW * t;
       float y0, y1;
       norm_rope<D>(qx0[t], qx1[t], qk_norm, gq0, gq1, a.eps, cs, y0, y1);
       if (a.round_q) {
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if constexpr (KVB) {
       y0 = round_bf16(y0); y1 = round_bf16(y1); v0 = round_bf16(v0); v1 = round_bf16(v1);
     }
-    if (has_new && wave == 3 && lane < HALF) {
+    if (has_new && wave == NW - 1 && lane < HALF) {
       const int64_t off = ((phys_new * hkv + g) * kPage + pos % kPage) * D + lane;
       if constexpr (KVB) {
         uint16_t* kp = static_cast<uint16_t*>(a.k_pool);
@@ -273,7 +279,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   } else {
 #pragma unroll
     for (int t = 0; t < QP; ++t) {
-      const int i = threadIdx.x + 256 * t;
+      const int i = threadIdx.x + NT * t;
       if (i < G * D) sq[i / D][i % D] = qop[t] * a.qscale;
     }
   }
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   // would make the compiler wait for it.
   auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
                        uint4 (&nv)[NI], int& tn, int ph1) {
-    request(nk, nv, tn, (pg + 4 < pg1) ? ph1 : tc);
+    request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
     // scores from K first; V is still arriving (loads complete in order)
     float s[G][NI];
 #pragma unroll
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[h][i], vf[e], acc[h][e]);
     }
-    pg += 4;
+    pg += NW;
   };
   // Fully unrolled over the at most NPH pages of the wave: every step's code follows the
   // previous one's with no loop back-edge, so each wait counts exactly the loads in flight (a
@@ -384,15 +390,15 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   }
   __syncthreads();
 
-  // combine the 4 waves; threads cover (head, dim) pairs
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  // combine the waves; threads cover (head, dim) pairs
+  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
     const int h = idx / D, r = idx % D;
     float M = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, sm_m[w][h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float c = fast_exp2(sm_m[w][h] - M);
       L = fmaf(sm_l[w][h], c, L);
       O = fmaf(sm_acc[w][h][r], c, O);
@@ -518,7 +524,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_merge(AttnArgs a) {
 
 template <int D, bool KVB, bool FUSED>
 static hipError_t launch_dkf(int group, const AttnArgs& a, int grid_parts, hipStream_t s) {
-  const dim3 grid((unsigned)(a.n_kv_heads * grid_parts)), block(256);
+  const dim3 grid((unsigned)(a.n_kv_heads * grid_parts)), block(kAttnThreads);
   switch (group) {
     case 1: hipLaunchKernelGGL((k_attn<D, KVB, 1, FUSED>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_attn<D, KVB, 2, FUSED>), grid, block, 0, s, a); break;
