@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-OR_F32, OR_BF16, OR_I8 = 0, 1, 2
+OR_F32, OR_BF16, OR_I8, OR_I8G, OR_I4G = 0, 1, 2, 3, 4
+GROUP = 128  # values per scale in the group-wise formats
 
 _P = C.c_void_p
 _I64 = C.c_int64
@@ -44,6 +45,7 @@ def lib():
             "or_rope": (None, [_P, _I32, _I64, _D]),
             "or_gemv": (None, [_P, _I32, _P, _P, _I64, _I64, _P]),
             "or_quantize_rows": (None, [_P, _I64, _I64, _P, _P]),
+            "or_quantize_groups": (None, [_P, _I64, _I64, _I32, _P, _P]),
             "or_attention": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
             "or_attention_online": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _P]),
             "or_attention_partitioned": (None, [_P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P]),
@@ -155,24 +157,33 @@ def rope(v, pos, theta) -> np.ndarray:
     return flat.reshape(v.shape)
 
 
-def _wtype(w):
+def _wtype(w, scale=None):
+    """Weight type from the array and its scales: float32, uint16 (bf16 bits), int8 codes with
+    per-row scales [n] (OR_I8) or per-group scales [n, k/128] (OR_I8G), or uint8 packed int4
+    codes [n, k/2] with per-group scales (OR_I4G)."""
     if w.dtype == np.float32:
         return OR_F32
     if w.dtype == np.uint16:
         return OR_BF16
     if w.dtype == np.int8:
-        return OR_I8
-    raise TypeError(f"unsupported weight dtype {w.dtype} (float32, uint16 bf16 bits, int8)")
+        return OR_I8G if scale is not None and np.ndim(scale) == 2 else OR_I8
+    if w.dtype == np.uint8:
+        return OR_I4G
+    raise TypeError(f"unsupported weight dtype {w.dtype} (float32, uint16 bf16 bits, int8, uint8)")
 
 
 def gemv(w, x, scale=None) -> np.ndarray:
-    """y = W x; w is float32, uint16 (bf16 bits) or int8 codes (then scale[n] is required)."""
+    """y = W x; w is float32, uint16 (bf16 bits), int8 codes with scale [n] (per row) or
+    [n, k/128] (per group), or uint8 packed int4 codes [n, k/2] with scale [n, k/128]."""
     w = np.ascontiguousarray(w)
-    n, k = w.shape
+    wt = _wtype(w, scale)
+    n = w.shape[0]
+    k = w.shape[1] * (2 if wt == OR_I4G else 1)
     x = _f64(x)
     assert x.size == k
-    wt = _wtype(w)
-    s = _f32(scale) if wt == OR_I8 else None
+    s = _f32(scale) if wt in (OR_I8, OR_I8G, OR_I4G) else None
+    if wt in (OR_I8G, OR_I4G):
+        assert k % GROUP == 0 and s.shape == (n, k // GROUP)
     y = np.empty(n, dtype=np.float64)
     lib().or_gemv(_ptr(w), wt, _ptr(s), _ptr(x), n, k, _ptr(y))
     return y
@@ -185,6 +196,19 @@ def quantize_rows(w):
     q = np.empty((n, k), dtype=np.int8)
     s = np.empty(n, dtype=np.float32)
     lib().or_quantize_rows(_ptr(w), n, k, _ptr(q), _ptr(s))
+    return q, s
+
+
+def quantize_groups(w, bits):
+    """Group-wise symmetric quantisation with 128-value groups: bits = 8 returns (codes int8
+    [n, k], scales float32 [n, k/128]); bits = 4 returns (packed uint8 [n, k/2], scales)."""
+    assert bits in (8, 4)
+    w = _f32(w)
+    n, k = w.shape
+    assert k % GROUP == 0
+    q = np.empty((n, k) if bits == 8 else (n, k // 2), dtype=np.int8 if bits == 8 else np.uint8)
+    s = np.empty((n, k // GROUP), dtype=np.float32)
+    lib().or_quantize_groups(_ptr(w), n, k, bits, _ptr(q), _ptr(s))
     return q, s
 
 
@@ -263,9 +287,10 @@ class Model:
     """Host-side model for ``or_decode_step``.
 
     ``weights`` is a dict: ``embed`` [V, d] (float32 or uint16 bf16 bits), ``lm_head`` (same
-    convention, or int8 codes with ``lm_scale``; ``None`` when tied), ``final_norm`` [d] float32,
-    and per-layer lists ``qkv``, ``o``, ``gate_up``, ``down`` (float32 / uint16 / int8 with
-    ``*_scale`` lists) and ``in_norm``, ``post_norm``, ``q_norm``, ``k_norm`` (float32).
+    convention, or quantised codes with ``lm_scale``; ``None`` when tied), ``final_norm`` [d]
+    float32, and per-layer lists ``qkv``, ``o``, ``gate_up``, ``down`` (float32 / uint16 /
+    quantised codes with ``*_scale`` lists, in the layouts ``gemv`` takes) and ``in_norm``,
+    ``post_norm``, ``q_norm``, ``k_norm`` (float32).
     The KV cache is held here as logical float32 arrays [max_ctx, Hkv, D] per layer.
     """
 
@@ -285,8 +310,9 @@ class Model:
         s.n_q_heads, s.n_kv_heads, s.head_dim = cfg["n_q_heads"], hkv, d
         s.ffn, s.vocab, s.qk_norm = cfg["ffn"], cfg["vocab"], int(cfg.get("qk_norm", 1))
         s.embed_type = _wtype(weights["embed"])
-        s.proj_type = _wtype(weights["qkv"][0])
-        s.lm_type = _wtype(lm)
+        qs = weights.get("qkv_scale")
+        s.proj_type = _wtype(weights["qkv"][0], qs[0] if qs else None)
+        s.lm_type = _wtype(lm, weights.get("lm_scale"))
         s.act_bf16 = int(cfg["act_bf16"])
         s.kv_bf16 = int(cfg["kv_bf16"])
         s.logits_bf16 = int(cfg.get("logits_bf16", cfg["kv_bf16"]))
@@ -294,7 +320,8 @@ class Model:
         s.eps, s.theta = float(cfg["eps"]), float(cfg["theta"])
         s.embed = self._hold(weights["embed"])
         s.lm_head = self._hold(lm)
-        s.lm_scale = self._hold(weights.get("lm_scale")) if s.lm_type == OR_I8 else None
+        s.lm_scale = (self._hold(_f32(weights.get("lm_scale")))
+                      if s.lm_type in (OR_I8, OR_I8G, OR_I4G) else None)
         s.final_norm = self._hold(_f32(weights["final_norm"]))
         for key in ("qkv", "o", "gate_up", "down"):
             setattr(s, key, self._ptr_array([np.ascontiguousarray(a) for a in weights[key]]))

@@ -9,7 +9,8 @@
  * function returns fp64 results.  Stored tensors are read exactly as stored (bf16 widened by the
  * 16-bit shift, int8 codes as integers, fp32 as is).  Where the pages fix a narrower precision the
  * oracle applies it at the same place:
- *   - the int8 quantiser computes its scale and codes in fp32 (scale = max|row| / 127);
+ *   - the quantisers compute their scales and codes in fp32 (scale = max|row| / 127 per row, or
+ *     max|group| / 127 or / 7 per 128-value group);
  *   - the KV cache stores values rounded to its storage type (bf16 or fp32), and the logits are
  *     rounded to their output type;
  *   - when the step keeps bf16 activations at op boundaries ([Qwen3-runtime] §0.1: bf16 in and
@@ -33,7 +34,11 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_I8 = 2, OR_I8G = 3, OR_I4G = 4 };
+
+/* Values per quantisation group of the group-wise formats ([Qwen3-runtime] §13.1: a warp walks a
+ * row in 128-value groups, each with its own scale). */
+#define OR_GROUP 128
 
 /* ------------------------------------------------------------------------------------------ */
 /* Number formats                                                                             */
@@ -165,10 +170,23 @@ void or_rope(double* v, int32_t d, int64_t pos, double base) {
 /* Projections ([Qwen3-runtime] §4.1: at batch 1 every linear layer is a GEMV)                   */
 /* ------------------------------------------------------------------------------------------ */
 
-/* y[n] = sum_k W[n][k] x[k] for W of type wt (OR_F32, OR_BF16, or OR_I8 codes).  For OR_I8 the
- * per-row scale multiplies the integer-weighted sum once: y = s_n * sum_k q_nk x_k, which equals
- * sum_k (q_nk s_n) x_k in exact arithmetic ([Qwen3-runtime] §13.1, the group-scale step, read per
- * row as [ETE] quantises per row). */
+/* Code of element c in row r of a group-wise matrix: an int8 byte (OR_I8G), or a nibble of the
+ * packed int4 layout (OR_I4G: element c sits in byte c / 2 of the row, even c in the low nibble,
+ * stored offset-binary as code + 8). */
+static double group_code(const void* w, int32_t wt, int64_t k, int64_t r, int64_t c) {
+  if (wt == OR_I8G) return (double)((const int8_t*)w)[r * k + c];
+  const uint8_t b = ((const uint8_t*)w)[r * (k / 2) + c / 2];
+  const int nib = (c % 2 == 0) ? (b & 0x0F) : (b >> 4);
+  return (double)(nib - 8);
+}
+
+/* y[n] = sum_k W[n][k] x[k] for W of type wt (OR_F32, OR_BF16, OR_I8 codes, or the group-wise
+ * OR_I8G / OR_I4G codes).  For OR_I8 the per-row scale multiplies the integer-weighted sum once:
+ * y = s_n * sum_k q_nk x_k, which equals sum_k (q_nk s_n) x_k in exact arithmetic
+ * ([Qwen3-runtime] §13.1, the group-scale step, read per row as [ETE] quantises per row).  For the
+ * group-wise types the steps are those of [Qwen3-runtime] §13.1: each 128-value group's
+ * integer-weighted partial sum is formed first, then multiplied by that group's scale
+ * (scale[n][k / 128]) and added to the row total. */
 void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int64_t n, int64_t k,
              double* y) {
   if (wt == OR_F32) {
@@ -187,13 +205,26 @@ void or_gemv(const void* w, int32_t wt, const float* scale, const double* x, int
       for (int64_t c = 0; c < k; ++c) s = F(s + bf16_bits_to_double(W[r * k + c]) * x[c]);
       y[r] = s;
     }
-  } else {
+  } else if (wt == OR_I8) {
     const int8_t* W = (const int8_t*)w;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < n; ++r) {
       double s = 0.0;
       for (int64_t c = 0; c < k; ++c) s = F(s + (double)W[r * k + c] * x[c]);
       y[r] = F(s * (double)scale[r]);
+    }
+  } else {
+    const int64_t ng = k / OR_GROUP;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+      double total = 0.0;
+      for (int64_t g = 0; g < ng; ++g) {
+        double part = 0.0;
+        for (int64_t c = g * OR_GROUP; c < (g + 1) * OR_GROUP; ++c)
+          part = F(part + group_code(w, wt, k, r, c) * x[c]);
+        total = F(total + F(part * (double)scale[r * ng + g]));
+      }
+      y[r] = total;
     }
   }
 }
@@ -220,6 +251,50 @@ void or_quantize_rows(const float* w, int64_t n, int64_t k, int8_t* q, float* s)
         if (v < -127.0f) v = -127.0f;
       }
       q[r * k + c] = (int8_t)v;
+    }
+  }
+}
+
+/* Group-wise symmetric quantisation: one fp32 scale per 128-value group of a row
+ * ([Qwen3-runtime] §13.1 keeps a scale per row and group), with 8-bit codes (qmax = 127) or the
+ * 4-bit codes [ETE] names as the next step (qmax = 7).  Within each group it is the per-row rule
+ * above: scale = max|w| / qmax in fp32, code = w / scale rounded to nearest (ties to even),
+ * clamped to [-qmax, qmax]; an all-zero group gets scale 0 and zero codes.  k % 128 == 0.
+ * Storage: bits = 8, int8 codes [n][k]; bits = 4, two codes per byte [n][k / 2] (element c in
+ * byte c / 2, even c in the low nibble, offset-binary code + 8).  s: [n][k / 128]. */
+void or_quantize_groups(const float* w, int64_t n, int64_t k, int32_t bits, void* q, float* s) {
+  const int64_t ng = k / OR_GROUP;
+  const float qmax = bits == 8 ? 127.0f : 7.0f;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < ng; ++g) {
+      const float* grp = w + r * k + g * OR_GROUP;
+      float mx = 0.0f;
+      for (int64_t c = 0; c < OR_GROUP; ++c) {
+        float a = fabsf(grp[c]);
+        if (a > mx) mx = a;
+      }
+      const float sc = mx / qmax;
+      s[r * ng + g] = sc;
+      for (int64_t c = 0; c < OR_GROUP; ++c) {
+        float v = 0.0f;
+        if (sc != 0.0f) {
+          v = rintf(grp[c] / sc);
+          if (v > qmax) v = qmax;
+          if (v < -qmax) v = -qmax;
+        }
+        const int64_t e = g * OR_GROUP + c;  /* element index within the row */
+        if (bits == 8) {
+          ((int8_t*)q)[r * k + e] = (int8_t)v;
+        } else {
+          uint8_t* byte = (uint8_t*)q + r * (k / 2) + e / 2;
+          const uint8_t nib = (uint8_t)((int)v + 8);
+          if (e % 2 == 0)
+            *byte = nib;  /* the even element comes first and starts the byte */
+          else
+            *byte = (uint8_t)(*byte | (nib << 4));
+        }
+      }
     }
   }
 }
@@ -373,7 +448,7 @@ void or_pool_scatter(const void* logical, int32_t elem, int32_t pos0, int32_t n,
 typedef struct or_model {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   int32_t qk_norm;
-  int32_t embed_type, proj_type, lm_type; /* OR_F32 / OR_BF16 / OR_I8 */
+  int32_t embed_type, proj_type, lm_type; /* OR_F32 / OR_BF16 / OR_I8 / OR_I8G / OR_I4G */
   int32_t act_bf16;                       /* 1: bf16 rounding of op-boundary activations */
   int32_t kv_bf16;                        /* 1: the KV cache stores bf16 values, else fp32 */
   int32_t logits_bf16;                    /* 1: logits are returned as bf16 values, else fp32 */
