@@ -20,6 +20,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
            ("gemv.hip", "gemv_bf16", ["-DQD_GEMV_PART=1"]),
            ("gemv.hip", "gemv_i8", ["-DQD_GEMV_PART=2"]),
+           ("gemv.hip", "gemv_i8g", ["-DQD_GEMV_PART=3"]),
+           ("gemv.hip", "gemv_i4g", ["-DQD_GEMV_PART=4"]),
            ("gemv.hip", "gemv_dispatch", ["-DQD_GEMV_PART=-1"]),
            ("attention.hip", "attention", []), ("misc.hip", "misc", []),
            ("runtime.hip", "runtime", [])]

@@ -13,7 +13,11 @@ namespace qd {
 constexpr int kWave = 64;
 constexpr int kPage = 16;  // tokens per KV page
 
-enum WType : int { W_F32 = 0, W_BF16 = 1, W_I8 = 2 };
+// Weight storage types of the GEMV (values equal the public qdec_dtype codes): fp32, bf16, int8
+// codes with a per-row scale, int8 codes with a scale per 128-value group, and int4 codes (two
+// per byte, offset-binary, even element in the low nibble) with a scale per 128-value group.
+enum WType : int { W_F32 = 0, W_BF16 = 1, W_I8 = 2, W_I8G = 3, W_I4G = 4 };
+constexpr int kQGroup = 128;  // values per scale of the group-wise types
 
 // ---- bf16 <-> fp32 -------------------------------------------------------------------------
 // bf16 is the upper half of an fp32 word: widening is a 16-bit shift.
@@ -140,7 +144,7 @@ struct StepDesc {
 
 struct GemvArgs {
   const void* w;          // [rows x k] (rows = n, or 2n for SwiGLU: gate rows then up rows)
-  const float* scale;     // [rows] fp32 row scales of int8 codes
+  const float* scale;     // fp32 scales: [rows] (W_I8) or [rows][k / 128] (W_I8G, W_I4G)
   const void* x;          // input vector [k]; the raw fp32 residual when gamma != nullptr
   int32_t x_bf16;         // x element type
   int32_t round_h;        // round the normalised input to bf16 (16-bit activations)

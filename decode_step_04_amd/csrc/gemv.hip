@@ -14,7 +14,10 @@
 //      epilogue operands of its rows (residual values, int8 row scales).  Then it issues the
 //      16-byte loads of its rows' K-slice for the first round (lane l reads elements
 //      kslice + c*64*VEC + l*VEC .. +VEC of each row: one wave-wide load is a contiguous 1 KiB of
-//      a row).  Loads complete in order, so the input is ready -- and normalised, with the sum
+//      a row; 8-byte loads, 512 B, for packed int4).  Group-wise int8 / int4 weights
+//      ([Qwen3-runtime] §13.1: a scale per 128-value group) also load, per lane and load, the
+//      scale of the group its VEC elements lie in; the lane multiplies its partial dot product
+//      by that scale before the row reduction.  Loads complete in order, so the input is ready -- and normalised, with the sum
 //      of squares reduced over the wave (and across the SPLIT waves of a group through LDS) --
 //      while the weights are still in flight.  Every load is unconditional (rows past the end
 //      are clamped to the last row, chunks past the slice to its start, results discarded), so
@@ -36,20 +39,37 @@ namespace qd {
 
 template <int WT>
 struct WTraits;
+// VEC: elements per lane per load; BITS: bits per element; Vec: the loaded vector type; GROUPED:
+// a scale per 128-value group; BIAS: what the unsigned reading of a code adds (dot16).
 template <>
 struct WTraits<W_F32> {
-  static constexpr int VEC = 4;
-  static constexpr int ELEM = 4;
+  static constexpr int VEC = 4, BITS = 32, BIAS = 0;
+  static constexpr bool GROUPED = false;
+  using Vec = uint4;
 };
 template <>
 struct WTraits<W_BF16> {
-  static constexpr int VEC = 8;
-  static constexpr int ELEM = 2;
+  static constexpr int VEC = 8, BITS = 16, BIAS = 0;
+  static constexpr bool GROUPED = false;
+  using Vec = uint4;
 };
 template <>
 struct WTraits<W_I8> {
-  static constexpr int VEC = 16;
-  static constexpr int ELEM = 1;
+  static constexpr int VEC = 16, BITS = 8, BIAS = 128;
+  static constexpr bool GROUPED = false;
+  using Vec = uint4;
+};
+template <>
+struct WTraits<W_I8G> {
+  static constexpr int VEC = 16, BITS = 8, BIAS = 128;
+  static constexpr bool GROUPED = true;
+  using Vec = uint4;
+};
+template <>
+struct WTraits<W_I4G> {
+  static constexpr int VEC = 16, BITS = 4, BIAS = 8;
+  static constexpr bool GROUPED = true;
+  using Vec = uint2;
 };
 
 // An int8 code q read as the unsigned byte u = q ^ 0x80 = q + 128: one conversion instruction per
@@ -57,10 +77,14 @@ struct WTraits<W_I8> {
 // subtracts once per row.
 __device__ __forceinline__ float u8_at(uint32_t u, int b) { return (float)((u >> (8 * b)) & 0xFFu); }
 
-// acc + sum over the VEC elements of one 16-byte weight vector times VEC fp32 values (for int8:
-// the codes plus 128, see u8_at).
+// acc + sum over the VEC elements of one weight vector times VEC fp32 values (for int8: the
+// codes plus 128, see u8_at; for int4: the stored nibbles, i.e. the codes plus 8).  int4: the
+// masks 0x0F0F0F0F and 0xF0F0F0F0 leave the even elements of a word in its bytes, and the odd
+// ones times 16 -- the caller has divided the odd inputs by 16, which is exact, so each product
+// equals nibble * x exactly -- and one byte conversion per element remains.
 template <int WT>
-__device__ __forceinline__ float dot16(uint4 w, const float* __restrict__ x, float acc) {
+__device__ __forceinline__ float dot16(typename WTraits<WT>::Vec w, const float* __restrict__ x,
+                                       float acc) {
   if constexpr (WT == W_F32) {
     acc = fmaf(__uint_as_float(w.x), x[0], acc);
     acc = fmaf(__uint_as_float(w.y), x[1], acc);
@@ -75,6 +99,20 @@ __device__ __forceinline__ float dot16(uint4 w, const float* __restrict__ x, flo
     acc = fmaf(bf16_hi(w.z), x[5], acc);
     acc = fmaf(bf16_lo(w.w), x[6], acc);
     acc = fmaf(bf16_hi(w.w), x[7], acc);
+  } else if constexpr (WT == W_I4G) {
+    const uint32_t wd[2] = {w.x, w.y};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t ev = wd[j] & 0x0F0F0F0Fu, od = wd[j] & 0xF0F0F0F0u;
+      acc = fmaf(u8_at(ev, 0), x[8 * j + 0], acc);
+      acc = fmaf(u8_at(od, 0), x[8 * j + 1], acc);
+      acc = fmaf(u8_at(ev, 1), x[8 * j + 2], acc);
+      acc = fmaf(u8_at(od, 1), x[8 * j + 3], acc);
+      acc = fmaf(u8_at(ev, 2), x[8 * j + 4], acc);
+      acc = fmaf(u8_at(od, 2), x[8 * j + 5], acc);
+      acc = fmaf(u8_at(ev, 3), x[8 * j + 6], acc);
+      acc = fmaf(u8_at(od, 3), x[8 * j + 7], acc);
+    }
   } else {
     const uint32_t ws[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
                             w.w ^ 0x80808080u};
@@ -126,8 +164,11 @@ __device__ __forceinline__ void load_vec(const void* x, int64_t k, float (&v)[VE
 template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = WTraits<WT>::VEC;
-  constexpr int ELEM = WTraits<WT>::ELEM;
+  constexpr int BITS = WTraits<WT>::BITS;
+  constexpr bool GROUPED = WTraits<WT>::GROUPED;
+  using Vec = typename WTraits<WT>::Vec;
   constexpr int CH = kWave * VEC;                  // elements per wave-wide load
+  constexpr int SR = GROUPED ? 1 : 0;              // group-scale arrays are [1][1] otherwise
   constexpr int NR = (EPI == EPI_SWIGLU) ? 2 * R : R;
   __shared__ float red_ss[4];
   __shared__ float red_acc[4][NR];
@@ -145,13 +186,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int64_t n = a.n;
   const int64_t ngroups = (n + R - 1) / R;
   const char* __restrict__ wbase = static_cast<const char*>(a.w);
-  const int64_t row_bytes = (int64_t)K * ELEM;
+  const int64_t row_bytes = (int64_t)K * BITS / 8;
+  const int ng = K / kQGroup;                      // scale groups per row (grouped types)
 
   auto row_of = [&](int64_t gg, int r) -> int64_t {
     const int64_t row = gg * R + r;
     return row < n ? row : n - 1;  // clamp: loads stay in bounds, results are discarded
   };
-  auto load_rows = [&](int64_t gg, uint4 (&dst)[NR][MAXCH]) {
+  // the weight vectors of group gg's rows, and for grouped types the scale of each vector's group
+  auto load_rows = [&](int64_t gg, Vec (&dst)[NR][MAXCH],
+                       float (&sdst)[SR ? NR : 1][SR ? MAXCH : 1]) {
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
       const int kk = c * CH + lane * VEC;
@@ -159,10 +203,18 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int64_t row = row_of(gg, r);
-        dst[r][c] = *reinterpret_cast<const uint4*>(wbase + row * row_bytes + (int64_t)kc * ELEM);
+        dst[r][c] = *reinterpret_cast<const Vec*>(wbase + row * row_bytes + (int64_t)kc * BITS / 8);
         if constexpr (EPI == EPI_SWIGLU)
-          dst[R + r][c] = *reinterpret_cast<const uint4*>(wbase + (row + n) * row_bytes +
-                                                          (int64_t)kc * ELEM);
+          dst[R + r][c] = *reinterpret_cast<const Vec*>(wbase + (row + n) * row_bytes +
+                                                        (int64_t)kc * BITS / 8);
+      }
+      if constexpr (GROUPED) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int64_t row = row_of(gg, r);
+          sdst[r][c] = a.scale[row * ng + kc / kQGroup];
+          if constexpr (EPI == EPI_SWIGLU) sdst[R + r][c] = a.scale[(row + n) * ng + kc / kQGroup];
+        }
       }
     }
   };
@@ -190,8 +242,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   const int64_t g = round0 * gpw + grp;
   float ep_res = 0.f, ep_s1 = 1.f, ep_s2 = 1.f;
   load_epi(g, ep_res, ep_s1, ep_s2);
-  uint4 wv[NR][MAXCH];
-  load_rows(g, wv);
+  Vec wv[NR][MAXCH];
+  float wsc[SR ? NR : 1][SR ? MAXCH : 1];
+  load_rows(g, wv, wsc);
 
   // 2. the input while the weights arrive: zero the chunks past the slice, copy the raw input
   //    (work-group 0), normalise
@@ -240,14 +293,32 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
   }
 
-  // int8: each row's sum over the lane's elements exceeds the true one by 128 * sum(x) (u8_at)
+  // int8 / int4 read unsigned: each sum over the lane's elements exceeds the true one by
+  // BIAS * sum(x), per row (per-row int8) or per vector (grouped types, whose scale is applied
+  // per vector); the correction is the same for every row
   float x_corr = 0.f;
+  float xc[SR ? MAXCH : 1];
   if constexpr (WT == W_I8) {
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c)
 #pragma unroll
       for (int e = 0; e < VEC; ++e) x_corr += xv[c][e];
     x_corr *= -128.f;
+  }
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      float t = 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) t += xv[c][e];
+      xc[c] = t * -(float)WTraits<WT>::BIAS;
+    }
+  }
+  if constexpr (WT == W_I4G) {  // odd elements meet their nibble times 16 (dot16)
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c)
+#pragma unroll
+      for (int e = 1; e < VEC; e += 2) xv[c][e] *= 0.0625f;
   }
 
   float best_v = -INFINITY;
@@ -259,15 +330,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   //    round's rows into `nw` -- the last round requests its own rows again (cached), so that no
   //    load sits under a branch.  Two register sets alternate between rounds: copying registers
   //    of an in-flight load would make the compiler wait for it.
-  auto do_round = [&](const uint4 (&cw)[NR][MAXCH], float c_res, float c_s1, float c_s2,
-                      uint4 (&nw)[NR][MAXCH], float& n_res, float& n_s1, float& n_s2,
-                      int64_t rnd) {
+  using Scl = float[SR ? NR : 1][SR ? MAXCH : 1];
+  auto do_round = [&](const Vec (&cw)[NR][MAXCH], const Scl& cs, float c_res, float c_s1,
+                      float c_s2, Vec (&nw)[NR][MAXCH], Scl& ns, float& n_res, float& n_s1,
+                      float& n_s2, int64_t rnd) {
     const int64_t gg = rnd * gpw + grp;
     if constexpr (PIPE) {
       const int64_t gn = (rnd + gridDim.x) * gpw + grp;
       const int64_t gl = gn < ngroups ? gn : gg;
       load_epi(gl, n_res, n_s1, n_s2);
-      load_rows(gl, nw);
+      load_rows(gl, nw, ns);
     }
     const bool active = gg < ngroups;
     float acc[NR];
@@ -276,7 +348,12 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c)
 #pragma unroll
-      for (int r = 0; r < NR; ++r) acc[r] = dot16<WT>(cw[r][c], xv[c], acc[r]);
+      for (int r = 0; r < NR; ++r) {
+        if constexpr (GROUPED)
+          acc[r] = fmaf(cs[r][c], dot16<WT>(cw[r][c], xv[c], xc[c]), acc[r]);
+        else
+          acc[r] = dot16<WT>(cw[r][c], xv[c], acc[r]);
+      }
     float tot[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) tot[r] = wave_sum(acc[r]);
@@ -332,25 +409,26 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
   };
   if constexpr (PIPE) {
-    uint4 wb[NR][MAXCH];
+    Vec wb[NR][MAXCH];
+    Scl wscb;
     float rb = 0.f, s1b = 1.f, s2b = 1.f;
     for (int64_t rnd = round0;;) {
-      do_round(wv, ep_res, ep_s1, ep_s2, wb, rb, s1b, s2b, rnd);
+      do_round(wv, wsc, ep_res, ep_s1, ep_s2, wb, wscb, rb, s1b, s2b, rnd);
       rnd += gridDim.x;
       if (rnd * gpw >= ngroups) break;
-      do_round(wb, rb, s1b, s2b, wv, ep_res, ep_s1, ep_s2, rnd);
+      do_round(wb, wscb, rb, s1b, s2b, wv, wsc, ep_res, ep_s1, ep_s2, rnd);
       rnd += gridDim.x;
       if (rnd * gpw >= ngroups) break;
     }
   } else {
     // rounds without lookahead (usually one: the grid covers every group)
     float d0, d1, d2;
-    do_round(wv, ep_res, ep_s1, ep_s2, wv, d0, d1, d2, round0);
+    do_round(wv, wsc, ep_res, ep_s1, ep_s2, wv, wsc, d0, d1, d2, round0);
     for (int64_t rnd = round0 + gridDim.x; rnd * gpw < ngroups; rnd += gridDim.x) {
       const int64_t gg = rnd * gpw + grp;
       load_epi(gg, ep_res, ep_s1, ep_s2);
-      load_rows(gg, wv);
-      do_round(wv, ep_res, ep_s1, ep_s2, wv, d0, d1, d2, rnd);
+      load_rows(gg, wv, wsc);
+      do_round(wv, wsc, ep_res, ep_s1, ep_s2, wv, wsc, d0, d1, d2, rnd);
     }
   }
 
@@ -425,6 +503,8 @@ constexpr int kStreamLoads = 8;
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int vec = wtype == W_F32 ? 4 : wtype == W_BF16 ? 8 : 16;
+  const int bits = wtype == W_F32 ? 32 : wtype == W_BF16 ? 16 : wtype == W_I4G ? 4 : 8;
+  const bool grouped = wtype == W_I8G || wtype == W_I4G;
   const int64_t ch = 64 * vec;
   const int pairs = epi == EPI_SWIGLU ? 2 : 1;
   auto chunks = [&](int s) { return (int)((k / s + ch - 1) / ch); };
@@ -440,7 +520,7 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   GemvPlan p{};
   p.split = split;
   const int c = chunks(split);
-  p.ok = c <= 8 && k % vec == 0;
+  p.ok = c <= 8 && k % vec == 0 && (!grouped || k % kQGroup == 0);
   p.maxch = c <= 4 ? (c <= 1 ? 1 : c) : c <= 6 ? 6 : 8;
   const int gpw = 4 / split;
   // loads per lane in flight: 16, or 8 per set when the next round is requested ahead
@@ -450,7 +530,7 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
         return cand;
     return 1;
   };
-  const int64_t wbytes = n * pairs * k * (vec == 4 ? 4 : vec == 8 ? 2 : 1);
+  const int64_t wbytes = n * pairs * k * bits / 8;
   int64_t wgs;
   if (wbytes > kStreamBytes) {
     p.r = pick_r(kStreamLoads);
@@ -512,8 +592,8 @@ static hipError_t go_r(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   }
 }
 
-// This file is compiled once per weight type (QD_GEMV_PART = W_F32, W_BF16, W_I8: the kernels
-// of that type) and once with QD_GEMV_PART = -1 (the dispatcher), so that the builds run in
+// This file is compiled once per weight type (QD_GEMV_PART = W_F32 .. W_I4G: the kernels of
+// that type) and once with QD_GEMV_PART = -1 (the dispatcher), so that the builds run in
 // parallel.
 template <int WT>
 hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s);
@@ -543,7 +623,10 @@ hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStre
   switch (wtype) {
     case W_F32: return launch_wt<W_F32>(epi, norm, a, s);
     case W_BF16: return launch_wt<W_BF16>(epi, norm, a, s);
-    default: return launch_wt<W_I8>(epi, norm, a, s);
+    case W_I8: return launch_wt<W_I8>(epi, norm, a, s);
+    case W_I8G: return launch_wt<W_I8G>(epi, norm, a, s);
+    case W_I4G: return launch_wt<W_I4G>(epi, norm, a, s);
+    default: return hipErrorInvalidValue;
   }
 }
 

@@ -16,8 +16,9 @@ enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s);
 // Number of work-groups (= partial argmax slots) launch_gemv uses for this shape.
 int gemv_partials(int wtype, int epi, int64_t n, int64_t k);
-// Whether launch_gemv handles this shape: k a multiple of the 16-byte vector and each wave's
-// K-slice within 8 wave-wide loads (k <= 8192 fp32, 16384 bf16, 32768 int8 weights).
+// Whether launch_gemv handles this shape: k a multiple of the lane vector (and of 128 for the
+// group-wise types) and each wave's K-slice within 8 wave-wide loads (k <= 8192 fp32, 16384
+// bf16, 32768 int8 or int4 weights).
 bool gemv_supported(int wtype, int epi, int64_t n, int64_t k);
 // Final reduction of per-work-group (value, index) partials to the argmax.
 hipError_t launch_argmax_partials(const float* val, const int32_t* idx, int n, int32_t* out,
@@ -38,6 +39,10 @@ const void* embed_kernel_fn();
 hipError_t launch_argmax(const void* x, int x_bf16, int64_t n, int32_t* out, hipStream_t s);
 hipError_t launch_quantize(const void* w, int src_bf16, int8_t* q, float* scale, int64_t n,
                            int64_t k, hipStream_t s);
+// Group-wise quantisation, 128-value groups: bits = 8 (int8 codes [n][k]) or 4 (packed int4
+// [n][k / 2]); scale [n][k / 128].  k % 128 == 0.
+hipError_t launch_quantize_groups(const void* w, int src_bf16, int bits, void* q, float* scale,
+                                  int64_t n, int64_t k, hipStream_t s);
 hipError_t launch_kv_copy(void* pool, void* linear, const int32_t* block_table, int pos0, int n,
                           int n_kv_heads, int head_dim, int elem, int to_pool, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, float theta, hipStream_t s);

@@ -272,6 +272,69 @@ hipError_t launch_quantize(const void* w, int src_bf16, int8_t* q, float* scale,
   return hipGetLastError();
 }
 
+// ---- group-wise symmetric quantisation, 128-value groups (upload time) ---------------------------
+// [Qwen3-runtime] §13.1 keeps a scale per 128-value group; 4-bit codes are the next step [ETE]
+// names.  Per group: scale = max|w| / QMAX in fp32 (QMAX = 127 or 7), code = round-half-even(w /
+// scale) clamped to [-QMAX, QMAX]; an all-zero group keeps scale 0 and zero codes.  One wave per
+// group, lane l taking elements 2l and 2l + 1: int8 codes are written as two bytes, int4 codes as
+// one byte (element 2l in the low nibble, each nibble code + 8).  k % 128 == 0.
+template <bool SRC_BF16, int BITS>
+__global__ __launch_bounds__(256) void k_quantize_groups(const void* w, uint8_t* q, float* scale,
+                                                         int64_t n, int64_t k) {
+  constexpr float QMAX = BITS == 8 ? 127.0f : 7.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t ng = k / kQGroup;
+  for (int64_t grp = (int64_t)blockIdx.x * 4 + wave; grp < n * ng; grp += (int64_t)gridDim.x * 4) {
+    const int64_t e = (grp / ng) * k + (grp % ng) * kQGroup + 2 * lane;  // element 2l of the group
+    float v0, v1;
+    if constexpr (SRC_BF16) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(w) + e);
+      v0 = bf16_lo(u);
+      v1 = bf16_hi(u);
+    } else {
+      const float2 f = *reinterpret_cast<const float2*>(static_cast<const float*>(w) + e);
+      v0 = f.x;
+      v1 = f.y;
+    }
+    const float mx = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float sc = mx / QMAX;
+    if (lane == 0) scale[grp] = sc;
+    float r0 = 0.f, r1 = 0.f;
+    if (sc != 0.f) {
+      r0 = fminf(fmaxf(rintf(v0 / sc), -QMAX), QMAX);
+      r1 = fminf(fmaxf(rintf(v1 / sc), -QMAX), QMAX);
+    }
+    if constexpr (BITS == 8) {
+      const uint32_t b0 = (uint8_t)(int8_t)(int)r0, b1 = (uint8_t)(int8_t)(int)r1;
+      *reinterpret_cast<uint16_t*>(q + e) = (uint16_t)(b0 | (b1 << 8));
+    } else {
+      const uint32_t n0 = (uint32_t)((int)r0 + 8), n1 = (uint32_t)((int)r1 + 8);
+      q[e / 2] = (uint8_t)(n0 | (n1 << 4));
+    }
+  }
+}
+
+hipError_t launch_quantize_groups(const void* w, int src_bf16, int bits, void* q, float* scale,
+                                  int64_t n, int64_t k, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t wgs = (n * (k / kQGroup) + 3) / 4;
+  if (wgs > 8192) wgs = 8192;
+  uint8_t* qb = static_cast<uint8_t*>(q);
+  const dim3 grid((unsigned)wgs), block(256);
+  if (src_bf16) {
+    if (bits == 8)
+      hipLaunchKernelGGL((k_quantize_groups<true, 8>), grid, block, 0, s, w, qb, scale, n, k);
+    else
+      hipLaunchKernelGGL((k_quantize_groups<true, 4>), grid, block, 0, s, w, qb, scale, n, k);
+  } else {
+    if (bits == 8)
+      hipLaunchKernelGGL((k_quantize_groups<false, 8>), grid, block, 0, s, w, qb, scale, n, k);
+    else
+      hipLaunchKernelGGL((k_quantize_groups<false, 4>), grid, block, 0, s, w, qb, scale, n, k);
+  }
+  return hipGetLastError();
+}
+
 // ---- KV pre-fill / read-back through the block table -------------------------------------------
 // [Qwen3-runtime] §7.2: position p lives in slot p % 16 of physical page bt[p / 16].  One thread
 // per 16-byte chunk of a (position, head) row.

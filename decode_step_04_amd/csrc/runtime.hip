@@ -51,6 +51,18 @@ qdec_status fail(std::string* dst, qdec_status s, const char* fmt, ...) {
 }
 
 int elem_size(int dtype) { return dtype == QDEC_F32 ? 4 : dtype == QDEC_BF16 ? 2 : 1; }
+// Storage of a [rows x cols] matrix of a weight dtype: code bytes, and fp32 scales (one per row for
+// I8_ROW, one per 128-value group for the group-wise types).
+static bool is_quant(int dt) { return dt == QDEC_I8_ROW || dt == QDEC_I8_G128 || dt == QDEC_I4_G128; }
+static bool is_grouped(int dt) { return dt == QDEC_I8_G128 || dt == QDEC_I4_G128; }
+static int64_t code_bytes(int dt, int64_t rows, int64_t cols) {
+  return dt == QDEC_I4_G128 ? rows * (cols / 2) : rows * cols * elem_size(dt);
+}
+static int64_t scale_count(int dt, int64_t rows, int64_t cols) {
+  return dt == QDEC_I8_ROW ? rows : is_grouped(dt) ? rows * (cols / kQGroup) : 0;
+}
+// GEMV weight type of a storage dtype (the codes coincide)
+static int wt_of(int32_t dt) { return dt; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 struct Mat {
@@ -58,9 +70,7 @@ struct Mat {
   float* scale = nullptr;
   int64_t rows = 0, cols = 0;
   int dtype = QDEC_F32;
-  int64_t bytes() const {
-    return rows * cols * elem_size(dtype) + (dtype == QDEC_I8_ROW ? rows * 4 : 0);
-  }
+  int64_t bytes() const { return code_bytes(dtype, rows, cols) + scale_count(dtype, rows, cols) * 4; }
 };
 
 struct Layer {
@@ -191,12 +201,17 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
     return fail(why, QDEC_E_INVAL, "rms_eps must be positive and finite");
   if (!(c->rope_theta > 1.f) || !std::isfinite(c->rope_theta))
     return fail(why, QDEC_E_INVAL, "rope_theta must be finite and above 1");
-  auto dt_ok = [](int d) { return d == QDEC_F32 || d == QDEC_BF16 || d == QDEC_I8_ROW; };
+  auto dt_ok = [](int d) { return d >= QDEC_F32 && d <= QDEC_I4_G128; };
   if (!dt_ok(c->proj_dtype) || !dt_ok(c->lm_head_dtype) || !dt_ok(c->io_dtype) ||
       !dt_ok(c->act_dtype) || !dt_ok(c->kv_dtype))
     return fail(why, QDEC_E_INVAL, "unknown dtype value");
-  if (c->act_dtype == QDEC_I8_ROW || c->io_dtype == QDEC_I8_ROW || c->kv_dtype == QDEC_I8_ROW)
+  if (is_quant(c->act_dtype) || is_quant(c->io_dtype) || is_quant(c->kv_dtype))
     return fail(why, QDEC_E_UNSUPPORTED, "io, act and kv dtypes must be F32 or BF16");
+  if ((is_grouped(c->proj_dtype) &&
+       (c->hidden % kQGroup || c->ffn % kQGroup || (c->n_q_heads * c->head_dim) % kQGroup)) ||
+      (is_grouped(c->lm_head_dtype) && c->hidden % kQGroup))
+    return fail(why, QDEC_E_UNSUPPORTED,
+                "group-wise weights need every projection's input length to be a multiple of 128");
   if (c->io_dtype == QDEC_F32) {
     if (c->proj_dtype != QDEC_F32 || c->lm_head_dtype != QDEC_F32 || c->kv_dtype != QDEC_F32 ||
         c->act_dtype != QDEC_F32)
@@ -205,7 +220,7 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   } else {
     if (c->proj_dtype == QDEC_F32 || c->lm_head_dtype == QDEC_F32 || c->kv_dtype != QDEC_BF16)
       return fail(why, QDEC_E_UNSUPPORTED,
-                  "the bf16 path needs bf16 or int8-row projections / LM head and a bf16 KV cache");
+                  "the bf16 path needs bf16 or quantised projections / LM head and a bf16 KV cache");
   }
   if (c->page_size != kPage)
     return fail(why, QDEC_E_UNSUPPORTED, "page_size %d: only 16 is implemented", c->page_size);
@@ -221,9 +236,8 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
     return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
                 kMaxMergeParts);
   {
-    const int wp = c->proj_dtype == QDEC_F32 ? W_F32 : c->proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
-    const int wl = c->lm_head_dtype == QDEC_F32 ? W_F32
-                   : c->lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+    const int wp = wt_of(c->proj_dtype);
+    const int wl = wt_of(c->lm_head_dtype);
     const int64_t d = c->hidden, f = c->ffn, qd = (int64_t)c->n_q_heads * c->head_dim,
                   nqkv = (int64_t)(c->n_q_heads + 2 * c->n_kv_heads) * c->head_dim;
     if (!gemv_supported(wp, EPI_STORE, nqkv, d) || !gemv_supported(wp, EPI_RESID, d, qd) ||
@@ -231,7 +245,7 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
         !gemv_supported(wl, EPI_STORE, c->vocab, d))
       return fail(why, QDEC_E_UNSUPPORTED,
                   "a projection's input length exceeds what the GEMV keeps in registers "
-                  "(8192 fp32, 16384 bf16, 32768 int8 values)");
+                  "(8192 fp32, 16384 bf16, 32768 int8 or int4 values)");
   }
   return QDEC_OK;
 }
@@ -245,9 +259,11 @@ static void fill_info(const qdec_config& c, qdec_info* o) {
   memset(o, 0, sizeof *o);
   o->params_per_layer = mats + norms;
   o->params_total = L * (mats + norms) + v * d * (c.tied_lm_head ? 1 : 2) + d;
-  o->layer_matrix_bytes = L * mats * elem_size(c.proj_dtype);
-  o->layer_scale_bytes = c.proj_dtype == QDEC_I8_ROW ? L * rows * 4 : 0;
-  o->lm_head_bytes = v * d * elem_size(c.lm_head_dtype) + (c.lm_head_dtype == QDEC_I8_ROW ? v * 4 : 0);
+  o->layer_matrix_bytes = L * code_bytes(c.proj_dtype, 1, mats);
+  // scales: per row (I8_ROW), or per 128-value group (every projection's k is a multiple of 128)
+  o->layer_scale_bytes = c.proj_dtype == QDEC_I8_ROW ? L * rows * 4
+                         : is_grouped(c.proj_dtype) ? L * (mats / kQGroup) * 4 : 0;
+  o->lm_head_bytes = code_bytes(c.lm_head_dtype, v, d) + scale_count(c.lm_head_dtype, v, d) * 4;
   o->kv_bytes_per_layer_token = 2 * hkv * hd * elem_size(c.kv_dtype);
   o->kv_pool_bytes = L * 2 * (int64_t)c.num_pages * kPage * hkv * hd * elem_size(c.kv_dtype);
   const int64_t mp = model_max_parts(c);
@@ -288,21 +304,25 @@ QDEC_API qdec_status qdec_bytes_model(const qdec_config* c, int32_t context, int
     return fail(nullptr, QDEC_E_RANGE, "context %d outside [1, %d]", context, c->max_context);
   const int64_t d = c->hidden, hq = c->n_q_heads, hkv = c->n_kv_heads, hd = c->head_dim,
                 f = c->ffn, v = c->vocab, L = c->n_layers, T = context;
-  const int64_t we = elem_size(c->proj_dtype), ke = elem_size(c->kv_dtype),
-                ae = elem_size(c->io_dtype), le = elem_size(c->lm_head_dtype);
-  const int64_t sc = c->proj_dtype == QDEC_I8_ROW ? 4 : 0;
+  const int64_t ke = elem_size(c->kv_dtype), ae = elem_size(c->io_dtype);
+  const int pt = c->proj_dtype;
+  // weight + scale bytes of a [rows x cols] projection
+  auto wb = [&](int64_t rows, int64_t cols) {
+    return code_bytes(pt, rows, cols) + scale_count(pt, rows, cols) * 4;
+  };
   memset(o, 0, sizeof *o);
   o->embed = d * ae;
-  o->qkv = L * ((hq + 2 * hkv) * hd * (d * we + sc) + d * 4);
+  o->qkv = L * (wb((hq + 2 * hkv) * hd, d) + d * 4);
   // the attention kernel also normalises/rotates Q and K and appends the new K/V row
   o->rope_append = 0;
   o->attention = L * (T * 2 * hkv * hd * ke + (c->qk_norm ? 2 * hd * 4 : 0) + 2 * hkv * hd * ke);
   o->merge = 0;
-  o->o_proj = L * (d * (hq * hd * we + sc));
-  o->gate_up = L * (2 * f * (d * we + sc) + d * 4);
-  o->down = L * (d * (f * we + sc));
+  o->o_proj = L * wb(d, hq * hd);
+  o->gate_up = L * (wb(2 * f, d) + d * 4);
+  o->down = L * wb(d, f);
   if (with_logits) {
-    o->lm_head = v * (d * le + (c->lm_head_dtype == QDEC_I8_ROW ? 4 : 0)) + d * 4 + v * ae;
+    o->lm_head = code_bytes(c->lm_head_dtype, v, d) + scale_count(c->lm_head_dtype, v, d) * 4 +
+                 d * 4 + v * ae;
     o->argmax = 0;  // reduces per-work-group partials written by the LM head
   }
   o->total = o->embed + o->qkv + o->rope_append + o->attention + o->o_proj + o->gate_up + o->down +
@@ -389,8 +409,9 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
     m.rows = rows;
     m.cols = cols;
     m.dtype = dtype;
-    qdec_status st = c->alloc(&m.data, rows * cols * elem_size(dtype), what);
-    if (st == QDEC_OK && dtype == QDEC_I8_ROW) st = c->alloc(&m.scale, rows * 4, what);
+    qdec_status st = c->alloc(&m.data, code_bytes(dtype, rows, cols), what);
+    if (st == QDEC_OK && is_quant(dtype))
+      st = c->alloc(&m.scale, scale_count(dtype, rows, cols) * 4, what);
     return st;
   };
 
@@ -430,10 +451,7 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   TRY(c->alloc(&c->attn, hq * hd * ae, "attention output"));
   TRY(c->alloc(&c->act, f * ae, "SwiGLU output"));
   TRY(c->alloc(&c->logits, v * ie, "logits"));
-  c->am_parts = gemv_partials(cfg->lm_head_dtype == QDEC_F32    ? W_F32
-                              : cfg->lm_head_dtype == QDEC_BF16 ? W_BF16
-                                                                : W_I8,
-                              EPI_STORE, v, d);
+  c->am_parts = gemv_partials(wt_of(cfg->lm_head_dtype), EPI_STORE, v, d);
   TRY(c->alloc(&c->am_val, (int64_t)c->am_parts * 4, "argmax partials"));
   TRY(c->alloc(&c->am_idx, (int64_t)c->am_parts * 4, "argmax partials"));
   TRY(c->alloc(&c->part_acc, hq * (int64_t)c->max_parts * hd * 4, "split-KV scratch"));
@@ -514,6 +532,11 @@ static qdec_status fill_mat(qdec_ctx* c, Mat& m, const void* src, int src_dtype,
     return c->hip(launch_quantize(src, src_dtype == QDEC_BF16, static_cast<int8_t*>(m.data),
                                   m.scale, m.rows, m.cols, s),
                   "quantize kernel");
+  if (is_grouped(m.dtype))
+    return c->hip(launch_quantize_groups(src, src_dtype == QDEC_BF16,
+                                         m.dtype == QDEC_I8_G128 ? 8 : 4, m.data, m.scale, m.rows,
+                                         m.cols, s),
+                  "group quantize kernel");
   return c->hip(launch_convert(m.data, m.dtype == QDEC_BF16 ? W_BF16 : W_F32, src,
                                src_dtype == QDEC_BF16 ? W_BF16 : W_F32, n, s),
                 "convert kernel");
@@ -553,6 +576,8 @@ QDEC_API qdec_status qdec_upload(qdec_ctx* c, int32_t layer, int32_t which, cons
   }
   if (m->dtype == QDEC_I8_ROW && m->cols % 16)
     return fail(&c->err, QDEC_E_UNSUPPORTED, "int8 rows need cols %% 16 == 0");
+  if (is_grouped(m->dtype) && m->cols % kQGroup)
+    return fail(&c->err, QDEC_E_UNSUPPORTED, "group-wise rows need cols %% 128 == 0");
   st = fill_mat(c, *m, src, src_dtype, src_is_device, s);
   if (st != QDEC_OK) return st;
   c->slot(lrow, which) = 1;
@@ -566,9 +591,9 @@ QDEC_API qdec_status qdec_upload(qdec_ctx* c, int32_t layer, int32_t which, cons
   return QDEC_OK;
 }
 
-QDEC_API qdec_status qdec_upload_i8(qdec_ctx* c, int32_t layer, int32_t which,
-                                    const int8_t* codes, const float* scales, int64_t rows,
-                                    int64_t cols, int32_t src_is_device, void* stream) {
+QDEC_API qdec_status qdec_upload_quantized(qdec_ctx* c, int32_t layer, int32_t which,
+                                           const void* codes, const float* scales, int64_t rows,
+                                           int64_t cols, int32_t src_is_device, void* stream) {
   if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
   if (!codes || !scales) return fail(&c->err, QDEC_E_INVAL, "codes/scales NULL");
   Mat* m;
@@ -576,16 +601,33 @@ QDEC_API qdec_status qdec_upload_i8(qdec_ctx* c, int32_t layer, int32_t which,
   int64_t er, ec;
   qdec_status st = resolve(c, layer, which, &m, &vec, &er, &ec);
   if (st != QDEC_OK) return st;
-  if (!m || m->dtype != QDEC_I8_ROW) return fail(&c->err, QDEC_E_INVAL, "slot is not int8-row");
+  if (!m || !is_quant(m->dtype)) return fail(&c->err, QDEC_E_INVAL, "slot is not quantised");
   if (which == QDEC_W_LM_HEAD && c->cfg.tied_lm_head && c->lm_alias)
     return fail(&c->err, QDEC_E_INVAL, "tied LM head aliases the embedding");
   if (rows != er || cols != ec) return fail(&c->err, QDEC_E_INVAL, "shape mismatch");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
-  if ((st = copy_in(c, m->data, codes, rows * cols, src_is_device, s)) != QDEC_OK) return st;
-  if ((st = copy_in(c, m->scale, scales, rows * 4, src_is_device, s)) != QDEC_OK) return st;
+  if ((st = copy_in(c, m->data, codes, code_bytes(m->dtype, rows, cols), src_is_device, s)) !=
+      QDEC_OK)
+    return st;
+  if ((st = copy_in(c, m->scale, scales, scale_count(m->dtype, rows, cols) * 4, src_is_device,
+                    s)) != QDEC_OK)
+    return st;
   c->slot(is_global(which) ? c->cfg.n_layers : layer, which) = 1;
   return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_upload_i8(qdec_ctx* c, int32_t layer, int32_t which,
+                                    const int8_t* codes, const float* scales, int64_t rows,
+                                    int64_t cols, int32_t src_is_device, void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  Mat* m;
+  float* vec;
+  int64_t er, ec;
+  qdec_status st = resolve(c, layer, which, &m, &vec, &er, &ec);
+  if (st != QDEC_OK) return st;
+  if (!m || m->dtype != QDEC_I8_ROW) return fail(&c->err, QDEC_E_INVAL, "slot is not int8-row");
+  return qdec_upload_quantized(c, layer, which, codes, scales, rows, cols, src_is_device, stream);
 }
 
 QDEC_API qdec_status qdec_weight_ptr(const qdec_ctx* c0, int32_t layer, int32_t which,
@@ -740,7 +782,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
   const qdec_config& k = c->cfg;
   const int64_t d = k.hidden, hq = k.n_q_heads, hkv = k.n_kv_heads, hd = k.head_dim, f = k.ffn;
   const bool ab = c->act_bf16();
-  const int wt = k.proj_dtype == QDEC_F32 ? W_F32 : k.proj_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+  const int wt = wt_of(k.proj_dtype);
   const Layer& ly = c->layers[(size_t)l];
   switch (cls) {
     case QDEC_K_QKV: {
@@ -821,8 +863,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       return launch_gemv(wt, EPI_RESID, false, dn, s);
     }
     case QDEC_K_LM_HEAD: {
-      const int lt =
-          k.lm_head_dtype == QDEC_F32 ? W_F32 : k.lm_head_dtype == QDEC_BF16 ? W_BF16 : W_I8;
+      const int lt = wt_of(k.lm_head_dtype);
       GemvArgs h{};
       h.w = c->lm.data;
       h.scale = c->lm.scale;
@@ -1078,23 +1119,25 @@ QDEC_API qdec_status qdec_profile_kernel(qdec_ctx* c, int32_t kclass, int32_t la
 // op-level entry points
 // =====================================================================================
 
-static int wt_of(int32_t dt) { return dt == QDEC_F32 ? W_F32 : dt == QDEC_BF16 ? W_BF16 : W_I8; }
+
 
 QDEC_API qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale,
                                   const void* x, int32_t x_dtype, void* y, int32_t y_dtype,
                                   int64_t n, int64_t k, void* stream) {
   if (!w || !x || !y) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
-  if (w_dtype < QDEC_F32 || w_dtype > QDEC_I8_ROW) return fail(nullptr, QDEC_E_INVAL, "bad w_dtype");
-  if ((w_dtype == QDEC_I8_ROW) != (w_scale != nullptr))
-    return fail(nullptr, QDEC_E_INVAL, "w_scale is required for (and only for) I8_ROW");
+  if (w_dtype < QDEC_F32 || w_dtype > QDEC_I4_G128) return fail(nullptr, QDEC_E_INVAL, "bad w_dtype");
+  if (is_quant(w_dtype) != (w_scale != nullptr))
+    return fail(nullptr, QDEC_E_INVAL, "w_scale is required for (and only for) quantised weights");
   if ((x_dtype != QDEC_F32 && x_dtype != QDEC_BF16) || (y_dtype != QDEC_F32 && y_dtype != QDEC_BF16))
     return fail(nullptr, QDEC_E_INVAL, "x/y dtype must be F32 or BF16");
   if (n < 1 || k < 1) return fail(nullptr, QDEC_E_INVAL, "n and k must be positive");
-  if ((k * elem_size(w_dtype)) % 16) return fail(nullptr, QDEC_E_INVAL, "rows must be 16-byte multiples");
+  if (code_bytes(w_dtype, 1, k) % 16) return fail(nullptr, QDEC_E_INVAL, "rows must be 16-byte multiples");
+  if (is_grouped(w_dtype) && k % kQGroup)
+    return fail(nullptr, QDEC_E_INVAL, "group-wise weights need k %% 128 == 0");
   if (!gemv_supported(wt_of(w_dtype), EPI_STORE, n, k))
     return fail(nullptr, QDEC_E_UNSUPPORTED,
                 "k = %lld exceeds what the GEMV keeps in registers (8192 fp32, 16384 bf16, "
-                "32768 int8 values)", (long long)k);
+                "32768 int8 or int4 values)", (long long)k);
   if (!aligned(w, 16) || !aligned(x, 16) || !aligned(y, 4) || (w_scale && !aligned(w_scale, 4)))
     return fail(nullptr, QDEC_E_INVAL, "misaligned pointer (w and x 16-byte, y 4-byte)");
   GemvArgs a{};
@@ -1120,6 +1163,21 @@ QDEC_API qdec_status qdec_op_quantize_rows(const void* w, int32_t w_dtype, int8_
     return fail(nullptr, QDEC_E_INVAL, "misaligned pointer");
   hipError_t e = launch_quantize(w, w_dtype == QDEC_BF16, codes, scales, n, k,
                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "quantize launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_quantize_groups(const void* w, int32_t w_dtype, int32_t dst_dtype,
+                                             void* codes, float* scales, int64_t n, int64_t k,
+                                             void* stream) {
+  if (!w || !codes || !scales) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (w_dtype != QDEC_F32 && w_dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad w_dtype");
+  if (!is_grouped(dst_dtype)) return fail(nullptr, QDEC_E_INVAL, "dst_dtype must be I8_G128 or I4_G128");
+  if (n < 1 || k < 1 || k % kQGroup) return fail(nullptr, QDEC_E_INVAL, "need n, k > 0 and k %% 128 == 0");
+  if (!aligned(w, 8) || !aligned(codes, 4) || !aligned(scales, 4))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer (w 8-byte, codes and scales 4-byte)");
+  hipError_t e = launch_quantize_groups(w, w_dtype == QDEC_BF16, dst_dtype == QDEC_I8_G128 ? 8 : 4,
+                                        codes, scales, n, k, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "quantize launch: %s", hipGetErrorString(e));
   return QDEC_OK;
 }

@@ -16,7 +16,7 @@ _lib = None
 # qdec_status
 OK, E_INVAL, E_UNSUPPORTED, E_STATE, E_RANGE, E_NOMEM, E_HIP = range(7)
 # qdec_dtype
-F32, BF16, I8_ROW = 0, 1, 2
+F32, BF16, I8_ROW, I8_G128, I4_G128 = 0, 1, 2, 3, 4
 # qdec_weight
 (W_EMBED, W_LM_HEAD, W_FINAL_NORM, W_IN_NORM, W_POST_NORM, W_Q_NORM, W_K_NORM, W_QKV, W_O,
  W_GATE_UP, W_DOWN) = range(11)
@@ -74,6 +74,7 @@ _SIGS = {
     "qdec_info_get": [_P, C.POINTER(qdec_info)],
     "qdec_upload": [_P, _I32, _I32, _P, _I32, _I64, _I64, _I32, _P],
     "qdec_upload_i8": [_P, _I32, _I32, _P, _P, _I64, _I64, _I32, _P],
+    "qdec_upload_quantized": [_P, _I32, _I32, _P, _P, _I64, _I64, _I32, _P],
     "qdec_weight_ptr": [_P, _I32, _I32, C.POINTER(_P), C.POINTER(_P)],
     "qdec_kv_set_block_table": [_P, _P, _I32, _P],
     "qdec_kv_write": [_P, _I32, _I32, _I32, _P, _P, _P],
@@ -89,6 +90,7 @@ _SIGS = {
     "qdec_profile_kernel": [_P, _I32, _I32, _I32, C.POINTER(qdec_step), _P],
     "qdec_op_gemv": [_P, _I32, _P, _P, _I32, _P, _I32, _I64, _I64, _P],
     "qdec_op_quantize_rows": [_P, _I32, _P, _P, _I64, _I64, _P],
+    "qdec_op_quantize_groups": [_P, _I32, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
     "qdec_op_rope_table": [_P, _I32, _I32, _F, _P],
     "qdec_op_qk_norm_rope_append": [_P, _P, _P, _F, _P, _I32, _P, _I32, _P, _P, _I32, _P, _I32,
@@ -211,6 +213,12 @@ def qdec_upload_i8(ctx, layer, which, codes, scales, rows, cols, src_is_device=1
           _p(stream), ctx=ctx)
 
 
+def qdec_upload_quantized(ctx, layer, which, codes, scales, rows, cols, src_is_device=1,
+                          stream=None):
+    _call("qdec_upload_quantized", ctx, layer, which, _p(codes), _p(scales), rows, cols,
+          src_is_device, _p(stream), ctx=ctx)
+
+
 def qdec_weight_ptr(ctx, layer, which):
     d, s = C.c_void_p(), C.c_void_p()
     _call("qdec_weight_ptr", ctx, layer, which, C.byref(d), C.byref(s), ctx=ctx)
@@ -301,6 +309,11 @@ def qdec_op_gemv(w, w_dtype, w_scale, x, x_dtype, y, y_dtype, n, k, stream=None)
 
 def qdec_op_quantize_rows(w, w_dtype, codes, scales, n, k, stream=None):
     _call("qdec_op_quantize_rows", _p(w), w_dtype, _p(codes), _p(scales), n, k, _p(stream))
+
+
+def qdec_op_quantize_groups(w, w_dtype, dst_dtype, codes, scales, n, k, stream=None):
+    _call("qdec_op_quantize_groups", _p(w), w_dtype, dst_dtype, _p(codes), _p(scales), n, k,
+          _p(stream))
 
 
 def qdec_op_rmsnorm(x, gamma, eps, y, y_dtype, n, stream=None):

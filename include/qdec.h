@@ -55,7 +55,16 @@ typedef enum qdec_status {
 /* Storage types.  [ETE] (the bf16 storage passage) and [Qwen3-runtime] §0.1: bf16 is a storage
  * format; every product and reduction is done in fp32.  QDEC_I8_ROW is W8A16 with one fp32 scale
  * per output row (symmetric, codes in [-127, 127]; [ETE], the int8 quantisation passage). */
-typedef enum qdec_dtype { QDEC_F32 = 0, QDEC_BF16 = 1, QDEC_I8_ROW = 2 } qdec_dtype;
+/* QDEC_I8_G128 and QDEC_I4_G128 keep one fp32 scale per 128-value group of a row
+ * ([Qwen3-runtime] §13.1: the W8A16 kernel walks a row in 128-value groups, each with its own
+ * scale; [ETE] names 4-bit codes as the next step).  Per group: scale = max|w| / 127 (int8) or
+ * / 7 (int4) in fp32, codes round-half-even(w / scale) clamped to [-127, 127] or [-7, 7].
+ * Layouts, row-major [rows x cols]: I8_G128 codes are int8 [rows][cols]; I4_G128 codes are two per
+ * byte, [rows][cols / 2], element 2j in the low nibble of byte j, each nibble stored as code + 8;
+ * scales [rows][cols / 128].  cols % 128 == 0. */
+typedef enum qdec_dtype {
+  QDEC_F32 = 0, QDEC_BF16 = 1, QDEC_I8_ROW = 2, QDEC_I8_G128 = 3, QDEC_I4_G128 = 4
+} qdec_dtype;
 
 /* Model and cache geometry.  [Qwen3-runtime] §1.1 (shapes), §2.1-2.7 (the layer), §3.3 (KV). */
 typedef struct qdec_config {
@@ -89,9 +98,11 @@ typedef struct qdec_config {
 
 /* Supported dtype combinations (checked by qdec_config_validate):
  *   io F32  : proj, lm_head, act and kv all F32                                  (the fp32 path)
- *   io BF16 : proj BF16 | I8_ROW, lm_head BF16 | I8_ROW, act F32 | BF16, kv BF16   (bf16 / W8A16) */
+ *   io BF16 : proj and lm_head each BF16 | I8_ROW | I8_G128 | I4_G128, act F32 | BF16, kv BF16
+ *             (bf16 / W8A16 / W4A16); the group-wise types need hidden, ffn and
+ *             n_q_heads * head_dim to be multiples of 128 */
 
-/* Weight slots for qdec_upload / qdec_upload_i8.  Norm gammas are always stored fp32 (small
+/* Weight slots for qdec_upload / qdec_upload_quantized.  Norm gammas are always stored fp32 (small
  * sensitive tensors stay fp32: [ETE], the int8 quantisation passage). */
 typedef enum qdec_weight {
   QDEC_W_EMBED = 0,      /* [vocab x hidden] in io_dtype; global (layer ignored) */
@@ -134,8 +145,8 @@ typedef struct qdec_step {
 typedef struct qdec_info {
   int64_t params_per_layer;        /* matrices + the four gammas of one layer */
   int64_t params_total;            /* all layers + embedding + final norm (+ LM head if untied) */
-  int64_t layer_matrix_bytes;      /* bytes of all layers' matrices as stored (codes for I8_ROW) */
-  int64_t layer_scale_bytes;       /* fp32 row scales of I8_ROW layer matrices (0 otherwise) */
+  int64_t layer_matrix_bytes;      /* bytes of all layers' matrices as stored (codes if quantised) */
+  int64_t layer_scale_bytes;       /* fp32 scales of quantised layer matrices (0 otherwise) */
   int64_t lm_head_bytes;           /* LM head as stored, scales included */
   int64_t kv_bytes_per_layer_token;
   int64_t kv_pool_bytes;           /* n_layers * 2 * num_pages * page_size * Hkv * D * elem */
@@ -196,22 +207,30 @@ qdec_status qdec_info_get(const qdec_ctx* ctx, qdec_info* out);
 /* Copies one weight tensor into the context, converting to the slot's storage dtype:
  * F32->BF16 rounds to nearest even, BF16->F32 widens exactly, F32|BF16 -> I8_ROW quantises each
  * row on the device (scale = max|row| / 127 in fp32, code = round-half-even(w / scale) clamped to
- * [-127, 127], zero rows get scale 0 and zero codes).  `src` is [rows x cols] of src_dtype
+ * [-127, 127], zero rows get scale 0 and zero codes), F32|BF16 -> I8_G128 | I4_G128 quantises
+ * each 128-value group the same way (qdec_dtype).  `src` is [rows x cols] of src_dtype
  * (QDEC_F32 or QDEC_BF16), contiguous; rows/cols must equal the slot's shape.  `layer` selects the
  * block for per-layer slots (ignored for global ones).  A host source (src_is_device = 0) is
  * accepted only when no conversion is needed.  Uploading QDEC_W_EMBED with tied_lm_head also
- * fills the LM head (quantising it when lm_head_dtype is I8_ROW).  Asynchronous on `stream`. */
+ * fills the LM head (quantising it when lm_head_dtype is quantised).  Asynchronous on `stream`. */
 qdec_status qdec_upload(qdec_ctx* ctx, int32_t layer, int32_t which, const void* src,
                         int32_t src_dtype, int64_t rows, int64_t cols, int32_t src_is_device,
                         void* stream);
 
-/* Copies pre-quantised codes [rows x cols] int8 and scales [rows] fp32 into an I8_ROW slot. */
+/* Copies pre-quantised codes and fp32 scales, in the layouts of the slot's dtype (qdec_dtype),
+ * into a quantised slot (I8_ROW, I8_G128 or I4_G128); QDEC_E_INVAL for another slot dtype or a
+ * shape mismatch.  Asynchronous on `stream`; a host source is copied synchronously. */
+qdec_status qdec_upload_quantized(qdec_ctx* ctx, int32_t layer, int32_t which, const void* codes,
+                                  const float* scales, int64_t rows, int64_t cols,
+                                  int32_t src_is_device, void* stream);
+
+/* qdec_upload_quantized for an I8_ROW slot only: codes [rows x cols] int8, scales [rows]. */
 qdec_status qdec_upload_i8(qdec_ctx* ctx, int32_t layer, int32_t which, const int8_t* codes,
                            const float* scales, int64_t rows, int64_t cols, int32_t src_is_device,
                            void* stream);
 
 /* Device pointers of a stored weight slot (for read-back in tests): *data receives the matrix as
- * stored, *scales the fp32 row scales (NULL unless I8_ROW). */
+ * stored, *scales the fp32 scales (NULL unless quantised). */
 qdec_status qdec_weight_ptr(const qdec_ctx* ctx, int32_t layer, int32_t which, void** data,
                             float** scales);
 
@@ -304,10 +323,12 @@ qdec_status qdec_profile_kernel(qdec_ctx* ctx, int32_t kclass, int32_t layer, in
 /* ---- op-level entry points on caller-owned device buffers ---------------------------------- */
 
 /* y = W x for one row-major matrix ([Qwen3-runtime] §4.1: M = 1 is a GEMV; §13.1 W8A16).
- * w: [n x k] of w_dtype (F32, BF16, or I8_ROW codes with w_scale = [n] fp32 row scales; w_scale
- * must be NULL otherwise).  x: [k] of x_dtype (F32 | BF16).  y: [n] of y_dtype (F32 | BF16, the
- * fp32 sum rounded to nearest even).  k must be a multiple of 16 / elem_size(w) and at most
- * 8192 (F32 weights), 16384 (BF16) or 32768 (I8_ROW): the kernel keeps each wave's slice of x
+ * w: [n x k] of w_dtype (F32, BF16, or quantised codes with w_scale: [n] fp32 row scales for
+ * I8_ROW, [n][k / 128] group scales for I8_G128 / I4_G128 (qdec_dtype), whose k must be a
+ * multiple of 128; w_scale must be NULL otherwise).  x: [k] of x_dtype (F32 | BF16).  y: [n] of
+ * y_dtype (F32 | BF16, the fp32 sum rounded to nearest even).  A row must fill whole 16-byte
+ * vectors (k a multiple of 4 fp32, 8 bf16, 16 int8 or 32 int4 values) and k be at most
+ * 8192 (F32 weights), 16384 (BF16) or 32768 (int8 / int4): the kernel keeps each wave's slice of x
  * in registers (QDEC_E_UNSUPPORTED beyond).  w and x 16-byte aligned, y and w_scale 4-byte
  * aligned (QDEC_E_INVAL otherwise). */
 qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale, const void* x,
@@ -318,6 +339,12 @@ qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale, c
  * codes [n x k] int8, scales [n] fp32.  k % 16 == 0. */
 qdec_status qdec_op_quantize_rows(const void* w, int32_t w_dtype, int8_t* codes, float* scales,
                                   int64_t n, int64_t k, void* stream);
+
+/* Group-wise quantisation (the rule of qdec_upload for I8_G128 / I4_G128): w [n x k] F32|BF16 ->
+ * codes and scales [n][k / 128] in the layouts of dst_dtype (qdec_dtype).  k % 128 == 0; w
+ * 8-byte aligned, codes and scales 4-byte aligned. */
+qdec_status qdec_op_quantize_groups(const void* w, int32_t w_dtype, int32_t dst_dtype, void* codes,
+                                    float* scales, int64_t n, int64_t k, void* stream);
 
 /* y = x / sqrt(mean(x^2) + eps) * gamma ([Qwen3-runtime] §2.1), x fp32 [n], y [n] of y_dtype. */
 qdec_status qdec_op_rmsnorm(const float* x, const float* gamma, float eps, void* y,

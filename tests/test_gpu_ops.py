@@ -118,6 +118,99 @@ def test_w8a16_gemv_full_size(n, k):
     assert _bf16_ulp_ok(got, exact).all()
 
 
+# ---- group-wise int8 / int4 (128-value groups) -------------------------------------------------------
+
+def _group_codes_torch(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
+
+
+@pytest.mark.parametrize("wdt", [Q.I8_G128, Q.I4_G128])
+@pytest.mark.parametrize("xdt", [Q.BF16, Q.F32])
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 256), (1001, 1152), (4096, 1024), (515, 3072),
+                                 (64, 12288), (3, 32768)])
+def test_group_gemv_matches_oracle(wdt, xdt, n, k):
+    print(f"group gemv wdt={wdt} xdt={xdt} n={n} k={k}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(n * 11 + k + wdt)
+    w32 = (torch.randn((n, k), generator=g, device=DEV) * 0.02).cpu().numpy()
+    xf = torch.randn((k,), generator=g, device=DEV)
+    x = xf.to(torch.bfloat16) if xdt == Q.BF16 else xf
+    xh = (synth.bf16_to_f32(x) if xdt == Q.BF16 else x.cpu().numpy()).astype(np.float64)
+    codes, sc = oracle.quantize_groups(w32, 8 if wdt == Q.I8_G128 else 4)
+    exact = oracle.gemv(codes, xh, sc)
+    w = _group_codes_torch(codes)
+    scale = torch.from_numpy(sc).to(DEV)
+    y32 = torch.empty(n, device=DEV)
+    ybf = torch.empty(n, device=DEV, dtype=torch.bfloat16)
+    Q.qdec_op_gemv(w, wdt, scale, x, xdt, y32, Q.F32, n, k)
+    Q.qdec_op_gemv(w, wdt, scale, x, xdt, ybf, Q.BF16, n, k)
+    _sync()
+    assert np.max(np.abs(y32.cpu().numpy() - exact)) <= 1e-4
+    assert _bf16_ulp_ok(synth.bf16_to_f32(ybf), exact).all()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_quantize_groups_bit_exact(bits, src):
+    n, k = 333, 1536
+    g = torch.Generator(device=DEV).manual_seed(12 + bits)
+    w = torch.randn((n, k), generator=g, device=DEV) * 0.02
+    w[5] = 0.0                                   # zero row: every group scale 0
+    w[6, 128:256] = 0.0                          # one zero group
+    w[7, 3] = 0.9                                # one dominant entry
+    w[9] = -w[9].abs()                           # all-negative row
+    if src == "bf16":
+        w = w.to(torch.bfloat16)
+    dst = Q.I8_G128 if bits == 8 else Q.I4_G128
+    codes = torch.empty((n, k) if bits == 8 else (n, k // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                        device=DEV)
+    scales = torch.empty((n, k // 128), device=DEV)
+    Q.qdec_op_quantize_groups(w, Q.BF16 if src == "bf16" else Q.F32, dst, codes, scales, n, k)
+    _sync()
+    wf = synth.bf16_to_f32(w) if src == "bf16" else w.cpu().numpy()
+    q_ref, s_ref = oracle.quantize_groups(wf, bits)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("n,k", synth.GEMV_SHAPES)
+def test_group_gemv_full_size(bits, n, k):
+    """The LM-head shapes at full size with group-wise codes: codes and scales bit-exact over the
+    whole matrix, outputs within one bf16 ulp of the oracle at 4096 sampled rows plus the
+    extreme rows."""
+    print(f"group gemv full bits={bits} n={n} k={k}", flush=True)
+    w, x = synth.gemv_inputs(n, k, device=DEV)
+    dst = Q.I8_G128 if bits == 8 else Q.I4_G128
+    codes = torch.empty((n, k) if bits == 8 else (n, k // 2), dtype=torch.int8 if bits == 8 else torch.uint8,
+                        device=DEV)
+    scales = torch.empty((n, k // 128), device=DEV)
+    Q.qdec_op_quantize_groups(w, Q.F32, dst, codes, scales, n, k)
+    y = torch.empty(n, device=DEV, dtype=torch.bfloat16)
+    Q.qdec_op_gemv(codes, dst, scales, x, Q.BF16, y, Q.BF16, n, k)
+    _sync()
+    q_ref, s_ref = oracle.quantize_groups(w.cpu().numpy(), bits)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    rows = np.unique(np.concatenate([np.random.default_rng(0).choice(n, 4096, replace=False),
+                                     [0, 1, n - 2, n - 1]]))
+    exact = oracle.gemv(q_ref[rows], synth.bf16_to_f32(x).astype(np.float64), s_ref[rows])
+    got = synth.bf16_to_f32(y)[rows]
+    assert _bf16_ulp_ok(got, exact).all()
+
+
+def test_group_gemv_rejects_bad_arguments():
+    w = torch.zeros((4, 256), dtype=torch.int8, device=DEV)
+    sc = torch.zeros((4, 2), device=DEV)
+    x = torch.zeros(256, device=DEV)
+    y = torch.zeros(4, device=DEV)
+    with pytest.raises(Q.QdecError):
+        Q.qdec_op_gemv(w, Q.I8_G128, None, x, Q.F32, y, Q.F32, 4, 256)   # scales missing
+    with pytest.raises(Q.QdecError):
+        Q.qdec_op_gemv(w, Q.I8_G128, sc, x, Q.F32, y, Q.F32, 4, 192)     # k % 128 != 0
+    with pytest.raises(Q.QdecError):
+        Q.qdec_op_quantize_groups(x, Q.F32, Q.I8_ROW, w, sc, 1, 256)     # not a group dtype
+
+
 # ---- RMSNorm, RoPE table, fused Q/K norm + RoPE + append ---------------------------------------------------
 
 def test_rmsnorm_op():
