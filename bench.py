@@ -31,7 +31,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--model", choices=["0.6b", "8b"], default="0.6b")
-    p.add_argument("--path", choices=["bf16", "w8a16"], default="bf16")
+    p.add_argument("--path", choices=["bf16", "w8a16", "w8a16g", "w4a16"], default="bf16",
+                   help="weights: bf16, int8 per row, int8 or int4 per 128-value group")
     p.add_argument("--act", choices=["f32", "bf16"], default=None,
                    help="activation precision at op boundaries (default f32)")
     p.add_argument("--ctx", type=int, default=None, help="context T (default 4096 / 8192 for 8b)")
@@ -150,26 +151,39 @@ def ops_bench():
                                      "bytes": kv_bytes, "gbps": round(kv_bytes / us / 1e3, 1)})
         del pools
         torch.cuda.empty_cache()
+    # weight formats of the GEMV workloads: (storage type, bytes of codes + scales)
+    gemv_formats = {"w8a16": (Q.I8_ROW, lambda n, k: n * k + 4 * n),
+                    "w8a16g": (Q.I8_G128, lambda n, k: n * k + 4 * n * (k // 128)),
+                    "w4a16": (Q.I4_G128, lambda n, k: n * k // 2 + 4 * n * (k // 128)),
+                    "bf16": (Q.BF16, lambda n, k: 2 * n * k)}
     for n, k in synth.GEMV_SHAPES:
-        for wt in ("w8a16", "bf16"):
-            wb = n * k * (1 if wt == "w8a16" else 2)
+        for wt, (wdt, wbytes) in gemv_formats.items():
+            wb = wbytes(n, k)
             copies = max(2, math.ceil((1 << 30) / wb))
-            if wt == "w8a16":
+            if wdt == Q.I8_ROW:
                 ws = [(torch.randint(-127, 128, (n, k), generator=gen, device=dev,
                                      dtype=torch.int8),
                        torch.rand((n,), generator=gen, device=dev) * 1e-3) for _ in range(copies)]
-                nbytes = n * k + 4 * n + 2 * k + 2 * n
+            elif wdt == Q.I8_G128:
+                ws = [(torch.randint(-127, 128, (n, k), generator=gen, device=dev,
+                                     dtype=torch.int8),
+                       torch.rand((n, k // 128), generator=gen, device=dev) * 1e-3)
+                      for _ in range(copies)]
+            elif wdt == Q.I4_G128:
+                ws = [(torch.randint(1, 256, (n, k // 2), generator=gen, device=dev,
+                                     dtype=torch.int32).to(torch.uint8),
+                       torch.rand((n, k // 128), generator=gen, device=dev) * 1e-3)
+                      for _ in range(copies)]
             else:
                 ws = [(torch.randn((n, k), generator=gen, device=dev).mul_(0.02).to(torch.bfloat16),
                        None) for _ in range(copies)]
-                nbytes = 2 * n * k + 2 * k + 2 * n
+            nbytes = wb + 2 * k + 2 * n
             x = torch.randn((k,), generator=gen, device=dev).to(torch.bfloat16)
             y = torch.empty((n,), dtype=torch.bfloat16, device=dev)
 
-            def enq(i, ws=ws, wt=wt):
+            def enq(i, ws=ws, wdt=wdt):
                 w, sc = ws[i % copies]
-                Q.qdec_op_gemv(w, Q.I8_ROW if wt == "w8a16" else Q.BF16, sc, x, Q.BF16, y, Q.BF16,
-                               n, k, stream=s.cuda_stream)
+                Q.qdec_op_gemv(w, wdt, sc, x, Q.BF16, y, Q.BF16, n, k, stream=s.cuda_stream)
 
             us = per_launch_us(enq, 2 * copies)
             out["gemv"].append({"shape": [n, k], "weights": wt, "us": round(us, 2),
@@ -321,14 +335,16 @@ def main():
         g_logits = synth.bf16_to_f32(logits).astype(np.float64)
         g_arg = int(amax.item())
         hw = synth.host_weights(w)
-        if args.path == "w8a16":
+        if args.path != "bf16":
+            quant = {"w8a16": oracle.quantize_rows,
+                     "w8a16g": lambda a: oracle.quantize_groups(a, 8),
+                     "w4a16": lambda a: oracle.quantize_groups(a, 4)}[args.path]
             for key in ("qkv", "o", "gate_up", "down"):
-                qs = [oracle.quantize_rows(oracle.bf16_bits_to_f64(b).astype(np.float32))
-                      for b in hw[key]]
+                qs = [quant(oracle.bf16_bits_to_f64(b).astype(np.float32)) for b in hw[key]]
                 hw[key] = [q for q, _ in qs]
                 hw[key + "_scale"] = [s for _, s in qs]
             lm_src = hw["lm_head"] if hw.get("lm_head") is not None else hw["embed"]
-            q, s = oracle.quantize_rows(oracle.bf16_bits_to_f64(lm_src).astype(np.float32))
+            q, s = quant(oracle.bf16_bits_to_f64(lm_src).astype(np.float32))
             hw["lm_head"], hw["lm_scale"] = q, s
         om = oracle.Model(dict(shape, act_bf16=int(cfg.act_dtype == Q.BF16), kv_bf16=1,
                                logits_bf16=1), hw, max_ctx=T)

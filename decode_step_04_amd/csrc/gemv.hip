@@ -475,6 +475,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 //   R:     rows per wave, the largest of 4, 2, 1 that keeps at most 16 loads per lane in flight
 //          (8 when the next round is prefetched) and at least 2048 waves in the grid (measured:
 //          the small projections of a 0.6B-class step ran 4% faster per step than at 1024);
+//          int4 lanes load 8 bytes, so their budgets double (larger int4 matrices: below);
 //   wgs:   enough work-groups for one round, up to 4096; beyond that 1024 work-groups (4096
 //          waves, all resident) each run several rounds with the next one requested ahead
 //          (PIPE), R re-chosen for two sets of 8 loads; matrices above 64 MiB are streamed by
@@ -500,11 +501,14 @@ constexpr int64_t kStreamBytes = int64_t(64) << 20;
 constexpr int64_t kStreamWgs = 512;
 constexpr bool kStreamPipe = false;
 constexpr int kStreamLoads = 8;
+constexpr int64_t kI4Bytes = int64_t(8) << 20;  // int4 matrices above this take their own plan
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int vec = wtype == W_F32 ? 4 : wtype == W_BF16 ? 8 : 16;
   const int bits = wtype == W_F32 ? 32 : wtype == W_BF16 ? 16 : wtype == W_I4G ? 4 : 8;
   const bool grouped = wtype == W_I8G || wtype == W_I4G;
+  // load budgets below count 16-byte lane loads; int4 lanes load 8 bytes, so twice as many fit
+  const int lmul = wtype == W_I4G ? 2 : 1;
   const int64_t ch = 64 * vec;
   const int pairs = epi == EPI_SWIGLU ? 2 : 1;
   auto chunks = [&](int s) { return (int)((k / s + ch - 1) / ch); };
@@ -525,6 +529,7 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int gpw = 4 / split;
   // loads per lane in flight: 16, or 8 per set when the next round is requested ahead
   auto pick_r = [&](int budget) {
+    budget *= lmul;
     for (int cand : {4, 2})
       if (cand * pairs * p.maxch <= budget && ((n + cand - 1) / cand) * split >= kMinWaves)
         return cand;
@@ -536,7 +541,7 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
     p.r = pick_r(kStreamLoads);
     // fewer than kStreamLoads loads per round (short int8 rows): request the next round ahead
     // so that a wave still keeps about that many in flight
-    p.pipe = kStreamPipe || p.r * pairs * p.maxch < kStreamLoads;
+    p.pipe = kStreamPipe || p.r * pairs * p.maxch < kStreamLoads * lmul;
     wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
     if (wgs > kStreamWgs) wgs = kStreamWgs;
   } else {
@@ -549,6 +554,20 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
       if (wgs > kPipeWgs) wgs = kPipeWgs;
     }
   }
+  if (wtype == W_I4G && wbytes > kI4Bytes) {
+    // int4 spends about as long converting codes as the bytes take to arrive, so it needs more
+    // waves per SIMD to overlap the two: 2 (4 above 64 MiB) rows per wave, up to 1024 (2048)
+    // work-groups, the next round requested ahead when there are several (measured on MI355X
+    // over R = 2/4/8, 512-4096 work-groups and both round modes for six matrix shapes)
+    const bool big = wbytes > kStreamBytes;
+    const int64_t cap = big ? 2048 : 1024;
+    for (p.r = big ? 4 : 2;; p.r /= 2) {  // fewer rows when the loads exceed the register budget
+      const int64_t need = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
+      wgs = need < cap ? need : cap;
+      p.pipe = need > wgs;
+      if (p.r == 1 || p.r * pairs * p.maxch <= (p.pipe ? 8 : 16) * lmul) break;
+    }
+  }
   p.wgs = (unsigned)(wgs < 1 ? 1 : wgs);
   return p;
 }
@@ -556,7 +575,8 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
 template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
 static hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   constexpr int loads = (EPI == EPI_SWIGLU ? 2 : 1) * R * MAXCH;
-  if constexpr (loads > (PIPE ? 8 : 16)) {
+  constexpr int lmul = WT == W_I4G ? 2 : 1;
+  if constexpr (loads > (PIPE ? 8 : 16) * lmul) {
     return hipErrorInvalidConfiguration;  // never planned: over the register budget
   } else {
     hipLaunchKernelGGL((k_gemv<WT, EPI, NORM, XB, R, MAXCH, PIPE>), dim3(p.wgs), dim3(256), 0, s,

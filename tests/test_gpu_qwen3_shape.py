@@ -34,6 +34,12 @@ MAXCTX = 4096
 CONTEXTS = (512, 2048, 4096)
 
 
+# the oracle's quantiser of each quantised path (the device quantises the same bf16 values)
+QUANTISERS = {"w8a16": oracle.quantize_rows,
+              "w8a16g": lambda w: oracle.quantize_groups(w, 8),
+              "w4a16": lambda w: oracle.quantize_groups(w, 4)}
+
+
 class Setup:
     def __init__(self, path, act):
         print(f"qwen3-0.6b setup path={path} act={act}", flush=True)
@@ -49,13 +55,13 @@ class Setup:
         kv = synth.kv_prefill(SHAPE, MAXCTX - 1, seed=1, device=DEV)
         loader.prefill_kv(self.ctx, kv)
         hw = synth.host_weights(self.w)
-        if path == "w8a16":
+        if path in QUANTISERS:
+            quant = QUANTISERS[path]
             for key in ("qkv", "o", "gate_up", "down"):
-                qs = [oracle.quantize_rows(oracle.bf16_bits_to_f64(b).astype(np.float32))
-                      for b in hw[key]]
+                qs = [quant(oracle.bf16_bits_to_f64(b).astype(np.float32)) for b in hw[key]]
                 hw[key] = [q for q, _ in qs]
                 hw[key + "_scale"] = [s for _, s in qs]
-            q, s = oracle.quantize_rows(oracle.bf16_bits_to_f64(hw["embed"]).astype(np.float32))
+            q, s = quant(oracle.bf16_bits_to_f64(hw["embed"]).astype(np.float32))
             hw["lm_head"], hw["lm_scale"] = q, s
         self.hw = hw
         self.om = oracle.Model(dict(SHAPE, act_bf16=int(act == "bf16"), kv_bf16=1, logits_bf16=1),
@@ -134,7 +140,10 @@ def _close_setups():
 # at op boundaries (the 16-bit activation policy) and the int8 per-row weights at both ends.
 CASES = ([("bf16", "f32", T) for T in CONTEXTS] +
          [("bf16", "bf16", 512), ("bf16", "bf16", 4096), ("w8a16", "bf16", 512),
-          ("w8a16", "bf16", 4096), ("w8a16", "f32", 4096)])
+          ("w8a16", "bf16", 4096), ("w8a16", "f32", 4096),
+          # group-wise int8 and int4 weights (128-value groups)
+          ("w8a16g", "f32", 4096), ("w4a16", "f32", 512), ("w4a16", "f32", 4096),
+          ("w4a16", "bf16", 4096)])
 
 
 @pytest.mark.parametrize("path,act,T", CASES)
@@ -178,15 +187,20 @@ def test_appended_kv_matches_oracle():
             assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0**-7 + atol), layer
 
 
-def test_w8a16_codes_bit_exact():
-    w8 = setup("w8a16", "bf16")
+def _tdt(codes):
+    return torch.int8 if codes.dtype == np.int8 else torch.uint8  # packed int4 bytes
+
+
+@pytest.mark.parametrize("path", ["w8a16", "w8a16g", "w4a16"])
+def test_quantised_codes_bit_exact(path):
+    w8 = setup(path, "bf16" if path == "w8a16" else "f32")
     for layer in (0, 27):
         for which, key in ((Q.W_QKV, "qkv"), (Q.W_O, "o"), (Q.W_GATE_UP, "gate_up"),
                            (Q.W_DOWN, "down")):
             data, scale = Q.qdec_weight_ptr(w8.ctx, layer, which)
             ref_q = w8.hw[key][layer]
             ref_s = w8.hw[key + "_scale"][layer]
-            q = torch.empty(ref_q.shape, dtype=torch.int8, device=DEV)
+            q = torch.empty(ref_q.shape, dtype=_tdt(ref_q), device=DEV)
             sc = torch.empty(ref_s.shape, dtype=torch.float32, device=DEV)
             Q.qdec_op_copy(q, data, q.numel())
             Q.qdec_op_copy(sc, scale, sc.numel() * 4)
@@ -194,7 +208,7 @@ def test_w8a16_codes_bit_exact():
             assert np.array_equal(q.cpu().numpy(), ref_q), (layer, key)
             assert np.array_equal(sc.cpu().numpy(), ref_s), (layer, key)
     data, scale = Q.qdec_weight_ptr(w8.ctx, 0, Q.W_LM_HEAD)
-    q = torch.empty(w8.hw["lm_head"].shape, dtype=torch.int8, device=DEV)
+    q = torch.empty(w8.hw["lm_head"].shape, dtype=_tdt(w8.hw["lm_head"]), device=DEV)
     sc = torch.empty(w8.hw["lm_scale"].shape, dtype=torch.float32, device=DEV)
     Q.qdec_op_copy(q, data, q.numel())
     Q.qdec_op_copy(sc, scale, sc.numel() * 4)
