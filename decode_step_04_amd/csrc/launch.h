@@ -33,6 +33,8 @@ hipError_t launch_attention_merge(int head_dim, const AttnArgs& a, hipStream_t s
 constexpr int kMaxMergeParts = 8192;  // partitions per head the split-KV scratch layout allows
 
 hipError_t launch_rope_append(int head_dim, const RopeAppendArgs& a, hipStream_t s);
+// Prefill GEMM on MFMA (epi: EPI_STORE, EPI_RESID or EPI_SWIGLU); k % 32 == 0.
+hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 const void* embed_kernel_fn();
 

@@ -1167,6 +1167,36 @@ QDEC_API qdec_status qdec_op_quantize_rows(const void* w, int32_t w_dtype, int8_
   return QDEC_OK;
 }
 
+QDEC_API qdec_status qdec_op_gemm(const void* a, const void* w, void* y, int32_t y_dtype,
+                                  float* resid, int32_t epilogue, int32_t m, int32_t n, int32_t k,
+                                  void* stream) {
+  if (!a || !w) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (epilogue < QDEC_GEMM_STORE || epilogue > QDEC_GEMM_SWIGLU)
+    return fail(nullptr, QDEC_E_INVAL, "bad epilogue");
+  if (m < 1 || n < 1 || k < 32 || k % 32) return fail(nullptr, QDEC_E_INVAL, "need m, n > 0 and k a positive multiple of 32");
+  if (epilogue == QDEC_GEMM_RESID ? !resid : !y) return fail(nullptr, QDEC_E_INVAL, "output is NULL");
+  if (epilogue == QDEC_GEMM_STORE && y_dtype != QDEC_F32 && y_dtype != QDEC_BF16)
+    return fail(nullptr, QDEC_E_INVAL, "y_dtype must be F32 or BF16");
+  if (epilogue == QDEC_GEMM_SWIGLU && y_dtype != QDEC_BF16)
+    return fail(nullptr, QDEC_E_INVAL, "the SwiGLU epilogue writes BF16");
+  if (!aligned(a, 16) || !aligned(w, 16) || (y && !aligned(y, 4)) || (resid && !aligned(resid, 4)))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer (a and w 16-byte)");
+  GemmArgs g{};
+  g.a = a;
+  g.w = w;
+  g.y = y;
+  g.y_bf16 = y_dtype == QDEC_BF16;
+  g.resid = resid;
+  g.m = m;
+  g.n = n;
+  g.k = k;
+  hipError_t e = launch_gemm(epilogue == QDEC_GEMM_STORE ? EPI_STORE
+                             : epilogue == QDEC_GEMM_RESID ? EPI_RESID : EPI_SWIGLU,
+                             g, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "gemm launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
 QDEC_API qdec_status qdec_op_quantize_groups(const void* w, int32_t w_dtype, int32_t dst_dtype,
                                              void* codes, float* scales, int64_t n, int64_t k,
                                              void* stream) {

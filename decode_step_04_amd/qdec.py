@@ -91,6 +91,7 @@ _SIGS = {
     "qdec_op_gemv": [_P, _I32, _P, _P, _I32, _P, _I32, _I64, _I64, _P],
     "qdec_op_quantize_rows": [_P, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_quantize_groups": [_P, _I32, _I32, _P, _P, _I64, _I64, _P],
+    "qdec_op_gemm": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
     "qdec_op_rope_table": [_P, _I32, _I32, _F, _P],
     "qdec_op_qk_norm_rope_append": [_P, _P, _P, _F, _P, _I32, _P, _I32, _P, _P, _I32, _P, _I32,
@@ -309,6 +310,13 @@ def qdec_op_gemv(w, w_dtype, w_scale, x, x_dtype, y, y_dtype, n, k, stream=None)
 
 def qdec_op_quantize_rows(w, w_dtype, codes, scales, n, k, stream=None):
     _call("qdec_op_quantize_rows", _p(w), w_dtype, _p(codes), _p(scales), n, k, _p(stream))
+
+
+GEMM_STORE, GEMM_RESID, GEMM_SWIGLU = 0, 1, 2
+
+
+def qdec_op_gemm(a, w, y, y_dtype, resid, epilogue, m, n, k, stream=None):
+    _call("qdec_op_gemm", _p(a), _p(w), _p(y), y_dtype, _p(resid), epilogue, m, n, k, _p(stream))
 
 
 def qdec_op_quantize_groups(w, w_dtype, dst_dtype, codes, scales, n, k, stream=None):

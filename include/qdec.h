@@ -340,6 +340,20 @@ qdec_status qdec_op_gemv(const void* w, int32_t w_dtype, const float* w_scale, c
 qdec_status qdec_op_quantize_rows(const void* w, int32_t w_dtype, int8_t* codes, float* scales,
                                   int64_t n, int64_t k, void* stream);
 
+/* Epilogues of qdec_op_gemm. */
+typedef enum qdec_gemm_epilogue {
+  QDEC_GEMM_STORE = 0,   /* y = A W^T, [m x n] of y_dtype (F32 | BF16) */
+  QDEC_GEMM_RESID = 1,   /* resid[m x n] (fp32) += A W^T */
+  QDEC_GEMM_SWIGLU = 2   /* W is [2n x k] (n gate rows, then n up rows); y = silu(g) * u, BF16 */
+} qdec_gemm_epilogue;
+
+/* Prefill GEMM on the matrix cores ([ETE], the batched-prefill next step: the [1, hidden] GEMVs
+ * become [P, hidden] GEMMs): A [m x k] and W [n x k] bf16 row-major (k contiguous, the weight
+ * layout of qdec_upload), fp32 accumulation.  k a positive multiple of 32; a and w 16-byte
+ * aligned.  QDEC_E_INVAL for bad sizes, dtypes or pointers. */
+qdec_status qdec_op_gemm(const void* a, const void* w, void* y, int32_t y_dtype, float* resid,
+                         int32_t epilogue, int32_t m, int32_t n, int32_t k, void* stream);
+
 /* Group-wise quantisation (the rule of qdec_upload for I8_G128 / I4_G128): w [n x k] F32|BF16 ->
  * codes and scales [n][k / 128] in the layouts of dst_dtype (qdec_dtype).  k % 128 == 0; w
  * 8-byte aligned, codes and scales 4-byte aligned. */
