@@ -216,6 +216,30 @@ struct RopeAppendArgs {
   int32_t n_q_heads, n_kv_heads;
 };
 
+// Batched prefill: Q/K RMSNorm + RoPE + paged K/V append of P tokens, and causal attention.
+struct PrefillRopeArgs {
+  const float* qkv;           // [P][(Hq + 2 Hkv) D] fp32
+  const float* q_gamma;       // [D] or nullptr (no Q/K norm)
+  const float* k_gamma;
+  float eps;
+  const float* table;         // [max_pos][D/2][2] (cos, sin)
+  uint16_t* q_out;            // [P][Hq][D] bf16 (normalised, rotated, not scaled)
+  uint16_t* k_pool;           // [pages][Hkv][16][D] bf16
+  uint16_t* v_pool;
+  const int32_t* block_table;
+  int32_t pos0, p, n_q_heads, n_kv_heads;
+};
+
+struct PrefillAttnArgs {
+  const uint16_t* q;          // [P][Hq][D] bf16
+  const uint16_t* k_pool;     // [pages][Hkv][16][D] bf16, holding positions 0 .. pos0 + P - 1
+  const uint16_t* v_pool;
+  const int32_t* block_table;
+  uint16_t* out;              // [P][Hq][D] bf16
+  int32_t pos0, p, n_q_heads, n_kv_heads;
+  float qscale;               // log2(e) / sqrt(D)
+};
+
 struct EmbedArgs {
   const void* table;          // [V x d] (bf16 or fp32), used when emb == nullptr
   int32_t table_bf16;

@@ -35,6 +35,9 @@ constexpr int kMaxMergeParts = 8192;  // partitions per head the split-KV scratc
 hipError_t launch_rope_append(int head_dim, const RopeAppendArgs& a, hipStream_t s);
 // Prefill GEMM on MFMA (epi: EPI_STORE, EPI_RESID or EPI_SWIGLU); k % 32 == 0.
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
+// Prefill: Q/K norm + RoPE + paged append of P tokens; causal GQA attention on the matrix cores.
+hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream_t s);
+hipError_t launch_prefill_attn(int head_dim, int group, const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 const void* embed_kernel_fn();
 

@@ -24,6 +24,8 @@
 namespace qd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
@@ -139,6 +141,223 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
     default: hipLaunchKernelGGL((k_gemm<EPI_SWIGLU>), grid, dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+// ---- Q/K RMSNorm + RoPE + paged K/V append for P tokens ([Qwen3-runtime] §2.3-2.4, §7.1-7.2) -----
+// One wave per (head, token): lane l < D/2 holds the pair (l, l + D/2) of the head's row, as the
+// decode path does.  Q is stored normalised and rotated, rounded to bf16, not yet scaled; K and V
+// go to slot pos % 16 of page bt[pos / 16].
+template <int D>
+__global__ __launch_bounds__(64) void k_prefill_rope(PrefillRopeArgs a) {
+  constexpr int HALF = D / 2;
+  const int lane = threadIdx.x, hh = blockIdx.x, t = blockIdx.y;
+  const int hq = a.n_q_heads, hkv = a.n_kv_heads;
+  const int pos = a.pos0 + t;
+  const bool act = lane < HALF;
+  const int hl = lane & (HALF - 1);
+  const bool is_q = hh < hq;
+  const int g = hh - hq;
+  const float* row = a.qkv + (int64_t)t * (hq + 2 * hkv) * D;
+  const float* src = row + (int64_t)(is_q ? hh : hq + g) * D;
+  float x0 = act ? src[hl] : 0.f, x1 = act ? src[hl + HALF] : 0.f;
+  const float* gam = is_q ? a.q_gamma : a.k_gamma;
+  if (gam != nullptr) {
+    const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+    const float rinv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    x0 = x0 * rinv * gam[hl];
+    x1 = x1 * rinv * gam[hl + HALF];
+  }
+  if (!act) return;
+  const float2 cs = reinterpret_cast<const float2*>(a.table)[(int64_t)pos * HALF + lane];
+  const float y0 = x0 * cs.x - x1 * cs.y;
+  const float y1 = x1 * cs.x + x0 * cs.y;
+  if (is_q) {
+    const int64_t o = ((int64_t)t * hq + hh) * D + lane;
+    a.q_out[o] = f32_to_bf16(y0);
+    a.q_out[o + HALF] = f32_to_bf16(y1);
+    return;
+  }
+  const int64_t phys = a.block_table[pos / kPage];
+  const int64_t off = ((phys * hkv + g) * kPage + pos % kPage) * D + lane;
+  const float* vs = row + (int64_t)(hq + hkv + g) * D;
+  a.k_pool[off] = f32_to_bf16(y0);
+  a.k_pool[off + HALF] = f32_to_bf16(y1);
+  a.v_pool[off] = f32_to_bf16(vs[lane]);
+  a.v_pool[off + HALF] = f32_to_bf16(vs[lane + HALF]);
+}
+
+hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream_t s) {
+  if (a.p <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(a.n_q_heads + a.n_kv_heads), (unsigned)a.p);
+  if (head_dim == 64)
+    hipLaunchKernelGGL((k_prefill_rope<64>), grid, dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_prefill_rope<128>), grid, dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---- causal GQA attention of P new tokens over the paged cache, on the matrix cores --------------
+// FlashAttention-style ([ETE], the batched-prefill next step; the (m, l, acc) state of
+// [Qwen3-runtime] §9.1 / [ETE] online softmax, per query row).  A work-group of 4 waves takes
+// kv head g and BQ = 64 / G consecutive queries; its 64 rows are (query, head) pairs, query-major,
+// 16 per wave.  Keys go in blocks of 32 (two pages):
+//   S = Q K^T: A = the wave's 16 query rows (bf16, D/32 k-steps, loaded once), B = K rows read
+//     straight from the page tiles (lane l: key l % 16 of a 16-key half, 16 contiguous bytes);
+//   S is scaled to log2 units, keys past a row's position masked, and the row state updated with
+//     16-lane DPP reductions (in the MFMA output layout a row's 16 columns sit in one DPP row);
+//   P = 2^(S - m) is rounded to bf16 (the MFMA operand type; the row sum l adds the rounded
+//     values, so O / l stays a normalised average) and passed through a per-wave LDS tile to
+//     become the A operand of O += P V; V tiles are staged transposed in LDS (double-buffered,
+//     one barrier per block) so that each B fragment is 16 contiguous bytes.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
+  constexpr int BQ = 64 / G;     // queries per work-group
+  constexpr int ROWS = BQ * G;   // active rows (64 unless G does not divide 64)
+  constexpr int KS = D / 32;     // MFMA k-steps over D
+  constexpr int ND = D / 16;     // 16-column blocks of D in the output
+  constexpr int VP = 40;         // LDS row stride in bf16 (32 keys + 8 pad: 80 bytes)
+  constexpr int VL = 32 * D / 8 / 256;  // 16-byte V loads per thread per block
+  __shared__ __align__(16) uint16_t vt[2][D][VP];
+  __shared__ __align__(16) uint16_t pl[4][16][VP];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r16 = lane & 15, q4 = lane >> 4;
+  const int g = blockIdx.y;
+  const int hq = a.n_q_heads, hkv = a.n_kv_heads;
+  const int t0 = blockIdx.x * BQ;
+  const int nq = min(BQ, a.p - t0);                      // valid queries of the block (>= 1)
+  const int kend = a.pos0 + t0 + nq;                     // keys 0 .. kend-1 are visible
+  const float NEG = -INFINITY;
+
+  // this lane's A-operand row, and the four output rows it holds in the MFMA result layout
+  const int ra = wave * 16 + r16;
+  const int qa = min(ra < ROWS ? ra / G : 0, nq - 1), ha = ra % G;
+  typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+  bf8 qf[KS];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)(t0 + qa) * hq + g * G + ha) * D + 8 * q4;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = load_frag(qrow + 32 * ks);
+  }
+  int qpos[4];
+  bool active[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rc = wave * 16 + 4 * q4 + i;
+    const int qc = rc / G;
+    active[i] = rc < ROWS && qc < nq;
+    qpos[i] = active[i] ? a.pos0 + t0 + qc : -1;       // an inactive row sees no key
+  }
+  float m[4], l[4];
+  f32x4 o[ND];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -1e30f;
+    l[i] = 0.f;
+  }
+#pragma unroll
+  for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nblk = (kend + 31) / 32;
+  const int64_t head_stride = (int64_t)kPage * D;        // one head's page tile, in elements
+  for (int kb = 0; kb < nblk; ++kb) {
+    const int key0 = kb * 32;
+    const int last = kend - 1;
+    // the block's two pages (the second clamped to the last visible key's page)
+    const int64_t ph0 = a.block_table[key0 / kPage];
+    const int64_t ph1 = a.block_table[min(key0 + 16, last) / kPage];
+    const uint16_t* kt0 = a.k_pool + (ph0 * hkv + g) * head_stride;
+    const uint16_t* kt1 = a.k_pool + (ph1 * hkv + g) * head_stride;
+    // V tile loads (cooperative): 16-byte chunk c of key kl, keys past `last` clamped
+    uint4 vv[VL];
+    int vkl[VL], vd8[VL];
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      const int idx = threadIdx.x + 256 * u;
+      vkl[u] = idx / (D / 8);
+      vd8[u] = idx % (D / 8);
+      const int key = min(key0 + vkl[u], last);
+      const uint16_t* vtile = a.v_pool + (((key - key0) < 16 ? ph0 : ph1) * hkv + g) * head_stride;
+      vv[u] = *reinterpret_cast<const uint4*>(vtile + (int64_t)(key % kPage) * D + 8 * vd8[u]);
+    }
+    // S = Q K^T for the two 16-key halves
+    f32x4 sc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int key = min(key0 + 16 * nb + r16, last);
+      const uint16_t* krow = (nb == 0 ? kt0 : kt1) + (int64_t)(key % kPage) * D + 8 * q4;
+      sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], load_frag(krow + 32 * ks), sc[nb], 0, 0, 0);
+    }
+    // online softmax per row (rows 4 q4 + i, columns r16 of each half)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s0 = sc[0][i] * a.qscale, s1 = sc[1][i] * a.qscale;
+      if (key0 + r16 > qpos[i]) s0 = NEG;
+      if (key0 + 16 + r16 > qpos[i]) s1 = NEG;
+      const float mx = group_max<16>(fmaxf(s0, s1));
+      const float mn = fmaxf(m[i], mx);
+      const float corr = pf_exp2(m[i] - mn);
+      const float p0 = round_bf16(pf_exp2(s0 - mn)), p1 = round_bf16(pf_exp2(s1 - mn));
+      pl[wave][4 * q4 + i][r16] = f32_to_bf16(p0);
+      pl[wave][4 * q4 + i][16 + r16] = f32_to_bf16(p1);
+      l[i] = fmaf(l[i], corr, group_sum<16>(p0 + p1));
+      m[i] = mn;
+#pragma unroll
+      for (int nd = 0; nd < ND; ++nd) o[nd][i] *= corr;
+    }
+    // V transposed into LDS
+    const int buf = kb & 1;
+#pragma unroll
+    for (int u = 0; u < VL; ++u) {
+      const uint32_t w4[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[buf][8 * vd8[u] + 2 * e][vkl[u]] = (uint16_t)(w4[e] & 0xFFFFu);
+        vt[buf][8 * vd8[u] + 2 * e + 1][vkl[u]] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+    __syncthreads();
+    // O += P V
+    const bf8 pa = load_frag(&pl[wave][r16][8 * q4]);
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd)
+      o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, load_frag(&vt[buf][16 * nd + r16][8 * q4]),
+                                                      o[nd], 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!active[i]) continue;
+    const int rc = wave * 16 + 4 * q4 + i;
+    const int qc = rc / G, hc = rc % G;
+    const float inv = 1.0f / l[i];
+    uint16_t* orow = a.out + ((int64_t)(t0 + qc) * hq + g * G + hc) * D;
+#pragma unroll
+    for (int nd = 0; nd < ND; ++nd) orow[16 * nd + r16] = f32_to_bf16(o[nd][i] * inv);
+  }
+}
+
+template <int D>
+static hipError_t launch_pa(int group, const PrefillAttnArgs& a, hipStream_t s) {
+  const unsigned hk = (unsigned)a.n_kv_heads;
+  switch (group) {
+#define QD_PA(G)                                                                           \
+  case G:                                                                                  \
+    hipLaunchKernelGGL((k_prefill_attn<D, G>), dim3((unsigned)((a.p + 64 / G - 1) / (64 / G)), hk), \
+                       dim3(256), 0, s, a);                                                \
+    break;
+    QD_PA(1) QD_PA(2) QD_PA(3) QD_PA(4) QD_PA(5) QD_PA(6) QD_PA(7) QD_PA(8)
+#undef QD_PA
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(int head_dim, int group, const PrefillAttnArgs& a, hipStream_t s) {
+  if (a.p <= 0) return hipSuccess;
+  return head_dim == 64 ? launch_pa<64>(group, a, s) : launch_pa<128>(group, a, s);
 }
 
 }  // namespace qd

@@ -1197,6 +1197,35 @@ QDEC_API qdec_status qdec_op_gemm(const void* a, const void* w, void* y, int32_t
   return QDEC_OK;
 }
 
+QDEC_API qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool,
+                                               const void* v_pool, const int32_t* block_table,
+                                               int32_t pos0, int32_t n_tokens, int32_t n_q_heads,
+                                               int32_t n_kv_heads, int32_t head_dim, void* out,
+                                               void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (head_dim != 64 && head_dim != 128) return fail(nullptr, QDEC_E_UNSUPPORTED, "head_dim");
+  if (n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || n_q_heads / n_kv_heads > 8)
+    return fail(nullptr, QDEC_E_INVAL, "bad head counts");
+  if (pos0 < 0 || n_tokens < 1) return fail(nullptr, QDEC_E_INVAL, "need pos0 >= 0 and n_tokens >= 1");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 4))
+    return fail(nullptr, QDEC_E_INVAL, "misaligned pointer (q and pools 16-byte)");
+  PrefillAttnArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.block_table = block_table;
+  a.out = static_cast<uint16_t*>(out);
+  a.pos0 = pos0;
+  a.p = n_tokens;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  hipError_t e = launch_prefill_attn(head_dim, n_q_heads / n_kv_heads, a,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "prefill attention launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
 QDEC_API qdec_status qdec_op_quantize_groups(const void* w, int32_t w_dtype, int32_t dst_dtype,
                                              void* codes, float* scales, int64_t n, int64_t k,
                                              void* stream) {

@@ -92,6 +92,7 @@ _SIGS = {
     "qdec_op_quantize_rows": [_P, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_quantize_groups": [_P, _I32, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_gemm": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P],
+    "qdec_op_prefill_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
     "qdec_op_rope_table": [_P, _I32, _I32, _F, _P],
     "qdec_op_qk_norm_rope_append": [_P, _P, _P, _F, _P, _I32, _P, _I32, _P, _P, _I32, _P, _I32,
@@ -317,6 +318,12 @@ GEMM_STORE, GEMM_RESID, GEMM_SWIGLU = 0, 1, 2
 
 def qdec_op_gemm(a, w, y, y_dtype, resid, epilogue, m, n, k, stream=None):
     _call("qdec_op_gemm", _p(a), _p(w), _p(y), y_dtype, _p(resid), epilogue, m, n, k, _p(stream))
+
+
+def qdec_op_prefill_attention(q, k_pool, v_pool, block_table, pos0, n_tokens, n_q_heads,
+                              n_kv_heads, head_dim, out, stream=None):
+    _call("qdec_op_prefill_attention", _p(q), _p(k_pool), _p(v_pool), _p(block_table), pos0,
+          n_tokens, n_q_heads, n_kv_heads, head_dim, _p(out), _p(stream))
 
 
 def qdec_op_quantize_groups(w, w_dtype, dst_dtype, codes, scales, n, k, stream=None):

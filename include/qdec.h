@@ -354,6 +354,20 @@ typedef enum qdec_gemm_epilogue {
 qdec_status qdec_op_gemm(const void* a, const void* w, void* y, int32_t y_dtype, float* resid,
                          int32_t epilogue, int32_t m, int32_t n, int32_t k, void* stream);
 
+/* Causal GQA attention of n_tokens new tokens at positions pos0 .. pos0 + n_tokens - 1 over a
+ * bf16 paged cache that already holds positions 0 .. pos0 + n_tokens - 1 ([ETE], the
+ * FlashAttention-style prefill next step; [Qwen3-runtime] §2.5-2.6 per token, §7.2 paging).
+ * q: [n_tokens][n_q_heads][head_dim] bf16, normalised and rotated (not scaled); pools
+ * [pages][n_kv_heads][16][head_dim] bf16; block_table maps every position below
+ * pos0 + n_tokens; out: [n_tokens][n_q_heads][head_dim] bf16.  Query t attends to keys
+ * 0 .. pos0 + t with scores q.k / sqrt(head_dim) on the matrix cores (bf16 operands, fp32
+ * softmax state; the probabilities are rounded to bf16 as the second product's operand).
+ * head_dim 64 or 128; n_q_heads / n_kv_heads <= 8; q and pools 16-byte aligned. */
+qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool, const void* v_pool,
+                                      const int32_t* block_table, int32_t pos0, int32_t n_tokens,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      void* out, void* stream);
+
 /* Group-wise quantisation (the rule of qdec_upload for I8_G128 / I4_G128): w [n x k] F32|BF16 ->
  * codes and scales [n][k / 128] in the layouts of dst_dtype (qdec_dtype).  k % 128 == 0; w
  * 8-byte aligned, codes and scales 4-byte aligned. */

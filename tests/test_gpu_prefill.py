@@ -90,3 +90,48 @@ def test_gemm_rejects_bad_arguments():
         Q.qdec_op_gemm(a, w, y, Q.F32, None, Q.GEMM_SWIGLU, 4, 4, 64)      # SwiGLU writes bf16
     with pytest.raises(Q.QdecError):
         Q.qdec_op_gemm(a, w, None, Q.F32, None, Q.GEMM_RESID, 4, 8, 64)    # no residual
+
+
+# ---- causal prefill attention -------------------------------------------------------------------------
+
+def _paged_bf16(kl, vl, bt, num_pages):
+    """Pool tensors holding logical bf16 K/V [T, Hkv, D] through block table bt (the oracle's
+    placement, bit for bit)."""
+    kp = oracle.pool_scatter(synth.bf16_to_bits(kl), 0, bt, num_pages, 16)
+    vp = oracle.pool_scatter(synth.bf16_to_bits(vl), 0, bt, num_pages, 16)
+    kp = torch.from_numpy(kp.view(np.int16)).view(torch.bfloat16)
+    vp = torch.from_numpy(vp.view(np.int16)).view(torch.bfloat16)
+    return kp.to(DEV), vp.to(DEV)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 16, 8), (128, 32, 8), (64, 4, 2), (128, 8, 8),
+                                      (128, 24, 8), (64, 16, 2), (128, 4, 1)])
+@pytest.mark.parametrize("pos0,P", [(0, 1), (0, 17), (0, 64), (5, 40), (100, 33), (0, 300),
+                                    (1000, 129)])
+def test_prefill_attention_matches_oracle(d, hq, hkv, pos0, P):
+    """Query t sees keys 0 .. pos0 + t.  The reference is the oracle's two-pass fp64 attention
+    of the same bf16 q, K and V per query.  Bar: the output is rounded to bf16 and the
+    probabilities are rounded to bf16 as the second product's operand, so |got - ref| <=
+    2^-7 |ref| + 4e-3 (values ~N(0, 1))."""
+    print(f"prefill attention d={d} hq={hq} hkv={hkv} pos0={pos0} P={P}", flush=True)
+    T = pos0 + P
+    g = torch.Generator(device=DEV).manual_seed(T * 7 + d + hq + P)
+    q = (torch.randn((P, hq, d), generator=g, device=DEV) * 0.5).to(torch.bfloat16)
+    kl = torch.randn((T, hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    vl = torch.randn((T, hkv, d), generator=g, device=DEV).to(torch.bfloat16)
+    n_pages = (T + 15) // 16
+    num_pages = n_pages + 3
+    bt = np.random.default_rng(T).permutation(num_pages)[:n_pages].astype(np.int32)
+    kp, vp = _paged_bf16(kl, vl, bt, num_pages)
+    out = torch.empty((P, hq, d), device=DEV, dtype=torch.bfloat16)
+    Q.qdec_op_prefill_attention(q, kp, vp, torch.from_numpy(bt).to(DEV), pos0, P, hq, hkv, d, out)
+    torch.cuda.synchronize()
+    got = synth.bf16_to_f32(out).astype(np.float64)
+    qh = synth.bf16_to_f32(q).astype(np.float64)
+    kh, vh = kl.float().cpu().numpy(), vl.float().cpu().numpy()
+    ts = np.unique(np.concatenate([np.random.default_rng(P).choice(P, min(P, 24), replace=False),
+                                   [0, P - 1]]))
+    for t in ts:
+        ref = oracle.attention(qh[t], kh[: pos0 + t + 1], vh[: pos0 + t + 1])
+        err = np.abs(got[t] - ref)
+        assert np.all(err <= 2.0**-7 * np.abs(ref) + 4e-3), (t, float(err.max()))
