@@ -56,5 +56,12 @@ hipError_t launch_convert(void* dst, int dst_type, const void* src, int src_type
                           hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y, int y_bf16,
                           int n, hipStream_t s);
+// RMSNorm of `rows` consecutive rows of n values (one work-group per row).
+hipError_t launch_rmsnorm_rows(const float* x, const float* gamma, float eps, void* y, int y_bf16,
+                               int n, int rows, hipStream_t s);
+// Prefill embedding: x[t] = E[tokens[t]] widened to fp32 for t < n; a bad id gives a zero row and
+// sets desc->error.
+hipError_t launch_embed_rows(const void* table, int table_bf16, const int32_t* tokens, int n,
+                             int d, int vocab, float* x, StepDesc* desc, hipStream_t s);
 
 }  // namespace qd

@@ -450,6 +450,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* ga
                                                  void* y, int y_bf16, int n) {
   __shared__ float red[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // one work-group per row
+  x += (int64_t)blockIdx.x * n;
+  y = static_cast<char*>(y) + (int64_t)blockIdx.x * n * (y_bf16 ? 2 : 4);
   float ss = 0.f;
   for (int i = tid; i < n; i += 256) ss = fmaf(x[i], x[i], ss);
   ss = wave_sum(ss);
@@ -468,7 +471,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* ga
 
 hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y, int y_bf16,
                           int n, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(1), dim3(256), 0, s, x, gamma, eps, y, y_bf16, n);
+  return launch_rmsnorm_rows(x, gamma, eps, y, y_bf16, n, 1, s);
+}
+
+hipError_t launch_rmsnorm_rows(const float* x, const float* gamma, float eps, void* y, int y_bf16,
+                               int n, int rows, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)rows), dim3(256), 0, s, x, gamma, eps, y, y_bf16, n);
   return hipGetLastError();
 }
 

@@ -143,6 +143,32 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- embedding rows of the P prompt tokens ([ETE]: the block pipeline starts from each token's
+//      embedding row) -----
+__global__ __launch_bounds__(256) void k_embed_rows(const void* table, int table_bf16,
+                                                    const int32_t* tokens, int d, int vocab,
+                                                    float* x, StepDesc* desc) {
+  const int t = blockIdx.x;
+  const int tok = tokens[t];
+  const bool bad = tok < 0 || tok >= vocab;
+  if (bad && threadIdx.x == 0 && desc != nullptr) desc->error = 1;
+  const int64_t base = bad ? 0 : (int64_t)tok * d;
+  for (int i = threadIdx.x; i < d; i += 256) {
+    float v = 0.f;
+    if (!bad) v = table_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(table)[base + i])
+                             : static_cast<const float*>(table)[base + i];
+    x[(int64_t)t * d + i] = v;
+  }
+}
+
+hipError_t launch_embed_rows(const void* table, int table_bf16, const int32_t* tokens, int n,
+                             int d, int vocab, float* x, StepDesc* desc, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_embed_rows, dim3((unsigned)n), dim3(256), 0, s, table, table_bf16, tokens,
+                     d, vocab, x, desc);
+  return hipGetLastError();
+}
+
 // ---- Q/K RMSNorm + RoPE + paged K/V append for P tokens ([Qwen3-runtime] §2.3-2.4, §7.1-7.2) -----
 // One wave per (head, token): lane l < D/2 holds the pair (l, l + D/2) of the head's row, as the
 // decode path does.  Q is stored normalised and rotated, rounded to bf16, not yet scaled; K and V

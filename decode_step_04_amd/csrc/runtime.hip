@@ -124,6 +124,13 @@ struct qdec_ctx {
   void* logits = nullptr;
   float* part_acc = nullptr;
   float* part_ml = nullptr;
+  // prefill buffers for max_prefill tokens (absent when max_prefill = 0)
+  float* px = nullptr;        // [P][d] fp32 residual streams
+  void* ph = nullptr;         // [P][d] bf16 normalised GEMM inputs
+  float* pqkv = nullptr;      // [P][(Hq + 2 Hkv) D] fp32
+  void* pq = nullptr;         // [P][Hq][D] bf16 rotated queries
+  void* pattn = nullptr;      // [P][Hq D] bf16 attention outputs
+  void* pact = nullptr;       // [P][F] bf16 SwiGLU outputs
   float* am_val = nullptr;    // per-work-group partial argmax of the LM head
   int32_t* am_idx = nullptr;
   int am_parts = 0;
@@ -232,6 +239,12 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if (c->partition_size < 0 || c->partition_size % 64 || c->partition_size > kMaxPartTokens)
     return fail(why, QDEC_E_INVAL, "partition_size must be 0 or a multiple of 64 up to %d",
                 kMaxPartTokens);
+  if (c->max_prefill < 0 || c->max_prefill > (1 << 16))
+    return fail(why, QDEC_E_INVAL, "max_prefill must be in [0, 65536]");
+  if (c->max_prefill > 0 &&
+      (c->proj_dtype != QDEC_BF16 || c->io_dtype != QDEC_BF16 || c->kv_dtype != QDEC_BF16))
+    return fail(why, QDEC_E_UNSUPPORTED,
+                "prefill runs bf16 GEMMs on the matrix cores: it needs bf16 projections, io and KV");
   if (model_max_parts(*c) > kMaxMergeParts)
     return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
                 kMaxMergeParts);
@@ -275,7 +288,8 @@ static void fill_info(const qdec_config& c, qdec_info* o) {
                     o->layer_matrix_bytes + o->layer_scale_bytes + L * norms * 4 + o->kv_pool_bytes +
                     block_table_entries(c) * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
                     (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ie +
-                    hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc);
+                    hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc) +
+                    (int64_t)c.max_prefill * (d * 6 + (hq + 2 * hkv) * hd * 4 + 4 * hq * hd + 2 * f);
 }
 
 QDEC_API qdec_status qdec_config_validate(const qdec_config* cfg, char* msg, size_t len) {
@@ -456,6 +470,15 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   TRY(c->alloc(&c->am_idx, (int64_t)c->am_parts * 4, "argmax partials"));
   TRY(c->alloc(&c->part_acc, hq * (int64_t)c->max_parts * hd * 4, "split-KV scratch"));
   TRY(c->alloc(&c->part_ml, hq * (int64_t)c->max_parts * 8, "split-KV scratch"));
+  if (cfg->max_prefill > 0) {
+    const int64_t P = cfg->max_prefill;
+    TRY(c->alloc(&c->px, P * d * 4, "prefill residual"));
+    TRY(c->alloc(&c->ph, P * d * 2, "prefill GEMM input"));
+    TRY(c->alloc(&c->pqkv, P * (hq + 2 * hkv) * hd * 4, "prefill qkv"));
+    TRY(c->alloc(&c->pq, P * hq * hd * 2, "prefill queries"));
+    TRY(c->alloc(&c->pattn, P * hq * hd * 2, "prefill attention output"));
+    TRY(c->alloc(&c->pact, P * f * 2, "prefill SwiGLU output"));
+  }
   TRY(c->alloc(&c->desc, (int64_t)sizeof(StepDesc), "step descriptor"));
   TRY(c->hip(hipMemset(c->desc, 0, sizeof(StepDesc)), "hipMemset descriptor"));
   TRY(c->hip(launch_rope_table(c->rope, cfg->max_context, (int)hd, cfg->rope_theta, nullptr),
@@ -953,6 +976,129 @@ QDEC_API qdec_status qdec_decode_step(qdec_ctx* c, const qdec_step* st, void* st
   if (c->prof) c->ev_used = 0;
   if ((r = enqueue_embed(c, st, st->pos, s)) != QDEC_OK) return r;
   return enqueue_layers(c, st, st->pos, s, false);
+}
+
+QDEC_API qdec_status qdec_prefill(qdec_ctx* c, const int32_t* token_ids, int32_t n, int32_t pos0,
+                                  float* hidden_out, void* logits_out, int32_t* argmax_out,
+                                  void* stream) {
+  if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  const qdec_config& k = c->cfg;
+  if (!token_ids) return fail(&c->err, QDEC_E_INVAL, "token_ids is NULL");
+  if (k.max_prefill == 0) return fail(&c->err, QDEC_E_INVAL, "created with max_prefill = 0");
+  if (n < 1 || n > k.max_prefill)
+    return fail(&c->err, QDEC_E_INVAL, "n_tokens %d outside [1, %d]", n, k.max_prefill);
+  if (hidden_out && !aligned(hidden_out, 16))
+    return fail(&c->err, QDEC_E_INVAL, "hidden_out must be 16-byte aligned");
+  if (logits_out && !aligned(logits_out, 4)) return fail(&c->err, QDEC_E_INVAL, "logits_out misaligned");
+  if (pos0 < 0 || (int64_t)pos0 + n > k.max_context)
+    return fail(&c->err, QDEC_E_RANGE, "positions %d .. %d outside [0, %d)", pos0, pos0 + n - 1,
+                k.max_context);
+  // the weight and block-table checks of a decode step at the last position
+  qdec_step probe{};
+  probe.token_id = token_ids;
+  probe.pos = pos0 + n - 1;
+  qdec_status r = check_step(c, &probe, true);
+  if (r != QDEC_OK) return r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((r = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return r;
+  const int d = k.hidden, hq = k.n_q_heads, hkv = k.n_kv_heads, hd = k.head_dim, f = k.ffn;
+  const int nqkv = (hq + 2 * hkv) * hd;
+#define P_TRY(call, what)                                \
+  do {                                                   \
+    if ((r = c->hip((call), what)) != QDEC_OK) return r; \
+  } while (0)
+  P_TRY(launch_embed_rows(c->embed.data, c->io_bf16(), token_ids, n, d, k.vocab, c->px, c->desc, s),
+        "prefill embedding");
+  for (int l = 0; l < k.n_layers; ++l) {
+    const Layer& ly = c->layers[(size_t)l];
+    GemmArgs g{};
+    g.m = n;
+    P_TRY(launch_rmsnorm_rows(c->px, ly.in_norm, k.rms_eps, c->ph, 1, d, n, s), "prefill norm");
+    g.a = c->ph;
+    g.w = ly.qkv.data;
+    g.y = c->pqkv;
+    g.y_bf16 = 0;
+    g.n = nqkv;
+    g.k = d;
+    P_TRY(launch_gemm(EPI_STORE, g, s), "prefill qkv gemm");
+    PrefillRopeArgs pr{};
+    pr.qkv = c->pqkv;
+    pr.q_gamma = ly.q_norm;
+    pr.k_gamma = ly.k_norm;
+    pr.eps = k.rms_eps;
+    pr.table = c->rope;
+    pr.q_out = static_cast<uint16_t*>(c->pq);
+    pr.k_pool = static_cast<uint16_t*>(ly.k_pool);
+    pr.v_pool = static_cast<uint16_t*>(ly.v_pool);
+    pr.block_table = c->block_table;
+    pr.pos0 = pos0;
+    pr.p = n;
+    pr.n_q_heads = hq;
+    pr.n_kv_heads = hkv;
+    P_TRY(launch_prefill_rope(hd, pr, s), "prefill rope/append");
+    PrefillAttnArgs pa{};
+    pa.q = static_cast<const uint16_t*>(c->pq);
+    pa.k_pool = static_cast<const uint16_t*>(ly.k_pool);
+    pa.v_pool = static_cast<const uint16_t*>(ly.v_pool);
+    pa.block_table = c->block_table;
+    pa.out = static_cast<uint16_t*>(c->pattn);
+    pa.pos0 = pos0;
+    pa.p = n;
+    pa.n_q_heads = hq;
+    pa.n_kv_heads = hkv;
+    pa.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+    P_TRY(launch_prefill_attn(hd, hq / hkv, pa, s), "prefill attention");
+    g.a = c->pattn;
+    g.w = ly.o.data;
+    g.y = nullptr;
+    g.resid = c->px;
+    g.n = d;
+    g.k = hq * hd;
+    P_TRY(launch_gemm(EPI_RESID, g, s), "prefill o gemm");
+    P_TRY(launch_rmsnorm_rows(c->px, ly.post_norm, k.rms_eps, c->ph, 1, d, n, s), "prefill norm");
+    g.a = c->ph;
+    g.w = ly.gu.data;
+    g.y = c->pact;
+    g.y_bf16 = 1;
+    g.resid = nullptr;
+    g.n = f;
+    g.k = d;
+    P_TRY(launch_gemm(EPI_SWIGLU, g, s), "prefill gate-up gemm");
+    g.a = c->pact;
+    g.w = ly.down.data;
+    g.y = nullptr;
+    g.resid = c->px;
+    g.n = d;
+    g.k = f;
+    P_TRY(launch_gemm(EPI_RESID, g, s), "prefill down gemm");
+  }
+  // the last token: hidden state, final norm + LM head + argmax (the decode path's GEMV)
+  float* xl = c->px + (int64_t)(n - 1) * d;
+  if (logits_out || argmax_out) {
+    GemvArgs h{};
+    h.w = c->lm.data;
+    h.scale = c->lm.scale;
+    h.x = xl;
+    h.gamma = c->final_norm;
+    h.eps = k.rms_eps;
+    h.round_h = 1;
+    h.y = logits_out ? logits_out : c->logits;
+    h.y_bf16 = c->io_bf16();
+    h.hidden_copy = hidden_out;
+    if (argmax_out) {
+      h.part_val = c->am_val;
+      h.part_idx = c->am_idx;
+    }
+    h.n = k.vocab;
+    h.k = d;
+    P_TRY(launch_gemv(wt_of(k.lm_head_dtype), EPI_STORE, true, h, s), "prefill LM head");
+    if (argmax_out)
+      P_TRY(launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, argmax_out, s), "argmax");
+  } else if (hidden_out) {
+    P_TRY(launch_copy(hidden_out, xl, (int64_t)d * 4, s), "hidden copy");
+  }
+#undef P_TRY
+  return QDEC_OK;
 }
 
 QDEC_API qdec_status qdec_graph_reset(qdec_ctx* c) {

@@ -14,7 +14,7 @@ QUANT_PATHS = {"w8a16": Q.I8_ROW, "w8a16g": Q.I8_G128, "w4a16": Q.I4_G128}
 
 
 def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
-               partition_size: int = 0, act: str = None) -> Q.qdec_config:
+               partition_size: int = 0, act: str = None, max_prefill: int = 0) -> Q.qdec_config:
     """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights, embedding, logits and KV), 'w8a16'
     (int8 per-row projections and LM head, bf16 embedding, logits and KV), 'w8a16g' (int8 with a
     scale per 128-value group) or 'w4a16' (int4 with a scale per 128-value group).  act: 'f32' or 'bf16',
@@ -40,7 +40,7 @@ def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
         vocab=shape["vocab"], tied_lm_head=int(shape["tied"]), qk_norm=int(shape["qk_norm"]),
         rms_eps=shape["eps"], rope_theta=shape["theta"], proj_dtype=proj, lm_head_dtype=lm,
         io_dtype=io, act_dtype=act, kv_dtype=kv, page_size=16, num_pages=num_pages, max_context=max_context,
-        partition_size=partition_size)
+        partition_size=partition_size, max_prefill=max_prefill)
 
 
 def _dt(t):

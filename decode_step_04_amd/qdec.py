@@ -40,7 +40,7 @@ class qdec_config(C.Structure):
                 ("lm_head_dtype", C.c_int32), ("io_dtype", C.c_int32), ("act_dtype", C.c_int32),
                 ("kv_dtype", C.c_int32),
                 ("page_size", C.c_int32), ("num_pages", C.c_int32), ("max_context", C.c_int32),
-                ("partition_size", C.c_int32)]
+                ("partition_size", C.c_int32), ("max_prefill", C.c_int32)]
 
 
 class qdec_step(C.Structure):
@@ -81,6 +81,7 @@ _SIGS = {
     "qdec_kv_read": [_P, _I32, _I32, _I32, _P, _P, _P],
     "qdec_kv_pool_ptr": [_P, _I32, C.POINTER(_P), C.POINTER(_P)],
     "qdec_decode_step": [_P, C.POINTER(qdec_step), _P],
+    "qdec_prefill": [_P, _P, _I32, _I32, _P, _P, _P, _P],
     "qdec_graph_capture": [_P, C.POINTER(qdec_step), _P],
     "qdec_graph_replay": [_P, _I32, _P],
     "qdec_graph_reset": [_P],
@@ -267,6 +268,12 @@ def make_step(pos, token_id=None, token_embedding=None, hidden_out=None, logits_
 
 def qdec_decode_step(ctx, step: qdec_step, stream=None):
     _call("qdec_decode_step", ctx, C.byref(step), _p(stream), ctx=ctx)
+
+
+def qdec_prefill(ctx, token_ids, n_tokens, pos0, hidden_out=None, logits_out=None,
+                 argmax_out=None, stream=None):
+    _call("qdec_prefill", ctx, _p(token_ids), n_tokens, pos0, _p(hidden_out), _p(logits_out),
+          _p(argmax_out), _p(stream), ctx=ctx)
 
 
 def qdec_graph_capture(ctx, templ: qdec_step, stream=None):

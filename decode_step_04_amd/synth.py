@@ -135,6 +135,11 @@ def token_id(vocab: int, seed: int = 3) -> int:
     return int(np.random.default_rng(seed).integers(0, vocab))
 
 
+def prompt_tokens(vocab: int, n: int, seed: int = 4) -> np.ndarray:
+    """n token ids, uniform in [0, vocab) (a synthetic prompt for prefill)."""
+    return np.random.default_rng(seed).integers(0, vocab, size=n).astype(np.int32)
+
+
 # ---- attention stress (one layer, 32 Q / 8 KV heads, D 128) ---------------------------------------
 
 STRESS = dict(n_q_heads=32, n_kv_heads=8, head_dim=128)

@@ -94,6 +94,9 @@ typedef struct qdec_config {
   int32_t max_context;    /* positions 0 .. max_context-1 may be decoded; <= num_pages*page_size */
   int32_t partition_size; /* split-KV partition length in tokens (multiple of 64, at most 512),
                            * 0 = automatic (about one GPU-full of work-groups at max_context) */
+  int32_t max_prefill;    /* most tokens one qdec_prefill call takes (its buffers are allocated
+                           * at create); 0 = no prefill.  Prefill needs bf16 projections, io and
+                           * KV. */
 } qdec_config;
 
 /* Supported dtype combinations (checked by qdec_config_validate):
@@ -271,6 +274,20 @@ qdec_status qdec_kv_pool_ptr(const qdec_ctx* ctx, int32_t layer, void** k_pool, 
  * weight slot uploaded (QDEC_E_STATE), a block table mapping pos (QDEC_E_RANGE), and
  * 0 <= pos < max_context (QDEC_E_RANGE). */
 qdec_status qdec_decode_step(qdec_ctx* ctx, const qdec_step* step, void* stream);
+
+/* Batched prefill of n_tokens prompt tokens at positions pos0 .. pos0 + n_tokens - 1 ([ETE], the
+ * batched-prefill next step: GEMMs on the matrix cores and FlashAttention-style causal attention
+ * over the paged cache, which it fills).  It computes what n_tokens decode steps would, with the
+ * 16-bit activation policy (act_dtype BF16) at every op boundary: the GEMM inputs, the rotated
+ * queries, the attention output and the SwiGLU output are bf16; the residual stream stays fp32.
+ * token_ids: device [n_tokens]; an id outside [0, vocab) gives a zero row and sets the device
+ * error flag.  Outputs, each optional, are those of the last token: hidden_out [hidden] fp32
+ * (the residual stream after the last layer), logits_out [vocab] of io_dtype, argmax_out.
+ * Requires max_prefill >= n_tokens >= 1 (QDEC_E_INVAL), every weight slot uploaded
+ * (QDEC_E_STATE), and a block table mapping pos0 + n_tokens - 1 < max_context (QDEC_E_RANGE).
+ * Allocates nothing and does not synchronise. */
+qdec_status qdec_prefill(qdec_ctx* ctx, const int32_t* token_ids, int32_t n_tokens, int32_t pos0,
+                         float* hidden_out, void* logits_out, int32_t* argmax_out, void* stream);
 
 /* Captures the step described by `templ` (its buffers, not its pos) into a HIP graph whose
  * kernels read pos from a device descriptor, and sizes the split-KV grid for max_context

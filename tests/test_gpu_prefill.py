@@ -135,3 +135,127 @@ def test_prefill_attention_matches_oracle(d, hq, hkv, pos0, P):
         ref = oracle.attention(qh[t], kh[: pos0 + t + 1], vh[: pos0 + t + 1])
         err = np.abs(got[t] - ref)
         assert np.all(err <= 2.0**-7 * np.abs(ref) + 4e-3), (t, float(err.max()))
+
+
+# ---- the whole prefill at the Qwen3-0.6B shape ------------------------------------------------------
+
+from decode_step_04_amd import loader  # noqa: E402
+
+SHAPE = synth.QWEN3_0P6B
+
+
+class PrefillSetup:
+    """bf16 weights and KV, the 16-bit activation policy (what prefill computes), an empty cache
+    of max_context positions behind a random block table, and the oracle model on the same
+    weights."""
+
+    def __init__(self, max_context=1024, max_prefill=256):
+        print(f"prefill setup max_context={max_context} max_prefill={max_prefill}", flush=True)
+        n_pages = max_context // 16
+        self.cfg = loader.config_for(SHAPE, path="bf16", num_pages=n_pages, max_context=max_context,
+                                     act="bf16", max_prefill=max_prefill)
+        self.ctx = Q.qdec_create(self.cfg, 0)
+        w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        loader.upload_weights(self.ctx, w, DEV)
+        self.table = synth.block_table(n_pages, n_pages, seed=2)
+        Q.qdec_kv_set_block_table(self.ctx, self.table)
+        self.hw = synth.host_weights(w)
+        del w
+        self.om = oracle.Model(dict(SHAPE, act_bf16=1, kv_bf16=1, logits_bf16=1), self.hw,
+                               max_ctx=max_context)
+        self.hidden = torch.empty(SHAPE["hidden"], device=DEV)
+        self.logits = torch.empty(SHAPE["vocab"], dtype=torch.bfloat16, device=DEV)
+        self.amax = torch.empty(1, dtype=torch.int32, device=DEV)
+
+    def prefill(self, tokens, pos0):
+        t = torch.from_numpy(tokens).to(DEV)
+        Q.qdec_prefill(self.ctx, t, len(tokens), pos0, self.hidden, self.logits, self.amax)
+        torch.cuda.synchronize()
+        return (self.hidden.cpu().numpy().astype(np.float64),
+                synth.bf16_to_f32(self.logits).astype(np.float64), int(self.amax.item()))
+
+    def oracle_run(self, tokens, pos0):
+        """(plain-fp32 oracle, fp64 oracle) results of the last token after decoding `tokens` one
+        by one from pos0; the fp64 pass runs last so the oracle's cache holds its rows."""
+        with oracle.fp32_arithmetic():
+            for i, tok in enumerate(tokens):
+                r32 = self.om.step(pos0 + i, token=int(tok))
+        for i, tok in enumerate(tokens):
+            r64 = self.om.step(pos0 + i, token=int(tok))
+        return r32, r64
+
+    def close(self):
+        Q.qdec_destroy(self.ctx)
+
+
+def _check_bf16_policy(got, ref, ref32, what):
+    gh, gl, ga = got
+    rh, rl, ra = ref
+    rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
+    lmax = np.max(np.abs(gl - rl))
+    d32 = np.linalg.norm(ref32[0] - rh) / np.linalg.norm(rh)
+    l32 = np.max(np.abs(ref32[1] - rl))
+    print(f"{what}: hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra} "
+          f"(plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
+    assert rel <= max(1.5e-2, 2 * d32)
+    assert lmax <= max(5e-2, 2 * l32)
+    assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max()) - 2 * l32
+
+
+def _check_kv(s, layer, n):
+    """The cache rows the prefill wrote against the oracle's (both bf16 values)."""
+    hkv, d = SHAPE["n_kv_heads"], SHAPE["head_dim"]
+    k = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
+    v = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
+    Q.qdec_kv_read(s.ctx, layer, 0, n, k, v)
+    torch.cuda.synchronize()
+    for got, ref in ((k.float().cpu().numpy(), s.om.k_cache[layer][:n]),
+                     (v.float().cpu().numpy(), s.om.v_cache[layer][:n])):
+        rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        assert rel <= 2e-2, (layer, rel)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_matches_token_by_token_decode():
+    """One prefill of 100 tokens, then a second of 37 at pos0 = 100 (queries over cached keys),
+    then a decode step at pos 137: each against the oracle decoding the same tokens one by one
+    under the same 16-bit activation policy; the cache rows the prefill wrote against the
+    oracle's."""
+    s = PrefillSetup()
+    try:
+        toks = synth.prompt_tokens(SHAPE["vocab"], 137, seed=4)
+        got = s.prefill(toks[:100], 0)
+        r32, r64 = s.oracle_run(toks[:100], 0)
+        _check_bf16_policy(got, r64, r32, "prefill 100")
+        _check_kv(s, 0, 100)
+        _check_kv(s, SHAPE["n_layers"] - 1, 100)
+        got = s.prefill(toks[100:], 100)
+        r32, r64 = s.oracle_run(toks[100:], 100)
+        _check_bf16_policy(got, r64, r32, "prefill 37 at 100")
+        # a decode step continues from the prefilled cache
+        tok = torch.tensor([int(toks[-1])], dtype=torch.int32, device=DEV)
+        st = Q.make_step(137, token_id=tok, hidden_out=s.hidden, logits_out=s.logits,
+                         argmax_out=s.amax)
+        Q.qdec_decode_step(s.ctx, st)
+        torch.cuda.synchronize()
+        got = (s.hidden.cpu().numpy().astype(np.float64),
+               synth.bf16_to_f32(s.logits).astype(np.float64), int(s.amax.item()))
+        r32, r64 = s.oracle_run(toks[-1:], 137)
+        _check_bf16_policy(got, r64, r32, "decode at 137")
+        assert Q.qdec_device_error(s.ctx) == 0
+    finally:
+        s.close()
+
+
+def test_prefill_rejects_bad_calls():
+    s = PrefillSetup(max_context=256, max_prefill=32)
+    try:
+        t = torch.zeros(64, dtype=torch.int32, device=DEV)
+        with pytest.raises(Q.QdecError):
+            Q.qdec_prefill(s.ctx, t, 33, 0)            # above max_prefill
+        with pytest.raises(Q.QdecError):
+            Q.qdec_prefill(s.ctx, t, 0, 0)             # empty
+        with pytest.raises(Q.QdecError):
+            Q.qdec_prefill(s.ctx, t, 8, 250)           # past max_context
+    finally:
+        s.close()
