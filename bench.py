@@ -22,6 +22,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs peak (Qwen3-0.6B shape, 4K ctx)"
 
 
@@ -44,6 +45,8 @@ def parse():
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--copy-calib", action="store_true",
                    help="only run the library's copy kernel on 1 GiB (counter calibration)")
+    p.add_argument("--prefill-tokens", type=int, default=2048,
+                   help="prompt tokens of the timed prefill (0: skip it)")
     p.add_argument("--no-ops", action="store_true",
                    help="skip the op-level workloads (attention stress, W8A16 GEMV, copy)")
     p.add_argument("--eager-only", type=int, default=0, metavar="N",
@@ -86,6 +89,55 @@ def copy_calibration():
     dt = (time.perf_counter() - t0) / 20
     print(json.dumps({"copy_bytes_each_way": n, "copy_ms": dt * 1e3,
                       "copy_gbps_read_plus_write": 2 * n / dt / 1e9}))
+
+
+def prefill_bench(shape, n_tok):
+    """One prefill of n_tok synthetic prompt tokens at position 0 (bf16 weights and KV, the 16-bit
+    activation policy), timed with HIP events around 5 calls after 2 warm-up calls.  FLOPs count
+    the GEMMs (2 per weight per token), the attention products (4 Hq D per visible key per token)
+    and the last token's LM head."""
+    import torch
+
+    from decode_step_04_amd import loader, synth
+    from decode_step_04_amd import qdec as Q
+
+    dev = "cuda"
+    n_pages = (n_tok + 15) // 16
+    cfg = loader.config_for(shape, path="bf16", num_pages=n_pages, max_context=n_pages * 16,
+                            act="bf16", max_prefill=n_tok)
+    ctx = Q.qdec_create(cfg, 0)
+    try:
+        w = synth.bf16_model(shape, seed=0, device=dev)
+        loader.upload_weights(ctx, w, dev)
+        del w
+        Q.qdec_kv_set_block_table(ctx, synth.block_table(n_pages, n_pages, seed=2))
+        toks = torch.from_numpy(synth.prompt_tokens(shape["vocab"], n_tok, seed=4)).to(dev)
+        amax = torch.empty(1, dtype=torch.int32, device=dev)
+        s = torch.cuda.current_stream()
+        for _ in range(2):
+            Q.qdec_prefill(ctx, toks, n_tok, 0, None, None, amax, s.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(s)
+        for _ in range(reps):
+            Q.qdec_prefill(ctx, toks, n_tok, 0, None, None, amax, s.cuda_stream)
+        e1.record(s)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+    finally:
+        Q.qdec_destroy(ctx)
+        torch.cuda.empty_cache()
+    d, hq, hkv, hd, f, L = (shape[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim",
+                                                 "ffn", "n_layers"))
+    gemm = 2 * n_tok * L * ((hq + 2 * hkv) * hd * d + d * hq * hd + 2 * f * d + d * f)
+    attn = 4 * hq * hd * L * (n_tok * (n_tok + 1) // 2)
+    flops = gemm + attn + 2 * shape["vocab"] * d
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"tokens": n_tok, "ms": round(ms, 3), "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+            "flops": flops, "tflops": round(tflops, 1), "bound": "mfma",
+            "peak_tflops": PEAK_BF16_TFLOPS, "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "policy": "bf16 weights and KV, bf16 activations at op boundaries, fp32 residual"}
 
 
 def ops_bench():
@@ -190,6 +242,24 @@ def ops_bench():
                                 "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1)})
             del ws
             torch.cuda.empty_cache()
+    out["gemm"] = []
+    for m, n, k in ((2048, 4096, 1024), (2048, 6144, 1024), (2048, 1024, 3072), (2048, 24576, 4096)):
+        copies = max(2, math.ceil((1 << 28) / (2 * n * k)))
+        ws = [torch.randn((n, k), generator=gen, device=dev).mul_(0.02).to(torch.bfloat16)
+              for _ in range(copies)]
+        a_in = torch.randn((m, k), generator=gen, device=dev).to(torch.bfloat16)
+        y = torch.empty((m, n), device=dev)
+
+        def enq(i, ws=ws, a_in=a_in, y=y, m=m, n=n, k=k):
+            Q.qdec_op_gemm(a_in, ws[i % copies], y, Q.F32, None, Q.GEMM_STORE, m, n, k,
+                           stream=s.cuda_stream)
+
+        us = per_launch_us(enq, 2 * copies)
+        tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        out["gemm"].append({"shape": [m, n, k], "us": round(us, 2), "tflops": round(tf, 1),
+                            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        del ws
+        torch.cuda.empty_cache()
     nb = 1 << 30
     a = torch.empty(nb, dtype=torch.uint8, device=dev)
     b = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -391,6 +461,7 @@ def main():
     Q.qdec_destroy(ctx)
     del w
     torch.cuda.empty_cache()
+    prefill = prefill_bench(shape, args.prefill_tokens) if args.prefill_tokens > 0 else None
     ops = None if args.no_ops else ops_bench()
     tok_s = 1.0 / graph_s
     out = {
@@ -413,6 +484,7 @@ def main():
         "kernels": kernels,
         "parity": parity,
         "cpu_baseline": cpu,
+        "prefill": prefill,
         "ops": ops,
     }
     print(json.dumps(out))
