@@ -54,6 +54,9 @@ def lib():
             "or_decode_step": (_I32, [_P, _I32, _P, _I32, _P, _P, _P]),
             "or_argmax": (_I64, [_P, _I64]),
             "or_set_fp32": (None, [_I32]),
+            "or_philox4x32_10": (None, [_P, _P, _P]),
+            "or_sample_uniform": (_D, [C.c_uint64, _I64]),
+            "or_sample": (_I64, [_P, _I64, _D, _D, _D, _P, _P]),
             "or_get_fp32": (_I32, []),
         }
         for name, (res, args) in sig.items():
@@ -210,6 +213,30 @@ def quantize_groups(w, bits):
     s = np.empty((n, k // GROUP), dtype=np.float32)
     lib().or_quantize_groups(_ptr(w), n, k, bits, _ptr(q), _ptr(s))
     return q, s
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32-10 block: counter (4 uint32), key (2 uint32) -> 4 uint32."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.empty(4, dtype=np.uint32)
+    lib().or_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def sample_uniform(seed, pos) -> float:
+    """The uniform draw of the sampling step at position pos under seed (Philox4x32-10)."""
+    return float(lib().or_sample_uniform(int(seed) & (2**64 - 1), int(pos)))
+
+
+def sample(logits, temperature, top_p, u):
+    """Temperature + top-p sampling by definition: (token, nucleus size, nucleus mass)."""
+    z = _f64(logits)
+    ns = C.c_int64(0)
+    nm = C.c_double(0.0)
+    tok = lib().or_sample(_ptr(z), z.size, float(temperature), float(top_p), float(u),
+                          C.byref(ns), C.byref(nm))
+    return int(tok), int(ns.value), float(nm.value)
 
 
 def _attn_args(q, K, V):

@@ -442,6 +442,103 @@ void or_pool_scatter(const void* logical, int32_t elem, int32_t pos0, int32_t n,
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* Sampling beyond greedy ([ETE] names temperature and top-p as missing; the method is the     */
+/* usual one, read plainly)                                                                    */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel random
+ * numbers: as easy as 1, 2, 3", SC 2011): ten rounds, each multiplying words 0 and 2 of the
+ * counter by 0xD2511F53 and 0xCD9E8D57 into 64-bit products, the new counter being
+ * (hi(c2*M1) ^ c1 ^ k0, lo(c2*M1), hi(c0*M0) ^ c3 ^ k1, lo(c0*M0)); the key is bumped by the
+ * Weyl constants 0x9E3779B9 and 0xBB67AE85 between rounds. */
+void or_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    const uint32_t n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    if (r < 9) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The uniform draw of a sampling step: Philox4x32-10 with key (seed low, seed high) and counter
+ * (position, 0, 0, 0); u = (first word >> 8) * 2^-24, in [0, 1). */
+double or_sample_uniform(uint64_t seed, int64_t pos) {
+  const uint32_t ctr[4] = {(uint32_t)pos, 0u, 0u, 0u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  or_philox4x32_10(ctr, key, out);
+  return (double)(out[0] >> 8) * (1.0 / 16777216.0);
+}
+
+/* Temperature + top-p (nucleus) sampling of one token from logits[n], by definition:
+ *   p_i = softmax(logits / temperature)_i (temperature > 0);
+ *   the nucleus is the shortest prefix of the tokens ordered by p descending (ties: lower index
+ *   first) whose probability mass reaches top_p (the token that reaches it is included);
+ *   the draw is the nucleus token, in index order, at which the cumulative nucleus mass first
+ *   exceeds u times the nucleus mass (the order of this inverse-CDF walk is a reading: any fixed
+ *   order gives the same distribution, and index order needs no sort).
+ * Returns the token index; writes the nucleus size and mass to *nsize / *nmass when non-NULL. */
+static const double* g_sort_p;
+static int cmp_desc(const void* a, const void* b) {
+  const int64_t i = *(const int64_t*)a, j = *(const int64_t*)b;
+  if (g_sort_p[i] > g_sort_p[j]) return -1;
+  if (g_sort_p[i] < g_sort_p[j]) return 1;
+  return i < j ? -1 : (i > j ? 1 : 0);
+}
+int64_t or_sample(const double* logits, int64_t n, double temperature, double top_p, double u,
+                  int64_t* nsize, double* nmass) {
+  double mx = -INFINITY;
+  for (int64_t i = 0; i < n; ++i)
+    if (logits[i] / temperature > mx) mx = logits[i] / temperature;
+  double* p = (double*)malloc((size_t)n * sizeof(double));
+  int64_t* idx = (int64_t*)malloc((size_t)n * sizeof(int64_t));
+  unsigned char* in = (unsigned char*)calloc((size_t)n, 1);
+  double z = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    p[i] = exp(logits[i] / temperature - mx);
+    z += p[i];
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    p[i] /= z;
+    idx[i] = i;
+  }
+  g_sort_p = p;
+  qsort(idx, (size_t)n, sizeof(int64_t), cmp_desc);
+  double mass = 0.0;
+  int64_t k = 0;
+  while (k < n) {
+    mass += p[idx[k]];
+    in[idx[k]] = 1;
+    ++k;
+    if (mass >= top_p) break;
+  }
+  double target = u * mass, cum = 0.0;
+  int64_t pick = idx[0];
+  for (int64_t i = 0; i < n; ++i) {
+    if (!in[i]) continue;
+    cum += p[i];
+    pick = i;
+    if (cum > target) break;
+  }
+  if (nsize) *nsize = k;
+  if (nmass) *nmass = mass;
+  free(p);
+  free(idx);
+  free(in);
+  return pick;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* One decode step of the whole model                                                          */
 /* ------------------------------------------------------------------------------------------ */
 
