@@ -240,6 +240,19 @@ struct PrefillAttnArgs {
   float qscale;               // log2(e) / sqrt(D)
 };
 
+// Temperature + top-p sampling of one token from logits[n].
+struct SampleArgs {
+  const void* logits;         // [n] bf16 or fp32
+  int32_t x_bf16;
+  int64_t n;
+  float inv_temperature;      // 1 / T, T > 0
+  float top_p;                // (0, 1]
+  uint64_t seed;              // Philox key
+  const StepDesc* desc;       // position from here when non-null (graph replay) ...
+  int32_t pos_arg;            // ... else this one; the Philox counter
+  int32_t* out;               // the sampled token
+};
+
 struct EmbedArgs {
   const void* table;          // [V x d] (bf16 or fp32), used when emb == nullptr
   int32_t table_bf16;

@@ -39,6 +39,8 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream_t s);
 hipError_t launch_prefill_attn(int head_dim, int group, const PrefillAttnArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
+// Temperature + top-p sampling (one 1024-thread work-group).
+hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
 const void* embed_kernel_fn();
 
 hipError_t launch_argmax(const void* x, int x_bf16, int64_t n, int32_t* out, hipStream_t s);

@@ -749,6 +749,14 @@ QDEC_API qdec_status qdec_kv_pool_ptr(const qdec_ctx* c, int32_t layer, void** k
 static qdec_status check_step(qdec_ctx* c, const qdec_step* st, bool check_pos) {
   if (!st) return fail(&c->err, QDEC_E_INVAL, "step is NULL");
   if (st->reserved != 0) return fail(&c->err, QDEC_E_INVAL, "step.reserved must be 0");
+  if (!(st->temperature >= 0.f) || !std::isfinite(st->temperature))
+    return fail(&c->err, QDEC_E_INVAL, "temperature must be >= 0 and finite");
+  if (st->temperature > 0.f) {
+    if (!(st->top_p > 0.f) || st->top_p > 1.f)
+      return fail(&c->err, QDEC_E_INVAL, "top_p must be in (0, 1] when sampling");
+    if (c->cfg.vocab > (1 << 18))
+      return fail(&c->err, QDEC_E_UNSUPPORTED, "sampling supports vocab <= 2^18");
+  }
   if (!st->token_embedding && !st->token_id)
     return fail(&c->err, QDEC_E_INVAL, "need token_embedding or token_id");
   if (st->token_embedding && !aligned(st->token_embedding, 4))
@@ -897,7 +905,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       h.y = st->logits_out ? st->logits_out : c->logits;
       h.y_bf16 = c->io_bf16();
       h.hidden_copy = st->hidden_out;
-      if (st->argmax_out) {
+      if (st->argmax_out && !(st->temperature > 0.f)) {
         h.part_val = c->am_val;
         h.part_idx = c->am_idx;
       }
@@ -905,8 +913,20 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       h.k = d;
       return launch_gemv(lt, EPI_STORE, true, h, s);
     }
-    case QDEC_K_ARGMAX:
-      return launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, st->argmax_out, s);
+    case QDEC_K_ARGMAX: {
+      if (!(st->temperature > 0.f))
+        return launch_argmax_partials(c->am_val, c->am_idx, c->am_parts, st->argmax_out, s);
+      SampleArgs sa{};
+      sa.logits = st->logits_out ? st->logits_out : c->logits;
+      sa.x_bf16 = c->io_bf16();
+      sa.n = k.vocab;
+      sa.inv_temperature = 1.0f / st->temperature;
+      sa.top_p = st->top_p;
+      sa.seed = st->seed;
+      sa.desc = c->desc;
+      sa.out = st->argmax_out;
+      return launch_sample(sa, s);
+    }
     default:
       return hipErrorInvalidValue;
   }
@@ -1369,6 +1389,30 @@ QDEC_API qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool
   hipError_t e = launch_prefill_attn(head_dim, n_q_heads / n_kv_heads, a,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "prefill attention launch: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_sample(const void* logits, int32_t dtype, int64_t n, float temperature,
+                                    float top_p, uint64_t seed, int32_t position, int32_t* out,
+                                    void* stream) {
+  if (!logits || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (dtype != QDEC_F32 && dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad dtype");
+  if (n < 1 || n > (int64_t(1) << 18)) return fail(nullptr, QDEC_E_INVAL, "n must be in [1, 2^18]");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(nullptr, QDEC_E_INVAL, "temperature must be positive and finite");
+  if (!(top_p > 0.f) || top_p > 1.f) return fail(nullptr, QDEC_E_INVAL, "top_p must be in (0, 1]");
+  if (position < 0) return fail(nullptr, QDEC_E_INVAL, "position must be >= 0");
+  SampleArgs a{};
+  a.logits = logits;
+  a.x_bf16 = dtype == QDEC_BF16;
+  a.n = n;
+  a.inv_temperature = 1.0f / temperature;
+  a.top_p = top_p;
+  a.seed = seed;
+  a.pos_arg = position;
+  a.out = out;
+  hipError_t e = launch_sample(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "sample launch: %s", hipGetErrorString(e));
   return QDEC_OK;
 }
 

@@ -46,7 +46,8 @@ class qdec_config(C.Structure):
 class qdec_step(C.Structure):
     _fields_ = [("token_embedding", C.c_void_p), ("token_id", C.c_void_p), ("pos", C.c_int32),
                 ("reserved", C.c_int32), ("hidden_out", C.c_void_p), ("logits_out", C.c_void_p),
-                ("argmax_out", C.c_void_p)]
+                ("argmax_out", C.c_void_p), ("temperature", C.c_float), ("top_p", C.c_float),
+                ("seed", C.c_uint64)]
 
 
 class qdec_info(C.Structure):
@@ -94,6 +95,7 @@ _SIGS = {
     "qdec_op_quantize_groups": [_P, _I32, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_gemm": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P],
     "qdec_op_prefill_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P],
+    "qdec_op_sample": [_P, _I32, _I64, _F, _F, C.c_uint64, _I32, _P, _P],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
     "qdec_op_rope_table": [_P, _I32, _I32, _F, _P],
     "qdec_op_qk_norm_rope_append": [_P, _P, _P, _F, _P, _I32, _P, _I32, _P, _P, _I32, _P, _I32,
@@ -254,8 +256,11 @@ def qdec_kv_pool_ptr(ctx, layer):
 # ---- the step -----------------------------------------------------------------------------------------
 
 def make_step(pos, token_id=None, token_embedding=None, hidden_out=None, logits_out=None,
-              argmax_out=None) -> qdec_step:
+              argmax_out=None, temperature=0.0, top_p=1.0, seed=0) -> qdec_step:
     s = qdec_step()
+    s.temperature = temperature
+    s.top_p = top_p
+    s.seed = int(seed) & (2**64 - 1)
     s.token_embedding = _p(token_embedding)
     s.token_id = _p(token_id)
     s.pos = pos
@@ -331,6 +336,11 @@ def qdec_op_prefill_attention(q, k_pool, v_pool, block_table, pos0, n_tokens, n_
                               n_kv_heads, head_dim, out, stream=None):
     _call("qdec_op_prefill_attention", _p(q), _p(k_pool), _p(v_pool), _p(block_table), pos0,
           n_tokens, n_q_heads, n_kv_heads, head_dim, _p(out), _p(stream))
+
+
+def qdec_op_sample(logits, dtype, n, temperature, top_p, seed, position, out, stream=None):
+    _call("qdec_op_sample", _p(logits), dtype, n, temperature, top_p, int(seed) & (2**64 - 1),
+          position, _p(out), _p(stream))
 
 
 def qdec_op_quantize_groups(w, w_dtype, dst_dtype, codes, scales, n, k, stream=None):

@@ -139,8 +139,15 @@ typedef struct qdec_step {
   void* logits_out;            /* optional [vocab] io_dtype logits.  NULL together with
                                   argmax_out == NULL skips the final norm and LM head (the
                                   prompt-token trim of [ETE]) */
-  int32_t* argmax_out;         /* optional device int32: index of the largest logit, the lowest
-                                  index winning ties; NaN logits never win */
+  int32_t* argmax_out;         /* optional device int32: the next token.  With temperature 0,
+                                  the index of the largest logit (the lowest index winning ties;
+                                  NaN logits never win); with temperature > 0, a token sampled
+                                  as qdec_op_sample does from the step's logits, with this
+                                  step's pos as the Philox counter */
+  float temperature;           /* 0: greedy; > 0 (finite): sampling temperature */
+  float top_p;                 /* sampling only: nucleus mass, in (0, 1] */
+  uint64_t seed;               /* sampling only: Philox key.  A captured graph keeps the
+                                  temperature, top_p and seed of its template step */
 } qdec_step;
 
 /* Sizes and byte counts derived from a config.  [Qwen3-runtime] §1.1 (parameter count),
@@ -384,6 +391,19 @@ qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool, const v
                                       const int32_t* block_table, int32_t pos0, int32_t n_tokens,
                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                                       void* out, void* stream);
+
+/* Temperature + top-p (nucleus) sampling of one token from logits [n] (F32 | BF16), n <= 2^18
+ * ([ETE], whose limitations passage names greedy-only decoding).  p = softmax(logits /
+ * temperature); the nucleus is the shortest prefix of the tokens ordered by p descending (ties:
+ * lower index first) whose mass reaches top_p; the token is the nucleus member, in index order,
+ * at which the cumulative nucleus mass first exceeds u times the nucleus mass, u in [0, 1) being
+ * the top 24 bits of the first word of Philox4x32-10 (Salmon et al., SC 2011) with key (seed
+ * low, seed high) and counter (position, 0, 0, 0).  Probabilities are summed as exact 64-bit
+ * fixed-point integers (2^-40 per unit of the largest), so the result is deterministic.
+ * temperature > 0 and finite, 0 < top_p <= 1, position >= 0; *out on the device. */
+qdec_status qdec_op_sample(const void* logits, int32_t dtype, int64_t n, float temperature,
+                           float top_p, uint64_t seed, int32_t position, int32_t* out,
+                           void* stream);
 
 /* Group-wise quantisation (the rule of qdec_upload for I8_G128 / I4_G128): w [n x k] F32|BF16 ->
  * codes and scales [n][k / 128] in the layouts of dst_dtype (qdec_dtype).  k % 128 == 0; w
