@@ -260,6 +260,21 @@ def ops_bench():
                             "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
         del ws
         torch.cuda.empty_cache()
+    out["sample"] = []
+    for n, dt in ((151936, Q.F32), (151936, Q.BF16), (128256, Q.F32)):
+        lg = torch.randn((n,), generator=gen, device=dev) * 3.0
+        if dt == Q.BF16:
+            lg = lg.to(torch.bfloat16)
+        tok_out = torch.empty(64, dtype=torch.int32, device=dev)
+        sws = torch.empty(Q.qdec_op_sample_workspace(n), dtype=torch.uint8, device=dev)
+
+        def enq(i, lg=lg, dt=dt, n=n, tok_out=tok_out, sws=sws):
+            Q.qdec_op_sample(lg, dt, n, 0.7, 0.9, 42, i, sws, sws.numel(), tok_out[i % 64:],
+                             stream=s.cuda_stream)
+
+        us = per_launch_us(enq, 64)
+        out["sample"].append({"vocab": n, "logits": "bf16" if dt == Q.BF16 else "f32",
+                              "temperature": 0.7, "top_p": 0.9, "us": round(us, 2)})
     nb = 1 << 30
     a = torch.empty(nb, dtype=torch.uint8, device=dev)
     b = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -458,6 +473,27 @@ def main():
                    "sample": f"{n} full decode steps of the same workload (same weights, KV and "
                              f"position) on {threads} OpenMP threads, {spent:.1f} s"}
 
+    # the same step drawing the token by temperature 0.7 / top-p 0.9 sampling instead of the argmax
+    sstep = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax,
+                        temperature=0.7, top_p=0.9, seed=42)
+    Q.qdec_graph_capture(ctx, sstep)
+    for _ in range(args.warmup):
+        Q.qdec_graph_replay(ctx, pos)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        Q.qdec_graph_replay(ctx, pos)
+    torch.cuda.synchronize()
+    sampled_s = (time.perf_counter() - t0) / args.steps
+    Q.qdec_profile_enable(ctx, 1)
+    for _ in range(args.profile_steps):
+        Q.qdec_decode_step(ctx, sstep)
+        sprof = Q.qdec_profile_collect(ctx)
+    Q.qdec_profile_enable(ctx, 0)
+    sampled = {"ms_per_step": round(sampled_s * 1e3, 5), "temperature": 0.7, "top_p": 0.9,
+               "sample_kernel_us": round(sprof["argmax"][0] * 1e3 / args.profile_steps, 3),
+               "lm_head_us": round(sprof["lm_head"][0] * 1e3 / args.profile_steps, 3)}
+
     Q.qdec_destroy(ctx)
     del w
     torch.cuda.empty_cache()
@@ -484,6 +520,7 @@ def main():
         "kernels": kernels,
         "parity": parity,
         "cpu_baseline": cpu,
+        "sampled_step": sampled,
         "prefill": prefill,
         "ops": ops,
     }

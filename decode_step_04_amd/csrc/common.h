@@ -251,6 +251,9 @@ struct SampleArgs {
   const StepDesc* desc;       // position from here when non-null (graph replay) ...
   int32_t pos_arg;            // ... else this one; the Philox counter
   int32_t* out;               // the sampled token
+  const float* part_val;      // optional: maxima of disjoint parts of the stored logits that
+  int32_t n_parts;            //   together cover all of them (the LM head's argmax partials)
+  void* ws;                   // sample_workspace_bytes(n) bytes, 256-byte aligned
 };
 
 struct EmbedArgs {

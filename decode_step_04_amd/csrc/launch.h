@@ -41,6 +41,7 @@ hipError_t launch_prefill_attn(int head_dim, int group, const PrefillAttnArgs& a
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 // Temperature + top-p sampling (one 1024-thread work-group).
 hipError_t launch_sample(const SampleArgs& a, hipStream_t s);
+int64_t sample_workspace_bytes(int64_t n);
 const void* embed_kernel_fn();
 
 hipError_t launch_argmax(const void* x, int x_bf16, int64_t n, int32_t* out, hipStream_t s);

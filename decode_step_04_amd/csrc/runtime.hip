@@ -133,6 +133,7 @@ struct qdec_ctx {
   void* pact = nullptr;       // [P][F] bf16 SwiGLU outputs
   float* am_val = nullptr;    // per-work-group partial argmax of the LM head
   int32_t* am_idx = nullptr;
+  void* sample_ws = nullptr;  // temperature / top-p sampling (vocab <= 2^18)
   int am_parts = 0;
   StepDesc* desc = nullptr;
   std::vector<uint8_t> uploaded;  // (n_layers + 1) x kNumSlots; row n_layers = global slots
@@ -289,7 +290,8 @@ static void fill_info(const qdec_config& c, qdec_info* o) {
                     block_table_entries(c) * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
                     (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ie +
                     hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc) +
-                    (int64_t)c.max_prefill * (d * 6 + (hq + 2 * hkv) * hd * 4 + 4 * hq * hd + 2 * f);
+                    (int64_t)c.max_prefill * (d * 6 + (hq + 2 * hkv) * hd * 4 + 4 * hq * hd + 2 * f) +
+                    (v <= (int64_t(1) << 18) ? sample_workspace_bytes(v) : 0);
 }
 
 QDEC_API qdec_status qdec_config_validate(const qdec_config* cfg, char* msg, size_t len) {
@@ -468,6 +470,8 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   c->am_parts = gemv_partials(wt_of(cfg->lm_head_dtype), EPI_STORE, v, d);
   TRY(c->alloc(&c->am_val, (int64_t)c->am_parts * 4, "argmax partials"));
   TRY(c->alloc(&c->am_idx, (int64_t)c->am_parts * 4, "argmax partials"));
+  if (v <= (int64_t(1) << 18))
+    TRY(c->alloc(&c->sample_ws, sample_workspace_bytes(v), "sampling workspace"));
   TRY(c->alloc(&c->part_acc, hq * (int64_t)c->max_parts * hd * 4, "split-KV scratch"));
   TRY(c->alloc(&c->part_ml, hq * (int64_t)c->max_parts * 8, "split-KV scratch"));
   if (cfg->max_prefill > 0) {
@@ -905,7 +909,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       h.y = st->logits_out ? st->logits_out : c->logits;
       h.y_bf16 = c->io_bf16();
       h.hidden_copy = st->hidden_out;
-      if (st->argmax_out && !(st->temperature > 0.f)) {
+      if (st->argmax_out) {  // the sampler takes its maximum from these too
         h.part_val = c->am_val;
         h.part_idx = c->am_idx;
       }
@@ -925,6 +929,9 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       sa.seed = st->seed;
       sa.desc = c->desc;
       sa.out = st->argmax_out;
+      sa.part_val = c->am_val;
+      sa.n_parts = c->am_parts;
+      sa.ws = c->sample_ws;
       return launch_sample(sa, s);
     }
     default:
@@ -1392,16 +1399,26 @@ QDEC_API qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool
   return QDEC_OK;
 }
 
+QDEC_API qdec_status qdec_op_sample_workspace(int64_t n, size_t* bytes) {
+  if (!bytes) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (n < 1 || n > (int64_t(1) << 18)) return fail(nullptr, QDEC_E_INVAL, "n must be in [1, 2^18]");
+  *bytes = (size_t)sample_workspace_bytes(n);
+  return QDEC_OK;
+}
+
 QDEC_API qdec_status qdec_op_sample(const void* logits, int32_t dtype, int64_t n, float temperature,
-                                    float top_p, uint64_t seed, int32_t position, int32_t* out,
-                                    void* stream) {
-  if (!logits || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+                                    float top_p, uint64_t seed, int32_t position, void* workspace,
+                                    size_t workspace_bytes, int32_t* out, void* stream) {
+  if (!logits || !out || !workspace) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (!aligned(workspace, 256)) return fail(nullptr, QDEC_E_INVAL, "workspace must be 256-byte aligned");
   if (dtype != QDEC_F32 && dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "bad dtype");
   if (n < 1 || n > (int64_t(1) << 18)) return fail(nullptr, QDEC_E_INVAL, "n must be in [1, 2^18]");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(nullptr, QDEC_E_INVAL, "temperature must be positive and finite");
   if (!(top_p > 0.f) || top_p > 1.f) return fail(nullptr, QDEC_E_INVAL, "top_p must be in (0, 1]");
   if (position < 0) return fail(nullptr, QDEC_E_INVAL, "position must be >= 0");
+  if (workspace_bytes < (size_t)sample_workspace_bytes(n))
+    return fail(nullptr, QDEC_E_INVAL, "workspace smaller than qdec_op_sample_workspace(n)");
   SampleArgs a{};
   a.logits = logits;
   a.x_bf16 = dtype == QDEC_BF16;
@@ -1411,6 +1428,7 @@ QDEC_API qdec_status qdec_op_sample(const void* logits, int32_t dtype, int64_t n
   a.seed = seed;
   a.pos_arg = position;
   a.out = out;
+  a.ws = workspace;
   hipError_t e = launch_sample(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "sample launch: %s", hipGetErrorString(e));
   return QDEC_OK;

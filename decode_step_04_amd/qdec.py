@@ -95,7 +95,8 @@ _SIGS = {
     "qdec_op_quantize_groups": [_P, _I32, _I32, _P, _P, _I64, _I64, _P],
     "qdec_op_gemm": [_P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _P],
     "qdec_op_prefill_attention": [_P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P],
-    "qdec_op_sample": [_P, _I32, _I64, _F, _F, C.c_uint64, _I32, _P, _P],
+    "qdec_op_sample": [_P, _I32, _I64, _F, _F, C.c_uint64, _I32, _P, _SZ, _P, _P],
+    "qdec_op_sample_workspace": [_I64, C.POINTER(_SZ)],
     "qdec_op_rmsnorm": [_P, _P, _F, _P, _I32, _I32, _P],
     "qdec_op_rope_table": [_P, _I32, _I32, _F, _P],
     "qdec_op_qk_norm_rope_append": [_P, _P, _P, _F, _P, _I32, _P, _I32, _P, _P, _I32, _P, _I32,
@@ -338,9 +339,16 @@ def qdec_op_prefill_attention(q, k_pool, v_pool, block_table, pos0, n_tokens, n_
           n_tokens, n_q_heads, n_kv_heads, head_dim, _p(out), _p(stream))
 
 
-def qdec_op_sample(logits, dtype, n, temperature, top_p, seed, position, out, stream=None):
+def qdec_op_sample_workspace(n):
+    b = C.c_size_t(0)
+    _call("qdec_op_sample_workspace", n, C.byref(b))
+    return b.value
+
+
+def qdec_op_sample(logits, dtype, n, temperature, top_p, seed, position, workspace,
+                   workspace_bytes, out, stream=None):
     _call("qdec_op_sample", _p(logits), dtype, n, temperature, top_p, int(seed) & (2**64 - 1),
-          position, _p(out), _p(stream))
+          position, _p(workspace), workspace_bytes, _p(out), _p(stream))
 
 
 def qdec_op_quantize_groups(w, w_dtype, dst_dtype, codes, scales, n, k, stream=None):

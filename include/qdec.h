@@ -399,11 +399,18 @@ qdec_status qdec_op_prefill_attention(const void* q, const void* k_pool, const v
  * at which the cumulative nucleus mass first exceeds u times the nucleus mass, u in [0, 1) being
  * the top 24 bits of the first word of Philox4x32-10 (Salmon et al., SC 2011) with key (seed
  * low, seed high) and counter (position, 0, 0, 0).  Probabilities are summed as exact 64-bit
- * fixed-point integers (2^-40 per unit of the largest), so the result is deterministic.
- * temperature > 0 and finite, 0 < top_p <= 1, position >= 0; *out on the device. */
+ * fixed-point integers (2^-40 per unit of the largest), so the result is deterministic; NaN
+ * logits are never drawn (all NaN: token 0).  temperature > 0 and finite, 0 < top_p <= 1,
+ * position >= 0; workspace: device memory of at least qdec_op_sample_workspace(n) bytes,
+ * 256-byte aligned, owned by the caller; calls that share a workspace must not overlap.  *out on
+ * the device. */
 qdec_status qdec_op_sample(const void* logits, int32_t dtype, int64_t n, float temperature,
-                           float top_p, uint64_t seed, int32_t position, int32_t* out,
-                           void* stream);
+                           float top_p, uint64_t seed, int32_t position, void* workspace,
+                           size_t workspace_bytes, int32_t* out, void* stream);
+
+/* Bytes of device workspace qdec_op_sample needs for n logits (1 <= n <= 2^18): per-slice
+ * histograms, their sum and the boundary candidates, all rewritten by every call. */
+qdec_status qdec_op_sample_workspace(int64_t n, size_t* bytes);
 
 /* Group-wise quantisation (the rule of qdec_upload for I8_G128 / I4_G128): w [n x k] F32|BF16 ->
  * codes and scales [n][k / 128] in the layouts of dst_dtype (qdec_dtype).  k % 128 == 0; w
