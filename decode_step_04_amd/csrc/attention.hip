@@ -406,14 +406,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
     const int hq = g * G + h;
     if (!live) {
       // nothing to store
-    } else if (np == 1) {
+    } else if (np == 1 && !a.to_partials) {
       const float o = O / L;
       if (a.out_bf16)
         static_cast<uint16_t*>(a.out)[hq * D + r] = f32_to_bf16(o);
       else
         static_cast<float*>(a.out)[hq * D + r] = o;
     } else {
-      const int64_t slot = (int64_t)hq * a.max_parts + pi;
+      const int64_t slot = (int64_t)hq * a.max_parts + a.part_base + pi;
       a.part_acc[slot * D + r] = O;
       if (r == 0) {
         a.part_ml[slot * 2 + 0] = M;
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_merge(AttnArgs a) {
       static_cast<float*>(a.out)[hq * D + dim] = o;
   };
   if (NW == 1 || np <= CH) {  // uniform; with one partition the partition kernel wrote the output
-    if (wave == 0 && np > 1) {
+    if (wave == 0 && (np > 1 || a.to_partials)) {
       fold(mlA, pA, 0);
       store(O / L);
     }

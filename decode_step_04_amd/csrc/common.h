@@ -192,6 +192,9 @@ struct AttnArgs {
   int32_t n_q_heads, n_kv_heads;
   int32_t part_tokens;        // partition length, a multiple of 64
   int32_t max_parts;          // scratch stride (partitions per head)
+  int32_t part_base;          // scratch slot of this launch's partition 0 (tiles of a longer context)
+  int32_t to_partials;        // always write (m, l, acc), even for a single partition; the merge
+                              // then normalises a lone partition too
   float* part_acc;            // [Hq][max_parts][D] unnormalised accumulators
   float* part_ml;             // [Hq][max_parts][2]: running max (log2 units) and denominator
   void* out;                  // [Hq x D]

@@ -1612,3 +1612,280 @@ QDEC_API qdec_status qdec_op_copy(void* dst, const void* src, int64_t bytes, voi
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "copy launch: %s", hipGetErrorString(e));
   return QDEC_OK;
 }
+
+// =====================================================================================
+// attention over host-resident K/V: tiles copied into device buffers, double-buffered
+// =====================================================================================
+
+namespace {
+// One record of the offload schedule (kinds as in qdec_offload_schedule).
+struct OffloadOp {
+  int kind, tile, slot, other;
+};
+enum { OFF_WAIT_FREE = 0, OFF_COPY = 1, OFF_WAIT_READY = 2, OFF_COMPUTE = 3, OFF_MERGE = 4 };
+
+// Tile i uses buffer i % n_slots.  Its copy may start once the compute of the tile that last used
+// that buffer (i - n_slots) has finished, and its compute once its own copy has finished.
+void offload_schedule(int n_tiles, int n_slots, std::vector<OffloadOp>* ops) {
+  ops->clear();
+  for (int i = 0; i < n_tiles; ++i) {
+    const int slot = i % n_slots;
+    if (i >= n_slots) ops->push_back({OFF_WAIT_FREE, i, slot, i - n_slots});
+    ops->push_back({OFF_COPY, i, slot, -1});
+    ops->push_back({OFF_WAIT_READY, i, slot, i});
+    ops->push_back({OFF_COMPUTE, i, slot, -1});
+  }
+  ops->push_back({OFF_MERGE, -1, -1, -1});
+}
+}  // namespace
+
+struct qdec_offload {
+  qdec_offload_config cfg{};
+  int part = 0;               // partition length
+  int max_parts = 0;          // partials per head (stride)
+  int tile_pages = 0;
+  int64_t page_bytes = 0;     // one page of K (or V): Hkv * 16 * D * elem
+  char* dev_k = nullptr;      // [n_slots][tile_pages] pages
+  char* dev_v = nullptr;
+  int32_t* bt = nullptr;      // identity page table of one buffer
+  float* part_acc = nullptr;
+  float* part_ml = nullptr;
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t start = nullptr, done = nullptr;
+  std::vector<hipEvent_t> copied, computed;
+  bool called = false;
+  int64_t device_bytes = 0;
+  std::vector<OffloadOp> ops;
+};
+
+static void offload_free(qdec_offload* o) {
+  if (!o) return;
+  (void)hipSetDevice(o->cfg.device);
+  if (o->copy_stream) (void)hipStreamSynchronize(o->copy_stream);
+  for (hipEvent_t e : o->copied)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : o->computed)
+    if (e) (void)hipEventDestroy(e);
+  if (o->start) (void)hipEventDestroy(o->start);
+  if (o->done) (void)hipEventDestroy(o->done);
+  if (o->copy_stream) (void)hipStreamDestroy(o->copy_stream);
+  for (void* p : {(void*)o->dev_k, (void*)o->dev_v, (void*)o->bt, (void*)o->part_acc,
+                  (void*)o->part_ml})
+    if (p) (void)hipFree(p);
+  delete o;
+}
+
+QDEC_API qdec_status qdec_offload_create(const qdec_offload_config* cfg, qdec_offload** out) {
+  if (!cfg || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  *out = nullptr;
+  const qdec_offload_config& c = *cfg;
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(nullptr, QDEC_E_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c.n_q_heads < 1 || c.n_kv_heads < 1 || c.n_q_heads % c.n_kv_heads || c.n_q_heads / c.n_kv_heads > 8)
+    return fail(nullptr, QDEC_E_INVAL, "bad head counts");
+  if (c.kv_dtype != QDEC_F32 && c.kv_dtype != QDEC_BF16) return fail(nullptr, QDEC_E_INVAL, "kv_dtype must be F32 or BF16");
+  if (c.max_context < 1) return fail(nullptr, QDEC_E_INVAL, "max_context must be positive");
+  if (c.tile_tokens < 64 || c.tile_tokens > 65536 || c.tile_tokens % 64)
+    return fail(nullptr, QDEC_E_INVAL, "tile_tokens must be a multiple of 64 in [64, 65536]");
+  if (c.n_slots < 1 || c.n_slots > 8) return fail(nullptr, QDEC_E_INVAL, "n_slots must be in [1, 8]");
+  if (c.partition_size < 0 || c.partition_size % 64 || c.partition_size > kMaxPartTokens ||
+      (c.partition_size > 0 && c.tile_tokens % c.partition_size))
+    return fail(nullptr, QDEC_E_INVAL,
+                "partition_size must be 0 or a multiple of 64 up to %d that divides tile_tokens",
+                kMaxPartTokens);
+  int part = c.partition_size;
+  if (part == 0) {  // the resident path's choice for one tile, lowered until it divides the tile
+    part = part_tokens_for(c.tile_tokens, 0, c.n_kv_heads, target_wgs(c.n_q_heads, c.n_kv_heads));
+    while (c.tile_tokens % part) part -= 64;
+  }
+  const int64_t max_parts = n_parts_for(c.max_context, part);
+  if (max_parts > kMaxMergeParts)
+    return fail(nullptr, QDEC_E_UNSUPPORTED, "more than %d partitions at max_context", kMaxMergeParts);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || c.device < 0 || c.device >= ndev)
+    return fail(nullptr, QDEC_E_INVAL, "no such device");
+  if (hipSetDevice(c.device) != hipSuccess) return fail(nullptr, QDEC_E_HIP, "hipSetDevice failed");
+  qdec_offload* o = new qdec_offload();
+  o->cfg = c;
+  o->part = part;
+  o->max_parts = (int)max_parts;
+  o->tile_pages = c.tile_tokens / kPage;
+  o->page_bytes = (int64_t)c.n_kv_heads * kPage * c.head_dim * elem_size(c.kv_dtype);
+  const int64_t buf_bytes = (int64_t)c.n_slots * o->tile_pages * o->page_bytes;
+  const AttnWs ws = attn_ws(c.n_q_heads, max_parts, c.head_dim);
+  auto alloc = [&](void** p, int64_t bytes) {
+    o->device_bytes += bytes;
+    return hipMalloc(p, (size_t)bytes) == hipSuccess;
+  };
+  bool ok = alloc((void**)&o->dev_k, buf_bytes) && alloc((void**)&o->dev_v, buf_bytes) &&
+            alloc((void**)&o->bt, (int64_t)o->tile_pages * 4) &&
+            alloc((void**)&o->part_acc, ws.ml_off) && alloc((void**)&o->part_ml, ws.bytes - ws.ml_off);
+  if (ok) {
+    std::vector<int32_t> ident(o->tile_pages);
+    for (int j = 0; j < o->tile_pages; ++j) ident[j] = j;
+    ok = hipMemcpy(o->bt, ident.data(), ident.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
+  }
+  ok = ok && hipStreamCreateWithFlags(&o->copy_stream, hipStreamNonBlocking) == hipSuccess &&
+       hipEventCreateWithFlags(&o->start, hipEventDisableTiming) == hipSuccess &&
+       hipEventCreateWithFlags(&o->done, hipEventDisableTiming) == hipSuccess;
+  o->copied.assign(c.n_slots, nullptr);
+  o->computed.assign(c.n_slots, nullptr);
+  for (int s = 0; ok && s < c.n_slots; ++s)
+    ok = hipEventCreateWithFlags(&o->copied[s], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&o->computed[s], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    const hipError_t e = hipGetLastError();
+    offload_free(o);
+    return fail(nullptr, QDEC_E_NOMEM, "offload allocation failed: %s", hipGetErrorString(e));
+  }
+  *out = o;
+  return QDEC_OK;
+}
+
+QDEC_API void qdec_offload_destroy(qdec_offload* o) { offload_free(o); }
+
+QDEC_API qdec_status qdec_offload_info(const qdec_offload* o, int64_t* device_bytes,
+                                       int32_t* partition_tokens) {
+  if (!o) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (device_bytes) *device_bytes = o->device_bytes;
+  if (partition_tokens) *partition_tokens = o->part;
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_offload_schedule(int32_t n_tiles, int32_t n_slots, int32_t* records,
+                                           int32_t cap, int32_t* n) {
+  if (!n || (cap > 0 && !records)) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  if (n_tiles < 1 || n_slots < 1 || n_slots > 8 || n_tiles > (1 << 24))
+    return fail(nullptr, QDEC_E_INVAL, "bad tile or slot count");
+  std::vector<OffloadOp> ops;
+  offload_schedule(n_tiles, n_slots, &ops);
+  *n = (int32_t)ops.size();
+  for (int32_t i = 0; i < cap && i < (int32_t)ops.size(); ++i) {
+    records[4 * i + 0] = ops[i].kind;
+    records[4 * i + 1] = ops[i].tile;
+    records[4 * i + 2] = ops[i].slot;
+    records[4 * i + 3] = ops[i].other;
+  }
+  return QDEC_OK;
+}
+
+static bool pinned_host(const void* p) {
+  hipPointerAttribute_t at{};
+  const hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // pageable memory: clear the error so no later call reports it
+    return false;
+  }
+  return at.type == hipMemoryTypeHost;
+}
+
+QDEC_API qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int32_t q_dtype,
+                                            const void* host_k, const void* host_v,
+                                            int32_t ctx_len, void* out, int32_t out_dtype,
+                                            void* stream) {
+  if (!o || !q || !host_k || !host_v || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  const qdec_offload_config& c = o->cfg;
+  if (ctx_len < 1 || ctx_len > c.max_context)
+    return fail(nullptr, QDEC_E_RANGE, "ctx_len must be in [1, %d]", c.max_context);
+  if ((q_dtype != QDEC_F32 && q_dtype != QDEC_BF16) || (out_dtype != QDEC_F32 && out_dtype != QDEC_BF16))
+    return fail(nullptr, QDEC_E_INVAL, "bad dtype");
+  if (hipSetDevice(c.device) != hipSuccess) return fail(nullptr, QDEC_E_HIP, "hipSetDevice failed");
+  if (!pinned_host(host_k) || !pinned_host(host_v))
+    return fail(nullptr, QDEC_E_INVAL, "host_k and host_v must be pinned host memory");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int n_tiles = (ctx_len + c.tile_tokens - 1) / c.tile_tokens;
+  const int tile_parts = c.tile_tokens / o->part;
+  const int64_t buf_bytes = (int64_t)o->tile_pages * o->page_bytes;
+  AttnArgs a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == QDEC_BF16;
+  a.block_table = o->bt;
+  a.desc = nullptr;
+  a.n_q_heads = c.n_q_heads;
+  a.n_kv_heads = c.n_kv_heads;
+  a.part_tokens = o->part;
+  a.max_parts = o->max_parts;
+  a.part_acc = o->part_acc;
+  a.part_ml = o->part_ml;
+  a.to_partials = 1;
+  a.out = out;
+  a.out_bf16 = out_dtype == QDEC_BF16;
+  a.qscale = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  const bool kvb = c.kv_dtype == QDEC_BF16;
+  const int group = c.n_q_heads / c.n_kv_heads;
+  hipError_t e = hipSuccess;
+  auto chk = [&](hipError_t r) {
+    if (e == hipSuccess) e = r;
+    return e == hipSuccess;
+  };
+  // the previous call's kernels (slots, partials) and everything before this call on the
+  // caller's stream come first
+  if (o->called) chk(hipStreamWaitEvent(s, o->done, 0));
+  chk(hipEventRecord(o->start, s));
+  chk(hipStreamWaitEvent(o->copy_stream, o->start, 0));
+  offload_schedule(n_tiles, c.n_slots, &o->ops);
+  for (const OffloadOp& op : o->ops) {
+    if (e != hipSuccess) break;
+    const int i = op.tile;
+    const int64_t t0 = (int64_t)i * c.tile_tokens;
+    const int len = i >= 0 ? (int)std::min<int64_t>(c.tile_tokens, ctx_len - t0) : 0;
+    const int pages = (len + kPage - 1) / kPage;
+    switch (op.kind) {
+      case OFF_WAIT_FREE:
+        chk(hipStreamWaitEvent(o->copy_stream, o->computed[op.slot], 0));
+        break;
+      case OFF_COPY: {
+        const int64_t src = t0 / kPage * o->page_bytes, bytes = pages * o->page_bytes;
+        chk(hipMemcpyAsync(o->dev_k + op.slot * buf_bytes, static_cast<const char*>(host_k) + src,
+                           (size_t)bytes, hipMemcpyHostToDevice, o->copy_stream));
+        chk(hipMemcpyAsync(o->dev_v + op.slot * buf_bytes, static_cast<const char*>(host_v) + src,
+                           (size_t)bytes, hipMemcpyHostToDevice, o->copy_stream));
+        chk(hipEventRecord(o->copied[op.slot], o->copy_stream));
+        break;
+      }
+      case OFF_WAIT_READY:
+        chk(hipStreamWaitEvent(s, o->copied[op.slot], 0));
+        break;
+      case OFF_COMPUTE: {
+        AttnArgs t = a;
+        t.k_pool = o->dev_k + op.slot * buf_bytes;
+        t.v_pool = o->dev_v + op.slot * buf_bytes;
+        t.bt_len = pages;
+        t.ctx_arg = len;
+        t.part_base = i * tile_parts;
+        chk(launch_attention(c.head_dim, kvb, group, false, t, n_parts_for(len, o->part), s));
+        chk(hipEventRecord(o->computed[op.slot], s));
+        break;
+      }
+      case OFF_MERGE: {
+        AttnArgs m = a;
+        m.ctx_arg = ctx_len;
+        chk(launch_attention_merge(c.head_dim, m, s));
+        chk(hipEventRecord(o->done, s));
+        break;
+      }
+    }
+  }
+  o->called = true;
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "offload attention: %s", hipGetErrorString(e));
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_host_alloc(size_t bytes, void** ptr) {
+  if (!ptr) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
+  *ptr = nullptr;
+  if (bytes == 0) return fail(nullptr, QDEC_E_INVAL, "bytes must be positive");
+  if (hipHostMalloc(ptr, bytes, hipHostMallocDefault) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    *ptr = nullptr;
+    return fail(nullptr, QDEC_E_NOMEM, "hipHostMalloc of %zu bytes: %s", bytes, hipGetErrorString(e));
+  }
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_host_free(void* ptr) {
+  if (ptr && hipHostFree(ptr) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    return fail(nullptr, QDEC_E_HIP, "hipHostFree: %s", hipGetErrorString(e));
+  }
+  return QDEC_OK;
+}

@@ -63,8 +63,21 @@ class qdec_bytes(C.Structure):
         "lm_head", "argmax", "total", "scratch")]
 
 
+class qdec_offload_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "device", "n_q_heads", "n_kv_heads", "head_dim", "kv_dtype", "max_context", "tile_tokens",
+        "n_slots", "partition_size")]
+
+
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 _SIGS = {
+    "qdec_offload_create": [C.POINTER(qdec_offload_config), C.POINTER(_P)],
+    "qdec_offload_destroy": [_P],
+    "qdec_offload_info": [_P, C.POINTER(_I64), C.POINTER(_I32)],
+    "qdec_offload_attention": [_P, _P, _I32, _P, _P, _I32, _P, _I32, _P],
+    "qdec_offload_schedule": [_I32, _I32, C.POINTER(_I32), _I32, C.POINTER(_I32)],
+    "qdec_host_alloc": [_SZ, C.POINTER(_P)],
+    "qdec_host_free": [_P],
     "qdec_config_validate": [C.POINTER(qdec_config), C.c_char_p, _SZ],
     "qdec_config_info": [C.POINTER(qdec_config), C.POINTER(qdec_info)],
     "qdec_bytes_model": [C.POINTER(qdec_config), _I32, _I32, C.POINTER(qdec_bytes)],
@@ -107,7 +120,7 @@ _SIGS = {
     "qdec_op_argmax": [_P, _I32, _I64, _P, _P],
     "qdec_op_copy": [_P, _P, _I64, _P],
 }
-_VOID = {"qdec_destroy"}
+_VOID = {"qdec_destroy", "qdec_offload_destroy"}
 _STR = {"qdec_last_error", "qdec_status_string"}
 
 
@@ -392,3 +405,49 @@ def qdec_op_argmax(x, x_dtype, n, out, stream=None):
 
 def qdec_op_copy(dst, src, nbytes, stream=None):
     _call("qdec_op_copy", _p(dst), _p(src), nbytes, _p(stream))
+
+
+# ---- attention over host-resident K/V ----
+
+def qdec_offload_create(n_q_heads, n_kv_heads, head_dim, kv_dtype, max_context, tile_tokens,
+                        n_slots=2, partition_size=0, device=0) -> int:
+    cfg = qdec_offload_config(device, n_q_heads, n_kv_heads, head_dim, kv_dtype, max_context,
+                              tile_tokens, n_slots, partition_size)
+    h = C.c_void_p()
+    _call("qdec_offload_create", C.byref(cfg), C.byref(h))
+    return h.value
+
+
+def qdec_offload_destroy(o) -> None:
+    lib().qdec_offload_destroy(o)
+
+
+def qdec_offload_info(o):
+    """(device bytes, partition length)."""
+    b, p = C.c_int64(0), C.c_int32(0)
+    _call("qdec_offload_info", o, C.byref(b), C.byref(p))
+    return b.value, p.value
+
+
+def qdec_offload_attention(o, q, q_dtype, host_k, host_v, ctx_len, out, out_dtype, stream=None):
+    _call("qdec_offload_attention", o, _p(q), q_dtype, _p(host_k), _p(host_v), ctx_len, _p(out),
+          out_dtype, _p(stream))
+
+
+def qdec_offload_schedule(n_tiles, n_slots):
+    """The enqueue order as a list of (kind, tile, slot, other) records."""
+    n = C.c_int32(0)
+    _call("qdec_offload_schedule", n_tiles, n_slots, None, 0, C.byref(n))
+    buf = (C.c_int32 * (4 * n.value))()
+    _call("qdec_offload_schedule", n_tiles, n_slots, buf, n.value, C.byref(n))
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(n.value)]
+
+
+def qdec_host_alloc(nbytes) -> int:
+    p = C.c_void_p()
+    _call("qdec_host_alloc", nbytes, C.byref(p))
+    return p.value
+
+
+def qdec_host_free(p) -> None:
+    _call("qdec_host_free", p)

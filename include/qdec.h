@@ -466,6 +466,66 @@ qdec_status qdec_op_argmax(const void* x, int32_t x_dtype, int64_t n, int32_t* o
  * own copy kernel: the reference point for achievable bandwidth and for scaling HBM counters. */
 qdec_status qdec_op_copy(void* dst, const void* src, int64_t bytes, void* stream);
 
+/* ---- Attention over host-resident K/V: tiles copied in, double-buffered ------------------------
+ * [ETE] KV-offload passage: the history K/V stay in host memory; one tile of positions at a time
+ * is copied into a device tile buffer, a tile pass folds it into (m, l, acc) state kept in global
+ * memory, and a last pass normalises (acc / l), so device memory is fixed by the tile, not the
+ * context.  [ETE] next-steps list: give the tiles several buffers with the event pattern of its
+ * layer streaming - a tile's compute waits for that tile's copy (data ready), and a copy into a
+ * buffer waits for the compute that last read it (buffer free).
+ *
+ * Each tile is a whole number of split-KV partitions.  A tile launch writes the (m, l, acc) of its
+ * partitions into the slots the resident path uses for them, and one exact merge ends the call,
+ * so the result is qdec_op_attention's on the same K/V and partition length (bit for bit when the
+ * context spans two or more partitions).  Copies run on the object's own stream (default
+ * priority), kernels on the caller's. */
+typedef struct qdec_offload qdec_offload;
+
+typedef struct qdec_offload_config {
+  int32_t device;
+  int32_t n_q_heads, n_kv_heads, head_dim; /* Hq % Hkv == 0, Hq / Hkv <= 8; head_dim 64 or 128 */
+  int32_t kv_dtype;                        /* QDEC_F32 | QDEC_BF16 */
+  int32_t max_context;                     /* positions one call may cover, >= 1 */
+  int32_t tile_tokens;                     /* positions per copy: a multiple of 64, 64 .. 65536 */
+  int32_t n_slots;                         /* device tile buffers, 1 .. 8 (1: copy, then compute) */
+  int32_t partition_size;                  /* 0 = automatic, else a multiple of 64 up to 512 that
+                                              divides tile_tokens */
+} qdec_offload_config;
+
+/* Validates cfg and allocates everything a call needs: n_slots K and V tile buffers, the (m, l,
+ * acc) partials for max_context, the copy stream and the events.  *out is NULL on failure. */
+qdec_status qdec_offload_create(const qdec_offload_config* cfg, qdec_offload** out);
+/* Waits for the object's copies, then frees it.  NULL is a no-op. */
+void qdec_offload_destroy(qdec_offload* o);
+/* Device bytes the object holds, and the partition length in effect. */
+qdec_status qdec_offload_info(const qdec_offload* o, int64_t* device_bytes,
+                              int32_t* partition_tokens);
+
+/* Causal GQA decode attention (as qdec_op_attention) of q [Hq x D] (device, q_dtype F32|BF16)
+ * over positions 0 .. ctx_len-1 (1 <= ctx_len <= max_context) whose K and V are in host memory:
+ * host_k / host_v hold ceil(ctx_len / 16) pages in position order, page p = positions 16p ..
+ * 16p+15 laid out [Hkv][16][D] of kv_dtype (the device pool's page layout), and must be pinned
+ * (qdec_host_alloc or another hipHostMalloc'd block; pageable memory is rejected).  out [Hq x D]
+ * on the device, out_dtype F32|BF16.  The call enqueues and returns: the host pages must stay
+ * unchanged, and out unread, until the caller's stream has passed it.  Calls on one object are
+ * ordered among themselves (each waits for the previous call's work); issue them from one host
+ * thread. */
+qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int32_t q_dtype,
+                                   const void* host_k, const void* host_v, int32_t ctx_len,
+                                   void* out, int32_t out_dtype, void* stream);
+
+/* The enqueue order qdec_offload_attention uses for n_tiles tiles over n_slots buffers, as
+ * records of four int32 (kind, tile, slot, other): kind 0 = the copy stream waits for the compute
+ * of tile `other` (buffer free), 1 = copy tile into slot, 2 = the compute stream waits for the
+ * copy of tile `other` (data ready), 3 = compute tile from slot, 4 = merge (tile, slot -1).
+ * Writes at most cap records; *n gets the number the schedule has.  Needs no GPU. */
+qdec_status qdec_offload_schedule(int32_t n_tiles, int32_t n_slots, int32_t* records,
+                                  int32_t cap, int32_t* n);
+
+/* Pinned host memory (hipHostMalloc) for host-resident K/V; freed by qdec_host_free. */
+qdec_status qdec_host_alloc(size_t bytes, void** ptr);
+qdec_status qdec_host_free(void* ptr);
+
 #ifdef __cplusplus
 }
 #endif
