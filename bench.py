@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+PEAK_PCIE_GBPS = 64.0  # host link, PCIe 5.0 x16, one direction
 METRIC = "batch-1 decode tokens/s + achieved HBM GB/s vs peak (Qwen3-0.6B shape, 4K ctx)"
 
 
@@ -141,11 +142,14 @@ def prefill_bench(shape, n_tok):
 
 
 def ops_bench():
-    """Op-level workloads timed in HIP graphs, each launch reading a different copy of its data so
-    that nothing is served by the 256 MB Infinity Cache: split-KV attention (32 Q / 8 KV heads,
-    D 128, bf16 K/V, contexts 8K / 32K / 128K, partitions of 512 tokens and automatic), the W8A16
-    GEMV at 130560x1536 and 151936x1024 (int8 codes, fp32 row scales, bf16 x and y) next to the
-    bf16 GEMV of the same shapes, and the copy kernel on 1 GiB (read + write)."""
+    """Op-level workloads.  Timed in HIP graphs, each launch reading a different copy of its data
+    so that nothing is served by the 256 MB Infinity Cache: split-KV attention (32 Q / 8 KV heads,
+    D 128, bf16 K/V, contexts 8K / 32K / 128K, partitions of 512 tokens and automatic); the GEMV at
+    130560x1536 and 151936x1024 for int8 rows, int8 and int4 groups of 128 and bf16 weights (bf16
+    x and y); the prefill GEMM on four shapes; the sampler at a 152K / 128K vocabulary; the copy
+    kernel on 1 GiB (read + write).  Timed with events around plain calls: attention over
+    host-resident K/V at 32K / 128K positions (tile and buffer counts), with a pinned
+    host-to-device copy of the same bytes."""
     import math
 
     import torch
@@ -275,6 +279,63 @@ def ops_bench():
         us = per_launch_us(enq, 64)
         out["sample"].append({"vocab": n, "logits": "bf16" if dt == Q.BF16 else "f32",
                               "temperature": 0.7, "top_p": 0.9, "us": round(us, 2)})
+    # attention over host-resident K/V: 32 Q / 8 KV heads, D 128, bf16 pages in pinned memory;
+    # the page's single-buffer copy-then-compute against several buffers and larger tiles, next to
+    # a plain pinned host-to-device copy of the same bytes (the PCIe ceiling)
+    out["offload"] = []
+    warm_h = torch.empty(1 << 29, dtype=torch.uint8, pin_memory=True)
+    warm_d = torch.empty(1 << 29, dtype=torch.uint8, device=dev)
+    for _ in range(4):  # bring the host link to its working speed before timing
+        warm_d.copy_(warm_h, non_blocking=True)
+    torch.cuda.synchronize()
+    del warm_h, warm_d
+    for T in (32768, 131072):
+        pages = T // 16
+        kv_bytes = 2 * T * hkv * d * 2
+        hk = torch.empty((pages, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty((pages, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+        hk.copy_(torch.randn((pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+        hv.copy_(torch.randn((pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+        q = synth.attention_stress(8192, device=dev)[0]
+        att = torch.empty((hq, d), device=dev)
+        dk = torch.empty_like(hk, device=dev)
+        dv = torch.empty_like(hv, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cs = torch.cuda.current_stream().cuda_stream
+
+        def best_us(fn, reps=5):
+            t = []
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                t.append(e0.elapsed_time(e1) * 1e3)
+            return min(t)
+
+        def h2d():
+            dk.copy_(hk, non_blocking=True)
+            dv.copy_(hv, non_blocking=True)
+
+        row = {"context": T, "kv_bytes": kv_bytes, "runs": []}
+        for tile, slots in ((512, 1), (512, 2), (4096, 1), (4096, 2), (16384, 2), (16384, 3),
+                            (512, 0)):
+            o = Q.qdec_offload_create(hq, hkv, d, Q.BF16, T, tile, slots, 0)
+            Q.qdec_offload_attention(o, q, Q.F32, hk, hv, T, att, Q.F32, cs)
+            copy_us = best_us(h2d)
+            us = best_us(lambda: Q.qdec_offload_attention(o, q, Q.F32, hk, hv, T, att, Q.F32, cs))
+            dev_bytes, part_eff = Q.qdec_offload_info(o)
+            Q.qdec_offload_destroy(o)
+            row["runs"].append({"tile": tile, "slots": slots, "partition": part_eff,
+                                "device_mib": round(dev_bytes / 2**20, 1), "us": round(us, 1),
+                                "gbps": round(kv_bytes / us / 1e3, 1),
+                                "frac_pcie_peak": round(kv_bytes / us / 1e3 / PEAK_PCIE_GBPS, 3),
+                                "h2d_copy_gbps": round(kv_bytes / copy_us / 1e3, 1),
+                                "of_copy": round(copy_us / us, 3)})
+        del dk, dv
+        out["offload"].append(row)
+        del hk, hv
     nb = 1 << 30
     a = torch.empty(nb, dtype=torch.uint8, device=dev)
     b = torch.empty(nb, dtype=torch.uint8, device=dev)

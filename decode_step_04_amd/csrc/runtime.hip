@@ -1686,15 +1686,17 @@ QDEC_API qdec_status qdec_offload_create(const qdec_offload_config* cfg, qdec_of
   if (c.max_context < 1) return fail(nullptr, QDEC_E_INVAL, "max_context must be positive");
   if (c.tile_tokens < 64 || c.tile_tokens > 65536 || c.tile_tokens % 64)
     return fail(nullptr, QDEC_E_INVAL, "tile_tokens must be a multiple of 64 in [64, 65536]");
-  if (c.n_slots < 1 || c.n_slots > 8) return fail(nullptr, QDEC_E_INVAL, "n_slots must be in [1, 8]");
+  if (c.n_slots < 0 || c.n_slots > 8) return fail(nullptr, QDEC_E_INVAL, "n_slots must be in [0, 8]");
   if (c.partition_size < 0 || c.partition_size % 64 || c.partition_size > kMaxPartTokens ||
       (c.partition_size > 0 && c.tile_tokens % c.partition_size))
     return fail(nullptr, QDEC_E_INVAL,
                 "partition_size must be 0 or a multiple of 64 up to %d that divides tile_tokens",
                 kMaxPartTokens);
   int part = c.partition_size;
-  if (part == 0) {  // the resident path's choice for one tile, lowered until it divides the tile
-    part = part_tokens_for(c.tile_tokens, 0, c.n_kv_heads, target_wgs(c.n_q_heads, c.n_kv_heads));
+  if (part == 0) {  // the resident path's choice for one tile (direct: for max_context), lowered
+                    // until it divides the tile
+    part = part_tokens_for(c.n_slots ? c.tile_tokens : c.max_context, 0, c.n_kv_heads,
+                           target_wgs(c.n_q_heads, c.n_kv_heads));
     while (c.tile_tokens % part) part -= 64;
   }
   const int64_t max_parts = n_parts_for(c.max_context, part);
@@ -1711,17 +1713,20 @@ QDEC_API qdec_status qdec_offload_create(const qdec_offload_config* cfg, qdec_of
   o->tile_pages = c.tile_tokens / kPage;
   o->page_bytes = (int64_t)c.n_kv_heads * kPage * c.head_dim * elem_size(c.kv_dtype);
   const int64_t buf_bytes = (int64_t)c.n_slots * o->tile_pages * o->page_bytes;
+  // identity page table: one buffer's pages, or (direct) every page of max_context
+  const int bt_pages = c.n_slots ? o->tile_pages : (c.max_context + kPage - 1) / kPage;
   const AttnWs ws = attn_ws(c.n_q_heads, max_parts, c.head_dim);
   auto alloc = [&](void** p, int64_t bytes) {
     o->device_bytes += bytes;
     return hipMalloc(p, (size_t)bytes) == hipSuccess;
   };
-  bool ok = alloc((void**)&o->dev_k, buf_bytes) && alloc((void**)&o->dev_v, buf_bytes) &&
-            alloc((void**)&o->bt, (int64_t)o->tile_pages * 4) &&
+  bool ok = (buf_bytes == 0 || (alloc((void**)&o->dev_k, buf_bytes) &&
+                                 alloc((void**)&o->dev_v, buf_bytes))) &&
+            alloc((void**)&o->bt, (int64_t)bt_pages * 4) &&
             alloc((void**)&o->part_acc, ws.ml_off) && alloc((void**)&o->part_ml, ws.bytes - ws.ml_off);
   if (ok) {
-    std::vector<int32_t> ident(o->tile_pages);
-    for (int j = 0; j < o->tile_pages; ++j) ident[j] = j;
+    std::vector<int32_t> ident(bt_pages);
+    for (int j = 0; j < bt_pages; ++j) ident[j] = j;
     ok = hipMemcpy(o->bt, ident.data(), ident.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
   }
   ok = ok && hipStreamCreateWithFlags(&o->copy_stream, hipStreamNonBlocking) == hipSuccess &&
@@ -1791,6 +1796,15 @@ QDEC_API qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int3
   if (hipSetDevice(c.device) != hipSuccess) return fail(nullptr, QDEC_E_HIP, "hipSetDevice failed");
   if (!pinned_host(host_k) || !pinned_host(host_v))
     return fail(nullptr, QDEC_E_INVAL, "host_k and host_v must be pinned host memory");
+  void* dk = nullptr;  // direct mode: the device's address of the host pages
+  void* dv = nullptr;
+  if (c.n_slots == 0 &&
+      (hipHostGetDevicePointer(&dk, const_cast<void*>(host_k), 0) != hipSuccess ||
+       hipHostGetDevicePointer(&dv, const_cast<void*>(host_v), 0) != hipSuccess || !dk || !dv ||
+       !aligned(dk, 16) || !aligned(dv, 16))) {
+    (void)hipGetLastError();
+    return fail(nullptr, QDEC_E_INVAL, "host_k and host_v must be device-mapped pinned memory");
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int n_tiles = (ctx_len + c.tile_tokens - 1) / c.tile_tokens;
   const int tile_parts = c.tile_tokens / o->part;
@@ -1820,6 +1834,19 @@ QDEC_API qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int3
   // the previous call's kernels (slots, partials) and everything before this call on the
   // caller's stream come first
   if (o->called) chk(hipStreamWaitEvent(s, o->done, 0));
+  if (c.n_slots == 0) {  // direct: the split-KV kernel reads the mapped host pages itself
+    AttnArgs t = a;
+    t.k_pool = dk;
+    t.v_pool = dv;
+    t.bt_len = (ctx_len + kPage - 1) / kPage;
+    t.ctx_arg = ctx_len;
+    chk(launch_attention(c.head_dim, kvb, group, false, t, n_parts_for(ctx_len, o->part), s));
+    chk(launch_attention_merge(c.head_dim, t, s));
+    chk(hipEventRecord(o->done, s));
+    o->called = true;
+    if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "offload attention: %s", hipGetErrorString(e));
+    return QDEC_OK;
+  }
   chk(hipEventRecord(o->start, s));
   chk(hipStreamWaitEvent(o->copy_stream, o->start, 0));
   offload_schedule(n_tiles, c.n_slots, &o->ops);

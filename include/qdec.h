@@ -478,7 +478,9 @@ qdec_status qdec_op_copy(void* dst, const void* src, int64_t bytes, void* stream
  * partitions into the slots the resident path uses for them, and one exact merge ends the call,
  * so the result is qdec_op_attention's on the same K/V and partition length (bit for bit when the
  * context spans two or more partitions).  Copies run on the object's own stream (default
- * priority), kernels on the caller's. */
+ * priority), kernels on the caller's.  With n_slots = 0 nothing is copied: pinned host memory is
+ * mapped into the GPU's address space, and the split-KV kernel streams the pages over the host
+ * link itself, every partition at once (partition_size 0 then sizes partitions for max_context). */
 typedef struct qdec_offload qdec_offload;
 
 typedef struct qdec_offload_config {
@@ -487,7 +489,9 @@ typedef struct qdec_offload_config {
   int32_t kv_dtype;                        /* QDEC_F32 | QDEC_BF16 */
   int32_t max_context;                     /* positions one call may cover, >= 1 */
   int32_t tile_tokens;                     /* positions per copy: a multiple of 64, 64 .. 65536 */
-  int32_t n_slots;                         /* device tile buffers, 1 .. 8 (1: copy, then compute) */
+  int32_t n_slots;                         /* device tile buffers, 1 .. 8 (1: copy, then compute);
+                                              0: no copies - the split-KV kernel reads the pinned
+                                              host pages through their device mapping */
   int32_t partition_size;                  /* 0 = automatic, else a multiple of 64 up to 512 that
                                               divides tile_tokens */
 } qdec_offload_config;

@@ -68,6 +68,11 @@ CASES = [  # (D, Hq, Hkv, kv dtype, T, tile, slots, partition)
     (64, 16, 2, torch.bfloat16, 2049, 1024, 2, 512),
     (128, 8, 8, torch.float32, 1000, 192, 4, 64),
     (128, 4, 1, torch.bfloat16, 5000, 2048, 8, 0),
+    # n_slots 0: the kernel reads the mapped host pages directly
+    (128, 16, 8, torch.bfloat16, 1, 512, 0, 0),
+    (128, 32, 8, torch.bfloat16, 3000, 512, 0, 0),
+    (64, 4, 2, torch.float32, 777, 128, 0, 64),
+    (128, 8, 8, torch.float32, 1000, 192, 0, 64),
 ]
 
 
@@ -104,17 +109,19 @@ def test_offload_full_size_128k():
     print(f"offload stress T={T}", flush=True)
     q, kl, vl, _ = synth.attention_stress(T, device=DEV)
     hk, hv = _host_pages(kl), _host_pages(vl)
-    o = Q.qdec_offload_create(32, 8, 128, Q.BF16, T, 4096, 2, 512)
-    try:
-        got = _offload(o, q, hk, hv, T, 32, 128)
-        torch.cuda.synchronize()
-        got = got.cpu().numpy()
-    finally:
-        Q.qdec_offload_destroy(o)
     ref = oracle.attention(q.cpu().numpy().astype(np.float64), kl.float().cpu().numpy(),
                            vl.float().cpu().numpy())
-    assert np.max(np.abs(got - ref)) <= 1e-4
-    assert np.array_equal(got, _resident(q, kl, vl, 32, 8, 128, 512))
+    res = _resident(q, kl, vl, 32, 8, 128, 512)
+    for tile, slots in ((4096, 2), (512, 0)):
+        o = Q.qdec_offload_create(32, 8, 128, Q.BF16, T, tile, slots, 512)
+        try:
+            got = _offload(o, q, hk, hv, T, 32, 128)
+            torch.cuda.synchronize()
+            got = got.cpu().numpy()
+        finally:
+            Q.qdec_offload_destroy(o)
+        assert np.max(np.abs(got - ref)) <= 1e-4
+        assert np.array_equal(got, res)
 
 
 def test_offload_back_to_back_calls_and_streams():
@@ -167,7 +174,7 @@ def test_offload_bf16_out():
 
 def test_offload_rejects():
     hq, hkv, d = 8, 8, 64
-    for bad in (dict(tile_tokens=100), dict(tile_tokens=0), dict(n_slots=0), dict(n_slots=9),
+    for bad in (dict(tile_tokens=100), dict(tile_tokens=0), dict(n_slots=-1), dict(n_slots=9),
                 dict(partition_size=192, tile_tokens=512), dict(head_dim=96), dict(max_context=0),
                 dict(n_kv_heads=3), dict(kv_dtype=Q.I8_ROW)):
         kw = dict(n_q_heads=hq, n_kv_heads=hkv, head_dim=d, kv_dtype=Q.F32, max_context=1024,
