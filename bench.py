@@ -141,6 +141,50 @@ def prefill_bench(shape, n_tok):
             "policy": "bf16 weights and KV, bf16 activations at op boundaries, fp32 residual"}
 
 
+def cpu_extra(oracle, om, pos, tok_id, step_bytes, threads):
+    """The oracle on one thread (one step), and per op with all threads and one: the attention
+    stress workload at 8K positions (32 Q / 8 KV heads, D 128) and the W8A16 GEMV at
+    130560x1536, on seeded synthetic inputs of those shapes; ms and effective GB/s over the same
+    algorithmic bytes as the GPU figures."""
+    import numpy as np
+
+    out = {}
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    om.step(pos, token=tok_id)
+    one = time.perf_counter() - t0
+    out["single_thread"] = {"tokens_per_s": round(1.0 / one, 4), "ms": round(one * 1e3, 1),
+                            "gbps": round(step_bytes / one / 1e9, 3)}
+    rng = np.random.default_rng(21)
+    T, hq, hkv, d = 8192, 32, 8, 128
+    q = rng.standard_normal((hq, d))
+    kv = [rng.standard_normal((T, hkv, d)).astype(np.float32) for _ in range(2)]
+    n, k = 130560, 1536
+    codes = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    scales = (rng.random(n) * 1e-3).astype(np.float32)
+    x = rng.standard_normal(k)
+    ops = []
+    for name, fn, nbytes in (
+            ("attention 8K, 32 Q / 8 KV heads, D 128", lambda: oracle.attention(q, kv[0], kv[1]),
+             T * hkv * d * 2 * 2),
+            ("W8A16 GEMV 130560x1536", lambda: oracle.gemv(codes, x, scales),
+             n * k + 4 * n + 2 * k + 2 * n)):
+        row = {"op": name, "bytes": nbytes}
+        for label, nt in (("all_threads", threads), ("one_thread", 1)):
+            oracle.set_threads(nt)
+            fn()
+            reps, t0 = 0, time.perf_counter()
+            while reps < 3 or (time.perf_counter() - t0 < 1.0 and reps < 50):
+                fn()
+                reps += 1
+            ms = (time.perf_counter() - t0) * 1e3 / reps
+            row[label] = {"ms": round(ms, 3), "gbps": round(nbytes / ms / 1e6, 3)}
+        ops.append(row)
+    oracle.set_threads(threads)
+    out["ops"] = ops
+    return out
+
+
 def ops_bench():
     """Op-level workloads.  Timed in HIP graphs, each launch reading a different copy of its data
     so that nothing is served by the 256 MB Infinity Cache: split-KV attention (32 Q / 8 KV heads,
@@ -528,11 +572,12 @@ def main():
                 om.step(pos, token=tok_id)
                 spent += time.perf_counter() - t0
                 n += 1
-            threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+            threads = oracle.get_threads()
             cpu = {"value": round(n / spent, 4), "unit": "tokens/s", "cores": threads,
                    "kind": "oracle",
                    "sample": f"{n} full decode steps of the same workload (same weights, KV and "
                              f"position) on {threads} OpenMP threads, {spent:.1f} s"}
+            cpu.update(cpu_extra(oracle, om, pos, tok_id, bm.total, threads))
 
     # the same step drawing the token by temperature 0.7 / top-p 0.9 sampling instead of the argmax
     sstep = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax,

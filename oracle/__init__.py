@@ -58,12 +58,23 @@ def lib():
             "or_sample_uniform": (_D, [C.c_uint64, _I64]),
             "or_sample": (_I64, [_P, _I64, _D, _D, _D, _P, _P]),
             "or_get_fp32": (_I32, []),
+            "or_set_threads": (None, [_I32]),
+            "or_get_threads": (_I32, []),
         }
         for name, (res, args) in sig.items():
             fn = getattr(_lib, name)
             fn.restype = res
             fn.argtypes = args
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads the OpenMP loops use (timing only; results do not depend on it)."""
+    lib().or_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().or_get_threads())
 
 
 def _ptr(a):

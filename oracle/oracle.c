@@ -87,6 +87,17 @@ static double round_f32(double v) { return (double)(float)v; }
 static int g_fp32 = 0;
 void or_set_fp32(int32_t on) { g_fp32 = on != 0; }
 int32_t or_get_fp32(void) { return g_fp32; }
+
+/* Threads that split independent rows and heads (timing only: each row's arithmetic is the same
+ * sequential order whatever the count). */
+#ifdef _OPENMP
+#include <omp.h>
+void or_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
+int32_t or_get_threads(void) { return omp_get_max_threads(); }
+#else
+void or_set_threads(int32_t n) { (void)n; }
+int32_t or_get_threads(void) { return 1; }
+#endif
 static double F(double v) { return g_fp32 ? round_f32(v) : v; }
 
 void or_round_bf16(const double* in, double* out, int64_t n) {
