@@ -24,6 +24,7 @@
 namespace qd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -130,9 +131,157 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+// k_gemm_lds: the same product and epilogues with the operand tiles staged in LDS.  A work-group
+// of 4 waves computes BM = 128 rows against BN weight rows (256, or 128 when N is small): per K
+// step of 64 it loads A[128 x 64] and W[BN x 64] into one of two LDS buffers (each thread 16-byte
+// loads, 8 threads per 128-byte row segment), while the MFMAs read the other buffer; one barrier
+// per step.  LDS rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of any 8
+// consecutive lanes (rows r .. r+7 at one k offset) then fall in distinct banks.  Wave w owns rows
+// 64 (w / 2) .. +63 and weight rows (w % 2) BN/2 .. +BN/2-1 of the tile: 4 x BN/32 MFMA tiles.
+// For SWIGLU a wave's BN/2 weight rows are BN/4 gate rows and the matching BN/4 up rows, so g and u
+// of an output meet in the same lanes.
+template <int EPI, int BN>
+__global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
+  constexpr int BM = 128, BK = 64, LDR = BK + 8;
+  constexpr int WN = BN / 2;          // weight rows per wave
+  constexpr int NJ = WN / 16;         // 16-row blocks of them
+  constexpr int AL = BM * BK / 8 / 256;  // 16-byte loads per thread per step
+  constexpr int BL = BN * BK / 8 / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * LDR];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int M = a.m, N = a.n, K = a.k;
+  const int m0 = blockIdx.y * BM;
+  const int nout = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per work-group
+  const int n0 = blockIdx.x * nout;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  // this thread's loads: row t / 8 + 32 r of a tile, 16 bytes at k offset 8 (t % 8); source rows
+  // past the end are clamped (their results are discarded)
+  const int trow = t >> 3, tkc = (t & 7) * 8;
+  auto wrow = [&](int row) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int h = row / WN, q = row % WN;
+      const int col = min(n0 + h * (WN / 2) + q % (WN / 2), N - 1);
+      return q < WN / 2 ? col : N + col;
+    } else {
+      return min(n0 + row, N - 1);
+    }
+  };
+  u32x4 ra[AL], rb[BL];
+  auto gload = [&](int k) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < AL; ++r)
+      ra[r] = *reinterpret_cast<const u32x4*>(
+          A + (int64_t)min(m0 + trow + 32 * r, M - 1) * K + k + tkc);
+#pragma unroll
+    for (int r = 0; r < BL; ++r)
+      rb[r] = *reinterpret_cast<const u32x4*>(W + (int64_t)wrow(trow + 32 * r) * K + k + tkc);
+  };
+  auto lstore = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < AL; ++r)
+      *reinterpret_cast<u32x4*>(&sa[st][(trow + 32 * r) * LDR + tkc]) = ra[r];
+#pragma unroll
+    for (int r = 0; r < BL; ++r)
+      *reinterpret_cast<u32x4*>(&sb[st][(trow + 32 * r) * LDR + tkc]) = rb[r];
+  };
+  f32x4 acc[4][NJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int arow = (wave >> 1) * 64 + r16, brow = (wave & 1) * WN + r16;
+  const int nk = K / BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 32) {
+      bf16x8 fa[4], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                               &sa[st][(arow + 16 * i) * LDR + ks + kq]));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                               &sb[st][(brow + 16 * j) * LDR + ks + kq]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds C[row 16 i + 4 (l/16) + e of the wave][weight row 16 j + l % 16]
+  const int mw = m0 + (wave >> 1) * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = mw + 16 * i + 4 * (lane >> 4) + e;
+      if (m >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+          const int n = n0 + (wave & 1) * (WN / 2) + 16 * j + r16;
+          if (n >= N) continue;
+          const float g = acc[i][j][e], u = acc[i][j + NJ / 2][e];
+          const float v = g / (1.0f + expf(-g)) * u;
+          static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + (wave & 1) * WN + 16 * j + r16;
+          if (n >= N) continue;
+          const float v = acc[i][j][e];
+          if constexpr (EPI == EPI_RESID)
+            a.resid[(int64_t)m * N + n] += v;
+          else if (a.y_bf16)
+            static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
+          else
+            static_cast<float*>(a.y)[(int64_t)m * N + n] = v;
+        }
+      }
+    }
+  }
+}
+
+template <int EPI>
+static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
+  // 256 weight rows per work-group when that still gives at least 256 work-groups
+  const int mt = (a.m + 127) / 128;
+  const int out256 = EPI == EPI_SWIGLU ? 128 : 256;
+  if ((int64_t)((a.n + out256 - 1) / out256) * mt >= 256) {
+    const dim3 grid((unsigned)((a.n + out256 - 1) / out256), (unsigned)mt);
+    hipLaunchKernelGGL((k_gemm_lds<EPI, 256>), grid, dim3(256), 0, s, a);
+  } else {
+    const int out128 = out256 / 2;
+    const dim3 grid((unsigned)((a.n + out128 - 1) / out128), (unsigned)mt);
+    hipLaunchKernelGGL((k_gemm_lds<EPI, 128>), grid, dim3(256), 0, s, a);
+  }
+}
+
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.m <= 0 || a.n <= 0) return hipSuccess;
   if (a.k % 32 || a.k < 32) return hipErrorInvalidValue;
+  if (a.k % 64 == 0) {
+    switch (epi) {
+      case EPI_STORE: launch_gemm_lds<EPI_STORE>(a, s); break;
+      case EPI_RESID: launch_gemm_lds<EPI_RESID>(a, s); break;
+      default: launch_gemm_lds<EPI_SWIGLU>(a, s); break;
+    }
+    return hipGetLastError();
+  }
   const int ncols = epi == EPI_SWIGLU ? 64 : 128;
   const dim3 grid((unsigned)((a.n + ncols - 1) / ncols), (unsigned)((a.m + 127) / 128));
   switch (epi) {

@@ -31,7 +31,7 @@ def _bf16_ulp_ok(got, exact, extra=1e-6):
 
 
 SHAPES = [(1, 16, 32), (5, 33, 64), (128, 128, 128), (200, 300, 1024), (17, 1024, 3072),
-          (2048, 4096, 1024), (130, 6144, 1024)]
+          (2048, 4096, 1024), (130, 6144, 1024), (2000, 4300, 1024), (300, 96, 96)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
@@ -52,7 +52,8 @@ def test_gemm_store_matches_oracle(m, n, k):
     assert _bf16_ulp_ok(synth.bf16_to_f32(ybf)[rows], exact).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(3, 48, 96), (300, 1024, 2048), (64, 4096, 4096)])
+@pytest.mark.parametrize("m,n,k", [(3, 48, 96), (300, 1024, 2048), (64, 4096, 4096),
+                                   (2048, 4096, 1024), (1999, 4200, 512)])
 def test_gemm_resid_adds_into_the_stream(m, n, k):
     g = torch.Generator(device=DEV).manual_seed(m + n + k)
     a = torch.randn((m, k), generator=g, device=DEV).to(torch.bfloat16)
@@ -66,7 +67,8 @@ def test_gemm_resid_adds_into_the_stream(m, n, k):
     assert np.max(np.abs(r.cpu().numpy()[rows] - exact)) <= 1e-4
 
 
-@pytest.mark.parametrize("m,f,k", [(2, 64, 64), (77, 200, 1024), (512, 3072, 1024)])
+@pytest.mark.parametrize("m,f,k", [(2, 64, 64), (77, 200, 1024), (512, 3072, 1024),
+                                   (2048, 3072, 1024), (2001, 3000, 1024)])
 def test_gemm_swiglu_epilogue(m, f, k):
     g = torch.Generator(device=DEV).manual_seed(m * 3 + f + k)
     a = torch.randn((m, k), generator=g, device=DEV).to(torch.bfloat16)
