@@ -132,20 +132,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 }
 
 // k_gemm_lds: the same product and epilogues with the operand tiles staged in LDS.  A work-group
-// of 4 waves computes BM = 128 rows against BN weight rows (256, or 128 when N is small): per K
-// step of 64 it loads A[128 x 64] and W[BN x 64] into one of two LDS buffers (each thread 16-byte
-// loads, 8 threads per 128-byte row segment), while the MFMAs read the other buffer; one barrier
-// per step.  LDS rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of any 8
-// consecutive lanes (rows r .. r+7 at one k offset) then fall in distinct banks.  Wave w owns rows
-// 64 (w / 2) .. +63 and weight rows (w % 2) BN/2 .. +BN/2-1 of the tile: 4 x BN/32 MFMA tiles.
-// For SWIGLU a wave's BN/2 weight rows are BN/4 gate rows and the matching BN/4 up rows, so g and u
-// of an output meet in the same lanes.
-template <int EPI, int BN>
+// of 4 waves computes BM rows (128 or 64) against BN weight rows (128 or 64): per K step of 64 it
+// loads A[BM x 64] and W[BN x 64] into one of two LDS buffers (16-byte loads, 8 threads per
+// 128-byte row segment) while the MFMAs read the other; one barrier per step.  The next step's
+// loads are issued before the current step's MFMAs and stored after them.  At most 54 KB of LDS
+// and ~180 registers keep two work-groups on a CU, so one's load latency hides under the other's
+// MFMAs.  LDS rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of any 8
+// consecutive lanes (rows r .. r+7 at one k offset) fall in distinct banks.  Wave w owns rows
+// (w / 2) BM/2 .. +BM/2-1 and weight rows (w % 2) BN/2 .. +BN/2-1 of the tile.  For SWIGLU a wave's
+// BN/2 weight rows are BN/4 gate rows and the matching BN/4 up rows, so g and u of an output meet
+// in the same lanes.
+template <int EPI, int BM, int BN>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
-  constexpr int BM = 128, BK = 64, LDR = BK + 8;
-  constexpr int WN = BN / 2;          // weight rows per wave
-  constexpr int NJ = WN / 16;         // 16-row blocks of them
-  constexpr int AL = BM * BK / 8 / 256;  // 16-byte loads per thread per step
+  constexpr int BK = 64, LDR = BK + 8;
+  constexpr int WM = BM / 2, WN = BN / 2;   // rows and weight rows per wave
+  constexpr int NI = WM / 16, NJ = WN / 16; // their 16-row blocks
+  constexpr int AL = BM * BK / 8 / 256;     // 16-byte loads per thread per step
   constexpr int BL = BN * BK / 8 / 256;
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * LDR];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * LDR];
@@ -186,13 +188,13 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
     for (int r = 0; r < BL; ++r)
       *reinterpret_cast<u32x4*>(&sb[st][(trow + 32 * r) * LDR + tkc]) = rb[r];
   };
-  f32x4 acc[4][NJ];
+  f32x4 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int arow = (wave >> 1) * 64 + r16, brow = (wave & 1) * WN + r16;
+  const int arow = (wave >> 1) * WM + r16, brow = (wave & 1) * WN + r16;
   const int nk = K / BK;
   gload(0);
   lstore(0);
@@ -202,9 +204,9 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
     if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < BK; ks += 32) {
-      bf16x8 fa[4], fb[NJ];
+      bf16x8 fa[NI], fb[NJ];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
         fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                &sa[st][(arow + 16 * i) * LDR + ks + kq]));
 #pragma unroll
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
         fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
                                                &sb[st][(brow + 16 * j) * LDR + ks + kq]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
@@ -222,9 +224,9 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   }
 
   // epilogue: lane holds C[row 16 i + 4 (l/16) + e of the wave][weight row 16 j + l % 16]
-  const int mw = m0 + (wave >> 1) * 64;
+  const int mw = m0 + (wave >> 1) * WM;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int m = mw + 16 * i + 4 * (lane >> 4) + e;
@@ -256,19 +258,22 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   }
 }
 
+// The largest tile that still gives two work-groups per CU (512), else the smallest.
 template <int EPI>
 static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
-  // 256 weight rows per work-group when that still gives at least 256 work-groups
-  const int mt = (a.m + 127) / 128;
-  const int out256 = EPI == EPI_SWIGLU ? 128 : 256;
-  if ((int64_t)((a.n + out256 - 1) / out256) * mt >= 256) {
-    const dim3 grid((unsigned)((a.n + out256 - 1) / out256), (unsigned)mt);
-    hipLaunchKernelGGL((k_gemm_lds<EPI, 256>), grid, dim3(256), 0, s, a);
-  } else {
-    const int out128 = out256 / 2;
-    const dim3 grid((unsigned)((a.n + out128 - 1) / out128), (unsigned)mt);
-    hipLaunchKernelGGL((k_gemm_lds<EPI, 128>), grid, dim3(256), 0, s, a);
-  }
+  const int64_t wide = EPI == EPI_SWIGLU ? 2 : 1;  // weight rows per output column
+  auto wgs = [&](int bm, int bn) {
+    return ((a.n * wide + bn - 1) / bn) * (int64_t)((a.m + bm - 1) / bm);
+  };
+  auto grid = [&](int bm, int bn) {
+    return dim3((unsigned)((a.n * wide + bn - 1) / bn), (unsigned)((a.m + bm - 1) / bm));
+  };
+  if (wgs(128, 128) >= 512)
+    hipLaunchKernelGGL((k_gemm_lds<EPI, 128, 128>), grid(128, 128), dim3(256), 0, s, a);
+  else if (wgs(64, 128) >= 512)
+    hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128>), grid(64, 128), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 64>), grid(64, 64), dim3(256), 0, s, a);
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
