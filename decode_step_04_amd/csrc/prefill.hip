@@ -380,30 +380,38 @@ hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream
 // FlashAttention-style ([ETE], the batched-prefill next step; the (m, l, acc) state of
 // [Qwen3-runtime] §9.1 / [ETE] online softmax, per query row).  A work-group of 4 waves takes
 // kv head g and BQ = 64 / G consecutive queries; its 64 rows are (query, head) pairs, query-major,
-// 16 per wave.  Keys go in blocks of 32 (two pages):
-//   S = Q K^T: A = the wave's 16 query rows (bf16, D/32 k-steps, loaded once), B = K rows read
-//     straight from the page tiles (lane l: key l % 16 of a 16-key half, 16 contiguous bytes);
-//   S is scaled to log2 units, keys past a row's position masked, and the row state updated with
-//     16-lane DPP reductions (in the MFMA output layout a row's 16 columns sit in one DPP row);
-//   P = 2^(S - m) is rounded to bf16 (the MFMA operand type; the row sum l adds the rounded
+// 16 per wave.  Keys go in blocks of 32 (two pages).  Each block's K and V are loaded once per
+// work-group (every thread 16-byte chunks, requested a block ahead) and staged in LDS, K row-major
+// and V transposed, in two alternating buffers; one barrier per block.
+//   S = Q K^T: A = the wave's 16 query rows (bf16, D/32 k-steps, held in registers), B = K rows
+//     from LDS (lane l: key l % 16 of a 16-key half, 16 contiguous bytes);
+//   the row state is updated with 16-lane DPP reductions (in the MFMA output layout a row's 16
+//     columns sit in one DPP row); only a block that reaches past the first query's position is
+//     masked;
+//   P = 2^(S - m) is rounded to bf16 (the MFMA operand type; the denominator adds the rounded
 //     values, so O / l stays a normalised average) and passed through a per-wave LDS tile to
-//     become the A operand of O += P V; V tiles are staged transposed in LDS (double-buffered,
-//     one barrier per block) so that each B fragment is 16 contiguous bytes.
+//     become the A operand of O += P V, whose B fragments are 16 contiguous bytes of V^T.
+// LDS row strides: K 136 bf16 (272 bytes: 8 consecutive key rows at one offset fall in distinct
+// banks), V^T and P 40 bf16 (80 bytes: a wave's transposed writes cover 32 keys of two d rows,
+// in disjoint banks).
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
   constexpr int BQ = 64 / G;     // queries per work-group
   constexpr int ROWS = BQ * G;   // active rows (64 unless G does not divide 64)
   constexpr int KS = D / 32;     // MFMA k-steps over D
   constexpr int ND = D / 16;     // 16-column blocks of D in the output
-  constexpr int VP = 40;         // LDS row stride in bf16 (32 keys + 8 pad: 80 bytes)
-  constexpr int VL = 32 * D / 8 / 256;  // 16-byte V loads per thread per block
+  constexpr int KP = D + 8;      // LDS row stride of K, in bf16
+  constexpr int VP = 40;         // LDS row stride of V^T and P, in bf16
+  constexpr int CL = 32 * D / 8 / 256;  // 16-byte chunks of K (and of V) per thread per block
+  __shared__ __align__(16) uint16_t kt[2][32][KP];
   __shared__ __align__(16) uint16_t vt[2][D][VP];
   __shared__ __align__(16) uint16_t pl[4][16][VP];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, q4 = lane >> 4;
   const int g = blockIdx.y;
   const int hq = a.n_q_heads, hkv = a.n_kv_heads;
-  const int t0 = blockIdx.x * BQ;
+  // the last queries (the most keys) first, so that the longest work-groups start earliest
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * BQ;
   const int nq = min(BQ, a.p - t0);                      // valid queries of the block (>= 1)
   const int kend = a.pos0 + t0 + nq;                     // keys 0 .. kend-1 are visible
   const float NEG = -INFINITY;
@@ -427,79 +435,114 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
     active[i] = rc < ROWS && qc < nq;
     qpos[i] = active[i] ? a.pos0 + t0 + qc : -1;       // an inactive row sees no key
   }
-  float m[4], l[4];
+  // m: the row's running maximum (log2 units); lp: this lane's part of the row's denominator
+  float m[4], lp[4];
   f32x4 o[ND];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     m[i] = -1e30f;
-    l[i] = 0.f;
+    lp[i] = 0.f;
   }
 #pragma unroll
   for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nblk = (kend + 31) / 32;
   const int64_t head_stride = (int64_t)kPage * D;        // one head's page tile, in elements
+  const int last = kend - 1;
+  // page numbers without a memory round trip in the loop: lane l holds pages 2l and 2l + 1 of the
+  // current chunk of 128 pages (64 blocks); the next chunk is loaded a whole chunk ahead.  Pages
+  // past the last visible one are clamped to it (every entry below npages is valid).
+  const int npages = (kend + kPage - 1) / kPage;
+  int pc0, pc1, pn0 = 0, pn1 = 0;
+  auto chunk = [&](int c, int& p0, int& p1) __attribute__((always_inline)) {
+    p0 = a.block_table[min(c * 128 + 2 * lane, npages - 1)];
+    p1 = a.block_table[min(c * 128 + 2 * lane + 1, npages - 1)];
+  };
+  chunk(0, pc0, pc1);
+  // this thread's chunks of a block: chunk idx = t + 256 u is 16 bytes at d 8 (idx / 32) of key
+  // idx % 32 (keys past `last` clamped); a wave covers 32 keys x 2 d-chunks
+  uint4 kc[CL], vc[CL];
+  auto fetch = [&](int kb) __attribute__((always_inline)) {
+    const int key0 = kb * 32;
+    const int64_t ph0 = __builtin_amdgcn_readlane(pc0, kb & 63);
+    const int64_t ph1 = __builtin_amdgcn_readlane(pc1, kb & 63);
+#pragma unroll
+    for (int u = 0; u < CL; ++u) {
+      const int idx = threadIdx.x + 256 * u, kl = idx & 31, d8 = idx >> 5;
+      const int key = min(key0 + kl, last);
+      const int64_t off = (((key - key0) < 16 ? ph0 : ph1) * hkv + g) * head_stride +
+                          (int64_t)(key % kPage) * D + 8 * d8;
+      kc[u] = *reinterpret_cast<const uint4*>(a.k_pool + off);
+      vc[u] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+    }
+  };
+  auto stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CL; ++u) {
+      const int idx = threadIdx.x + 256 * u, kl = idx & 31, d8 = idx >> 5;
+      *reinterpret_cast<uint4*>(&kt[buf][kl][8 * d8]) = kc[u];
+      const uint32_t w4[4] = {vc[u].x, vc[u].y, vc[u].z, vc[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[buf][8 * d8 + 2 * e][kl] = (uint16_t)(w4[e] & 0xFFFFu);
+        vt[buf][8 * d8 + 2 * e + 1][kl] = (uint16_t)(w4[e] >> 16);
+      }
+    }
+  };
+  fetch(0);
   for (int kb = 0; kb < nblk; ++kb) {
     const int key0 = kb * 32;
-    const int last = kend - 1;
-    // the block's two pages (the second clamped to the last visible key's page)
-    const int64_t ph0 = a.block_table[key0 / kPage];
-    const int64_t ph1 = a.block_table[min(key0 + 16, last) / kPage];
-    const uint16_t* kt0 = a.k_pool + (ph0 * hkv + g) * head_stride;
-    const uint16_t* kt1 = a.k_pool + (ph1 * hkv + g) * head_stride;
-    // V tile loads (cooperative): 16-byte chunk c of key kl, keys past `last` clamped
-    uint4 vv[VL];
-    int vkl[VL], vd8[VL];
-#pragma unroll
-    for (int u = 0; u < VL; ++u) {
-      const int idx = threadIdx.x + 256 * u;
-      vkl[u] = idx / (D / 8);
-      vd8[u] = idx % (D / 8);
-      const int key = min(key0 + vkl[u], last);
-      const uint16_t* vtile = a.v_pool + (((key - key0) < 16 ? ph0 : ph1) * hkv + g) * head_stride;
-      vv[u] = *reinterpret_cast<const uint4*>(vtile + (int64_t)(key % kPage) * D + 8 * vd8[u]);
+    const int buf = kb & 1;
+    if ((kb & 63) == 0 && kb + 64 < nblk) chunk((kb >> 6) + 1, pn0, pn1);  // wave-uniform
+    if (((kb + 1) & 63) == 0) {  // the next block opens a new chunk
+      pc0 = pn0;
+      pc1 = pn1;
     }
+    stage(buf);
+    if (kb + 1 < nblk) fetch(kb + 1);
+    __syncthreads();
     // S = Q K^T for the two 16-key halves
     f32x4 sc[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const int key = min(key0 + 16 * nb + r16, last);
-      const uint16_t* krow = (nb == 0 ? kt0 : kt1) + (int64_t)(key % kPage) * D + 8 * q4;
       sc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], load_frag(krow + 32 * ks), sc[nb], 0, 0, 0);
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qf[ks], load_frag(&kt[buf][16 * nb + r16][32 * ks + 8 * q4]), sc[nb], 0, 0, 0);
     }
-    // online softmax per row (rows 4 q4 + i, columns r16 of each half)
+    // online softmax per row (rows 4 q4 + i, columns r16 of each half): the maximum on the
+    // unscaled scores (qscale > 0), the scale folded into the exponent's fma, P rounded to bf16
+    // once for the PV operand and the denominator alike.  When no row's maximum grew, every
+    // rescale factor is exactly 1 and the accumulator is left as it is.
+    const bool masked = key0 + 31 > a.pos0 + t0;
+    float corr[4];
+    bool grew = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float s0 = sc[0][i] * a.qscale, s1 = sc[1][i] * a.qscale;
-      if (key0 + r16 > qpos[i]) s0 = NEG;
-      if (key0 + 16 + r16 > qpos[i]) s1 = NEG;
-      const float mx = group_max<16>(fmaxf(s0, s1));
-      const float mn = fmaxf(m[i], mx);
-      const float corr = pf_exp2(m[i] - mn);
-      const float p0 = round_bf16(pf_exp2(s0 - mn)), p1 = round_bf16(pf_exp2(s1 - mn));
-      pl[wave][4 * q4 + i][r16] = f32_to_bf16(p0);
-      pl[wave][4 * q4 + i][16 + r16] = f32_to_bf16(p1);
-      l[i] = fmaf(l[i], corr, group_sum<16>(p0 + p1));
-      m[i] = mn;
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) o[nd][i] *= corr;
-    }
-    // V transposed into LDS
-    const int buf = kb & 1;
-#pragma unroll
-    for (int u = 0; u < VL; ++u) {
-      const uint32_t w4[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt[buf][8 * vd8[u] + 2 * e][vkl[u]] = (uint16_t)(w4[e] & 0xFFFFu);
-        vt[buf][8 * vd8[u] + 2 * e + 1][vkl[u]] = (uint16_t)(w4[e] >> 16);
+      float s0 = sc[0][i], s1 = sc[1][i];
+      if (masked) {
+        if (key0 + r16 > qpos[i]) s0 = NEG;
+        if (key0 + 16 + r16 > qpos[i]) s1 = NEG;
       }
+      const float mx = group_max<16>(fmaxf(s0, s1)) * a.qscale;
+      const float mn = fmaxf(m[i], mx);
+      corr[i] = pf_exp2(m[i] - mn);
+      grew |= mn != m[i];
+      const __bf16 b0 = (__bf16)pf_exp2(fmaf(s0, a.qscale, -mn));
+      const __bf16 b1 = (__bf16)pf_exp2(fmaf(s1, a.qscale, -mn));
+      pl[wave][4 * q4 + i][r16] = __builtin_bit_cast(uint16_t, b0);
+      pl[wave][4 * q4 + i][16 + r16] = __builtin_bit_cast(uint16_t, b1);
+      lp[i] = fmaf(lp[i], corr[i], (float)b0 + (float)b1);
+      m[i] = mn;
     }
-    __syncthreads();
-    // O += P V
+    if (__ballot(grew) != 0) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nd = 0; nd < ND; ++nd) o[nd][i] *= corr[i];
+    }
+    // O += P V (the P tile is this wave's own: no barrier)
     const bf8 pa = load_frag(&pl[wave][r16][8 * q4]);
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd)
@@ -507,12 +550,15 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
                                                       o[nd], 0, 0, 0);
   }
 
+  float lsum[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lsum[i] = group_sum<16>(lp[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!active[i]) continue;
     const int rc = wave * 16 + 4 * q4 + i;
     const int qc = rc / G, hc = rc % G;
-    const float inv = 1.0f / l[i];
+    const float inv = 1.0f / lsum[i];
     uint16_t* orow = a.out + ((int64_t)(t0 + qc) * hq + g * G + hc) * D;
 #pragma unroll
     for (int nd = 0; nd < ND; ++nd) orow[16 * nd + r16] = f32_to_bf16(o[nd][i] * inv);
