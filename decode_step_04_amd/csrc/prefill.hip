@@ -460,9 +460,10 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
   };
   chunk(0, pc0, pc1);
   // this thread's chunks of a block: chunk idx = t + 256 u is 16 bytes at d 8 (idx / 32) of key
-  // idx % 32 (keys past `last` clamped); a wave covers 32 keys x 2 d-chunks
-  uint4 kc[CL], vc[CL];
-  auto fetch = [&](int kb) __attribute__((always_inline)) {
+  // idx % 32 (keys past `last` clamped); a wave covers 32 keys x 2 d-chunks.  Two register sets
+  // alternate: a block's chunks are requested two blocks ahead.
+  u32x4 kc0[CL], vc0[CL], kc1[CL], vc1[CL];
+  auto fetch = [&](int kb, u32x4 (&kc)[CL], u32x4 (&vc)[CL]) __attribute__((always_inline)) {
     const int key0 = kb * 32;
     const int64_t ph0 = __builtin_amdgcn_readlane(pc0, kb & 63);
     const int64_t ph1 = __builtin_amdgcn_readlane(pc1, kb & 63);
@@ -472,16 +473,17 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
       const int key = min(key0 + kl, last);
       const int64_t off = (((key - key0) < 16 ? ph0 : ph1) * hkv + g) * head_stride +
                           (int64_t)(key % kPage) * D + 8 * d8;
-      kc[u] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-      vc[u] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+      kc[u] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
+      vc[u] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
     }
   };
-  auto stage = [&](int buf) __attribute__((always_inline)) {
+  auto stage = [&](int buf, const u32x4 (&kc)[CL], const u32x4 (&vc)[CL])
+                   __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CL; ++u) {
       const int idx = threadIdx.x + 256 * u, kl = idx & 31, d8 = idx >> 5;
-      *reinterpret_cast<uint4*>(&kt[buf][kl][8 * d8]) = kc[u];
-      const uint32_t w4[4] = {vc[u].x, vc[u].y, vc[u].z, vc[u].w};
+      *reinterpret_cast<u32x4*>(&kt[buf][kl][8 * d8]) = kc[u];
+      const uint32_t w4[4] = {vc[u][0], vc[u][1], vc[u][2], vc[u][3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         vt[buf][8 * d8 + 2 * e][kl] = (uint16_t)(w4[e] & 0xFFFFu);
@@ -489,17 +491,16 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
       }
     }
   };
-  fetch(0);
-  for (int kb = 0; kb < nblk; ++kb) {
+  auto block = [&](int kb, u32x4 (&kc)[CL], u32x4 (&vc)[CL]) __attribute__((always_inline)) {
     const int key0 = kb * 32;
     const int buf = kb & 1;
     if ((kb & 63) == 0 && kb + 64 < nblk) chunk((kb >> 6) + 1, pn0, pn1);  // wave-uniform
-    if (((kb + 1) & 63) == 0) {  // the next block opens a new chunk
+    if (((kb + 2) & 63) == 0) {  // the block fetched next opens a new chunk
       pc0 = pn0;
       pc1 = pn1;
     }
-    stage(buf);
-    if (kb + 1 < nblk) fetch(kb + 1);
+    stage(buf, kc, vc);
+    if (kb + 2 < nblk) fetch(kb + 2, kc, vc);
     __syncthreads();
     // S = Q K^T for the two 16-key halves
     f32x4 sc[2];
@@ -548,6 +549,13 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
     for (int nd = 0; nd < ND; ++nd)
       o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, load_frag(&vt[buf][16 * nd + r16][8 * q4]),
                                                       o[nd], 0, 0, 0);
+  };
+  fetch(0, kc0, vc0);
+  if (nblk > 1) fetch(1, kc1, vc1);
+  for (int kb = 0; kb < nblk; kb += 2) {
+    block(kb, kc0, vc0);
+    if (kb + 1 >= nblk) break;
+    block(kb + 1, kc1, vc1);
   }
 
   float lsum[4];
