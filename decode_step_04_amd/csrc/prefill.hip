@@ -390,7 +390,9 @@ hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream
 //     masked;
 //   P = 2^(S - m) is rounded to bf16 (the MFMA operand type; the denominator adds the rounded
 //     values, so O / l stays a normalised average) and passed through a per-wave LDS tile to
-//     become the A operand of O += P V, whose B fragments are 16 contiguous bytes of V^T.
+//     become the A operand of O += P V, whose B fragments are 16 contiguous bytes of V^T.  The P
+//     tile holds keys c and 16 + c side by side (one 4-byte write per lane and row) and V^T's key
+//     columns follow the same order, which leaves the sum over keys unchanged.
 // LDS row strides: K 136 bf16 (272 bytes: 8 consecutive key rows at one offset fall in distinct
 // banks), V^T and P 40 bf16 (80 bytes: a wave's transposed writes cover 32 keys of two d rows,
 // in disjoint banks).
@@ -482,12 +484,13 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
 #pragma unroll
     for (int u = 0; u < CL; ++u) {
       const int idx = threadIdx.x + 256 * u, kl = idx & 31, d8 = idx >> 5;
+      const int kcol = kl < 16 ? 2 * kl : 2 * (kl - 16) + 1;  // the P tile's key order
       *reinterpret_cast<u32x4*>(&kt[buf][kl][8 * d8]) = kc[u];
       const uint32_t w4[4] = {vc[u][0], vc[u][1], vc[u][2], vc[u][3]};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vt[buf][8 * d8 + 2 * e][kl] = (uint16_t)(w4[e] & 0xFFFFu);
-        vt[buf][8 * d8 + 2 * e + 1][kl] = (uint16_t)(w4[e] >> 16);
+        vt[buf][8 * d8 + 2 * e][kcol] = (uint16_t)(w4[e] & 0xFFFFu);
+        vt[buf][8 * d8 + 2 * e + 1][kcol] = (uint16_t)(w4[e] >> 16);
       }
     }
   };
@@ -532,8 +535,9 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
       grew |= mn != m[i];
       const __bf16 b0 = (__bf16)pf_exp2(fmaf(s0, a.qscale, -mn));
       const __bf16 b1 = (__bf16)pf_exp2(fmaf(s1, a.qscale, -mn));
-      pl[wave][4 * q4 + i][r16] = __builtin_bit_cast(uint16_t, b0);
-      pl[wave][4 * q4 + i][16 + r16] = __builtin_bit_cast(uint16_t, b1);
+      // keys r16 and 16 + r16 side by side: one 4-byte write (V^T's columns use the same order)
+      *reinterpret_cast<uint32_t*>(&pl[wave][4 * q4 + i][2 * r16]) =
+          (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
       lp[i] = fmaf(lp[i], corr[i], (float)b0 + (float)b1);
       m[i] = mn;
     }
