@@ -391,7 +391,7 @@ def ops_bench():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path does not shard across GPUs)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calib:
