@@ -78,10 +78,15 @@ struct WTraits<W_I4G> {
 __device__ __forceinline__ float u8_at(uint32_t u, int b) { return (float)((u >> (8 * b)) & 0xFFu); }
 
 // acc + sum over the VEC elements of one weight vector times VEC fp32 values (for int8: the
-// codes plus 128, see u8_at; for int4: the stored nibbles, i.e. the codes plus 8).  int4: the
-// masks 0x0F0F0F0F and 0xF0F0F0F0 leave the even elements of a word in its bytes, and the odd
-// ones times 16 -- the caller has divided the odd inputs by 16, which is exact, so each product
-// equals nibble * x exactly -- and one byte conversion per element remains.
+// codes plus 128, see u8_at; for int4: the stored nibbles, i.e. the codes plus 8, times 2^-24).
+// int4: a nibble u masked into a 16-bit half, read as fp16, is the subnormal u * 2^-24, which
+// v_fma_mix_f32 takes directly as one factor of an fp32 fma (exactly: it converts the half to
+// fp32 first, and fp16 subnormals are kept).  A word holds elements e = 0..7 at bits 4e; the
+// masks 0x000F000F and 0x00F000F0, on the word and on the word shifted right by 8, leave the
+// element pairs (0,4), (1,5) times 16, (2,6) and (3,7) times 16 in the two halves -- the caller
+// has divided the odd inputs by 16, which is exact -- so 5 bit operations and 8 fmas per 8
+// elements remain, and the sum is the plain fp32 one scaled by 2^-24 (the caller undoes it).
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 template <int WT>
 __device__ __forceinline__ float dot16(typename WTraits<WT>::Vec w, const float* __restrict__ x,
                                        float acc) {
@@ -103,15 +108,15 @@ __device__ __forceinline__ float dot16(typename WTraits<WT>::Vec w, const float*
     const uint32_t wd[2] = {w.x, w.y};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t ev = wd[j] & 0x0F0F0F0Fu, od = wd[j] & 0xF0F0F0F0u;
-      acc = fmaf(u8_at(ev, 0), x[8 * j + 0], acc);
-      acc = fmaf(u8_at(od, 0), x[8 * j + 1], acc);
-      acc = fmaf(u8_at(ev, 1), x[8 * j + 2], acc);
-      acc = fmaf(u8_at(od, 1), x[8 * j + 3], acc);
-      acc = fmaf(u8_at(ev, 2), x[8 * j + 4], acc);
-      acc = fmaf(u8_at(od, 2), x[8 * j + 5], acc);
-      acc = fmaf(u8_at(ev, 3), x[8 * j + 6], acc);
-      acc = fmaf(u8_at(od, 3), x[8 * j + 7], acc);
+      const uint32_t sh = wd[j] >> 8;
+      const half2v p[4] = {__builtin_bit_cast(half2v, wd[j] & 0x000F000Fu),
+                           __builtin_bit_cast(half2v, wd[j] & 0x00F000F0u),
+                           __builtin_bit_cast(half2v, sh & 0x000F000Fu),
+                           __builtin_bit_cast(half2v, sh & 0x00F000F0u)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf((float)p[i].x, x[8 * j + i], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc = fmaf((float)p[i].y, x[8 * j + 4 + i], acc);
     }
   } else {
     const uint32_t ws[4] = {w.x ^ 0x80808080u, w.y ^ 0x80808080u, w.z ^ 0x80808080u,
@@ -175,7 +180,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   __shared__ float red_bv[4];
   __shared__ int red_bi[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform over the wave: readfirstlane lets the compiler keep it, and with
+  // it every row index and row address, in scalar registers (a load is then a scalar base plus a
+  // per-lane 32-bit offset, with no per-lane address arithmetic)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int split = a.split;
   const int gpw = 4 / split;                       // row groups per work-group round
   const int sub = wave % split;                    // K-slice of this wave
@@ -193,27 +201,39 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     const int64_t row = gg * R + r;
     return row < n ? row : n - 1;  // clamp: loads stay in bounds, results are discarded
   };
+  // per-lane byte offset of each chunk within a row, and its scale group (grouped types)
+  uint32_t loff[MAXCH], lgrp[MAXCH];
+#pragma unroll
+  for (int c = 0; c < MAXCH; ++c) {
+    const int kk = c * CH + lane * VEC;
+    const int kc = kbase + (kk < KW ? kk : 0);
+    loff[c] = (uint32_t)kc * BITS / 8;
+    lgrp[c] = (uint32_t)kc / kQGroup;
+  }
   // the weight vectors of group gg's rows, and for grouped types the scale of each vector's group
   auto load_rows = [&](int64_t gg, Vec (&dst)[NR][MAXCH],
                        float (&sdst)[SR ? NR : 1][SR ? MAXCH : 1]) {
 #pragma unroll
-    for (int c = 0; c < MAXCH; ++c) {
-      const int kk = c * CH + lane * VEC;
-      const int kc = kbase + (kk < KW ? kk : 0);
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = row_of(gg, r);
+      const char* __restrict__ rp = wbase + row * row_bytes;
+      const char* __restrict__ up = rp + n * row_bytes;
+#pragma unroll
+      for (int c = 0; c < MAXCH; ++c) {
+        dst[r][c] = *reinterpret_cast<const Vec*>(rp + loff[c]);
+        if constexpr (EPI == EPI_SWIGLU) dst[R + r][c] = *reinterpret_cast<const Vec*>(up + loff[c]);
+      }
+    }
+    if constexpr (GROUPED) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int64_t row = row_of(gg, r);
-        dst[r][c] = *reinterpret_cast<const Vec*>(wbase + row * row_bytes + (int64_t)kc * BITS / 8);
-        if constexpr (EPI == EPI_SWIGLU)
-          dst[R + r][c] = *reinterpret_cast<const Vec*>(wbase + (row + n) * row_bytes +
-                                                        (int64_t)kc * BITS / 8);
-      }
-      if constexpr (GROUPED) {
+        const float* __restrict__ sp = a.scale + row * ng;
+        const float* __restrict__ su = sp + n * ng;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int64_t row = row_of(gg, r);
-          sdst[r][c] = a.scale[row * ng + kc / kQGroup];
-          if constexpr (EPI == EPI_SWIGLU) sdst[R + r][c] = a.scale[(row + n) * ng + kc / kQGroup];
+        for (int c = 0; c < MAXCH; ++c) {
+          sdst[r][c] = sp[lgrp[c]];
+          if constexpr (EPI == EPI_SWIGLU) sdst[R + r][c] = su[lgrp[c]];
         }
       }
     }
@@ -312,6 +332,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) t += xv[c][e];
       xc[c] = t * -(float)WTraits<WT>::BIAS;
+      if constexpr (WT == W_I4G) xc[c] *= 0x1p-24f;  // the units of dot16's int4 sums
     }
   }
   if constexpr (WT == W_I4G) {  // odd elements meet their nibble times 16 (dot16)
@@ -354,6 +375,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         else
           acc[r] = dot16<WT>(cw[r][c], xv[c], acc[r]);
       }
+    if constexpr (WT == W_I4G) {  // dot16's int4 sums carry a factor 2^-24: exact to undo
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r] *= 0x1p24f;
+    }
     float tot[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) tot[r] = wave_sum(acc[r]);
@@ -501,7 +526,7 @@ constexpr int64_t kStreamBytes = int64_t(64) << 20;
 constexpr int64_t kStreamWgs = 512;
 constexpr bool kStreamPipe = false;
 constexpr int kStreamLoads = 8;
-constexpr int64_t kI4Bytes = int64_t(8) << 20;  // int4 matrices above this take their own plan
+constexpr int64_t kI4Bytes = int64_t(4) << 20;  // int4 matrices above this take their own plan
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   const int vec = wtype == W_F32 ? 4 : wtype == W_BF16 ? 8 : 16;
