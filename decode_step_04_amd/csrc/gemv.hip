@@ -166,7 +166,18 @@ __device__ __forceinline__ void load_vec(const void* x, int64_t k, float (&v)[VE
   }
 }
 
-template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
+// RMSNorm prologue: float4s of the input (and of gamma) each thread loads before the weights are
+// requested (inputs up to 4096 values in one pass); x * gamma is staged in LDS, K floats, so
+// norm inputs are limited to kGemvNormMaxK values.
+constexpr int kNormThreads = 256;
+constexpr int kNormSlots = 4;
+// The NORM template argument: no RMSNorm prologue, the per-wave one (split 4: each wave loads
+// its own quarter of the row) or the shared one (split 2 or 1, where waves would load the same
+// slice).  The two prologues are separate instantiations: compiled into one kernel, the unused
+// one's registers cost the other its occupancy (measured 1-7 % per step).
+constexpr int kNormNone = 0, kNormWave = 1, kNormShared = 2;
+
+template <int WT, int EPI, int NORM, bool XB, int R, int MAXCH, bool PIPE>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int VEC = WTraits<WT>::VEC;
   constexpr int BITS = WTraits<WT>::BITS;
@@ -248,15 +259,36 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
   };
 
-  // 1. input slice (+ gamma), epilogue operands, then the first round's weights
+  // 1. the input (and gamma), the epilogue operands, then the first round's weights.  RMSNorm
+  //    prologue: with split 4 each wave loads its own quarter of the input and gamma; with a
+  //    smaller split several waves would load the same slice, so the work-group's 256 threads
+  //    instead load the input and gamma once between them (thread t the float4s t + 256 i, the
+  //    first kNormSlots of them here), and each value crosses a CU's memory pipeline once per
+  //    work-group instead of once per wave that uses it (kNormShared)
+  constexpr bool shared = NORM == kNormShared;
   float xv[MAXCH][VEC];
-  float gv[NORM ? MAXCH : 1][VEC];
+  float gv[NORM == kNormWave ? MAXCH : 1][VEC];
+  float4 xs[shared ? kNormSlots : 1], gs[shared ? kNormSlots : 1];
+  const float4* __restrict__ x4 = static_cast<const float4*>(a.x);
+  const float4* __restrict__ g4 = reinterpret_cast<const float4*>(a.gamma);
+  if constexpr (shared) {
 #pragma unroll
-  for (int c = 0; c < MAXCH; ++c) {
-    const int kk = c * CH + lane * VEC;
-    const int64_t kc = kbase + (kk < KW ? kk : 0);
-    load_vec<XB, VEC>(a.x, kc, xv[c]);
-    if constexpr (NORM) load_vec<false, VEC>(a.gamma, kc, gv[c]);
+    for (int i = 0; i < kNormSlots; ++i) {
+      const int j = tid + kNormThreads * i;
+      xs[i] = gs[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (4 * j < K) {
+        xs[i] = x4[j];
+        gs[i] = g4[j];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      const int kk = c * CH + lane * VEC;
+      const int64_t kc = kbase + (kk < KW ? kk : 0);
+      load_vec<XB, VEC>(a.x, kc, xv[c]);
+      if constexpr (NORM == kNormWave) load_vec<false, VEC>(a.gamma, kc, gv[c]);
+    }
   }
   const int64_t round0 = blockIdx.x;
   const int64_t g = round0 * gpw + grp;
@@ -266,8 +298,75 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   float wsc[SR ? NR : 1][SR ? MAXCH : 1];
   load_rows(g, wv, wsc);
 
-  // 2. the input while the weights arrive: zero the chunks past the slice, copy the raw input
-  //    (work-group 0), normalise
+  // 2. the input while the weights arrive.  RMSNorm: the sum of squares over the whole row (one
+  //    block reduction; work-group 0 also copies the raw input out) and x * gamma / rms.  Shared
+  //    prologue: x * gamma goes through LDS, from which each wave reads its slice back; inputs
+  //    longer than kNormSlots float4s per thread take further passes, after the weights were
+  //    requested.
+  if constexpr (NORM) {
+    extern __shared__ float4 s_xg[];  // [K / 4], shared prologue only
+    const bool copy_out = a.hidden_copy != nullptr && blockIdx.x == 0;
+    const bool rh = a.round_h != 0;
+    float ss = 0.f;
+    if constexpr (shared) {
+      auto stage = [&](int j, const float4 xx, const float4 gg) {
+        ss = fmaf(xx.x, xx.x, ss);
+        ss = fmaf(xx.y, xx.y, ss);
+        ss = fmaf(xx.z, xx.z, ss);
+        ss = fmaf(xx.w, xx.w, ss);
+        s_xg[j] = make_float4(xx.x * gg.x, xx.y * gg.y, xx.z * gg.z, xx.w * gg.w);
+        if (copy_out) reinterpret_cast<float4*>(a.hidden_copy)[j] = xx;
+      };
+#pragma unroll
+      for (int i = 0; i < kNormSlots; ++i) {
+        const int j = tid + kNormThreads * i;
+        if (4 * j < K) stage(j, xs[i], gs[i]);
+      }
+      for (int j = tid + kNormThreads * kNormSlots; 4 * j < K; j += kNormThreads)
+        stage(j, x4[j], g4[j]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < MAXCH; ++c) {
+        const int kk = c * CH + lane * VEC;
+        if (kk < KW) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) ss = fmaf(xv[c][e], xv[c][e], ss);
+          if (copy_out && grp == 0) {
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4)
+              *reinterpret_cast<float4*>(a.hidden_copy + kbase + kk + e) =
+                  make_float4(xv[c][e], xv[c][e + 1], xv[c][e + 2], xv[c][e + 3]);
+          }
+        }
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red_ss[wave] = ss;
+    __syncthreads();
+    // split 4: the four waves' slices make up the row; shared: the four waves' shares of the
+    // work-group's loads do
+    ss = (red_ss[0] + red_ss[1]) + (red_ss[2] + red_ss[3]);
+    const float rinv = 1.0f / sqrtf(ss / (float)K + a.eps);
+#pragma unroll
+    for (int c = 0; c < MAXCH; ++c) {
+      const int kk = c * CH + lane * VEC;
+      const int kc = kbase + (kk < KW ? kk : 0);
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) {
+        float4 t;
+        if constexpr (shared) {
+          t = s_xg[(kc + e) / 4];
+        } else {
+          t = make_float4(xv[c][e] * gv[c][e], xv[c][e + 1] * gv[c][e + 1],
+                          xv[c][e + 2] * gv[c][e + 2], xv[c][e + 3] * gv[c][e + 3]);
+        }
+        const float v4[4] = {t.x * rinv, t.y * rinv, t.z * rinv, t.w * rinv};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xv[c][e + q] = rh ? round_bf16(v4[q]) : v4[q];
+      }
+    }
+  }
+  // chunks past the slice contribute nothing
 #pragma unroll
   for (int c = 0; c < MAXCH; ++c) {
     const int kk = c * CH + lane * VEC;
@@ -275,42 +374,6 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) xv[c][e] = 0.f;
     }
-  }
-  if constexpr (NORM) {
-    if (a.hidden_copy != nullptr && blockIdx.x == 0 && grp == 0) {
-#pragma unroll
-      for (int c = 0; c < MAXCH; ++c) {
-        const int kk = c * CH + lane * VEC;
-        if (kk < KW) {
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4*>(a.hidden_copy + kbase + kk + e) =
-                make_float4(xv[c][e], xv[c][e + 1], xv[c][e + 2], xv[c][e + 3]);
-        }
-      }
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < MAXCH; ++c)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) ss = fmaf(xv[c][e], xv[c][e], ss);
-    ss = wave_sum(ss);
-    if (split > 1) {
-      if (lane == 0) red_ss[wave] = ss;
-      __syncthreads();
-      float t = 0.f;
-      for (int s2 = 0; s2 < split; ++s2) t += red_ss[grp * split + s2];
-      ss = t;
-    }
-    const float rinv = 1.0f / sqrtf(ss / (float)K + a.eps);
-#pragma unroll
-    for (int c = 0; c < MAXCH; ++c)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        float v = xv[c][e] * gv[c][e] * rinv;
-        if (a.round_h) v = round_bf16(v);
-        xv[c][e] = v;
-      }
   }
 
   // int8 / int4 read unsigned: each sum over the lane's elements exceeds the true one by
@@ -597,26 +660,27 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
   return p;
 }
 
-template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH, bool PIPE>
+template <int WT, int EPI, int NORM, bool XB, int R, int MAXCH, bool PIPE>
 static hipError_t go(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   constexpr int loads = (EPI == EPI_SWIGLU ? 2 : 1) * R * MAXCH;
   constexpr int lmul = WT == W_I4G ? 2 : 1;
   if constexpr (loads > (PIPE ? 8 : 16) * lmul) {
     return hipErrorInvalidConfiguration;  // never planned: over the register budget
   } else {
-    hipLaunchKernelGGL((k_gemv<WT, EPI, NORM, XB, R, MAXCH, PIPE>), dim3(p.wgs), dim3(256), 0, s,
+    const unsigned lds = NORM == kNormShared ? (unsigned)(a.k * 4) : 0u;  // x * gamma
+    hipLaunchKernelGGL((k_gemv<WT, EPI, NORM, XB, R, MAXCH, PIPE>), dim3(p.wgs), dim3(256), lds, s,
                        a);
     return hipGetLastError();
   }
 }
 
-template <int WT, int EPI, bool NORM, bool XB, int R, int MAXCH>
+template <int WT, int EPI, int NORM, bool XB, int R, int MAXCH>
 static hipError_t go_p(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   return p.pipe ? go<WT, EPI, NORM, XB, R, MAXCH, true>(a, p, s)
                 : go<WT, EPI, NORM, XB, R, MAXCH, false>(a, p, s);
 }
 
-template <int WT, int EPI, bool NORM, bool XB, int R>
+template <int WT, int EPI, int NORM, bool XB, int R>
 static hipError_t go_ch(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   switch (p.maxch) {
     case 1: return go_p<WT, EPI, NORM, XB, R, 1>(a, p, s);
@@ -628,7 +692,7 @@ static hipError_t go_ch(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   }
 }
 
-template <int WT, int EPI, bool NORM, bool XB>
+template <int WT, int EPI, int NORM, bool XB>
 static hipError_t go_r(const GemvArgs& a, const GemvPlan& p, hipStream_t s) {
   switch (p.r) {
     case 4: return go_ch<WT, EPI, NORM, XB, 4>(a, p, s);
@@ -648,18 +712,24 @@ hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s);
 template <int WT>
 hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
   const GemvPlan p = plan_gemv(WT, epi, a.n, a.k);
-  if (!p.ok) return hipErrorInvalidValue;
+  if (!p.ok || (norm && a.k > kGemvNormMaxK)) return hipErrorInvalidValue;
   a.split = p.split;
   const bool xb = a.x_bf16 != 0;
   if (norm && xb) return hipErrorInvalidValue;
+  const bool sh = p.split < 4;  // norm: waves would share input slices
   if (epi == EPI_STORE) {
-    if (norm) return go_r<WT, EPI_STORE, true, false>(a, p, s);
-    return xb ? go_r<WT, EPI_STORE, false, true>(a, p, s) : go_r<WT, EPI_STORE, false, false>(a, p, s);
+    if (norm)
+      return sh ? go_r<WT, EPI_STORE, kNormShared, false>(a, p, s)
+                : go_r<WT, EPI_STORE, kNormWave, false>(a, p, s);
+    return xb ? go_r<WT, EPI_STORE, kNormNone, true>(a, p, s)
+              : go_r<WT, EPI_STORE, kNormNone, false>(a, p, s);
   }
   if (epi == EPI_RESID)
-    return xb ? go_r<WT, EPI_RESID, false, true>(a, p, s) : go_r<WT, EPI_RESID, false, false>(a, p, s);
+    return xb ? go_r<WT, EPI_RESID, kNormNone, true>(a, p, s)
+              : go_r<WT, EPI_RESID, kNormNone, false>(a, p, s);
   if (!norm) return hipErrorInvalidValue;
-  return go_r<WT, EPI_SWIGLU, true, false>(a, p, s);
+  return sh ? go_r<WT, EPI_SWIGLU, kNormShared, false>(a, p, s)
+            : go_r<WT, EPI_SWIGLU, kNormWave, false>(a, p, s);
 }
 template hipError_t launch_wt<QD_GEMV_PART>(int, bool, GemvArgs, hipStream_t);
 #else

@@ -13,6 +13,8 @@ namespace qd {
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 
+// The RMSNorm prologue stages x * gamma in LDS: norm GEMVs take inputs of at most this length.
+constexpr int64_t kGemvNormMaxK = 16384;
 hipError_t launch_gemv(int wtype, int epi, bool norm, const GemvArgs& a, hipStream_t s);
 // Number of work-groups (= partial argmax slots) launch_gemv uses for this shape.
 int gemv_partials(int wtype, int epi, int64_t n, int64_t k);

@@ -260,6 +260,9 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
       return fail(why, QDEC_E_UNSUPPORTED,
                   "a projection's input length exceeds what the GEMV keeps in registers "
                   "(8192 fp32, 16384 bf16, 32768 int8 or int4 values)");
+    if (d > kGemvNormMaxK)
+      return fail(why, QDEC_E_UNSUPPORTED, "hidden size %lld above %lld (the fused RMSNorm stages "
+                  "the normalised input in LDS)", (long long)d, (long long)kGemvNormMaxK);
   }
   return QDEC_OK;
 }
