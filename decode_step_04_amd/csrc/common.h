@@ -27,11 +27,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.  Branch-free.
+// Round to nearest even (ties to even, overflow to infinity, NaN stays NaN): one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t r = u + 0x7FFFu + ((u >> 16) & 1u);
-  const bool nan = (u & 0x7FFFFFFFu) > 0x7F800000u;
-  return (uint16_t)((nan ? (u | 0x00400000u) : r) >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 

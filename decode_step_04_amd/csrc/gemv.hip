@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     // split 4: the four waves' slices make up the row; shared: the four waves' shares of the
     // work-group's loads do
     ss = (red_ss[0] + red_ss[1]) + (red_ss[2] + red_ss[3]);
-    const float rinv = 1.0f / sqrtf(ss / (float)K + a.eps);
+    const float rinv = __builtin_amdgcn_rsqf(ss / (float)K + a.eps);  // v_rsq_f32, 1 ulp
 #pragma unroll
     for (int c = 0; c < MAXCH; ++c) {
       const int kk = c * CH + lane * VEC;
