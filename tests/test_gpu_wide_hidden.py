@@ -1,0 +1,101 @@
+"""The decode step with a hidden size that takes more than one pass of the shared RMSNorm prologue.
+
+The norm-fused GEMVs (QKV, gate-up, LM head) load the input row and gamma cooperatively, four
+float4s per thread (4096 values) before the weights are requested and the rest in further
+passes; that sharing is used when a work-group's waves would otherwise load the same K-slice
+(split 2 or 1).  Hidden sizes are multiples of 64, so with bf16 weights every size above 4096
+splits K four ways; with int4 weights (16 values per lane load) hidden 4224 splits it two ways
+and needs a second pass.  Hidden 1152 (split 1, one pass) is the control.
+
+Recipe: 2 layers, 4 Q / 2 KV heads, D 64, FFN 512, vocab 2048 tied; random-init weights
+N(0, 0.02) stored bf16 (seed 5) and quantised on the device to int4 with a scale per 128 values
+(the oracle quantises the same bf16 values), gammas 1 + N(0, 0.1); KV positions 0..46 pre-filled
+with N(0, 1) bf16 values through a random permutation of 4 pages; a step at pos 47, eager and
+graph-replayed.  Bar: the one the Qwen3-0.6B-shape test derives from the arithmetic (hidden
+relative L2 and logits against the oracle, scaled by the distance of the oracle's own plain-fp32
+mode), the greedy id a maximiser of the oracle's logits up to bf16 rounding, graph replay
+bit-identical to the eager step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_step_04_amd import loader, synth
+from decode_step_04_amd import qdec as Q
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+T = 48
+N_PAGES = 4
+
+
+def _shape(hidden):
+    return dict(name=f"wide-hidden-{hidden}", n_layers=2, hidden=hidden, n_q_heads=4,
+                n_kv_heads=2, head_dim=64, ffn=512, vocab=2048, tied=1, qk_norm=1, eps=1e-6,
+                theta=1e6)
+
+
+@pytest.mark.parametrize("hidden", [4224, 1152])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_step_matches_oracle(hidden, act):
+    print(f"wide hidden={hidden} act={act}", flush=True)
+    shape = _shape(hidden)
+    cfg = loader.config_for(shape, path="w4a16", num_pages=N_PAGES, max_context=T, act=act)
+    ctx = Q.qdec_create(cfg, 0)
+    try:
+        w = synth.bf16_model(shape, seed=5, device=DEV)
+        loader.upload_weights(ctx, w, DEV)
+        table = synth.block_table(N_PAGES, N_PAGES, seed=6)
+        Q.qdec_kv_set_block_table(ctx, table)
+        kv = synth.kv_prefill(shape, T - 1, seed=7, device=DEV)
+        loader.prefill_kv(ctx, kv)
+        hw = synth.host_weights(w)
+        for key in ("qkv", "o", "gate_up", "down"):
+            qs = [oracle.quantize_groups(oracle.bf16_bits_to_f64(b).astype(np.float32), 4)
+                  for b in hw[key]]
+            hw[key] = [q for q, _ in qs]
+            hw[key + "_scale"] = [sc for _, sc in qs]
+        hw["lm_head"], hw["lm_scale"] = oracle.quantize_groups(
+            oracle.bf16_bits_to_f64(hw["embed"]).astype(np.float32), 4)
+        om = oracle.Model(dict(shape, act_bf16=int(act == "bf16"), kv_bf16=1, logits_bf16=1),
+                          hw, max_ctx=T)
+        for l, (k, v) in enumerate(kv):
+            om.k_cache[l][: T - 1] = k.float().cpu().numpy()
+            om.v_cache[l][: T - 1] = v.float().cpu().numpy()
+        tok_id = synth.token_id(shape["vocab"], seed=8)
+        tok = torch.tensor([tok_id], dtype=torch.int32, device=DEV)
+        hid = torch.empty(hidden, device=DEV)
+        lg = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=DEV)
+        amax = torch.empty(1, dtype=torch.int32, device=DEV)
+        st = Q.make_step(T - 1, token_id=tok, hidden_out=hid, logits_out=lg, argmax_out=amax)
+        Q.qdec_decode_step(ctx, st)
+        torch.cuda.synchronize()
+        gh = hid.cpu().numpy().astype(np.float64)
+        gl = synth.bf16_to_f32(lg).astype(np.float64)
+        ga = int(amax.item())
+        # graph replay of the same step: the appended K/V row is rewritten with the same values
+        Q.qdec_graph_capture(ctx, st)
+        Q.qdec_graph_replay(ctx, T - 1)
+        torch.cuda.synchronize()
+        assert np.array_equal(hid.cpu().numpy(), gh.astype(np.float32))
+        assert np.array_equal(synth.bf16_to_f32(lg), gl.astype(np.float32))
+        assert int(amax.item()) == ga
+
+        with oracle.fp32_arithmetic():
+            r32 = om.step(T - 1, token=tok_id)
+        rh, rl, _ = om.step(T - 1, token=tok_id)
+        rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
+        d32 = np.linalg.norm(r32[0] - rh) / np.linalg.norm(rh)
+        l32 = np.max(np.abs(r32[1] - rl))
+        print(f"hidden rel-L2 {rel:.3e} (plain fp32 {d32:.3e}); logits max-abs "
+              f"{np.max(np.abs(gl - rl)):.3e} (plain fp32 {l32:.3e})", flush=True)
+        if act == "f32":
+            assert rel <= max(1e-4, 4 * d32)
+            assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max() + 4 * l32)
+        else:
+            assert rel <= max(1.5e-2, 2 * d32)
+            assert np.max(np.abs(gl - rl)) <= max(5e-2, 2 * l32)
+        assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+    finally:
+        Q.qdec_destroy(ctx)
