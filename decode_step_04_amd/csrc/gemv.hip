@@ -456,7 +456,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         for (int s2 = 0; s2 < split; ++s2) t += red_acc[grp * split + s2][r];
         tot[r] = t;
       }
-      __syncthreads();  // red_acc is reused next round
+      // red_acc is reused by the work-group's next round, if it has one (uniform: every wave of
+      // the work-group runs the same rounds)
+      if ((rnd + gridDim.x) * gpw < ngroups) __syncthreads();
     }
     // lane r takes row r of the group
     float vg = tot[0], vu = 0.f;
