@@ -435,8 +435,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       for (int r = 0; r < NR; ++r) {
         if constexpr (GROUPED)
           acc[r] = fmaf(cs[r][c], dot16<WT>(cw[r][c], xv[c], xc[c]), acc[r]);
-        else
-          acc[r] = dot16<WT>(cw[r][c], xv[c], acc[r]);
+        else  // a sum per vector, added to the row's: independent chains for the FMA pipeline
+          acc[r] += dot16<WT>(cw[r][c], xv[c], 0.f);
       }
     if constexpr (WT == W_I4G) {  // dot16's int4 sums carry a factor 2^-24: exact to undo
 #pragma unroll
