@@ -9,19 +9,21 @@
 //
 // k_gemv: a work-group of 4 waves handles 4/SPLIT row groups per round; a row group is R output
 // rows (R gate + R up rows for SwiGLU, [Qwen3-runtime] §2.7) split along K over SPLIT waves.
-//   1. Every wave first requests what does not depend on the weights: its K-slice of the input
-//      vector (and of gamma when the RMSNorm prologue of [Qwen3-runtime] §2.1 is fused) and the
-//      epilogue operands of its rows (residual values, int8 row scales).  Then it issues the
-//      16-byte loads of its rows' K-slice for the first round (lane l reads elements
+//   1. Every wave first requests what does not depend on the weights: the input (its K-slice,
+//      or, with the RMSNorm prologue of [Qwen3-runtime] §2.1 fused, the row and gamma -- per
+//      wave when each wave has its own quarter of K, shared by the work-group otherwise) and
+//      the epilogue operands of its rows (residual values, int8 row scales).  Then it issues the
+//      loads of its rows' K-slice for the first round (lane l reads elements
 //      kslice + c*64*VEC + l*VEC .. +VEC of each row: one wave-wide load is a contiguous 1 KiB of
-//      a row; 8-byte loads, 512 B, for packed int4).  Group-wise int8 / int4 weights
+//      a row; 8-byte loads, 512 B, for packed int4).  Row addresses are scalar: a load is a
+//      scalar row base plus the lane's fixed 32-bit offset.  Group-wise int8 / int4 weights
 //      ([Qwen3-runtime] §13.1: a scale per 128-value group) also load, per lane and load, the
 //      scale of the group its VEC elements lie in; the lane multiplies its partial dot product
-//      by that scale before the row reduction.  Loads complete in order, so the input is ready -- and normalised, with the sum
-//      of squares reduced over the wave (and across the SPLIT waves of a group through LDS) --
-//      while the weights are still in flight.  Every load is unconditional (rows past the end
-//      are clamped to the last row, chunks past the slice to its start, results discarded), so
-//      each compiler-inserted wait covers exactly what its consumer needs.
+//      by that scale before the row reduction.  Loads complete in order, so the input is ready
+//      -- and normalised, with one block reduction of the sum of squares -- while the weights
+//      are still in flight.  Every weight load is unconditional (rows past the end are clamped
+//      to the last row, chunks past the slice to its start, results discarded), so each
+//      compiler-inserted wait covers exactly what its consumer needs.
 //   2. Rounds: FMAs over the registers, a DPP + readlane reduction per row, a reduction over the
 //      SPLIT waves through LDS, and the epilogue on lane r of row r: store (fp32 / bf16), the
 //      residual add (from the prefetched residual value), or silu(gate) * up.  With several
