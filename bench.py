@@ -33,13 +33,16 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--model", choices=["0.6b", "8b"], default="0.6b")
-    p.add_argument("--path", choices=["bf16", "w8a16", "w8a16g", "w4a16"], default="bf16",
-                   help="weights: bf16, int8 per row, int8 or int4 per 128-value group")
+    p.add_argument("--path", choices=["bf16", "w8a16", "w8a16g", "w4a16", "bf16-w8head"],
+                   default="bf16",
+                   help="weights: bf16, int8 per row, int8 or int4 per 128-value group, or bf16 "
+                        "layers with an int8 per-row LM head")
     p.add_argument("--act", choices=["f32", "bf16"], default=None,
                    help="activation precision at op boundaries (default f32)")
     p.add_argument("--ctx", type=int, default=None, help="context T (default 4096 / 8192 for 8b)")
     p.add_argument("--partition", type=int, default=0,
-                   help="split-KV partition length in tokens (multiple of 16; 0 = automatic)")
+                   help="split-KV partition length in tokens (multiple of 64, at most 512; "
+                        "0 = automatic)")
     p.add_argument("--profile-steps", type=int, default=20)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="wall-clock budget of the CPU-oracle baseline (0 disables it)")
@@ -48,6 +51,9 @@ def parse():
                    help="only run the library's copy kernel on 1 GiB (counter calibration)")
     p.add_argument("--prefill-tokens", type=int, default=2048,
                    help="prompt tokens of the timed prefill (0: skip it)")
+    p.add_argument("--no-legs", action="store_true",
+                   help="skip the other decode workloads (0.6B W8A16 and W8A16 LM head, 8B bf16 "
+                        "and W4A16)")
     p.add_argument("--no-ops", action="store_true",
                    help="skip the op-level workloads (attention stress, W8A16 GEMV, copy)")
     p.add_argument("--eager-only", type=int, default=0, metavar="N",
@@ -388,6 +394,362 @@ def ops_bench():
     return out
 
 
+def host_cpu():
+    """Sockets, physical cores and logical CPUs of the host (lscpu's parseable listing, or
+    /proc/cpuinfo), and the CPU model name."""
+    import subprocess
+
+    sockets, cores, logical, model = set(), set(), 0, ""
+    try:
+        out = subprocess.run(["lscpu", "-p=SOCKET,CORE"], capture_output=True, text=True,
+                             timeout=10).stdout
+        for ln in out.splitlines():
+            if ln and not ln.startswith("#"):
+                so, co = ln.split(",")[:2]
+                sockets.add(so)
+                cores.add((so, co))
+                logical += 1
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            phys, core = None, None
+            for ln in f:
+                k, _, v = ln.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and not model:
+                    model = v
+                if not logical:
+                    if k == "physical id":
+                        phys = v
+                    elif k == "core id":
+                        core = v
+                    elif k == "" and phys is not None:
+                        sockets.add(phys)
+                        cores.add((phys, core))
+                        phys = core = None
+    except OSError:
+        pass
+    if not logical:
+        logical = os.cpu_count() or 0
+    return {"sockets": len(sockets) or None, "physical_cores": len(cores) or None,
+            "logical_cpus": logical, "model": model,
+            "cpus_usable_here": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+            else None}
+
+
+def cpu_extra(oracle, om, pos, tok_id, step_bytes, threads):
+    """The oracle on one thread (one step), and per op with all threads and one: the attention
+    stress workload (32 Q / 8 KV heads, D 128) at 8K, 32K and 128K positions and the W8A16 GEMV
+    at 130560x1536 and 151936x1024, on seeded synthetic inputs of those shapes; ms and effective
+    GB/s over the same algorithmic bytes as the GPU figures."""
+    import numpy as np
+
+    out = {}
+    oracle.set_threads(1)
+    t0 = time.perf_counter()
+    om.step(pos, token=tok_id)
+    one = time.perf_counter() - t0
+    out["single_thread"] = {"tokens_per_s": round(1.0 / one, 4), "ms": round(one * 1e3, 1),
+                            "gbps": round(step_bytes / one / 1e9, 3)}
+    rng = np.random.default_rng(21)
+    hq, hkv, d = 32, 8, 128
+    q = rng.standard_normal((hq, d))
+    kv = [rng.standard_normal((131072, hkv, d)).astype(np.float32) for _ in range(2)]
+    ops = []
+    cases = [(f"attention {T // 1024}K, 32 Q / 8 KV heads, D 128",
+              (lambda T=T: oracle.attention(q, kv[0][:T], kv[1][:T])), T * hkv * d * 2 * 2, T)
+             for T in (8192, 32768, 131072)]
+    for n, k in ((130560, 1536), (151936, 1024)):
+        codes = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+        scales = (rng.random(n) * 1e-3).astype(np.float32)
+        x = rng.standard_normal(k)
+        cases.append((f"W8A16 GEMV {n}x{k}",
+                      (lambda codes=codes, x=x, scales=scales: oracle.gemv(codes, x, scales)),
+                      n * k + 4 * n + 2 * k + 2 * n, 0))
+    for name, fn, nbytes, T in cases:
+        row = {"op": name, "bytes": nbytes}
+        for label, nt in (("all_threads", threads), ("one_thread", 1)):
+            oracle.set_threads(nt)
+            if nt == 1 and T > 32768:
+                continue  # about a second per call on one thread: timed on all threads only
+            fn()
+            reps, t0 = 0, time.perf_counter()
+            while reps < 2 or (time.perf_counter() - t0 < 0.6 and reps < 50):
+                fn()
+                reps += 1
+            ms = (time.perf_counter() - t0) * 1e3 / reps
+            row[label] = {"ms": round(ms, 3), "gbps": round(nbytes / ms / 1e6, 3)}
+        ops.append(row)
+    oracle.set_threads(threads)
+    out["ops"] = ops
+    return out
+
+
+def oracle_weights(oracle, hw, path):
+    """The oracle's weight dict for a weight path: the device quantises the same bf16 values the
+    oracle's quantiser takes (per-row int8, int8 or int4 per 128-value group)."""
+    import numpy as np
+
+    hw = dict(hw)
+    quant = {"w8a16": oracle.quantize_rows,
+             "w8a16g": lambda a: oracle.quantize_groups(a, 8),
+             "w4a16": lambda a: oracle.quantize_groups(a, 4),
+             "bf16-w8head": oracle.quantize_rows}.get(path)
+    if quant is None:
+        return hw
+    if path != "bf16-w8head":
+        for key in ("qkv", "o", "gate_up", "down"):
+            qs = [quant(oracle.bf16_bits_to_f64(b).astype(np.float32)) for b in hw[key]]
+            hw[key] = [q for q, _ in qs]
+            hw[key + "_scale"] = [s for _, s in qs]
+    lm_src = hw["lm_head"] if hw.get("lm_head") is not None else hw["embed"]
+    q, s = quant(oracle.bf16_bits_to_f64(lm_src).astype(np.float32))
+    hw["lm_head"], hw["lm_scale"] = q, s
+    return hw
+
+
+def time_class(Q, ctx, kclass, step, reps, stream):
+    """Microseconds per launch of kernel class `kclass` launched alone as the step issues it,
+    `reps` launches cycling through the layers (each reads other weights / KV than the previous
+    one, as in the step), captured in a HIP graph, bracketed by HIP events on that stream."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        Q.qdec_profile_kernel(ctx, Q.K_NAMES.index(kclass), -1, reps, step, stream.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            Q.qdec_profile_kernel(ctx, Q.K_NAMES.index(kclass), -1, reps, step, stream.cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (5 * reps)
+    del g
+    return us
+
+
+def class_table(Q, ctx, cfg, step, shape, T, stream):
+    """Per-class graph-timed periods (time_class) and the class with the largest share of the
+    step.  The embedding kernel, which writes the step descriptor, is the one launch not timed
+    alone."""
+    bm = Q.qdec_bytes_model(cfg, T, 1)
+    L = shape["n_layers"]
+    per_step = {"qkv": L, "attention": L, "merge": L, "o_proj": L, "gate_up": L, "down": L,
+                "lm_head": 1, "argmax": 1}
+    table = {}
+    for k, nper in per_step.items():
+        reps = L * max(1, 112 // L) if nper == L else 32
+        us = time_class(Q, ctx, k, step, reps, stream)
+        b = getattr(bm, k)
+        table[k] = {"launches_per_step": nper, "us_per_launch": round(us, 3),
+                    "ms_per_step": round(us * nper * 1e-3, 4),
+                    "bytes_per_launch": b // nper,
+                    "gbps": round(b / nper / (us * 1e-6) / 1e9, 1) if b else None,
+                    "timing": f"{reps} launches in a HIP graph, HIP events on its stream"}
+    dominant = max(table, key=lambda k: table[k]["ms_per_step"])
+    return table, dominant, bm
+
+
+def decode_leg(args, model, path, T, act=None, steps=None, warmup=None, parity=True,
+               cpu_seconds=0.0, sampled=False, kv_dump=None):
+    """One decode workload: set up the model (random-init weights of the shape, KV positions
+    0..T-2 pre-filled, a random block table), capture the step at pos T-1 into a HIP graph and
+    time its replays; the per-class table; parity of the timed step against the oracle; and,
+    when cpu_seconds > 0, the oracle's own rate on the host CPU."""
+    import numpy as np
+    import torch
+
+    from decode_step_04_amd import loader, synth
+    from decode_step_04_amd import qdec as Q
+
+    steps = steps or args.steps
+    warmup = warmup if warmup is not None else args.warmup
+    shape = synth.QWEN3_0P6B if model == "0.6b" else synth.DENSE_8B
+    dev = "cuda"
+    n_pages = (T + 15) // 16
+    cfg = loader.config_for(shape, path=path, num_pages=n_pages, max_context=T,
+                            partition_size=args.partition, act=act)
+    act_name = "bf16" if cfg.act_dtype == Q.BF16 else "f32"
+    print(f"[bench] decode {shape['name']} {path} act {act_name} ctx {T}: setting up",
+          file=sys.stderr, flush=True)
+    ctx = Q.qdec_create(cfg, 0)
+    out = {}
+    try:
+        part_tokens = Q.qdec_info_get(ctx).partition_tokens
+        w = synth.bf16_model(shape, seed=0, device=dev)
+        loader.upload_weights(ctx, w, dev)
+        table = synth.block_table(n_pages, n_pages, seed=2)
+        Q.qdec_kv_set_block_table(ctx, table)
+        kv = synth.kv_prefill(shape, T - 1, seed=1, device=dev)
+        loader.prefill_kv(ctx, kv)
+        tok_id = synth.token_id(shape["vocab"], seed=3)
+        tok = torch.tensor([tok_id], dtype=torch.int32, device=dev)
+        logits = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=dev)
+        hidden = torch.empty(shape["hidden"], dtype=torch.float32, device=dev)
+        amax = torch.empty(1, dtype=torch.int32, device=dev)
+        pos = T - 1
+        step = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits,
+                           argmax_out=amax)
+        torch.cuda.synchronize()
+        if args.eager_only:
+            for _ in range(args.eager_only):
+                Q.qdec_decode_step(ctx, step)
+            torch.cuda.synchronize()
+            return {"eager_steps": args.eager_only, "argmax": int(amax.item())}
+
+        # eager warm-up, then capture the step into a graph
+        for _ in range(3):
+            Q.qdec_decode_step(ctx, step)
+        torch.cuda.synchronize()
+        Q.qdec_graph_capture(ctx, step)
+        for _ in range(warmup):
+            Q.qdec_graph_replay(ctx, pos)
+        # timed region: graph replays
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            Q.qdec_graph_replay(ctx, pos)
+        torch.cuda.synchronize()
+        graph_s = (time.perf_counter() - t0) / steps
+        # eager steps for comparison
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            Q.qdec_decode_step(ctx, step)
+        torch.cuda.synchronize()
+        eager_s = (time.perf_counter() - t0) / steps
+
+        ks = torch.cuda.Stream()
+        kernels, dominant, bm = class_table(Q, ctx, cfg, step, shape, T, ks)
+        dk = kernels[dominant]
+        achieved = dk["bytes_per_launch"] / (dk["us_per_launch"] * 1e-6) / 1e9
+        workload = f"{shape['name']}-{path}-act{act_name}-ctx{T}"
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                    "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                    "traffic": load_traffic(dominant, workload),
+                    "bytes_per_launch": dk["bytes_per_launch"],
+                    "avg_launch_us": dk["us_per_launch"], "timing": dk["timing"]}
+        out.update({
+            "workload": f"{shape['name']} batch-1 decode step, ctx {T}, {path} weights, bf16 KV, "
+                        f"{act_name} activations, graph replay",
+            "model": shape["name"], "weights": path, "activations": act_name, "context": T,
+            "partition_tokens": part_tokens,
+            "tokens_per_s": round(1.0 / graph_s, 2), "ms_per_step": round(graph_s * 1e3, 5),
+            "steps": steps, "warmup": warmup, "eager_ms_per_step": round(eager_s * 1e3, 5),
+            "bytes_per_step": bm.total, "hbm_gbps": round(bm.total / graph_s / 1e9, 1),
+            "hbm_frac": round(bm.total / graph_s / 1e9 / PEAK_HBM_GBPS, 4),
+            "roofline": roofline, "kernels": kernels,
+            "kernels_sum_ms": round(sum(v["ms_per_step"] for v in kernels.values()), 4),
+        })
+
+        if parity or cpu_seconds > 0:
+            import oracle
+
+            Q.qdec_graph_replay(ctx, pos)
+            torch.cuda.synchronize()
+            g_hidden = hidden.cpu().numpy().astype(np.float64)
+            g_logits = synth.bf16_to_f32(logits).astype(np.float64)
+            g_arg = int(amax.item())
+            print(f"[bench] decode {shape['name']} {path}: oracle", file=sys.stderr, flush=True)
+            hw = oracle_weights(oracle, synth.host_weights(w), path)
+            om = oracle.Model(dict(shape, act_bf16=int(act_name == "bf16"), kv_bf16=1,
+                                   logits_bf16=1), hw, max_ctx=T)
+            for l, (k, v) in enumerate(kv):
+                om.k_cache[l][: T - 1] = k.float().cpu().numpy()
+                om.v_cache[l][: T - 1] = v.float().cpu().numpy()
+            del kv
+            with oracle.fp32_arithmetic():  # the plain-fp32 oracle's distance bounds the drift
+                ref32 = om.step(pos, token=tok_id)
+            t0 = time.perf_counter()
+            oh, ol, oa = om.step(pos, token=tok_id)
+            first = time.perf_counter() - t0
+            rel = float(np.linalg.norm(g_hidden - oh) / np.linalg.norm(oh))
+            lmax = float(np.max(np.abs(g_logits - ol)))
+            d32 = float(np.linalg.norm(ref32[0] - oh) / np.linalg.norm(oh))
+            l32 = float(np.max(np.abs(ref32[1] - ol)))
+            par = {"hidden_rel_l2": rel, "logits_max_abs": lmax, "argmax_gpu": g_arg,
+                   "argmax_oracle": oa,
+                   "argmax_valid": bool(ol[g_arg] >= ol.max() - 2 * 2.0**-8 * abs(ol.max())),
+                   "fp32_oracle_hidden_rel_l2": d32, "fp32_oracle_logits_max_abs": l32,
+                   "oracle_step_ms": round(first * 1e3, 1)}
+            fixed = rel <= 1.5e-2 and lmax <= 5e-2
+            if act_name == "f32":
+                par["bar"] = ("hidden rel-L2 <= 1.5e-2 and logits max-abs <= 5e-2 (fixed), and "
+                              "hidden rel-L2 <= max(1e-4, 4 d32), each logit within one bf16 "
+                              "spacing + 4 l32 (d32/l32: the plain-fp32 oracle's distance)")
+                par["ok"] = fixed and rel <= max(1e-4, 4 * d32) and bool(np.all(
+                    np.abs(g_logits - ol) <= 2.0**-7 * np.abs(ol) + 1e-5 * np.abs(ol).max()
+                    + 4 * l32)) and par["argmax_valid"]
+            else:
+                par["bar"] = "hidden rel-L2 <= 1.5e-2 and logits max-abs <= 5e-2 (fixed)"
+                par["ok"] = fixed and par["argmax_valid"]
+            out["parity"] = par
+            if cpu_seconds > 0:
+                n, spent = 1, first
+                while spent < cpu_seconds and n < 5000:
+                    t0 = time.perf_counter()
+                    om.step(pos, token=tok_id)
+                    spent += time.perf_counter() - t0
+                    n += 1
+                threads = oracle.get_threads()
+                cpu = {"value": round(n / spent, 4), "unit": "tokens/s", "cores": threads,
+                       "kind": "oracle", "threads": threads, "host": host_cpu(),
+                       "sample": f"{n} full decode steps of the same workload (same weights, KV "
+                                 f"and position) on {threads} OpenMP threads, {spent:.1f} s"}
+                # the other contexts of the shape: 3 steps each, over the first T' positions
+                ctxs = []
+                for Tc in (512, 2048):
+                    if Tc < T:
+                        t0 = time.perf_counter()
+                        for _ in range(3):
+                            om.step(Tc - 1, token=tok_id, want_logits=True)
+                        dt = (time.perf_counter() - t0) / 3
+                        bmc = Q.qdec_bytes_model(cfg, Tc, 1)
+                        ctxs.append({"context": Tc, "ms": round(dt * 1e3, 1),
+                                     "tokens_per_s": round(1 / dt, 3),
+                                     "gbps": round(bmc.total / dt / 1e9, 3)})
+                cpu["contexts"] = ctxs
+                cpu.update(cpu_extra(oracle, om, pos, tok_id, bm.total, threads))
+                out["cpu_baseline"] = cpu
+            del om, hw
+
+        if sampled:
+            # the same step drawing its token by temperature 0.7 / top-p 0.9 sampling
+            sstep = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits,
+                                argmax_out=amax, temperature=0.7, top_p=0.9, seed=42)
+            Q.qdec_graph_capture(ctx, sstep)
+            for _ in range(warmup):
+                Q.qdec_graph_replay(ctx, pos)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                Q.qdec_graph_replay(ctx, pos)
+            torch.cuda.synchronize()
+            sampled_s = (time.perf_counter() - t0) / steps
+            out["sampled_step"] = {"ms_per_step": round(sampled_s * 1e3, 5), "temperature": 0.7,
+                                   "top_p": 0.9,
+                                   "sample_kernels_us": round(time_class(Q, ctx, "argmax", sstep,
+                                                                         32, ks), 3),
+                                   "greedy_argmax_us": out["kernels"]["argmax"]["us_per_launch"]}
+        del w
+    finally:
+        Q.qdec_destroy(ctx)
+        torch.cuda.empty_cache()
+    return out
+
+
+# the workloads besides the headline one, each timed like it (bytes, ms per step, roofline of its
+# dominant kernel, parity against the oracle): (model, weights, context)
+EXTRA_LEGS = (("0.6b", "w8a16", 4096), ("0.6b", "bf16-w8head", 4096), ("8b", "bf16", 8192),
+              ("8b", "w4a16", 8192))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -398,235 +760,45 @@ def main():
         copy_calibration()
         return
 
-    import numpy as np
     import torch
 
-    from decode_step_04_amd import loader, synth
-    from decode_step_04_amd import qdec as Q
+    T = args.ctx or (4096 if args.model == "0.6b" else 8192)
+    head = decode_leg(args, args.model, args.path, T, act=args.act, parity=not args.no_parity,
+                      cpu_seconds=args.cpu_seconds, sampled=True)
+    if args.eager_only:
+        print(json.dumps(head))
+        return
+    legs = []
+    if not args.no_legs:
+        for model, path, Tl in EXTRA_LEGS:
+            if (model, path, Tl) == (args.model, args.path, T):
+                continue
+            legs.append(decode_leg(args, model, path, Tl, steps=min(args.steps, 50),
+                                   warmup=min(args.warmup, 5), parity=not args.no_parity))
+    torch.cuda.empty_cache()
+    from decode_step_04_amd import synth
 
     shape = synth.QWEN3_0P6B if args.model == "0.6b" else synth.DENSE_8B
-    T = args.ctx or (4096 if args.model == "0.6b" else 8192)
-    dev = "cuda"
-    n_pages = (T + 15) // 16
-    cfg = loader.config_for(shape, path=args.path, num_pages=n_pages, max_context=T,
-                            partition_size=args.partition, act=args.act)
-    act_name = "bf16" if cfg.act_dtype == Q.BF16 else "f32"
-    ctx = Q.qdec_create(cfg, 0)
-    part_tokens = Q.qdec_info_get(ctx).partition_tokens
-    w = synth.bf16_model(shape, seed=0, device=dev)
-    loader.upload_weights(ctx, w, dev)
-    table = synth.block_table(n_pages, n_pages, seed=2)
-    Q.qdec_kv_set_block_table(ctx, table)
-    kv = synth.kv_prefill(shape, T - 1, seed=1, device=dev)
-    loader.prefill_kv(ctx, kv)
-    tok_id = synth.token_id(shape["vocab"], seed=3)
-    tok = torch.tensor([tok_id], dtype=torch.int32, device=dev)
-    logits = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=dev)
-    hidden = torch.empty(shape["hidden"], dtype=torch.float32, device=dev)
-    amax = torch.empty(1, dtype=torch.int32, device=dev)
-    pos = T - 1
-    step = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax)
-    torch.cuda.synchronize()
-    if args.eager_only:
-        for _ in range(args.eager_only):
-            Q.qdec_decode_step(ctx, step)
-        torch.cuda.synchronize()
-        Q.qdec_destroy(ctx)
-        print(json.dumps({"eager_steps": args.eager_only, "argmax": int(amax.item())}))
-        return
-
-    # eager warm-up, then capture the step into a graph
-    for _ in range(3):
-        Q.qdec_decode_step(ctx, step)
-    torch.cuda.synchronize()
-    Q.qdec_graph_capture(ctx, step)
-    for _ in range(args.warmup):
-        Q.qdec_graph_replay(ctx, pos)
-    torch.cuda.synchronize()
-
-    # timed region: graph replays
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        Q.qdec_graph_replay(ctx, pos)
-    torch.cuda.synchronize()
-    graph_s = (time.perf_counter() - t0) / args.steps
-
-    # eager steps for comparison
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        Q.qdec_decode_step(ctx, step)
-    torch.cuda.synchronize()
-    eager_s = (time.perf_counter() - t0) / args.steps
-
-    # per-kernel durations with HIP events on the step's stream
-    Q.qdec_profile_enable(ctx, 1)
-    for _ in range(args.profile_steps):
-        Q.qdec_decode_step(ctx, step)
-        prof = Q.qdec_profile_collect(ctx)
-    Q.qdec_profile_enable(ctx, 0)
-    bm = Q.qdec_bytes_model(cfg, T, 1)
-    per_step_ms = {k: v[0] / args.profile_steps for k, v in prof.items()}
-    launches = {k: v[1] // args.profile_steps for k, v in prof.items()}
-    kernels = {}
-    for k in Q.K_NAMES:
-        if launches[k] == 0:
-            continue
-        b = getattr(bm, k)
-        avg_us = per_step_ms[k] * 1e3 / launches[k]
-        kernels[k] = {"launches_per_step": launches[k], "avg_us": round(avg_us, 3),
-                      "ms_per_step": round(per_step_ms[k], 4),
-                      "bytes_per_launch": b // launches[k],
-                      "gbps": round(b / launches[k] / (avg_us * 1e-6) / 1e9, 1) if b else None}
-    # the dominant kernel (largest share of the event-timed step) is then timed alone: launches of
-    # it exactly as the step issues them, cycling through the layers so that each launch reads
-    # other weights / KV than the previous one (as in the step), captured in a graph and bracketed
-    # by HIP events on the stream it runs on; the per-launch figure matches a rocprofv3 trace
-    dominant = max((k for k in kernels if k != "embed"), key=lambda k: kernels[k]["ms_per_step"])
-    dk = kernels[dominant]
-    kreps = shape["n_layers"] * max(1, 112 // shape["n_layers"])
-    ks = torch.cuda.Stream()
-    kg = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(ks):
-        Q.qdec_profile_kernel(ctx, Q.K_NAMES.index(dominant), -1, kreps, step, ks.cuda_stream)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(kg, stream=ks):
-            Q.qdec_profile_kernel(ctx, Q.K_NAMES.index(dominant), -1, kreps, step, ks.cuda_stream)
-        torch.cuda.synchronize()
-        kg.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(ks)
-        for _ in range(5):
-            kg.replay()
-        e1.record(ks)
-    torch.cuda.synchronize()
-    launch_us = e0.elapsed_time(e1) * 1e3 / (5 * kreps)
-    del kg
-    achieved = dk["bytes_per_launch"] / (launch_us * 1e-6) / 1e9
-    workload = f"{shape['name']}-{args.path}-act{act_name}-ctx{T}"
-    traffic = load_traffic(dominant, workload)
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                "traffic": traffic, "bytes_per_launch": dk["bytes_per_launch"],
-                "avg_launch_us": round(launch_us, 3),
-                "timing": f"{kreps} launches cycling through the layers in a HIP graph, "
-                          "HIP events on its stream"}
-
-    # parity of the timed step against the oracle, and the oracle's own rate
-    parity = None
-    cpu = None
-    if not args.no_parity or args.cpu_seconds > 0:
-        import oracle
-
-        Q.qdec_graph_replay(ctx, pos)
-        torch.cuda.synchronize()
-        g_hidden = hidden.cpu().numpy().astype(np.float64)
-        g_logits = synth.bf16_to_f32(logits).astype(np.float64)
-        g_arg = int(amax.item())
-        hw = synth.host_weights(w)
-        if args.path != "bf16":
-            quant = {"w8a16": oracle.quantize_rows,
-                     "w8a16g": lambda a: oracle.quantize_groups(a, 8),
-                     "w4a16": lambda a: oracle.quantize_groups(a, 4)}[args.path]
-            for key in ("qkv", "o", "gate_up", "down"):
-                qs = [quant(oracle.bf16_bits_to_f64(b).astype(np.float32)) for b in hw[key]]
-                hw[key] = [q for q, _ in qs]
-                hw[key + "_scale"] = [s for _, s in qs]
-            lm_src = hw["lm_head"] if hw.get("lm_head") is not None else hw["embed"]
-            q, s = quant(oracle.bf16_bits_to_f64(lm_src).astype(np.float32))
-            hw["lm_head"], hw["lm_scale"] = q, s
-        om = oracle.Model(dict(shape, act_bf16=int(cfg.act_dtype == Q.BF16), kv_bf16=1,
-                               logits_bf16=1), hw, max_ctx=T)
-        for l, (k, v) in enumerate(kv):
-            om.k_cache[l][: T - 1] = k.float().cpu().numpy()
-            om.v_cache[l][: T - 1] = v.float().cpu().numpy()
-        del kv
-        with oracle.fp32_arithmetic():  # the plain-fp32 oracle's distance bounds the drift
-            ref32 = om.step(pos, token=tok_id)
-        t0 = time.perf_counter()
-        oh, ol, oa = om.step(pos, token=tok_id)
-        first = time.perf_counter() - t0
-        rel = float(np.linalg.norm(g_hidden - oh) / np.linalg.norm(oh))
-        parity = {"hidden_rel_l2": rel, "logits_max_abs": float(np.max(np.abs(g_logits - ol))),
-                  "argmax_gpu": g_arg, "argmax_oracle": oa,
-                  "argmax_valid": bool(ol[g_arg] >= ol.max() - 2 * 2.0**-8 * abs(ol.max())),
-                  "bar": "d32/l32 = the plain-fp32 oracle's distance; fp32 activations: hidden "
-                         "rel-L2 <= max(1e-4, 4 d32), each logit within one bf16 spacing + 4 l32; "
-                         "bf16 activations: rel-L2 <= max(1.5e-2, 2 d32), logits max-abs <= "
-                         "max(5e-2, 2 l32)"}
-        d32 = float(np.linalg.norm(ref32[0] - oh) / np.linalg.norm(oh))
-        l32 = float(np.max(np.abs(ref32[1] - ol)))
-        parity["fp32_oracle_hidden_rel_l2"] = d32
-        parity["fp32_oracle_logits_max_abs"] = l32
-        if act_name == "f32":
-            parity["ok"] = rel <= max(1e-4, 4 * d32) and bool(np.all(
-                np.abs(g_logits - ol) <= 2.0**-7 * np.abs(ol) + 1e-5 * np.abs(ol).max() + 4 * l32))
-        else:
-            parity["ok"] = rel <= max(1.5e-2, 2 * d32) and \
-                parity["logits_max_abs"] <= max(5e-2, 2 * l32)
-        if args.cpu_seconds > 0:
-            n, spent = 1, first
-            while spent < args.cpu_seconds and n < 5000:
-                t0 = time.perf_counter()
-                om.step(pos, token=tok_id)
-                spent += time.perf_counter() - t0
-                n += 1
-            threads = oracle.get_threads()
-            cpu = {"value": round(n / spent, 4), "unit": "tokens/s", "cores": threads,
-                   "kind": "oracle",
-                   "sample": f"{n} full decode steps of the same workload (same weights, KV and "
-                             f"position) on {threads} OpenMP threads, {spent:.1f} s"}
-            cpu.update(cpu_extra(oracle, om, pos, tok_id, bm.total, threads))
-
-    # the same step drawing the token by temperature 0.7 / top-p 0.9 sampling instead of the argmax
-    sstep = Q.make_step(pos, token_id=tok, hidden_out=hidden, logits_out=logits, argmax_out=amax,
-                        temperature=0.7, top_p=0.9, seed=42)
-    Q.qdec_graph_capture(ctx, sstep)
-    for _ in range(args.warmup):
-        Q.qdec_graph_replay(ctx, pos)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        Q.qdec_graph_replay(ctx, pos)
-    torch.cuda.synchronize()
-    sampled_s = (time.perf_counter() - t0) / args.steps
-    Q.qdec_profile_enable(ctx, 1)
-    for _ in range(args.profile_steps):
-        Q.qdec_decode_step(ctx, sstep)
-        sprof = Q.qdec_profile_collect(ctx)
-    Q.qdec_profile_enable(ctx, 0)
-    sampled = {"ms_per_step": round(sampled_s * 1e3, 5), "temperature": 0.7, "top_p": 0.9,
-               "sample_kernel_us": round(sprof["argmax"][0] * 1e3 / args.profile_steps, 3),
-               "lm_head_us": round(sprof["lm_head"][0] * 1e3 / args.profile_steps, 3)}
-
-    Q.qdec_destroy(ctx)
-    del w
-    torch.cuda.empty_cache()
     prefill = prefill_bench(shape, args.prefill_tokens) if args.prefill_tokens > 0 else None
     ops = None if args.no_ops else ops_bench()
-    tok_s = 1.0 / graph_s
     out = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(graph_s * 1e3, 5),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{shape['name']} batch-1 decode step, ctx {T}, {args.path} "
-                               "weights, bf16 KV, graph replay",
-                   "context": T, "batch": 1, "weights": args.path, "kv_cache": "bf16",
-                   "activations": act_name,
-                   "page_size": 16, "partition_tokens": part_tokens,
-                   "block_table": "random permutation",
-                   "parallelism": "single GPU"},
-        "hbm_gbps": round(bm.total / graph_s / 1e9, 1),
-        "hbm_frac": round(bm.total / graph_s / 1e9 / PEAK_HBM_GBPS, 4),
-        "bytes_per_step": bm.total,
-        "eager_ms_per_step": round(eager_s * 1e3, 5),
-        "roofline": roofline,
-        "kernels": kernels,
-        "parity": parity,
-        "cpu_baseline": cpu,
-        "sampled_step": sampled,
+        "config": {"workload": head["workload"], "context": T, "batch": 1,
+                   "weights": args.path, "kv_cache": "bf16", "activations": head["activations"],
+                   "page_size": 16, "partition_tokens": head["partition_tokens"],
+                   "block_table": "random permutation", "parallelism": "single GPU"},
+        "hbm_gbps": head["hbm_gbps"], "hbm_frac": head["hbm_frac"],
+        "bytes_per_step": head["bytes_per_step"],
+        "eager_ms_per_step": head["eager_ms_per_step"],
+        "roofline": head["roofline"],
+        "kernels": head["kernels"], "kernels_sum_ms": head["kernels_sum_ms"],
+        "parity": head.get("parity"),
+        "cpu_baseline": head.get("cpu_baseline"),
+        "sampled_step": head.get("sampled_step"),
+        "legs": legs,
         "prefill": prefill,
         "ops": ops,
     }

@@ -11,13 +11,17 @@ from . import qdec as Q
 
 # quantised paths: weight storage type of the projections and the LM head
 QUANT_PATHS = {"w8a16": Q.I8_ROW, "w8a16g": Q.I8_G128, "w4a16": Q.I4_G128}
+# bf16 layers with an int8 per-row LM head only: the shipped mode of the Qwen3 runtime page
+# (its W8A16 section quantises the LM head alone)
+LM_ONLY_PATHS = {"bf16-w8head": Q.I8_ROW}
 
 
 def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
                partition_size: int = 0, act: str = None, max_prefill: int = 0) -> Q.qdec_config:
     """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights, embedding, logits and KV), 'w8a16'
     (int8 per-row projections and LM head, bf16 embedding, logits and KV), 'w8a16g' (int8 with a
-    scale per 128-value group) or 'w4a16' (int4 with a scale per 128-value group).  act: 'f32' or 'bf16',
+    scale per 128-value group), 'w4a16' (int4 with a scale per 128-value group) or 'bf16-w8head'
+    (bf16 projections, int8 per-row LM head, bf16 embedding, logits and KV).  act: 'f32' or 'bf16',
     the precision of activations crossing op boundaries; default 'f32' for every path (the weight
     and cache formats are storage formats; activations are a few KiB per step, so their precision
     costs no bandwidth), 'bf16' rounds them to 16 bits at every op boundary."""
@@ -30,6 +34,10 @@ def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
     elif path in QUANT_PATHS:
         proj = lm = QUANT_PATHS[path]
         io = kv = Q.BF16
+        act = act or "f32"
+    elif path in LM_ONLY_PATHS:
+        proj = io = kv = Q.BF16
+        lm = LM_ONLY_PATHS[path]
         act = act or "f32"
     else:
         raise ValueError(path)

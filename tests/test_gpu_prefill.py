@@ -62,7 +62,7 @@ def test_gemm_resid_adds_into_the_stream(m, n, k):
     r = r0.clone()
     Q.qdec_op_gemm(a, w, None, Q.F32, r, Q.GEMM_RESID, m, n, k)
     torch.cuda.synchronize()
-    rows = np.unique([0, m // 2, m - 1])
+    rows = np.arange(m)                          # every row, every column
     exact = _rows_exact(_bits(a), _bits(w), rows) + r0.cpu().numpy()[rows].astype(np.float64)
     assert np.max(np.abs(r.cpu().numpy()[rows] - exact)) <= 1e-4
 
@@ -76,7 +76,7 @@ def test_gemm_swiglu_epilogue(m, f, k):
     y = torch.empty((m, f), device=DEV, dtype=torch.bfloat16)
     Q.qdec_op_gemm(a, w, y, Q.BF16, None, Q.GEMM_SWIGLU, m, f, k)
     torch.cuda.synchronize()
-    rows = np.unique([0, m // 3, m - 1])
+    rows = np.arange(m)                          # every row, every column
     gu = _rows_exact(_bits(a), _bits(w), rows)
     exact = oracle.silu(gu[:, :f]) * gu[:, f:]
     assert _bf16_ulp_ok(synth.bf16_to_f32(y)[rows], exact, extra=1e-5).all()
@@ -144,6 +144,8 @@ def test_prefill_attention_matches_oracle(d, hq, hkv, pos0, P):
 from decode_step_04_amd import loader  # noqa: E402
 
 SHAPE = synth.QWEN3_0P6B
+# the same widths with 2 layers: the first two layers of the 28-layer model (same draw order)
+SHAPE2 = dict(SHAPE, name="qwen3-0.6b-shape-2-layers", n_layers=2)
 
 
 class PrefillSetup:
@@ -151,22 +153,24 @@ class PrefillSetup:
     of max_context positions behind a random block table, and the oracle model on the same
     weights."""
 
-    def __init__(self, max_context=1024, max_prefill=256):
-        print(f"prefill setup max_context={max_context} max_prefill={max_prefill}", flush=True)
+    def __init__(self, shape=SHAPE, max_context=1024, max_prefill=256, oracle_model=True):
+        print(f"prefill setup {shape['name']} max_context={max_context} "
+              f"max_prefill={max_prefill}", flush=True)
+        self.shape = shape
         n_pages = max_context // 16
-        self.cfg = loader.config_for(SHAPE, path="bf16", num_pages=n_pages, max_context=max_context,
+        self.cfg = loader.config_for(shape, path="bf16", num_pages=n_pages, max_context=max_context,
                                      act="bf16", max_prefill=max_prefill)
         self.ctx = Q.qdec_create(self.cfg, 0)
-        w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        w = synth.bf16_model(shape, seed=0, device=DEV)
         loader.upload_weights(self.ctx, w, DEV)
         self.table = synth.block_table(n_pages, n_pages, seed=2)
         Q.qdec_kv_set_block_table(self.ctx, self.table)
-        self.hw = synth.host_weights(w)
+        self.hw = synth.host_weights(w) if oracle_model else None
         del w
-        self.om = oracle.Model(dict(SHAPE, act_bf16=1, kv_bf16=1, logits_bf16=1), self.hw,
-                               max_ctx=max_context)
-        self.hidden = torch.empty(SHAPE["hidden"], device=DEV)
-        self.logits = torch.empty(SHAPE["vocab"], dtype=torch.bfloat16, device=DEV)
+        self.om = oracle.Model(dict(shape, act_bf16=1, kv_bf16=1, logits_bf16=1), self.hw,
+                               max_ctx=max_context) if oracle_model else None
+        self.hidden = torch.empty(shape["hidden"], device=DEV)
+        self.logits = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=DEV)
         self.amax = torch.empty(1, dtype=torch.int32, device=DEV)
 
     def prefill(self, tokens, pos0):
@@ -176,21 +180,49 @@ class PrefillSetup:
         return (self.hidden.cpu().numpy().astype(np.float64),
                 synth.bf16_to_f32(self.logits).astype(np.float64), int(self.amax.item()))
 
-    def oracle_run(self, tokens, pos0):
-        """(plain-fp32 oracle, fp64 oracle) results of the last token after decoding `tokens` one
-        by one from pos0; the fp64 pass runs last so the oracle's cache holds its rows."""
-        with oracle.fp32_arithmetic():
-            for i, tok in enumerate(tokens):
-                r32 = self.om.step(pos0 + i, token=int(tok))
+    def oracle_run(self, tokens, pos0, fp32_pass=True):
+        """(plain-fp32 oracle or None, fp64 oracle) results of the last token after decoding
+        `tokens` one by one from pos0 (logits for the last token only); the fp64 pass runs last
+        so the oracle's cache holds its rows."""
+        r32 = None
+        last = len(tokens) - 1
+        if fp32_pass:
+            with oracle.fp32_arithmetic():
+                for i, tok in enumerate(tokens):
+                    r32 = self.om.step(pos0 + i, token=int(tok), want_logits=i == last)
         for i, tok in enumerate(tokens):
-            r64 = self.om.step(pos0 + i, token=int(tok))
+            r64 = self.om.step(pos0 + i, token=int(tok), want_logits=i == last)
         return r32, r64
+
+    def kv_rows(self, layer, n):
+        hkv, d = self.shape["n_kv_heads"], self.shape["head_dim"]
+        k = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
+        v = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
+        Q.qdec_kv_read(self.ctx, layer, 0, n, k, v)
+        torch.cuda.synchronize()
+        return k.float().cpu().numpy(), v.float().cpu().numpy()
 
     def close(self):
         Q.qdec_destroy(self.ctx)
 
 
-def _check_bf16_policy(got, ref, ref32, what):
+def _fixed_bar(got, ref, what):
+    """The fixed bar of the bf16 path: hidden relative L2 <= 1.5e-2, logits max-abs <= 5e-2, and
+    the greedy id a maximiser of the oracle's logits up to bf16 rounding."""
+    gh, gl, ga = got
+    rh, rl, ra = ref
+    rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
+    lmax = np.max(np.abs(gl - rl))
+    print(f"{what}: hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra}",
+          flush=True)
+    assert rel <= 1.5e-2
+    assert lmax <= 5e-2
+    assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+
+
+def _tracks_plain_fp32(got, ref, ref32, what):
+    """28 layers of bf16 activations: the GPU lands no further from the fp64 oracle than twice a
+    plain fp32 implementation of the method does (evidence, not the fixed bar)."""
     gh, gl, ga = got
     rh, rl, ra = ref
     rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
@@ -199,58 +231,114 @@ def _check_bf16_policy(got, ref, ref32, what):
     l32 = np.max(np.abs(ref32[1] - rl))
     print(f"{what}: hidden rel-L2 {rel:.3e} logits max-abs {lmax:.3e} argmax {ga} vs {ra} "
           f"(plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
-    assert rel <= max(1.5e-2, 2 * d32)
-    assert lmax <= max(5e-2, 2 * l32)
+    assert rel <= 2 * d32
+    assert lmax <= 2 * l32
     assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max()) - 2 * l32
 
 
-def _check_kv(s, layer, n):
-    """The cache rows the prefill wrote against the oracle's (both bf16 values)."""
-    hkv, d = SHAPE["n_kv_heads"], SHAPE["head_dim"]
-    k = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
-    v = torch.empty((n, hkv, d), dtype=torch.bfloat16, device=DEV)
-    Q.qdec_kv_read(s.ctx, layer, 0, n, k, v)
-    torch.cuda.synchronize()
-    for got, ref in ((k.float().cpu().numpy(), s.om.k_cache[layer][:n]),
-                     (v.float().cpu().numpy(), s.om.v_cache[layer][:n])):
+def _check_kv(s, layer, n, oracle_model=None, min_equal=None):
+    """The cache rows the prefill wrote against the oracle's (both bf16 values): relative L2 of
+    K and of V within the fixed bar, and, when min_equal is given, at least that fraction of the
+    elements bit-identical (layer 0, whose rows depend on the exact embedding rows only through
+    roundings that rarely flip apart; later layers inherit the flips of the layers before)."""
+    om = oracle_model or s.om
+    kg, vg = s.kv_rows(layer, n)
+    for got, ref in ((kg, om.k_cache[layer][:n]), (vg, om.v_cache[layer][:n])):
         rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-        assert rel <= 2e-2, (layer, rel)
+        eq = float(np.mean(got == ref))
+        print(f"  kv layer {layer}: rel-L2 {rel:.3e}, identical {eq:.5f}", flush=True)
+        assert rel <= 1.5e-2, (layer, rel)
+        if min_equal is not None:
+            assert eq >= min_equal, (layer, eq)
 
 
 @pytest.mark.timeout(600)
-def test_prefill_matches_token_by_token_decode():
-    """One prefill of 100 tokens, then a second of 37 at pos0 = 100 (queries over cached keys),
-    then a decode step at pos 137: each against the oracle decoding the same tokens one by one
-    under the same 16-bit activation policy; the cache rows the prefill wrote against the
-    oracle's."""
-    s = PrefillSetup()
+def test_prefill_two_layers_fixed_bar():
+    """2 layers at the Qwen3-0.6B widths: a prefill of 100 tokens, a second of 37 at pos0 = 100
+    (queries over cached keys), then a decode step at pos 137, each against the oracle decoding
+    the same tokens one by one under the same 16-bit activation policy, at the fixed bar; the
+    cache rows both prefills wrote against the oracle's."""
+    s = PrefillSetup(SHAPE2)
     try:
-        toks = synth.prompt_tokens(SHAPE["vocab"], 137, seed=4)
+        toks = synth.prompt_tokens(SHAPE["vocab"], 138, seed=4)
         got = s.prefill(toks[:100], 0)
-        r32, r64 = s.oracle_run(toks[:100], 0)
-        _check_bf16_policy(got, r64, r32, "prefill 100")
-        _check_kv(s, 0, 100)
-        _check_kv(s, SHAPE["n_layers"] - 1, 100)
-        got = s.prefill(toks[100:], 100)
-        r32, r64 = s.oracle_run(toks[100:], 100)
-        _check_bf16_policy(got, r64, r32, "prefill 37 at 100")
-        # a decode step continues from the prefilled cache
-        tok = torch.tensor([int(toks[-1])], dtype=torch.int32, device=DEV)
+        _, r64 = s.oracle_run(toks[:100], 0, fp32_pass=False)
+        _fixed_bar(got, r64, "prefill 100")
+        got = s.prefill(toks[100:137], 100)
+        _, r64 = s.oracle_run(toks[100:137], 100, fp32_pass=False)
+        _fixed_bar(got, r64, "prefill 37 at 100")
+        for layer in range(2):
+            _check_kv(s, layer, 137, min_equal=0.99 if layer == 0 else None)
+        tok = torch.tensor([int(toks[137])], dtype=torch.int32, device=DEV)
         st = Q.make_step(137, token_id=tok, hidden_out=s.hidden, logits_out=s.logits,
                          argmax_out=s.amax)
         Q.qdec_decode_step(s.ctx, st)
         torch.cuda.synchronize()
         got = (s.hidden.cpu().numpy().astype(np.float64),
                synth.bf16_to_f32(s.logits).astype(np.float64), int(s.amax.item()))
-        r32, r64 = s.oracle_run(toks[-1:], 137)
-        _check_bf16_policy(got, r64, r32, "decode at 137")
+        _, r64 = s.oracle_run(toks[137:], 137, fp32_pass=False)
+        _fixed_bar(got, r64, "decode at 137")
         assert Q.qdec_device_error(s.ctx) == 0
     finally:
         s.close()
 
 
+@pytest.mark.timeout(900)
+def test_prefill_2048_tokens():
+    """The benchmark's prefill: 2048 prompt tokens from position 0 in one call (every GEMM at
+    m = 2048, the same launches the benchmark times).  At the Qwen3-0.6B widths with 2 layers:
+    the last token's hidden state and logits at the fixed bar against the oracle decoding the
+    2048 tokens one by one, and every K/V row the prefill wrote (2 layers x 2048 positions x 8
+    heads) against the oracle's.  At the full 28 layers (the benchmark's model): the rows of
+    layers 0 and 1 -- which depend only on the first two layers -- against the same oracle run,
+    and the last token's greedy id valid for its own logits."""
+    n = 2048
+    toks = synth.prompt_tokens(SHAPE["vocab"], n, seed=4)
+    s2 = PrefillSetup(SHAPE2, max_context=n, max_prefill=n)
+    try:
+        got = s2.prefill(toks, 0)
+        print("prefill 2048 (2 layers) done; oracle decoding 2048 tokens", flush=True)
+        _, r64 = s2.oracle_run(toks, 0, fp32_pass=False)
+        _fixed_bar(got, r64, "prefill 2048, 2 layers")
+        for layer in range(2):
+            _check_kv(s2, layer, n, min_equal=0.99 if layer == 0 else None)
+        om = s2.om
+    finally:
+        s2.close()
+    s28 = PrefillSetup(SHAPE, max_context=n, max_prefill=n, oracle_model=False)
+    try:
+        gh, gl, ga = s28.prefill(toks, 0)
+        print("prefill 2048 (28 layers) done", flush=True)
+        assert np.all(np.isfinite(gh)) and np.all(np.isfinite(gl))
+        assert gl[ga] == gl.max() and ga == int(np.flatnonzero(gl == gl.max())[0])
+        for layer in range(2):
+            _check_kv(s28, layer, n, oracle_model=om, min_equal=0.99 if layer == 0 else None)
+        assert Q.qdec_device_error(s28.ctx) == 0
+    finally:
+        s28.close()
+
+
+@pytest.mark.timeout(600)
+def test_prefill_28_layers_track_plain_fp32():
+    """The full 28 layers: a prefill of 100 tokens against the oracle decoding them one by one
+    (evidence that the GPU lands where a plain fp32 implementation does after 28 layers of
+    bf16 activations), and the cache rows of the first and last layer."""
+    s = PrefillSetup()
+    try:
+        toks = synth.prompt_tokens(SHAPE["vocab"], 100, seed=4)
+        got = s.prefill(toks, 0)
+        r32, r64 = s.oracle_run(toks, 0)
+        _tracks_plain_fp32(got, r64, r32, "prefill 100, 28 layers")
+        _check_kv(s, 0, 100, min_equal=0.99)
+        kg, vg = s.kv_rows(SHAPE["n_layers"] - 1, 100)
+        for got_kv, ref in ((kg, s.om.k_cache[-1][:100]), (vg, s.om.v_cache[-1][:100])):
+            assert np.linalg.norm(got_kv - ref) / np.linalg.norm(ref) <= 3e-2
+    finally:
+        s.close()
+
+
 def test_prefill_rejects_bad_calls():
-    s = PrefillSetup(max_context=256, max_prefill=32)
+    s = PrefillSetup(max_context=256, max_prefill=32, oracle_model=False)
     try:
         t = torch.zeros(64, dtype=torch.int32, device=DEV)
         with pytest.raises(Q.QdecError):

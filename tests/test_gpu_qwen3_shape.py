@@ -1,23 +1,24 @@
-"""The decode step at the Qwen3-0.6B shape against the oracle (bf16 and W8A16 paths).
+"""The decode step at the Qwen3-0.6B shape against the oracle (bf16, W8A16 and W4A16 paths).
 
 Recipe: random-init weights N(0, 0.02) stored bf16 (seed 0), gammas 1 + N(0, 0.1), KV positions
 0..4094 pre-filled with N(0, 1) bf16 values through a random permutation of the 256 pool pages,
 one token id drawn uniformly; a decode step at pos T-1 for T in 512, 2048, 4096.
-Bar, derived from the arithmetic: d32 and l32 are the distances (hidden relative L2, logits
-max-abs) of the oracle's own plain-fp32 arithmetic mode from its fp64 result on the same inputs,
-i.e. how far a correct fp32 implementation of the method lands.  Wherever the step rounds to bf16
-(the appended K/V row always, activations at op boundaries with 16-bit activations), values that
-differ by a tiny amount before rounding flip with some probability and the flips compound over
-the layers, so the GPU's distance and d32 are two samples of the same process:
-  - fp32 activations: hidden relative L2 <= max(1e-4, 4 d32) and every logit within one bf16
-    spacing of the oracle's (2^-7 |logit| plus 1e-5 of the largest) plus 4 l32.  Long contexts
-    measure ~2e-6 (d32 ~1e-5); at pos 0-1 the appended V row is most of the attention output,
-    only a handful of roundings flip, and single samples differ by up to 3x (d32 0.5-1.6e-3);
-  - bf16 activations: hidden relative L2 <= max(1.5e-2, 2 d32) and logits max-abs
-    <= max(5e-2, 2 l32): thousands of flips, so samples agree more closely (a plain fp32
-    implementation lands 0.9-1.7e-2 away at this shape, the GPU 0.4-1.6e-2).
+
+Bars.  The fixed bar of the bf16 path -- hidden-state relative L2 <= 1.5e-2 and logits max-abs
+<= 5e-2 against the fp64 oracle -- is asserted wherever it is met by the arithmetic itself:
+  - fp32 activations (bf16 / int8 / int4 as storage formats only), at every depth: the fixed bar,
+    and a tighter one derived from the arithmetic: hidden relative L2 <= max(1e-4, 4 d32) and
+    every logit within one bf16 spacing of the oracle's plus 4 l32, where d32 and l32 are the
+    distances of the oracle's own plain-fp32 mode from its fp64 result on the same inputs;
+  - bf16 activations (every op-boundary activation rounded to 16 bits), on a full-width model of
+    2 layers: the fixed bar.
+With bf16 activations the roundings of two correct implementations flip apart and the flips
+compound over the layers: after 28 layers a plain fp32 implementation of the method itself lands
+0.9-1.7e-2 from the fp64 result, so no implementation meets the fixed bar there reliably.  The
+28-layer bf16-activation comparison is kept as evidence that the GPU tracks a plain fp32
+implementation (its distance at most twice d32 and l32); it is not the fixed bar.
 In every case the GPU's greedy id must be a maximiser of the oracle's logits up to bf16 rounding;
-int8 codes and scales bit-exact; graph replay bit-identical to the eager step.
+int8 / int4 codes and scales bit-exact; graph replay bit-identical to the eager step.
 """
 import numpy as np
 import pytest
@@ -30,6 +31,8 @@ from decode_step_04_amd import qdec as Q
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 SHAPE = synth.QWEN3_0P6B
+# the same widths with 2 layers (the first two layers of the 28-layer model: same draw order)
+SHAPE2 = dict(SHAPE, name="qwen3-0.6b-shape-2-layers", n_layers=2)
 MAXCTX = 4096
 CONTEXTS = (512, 2048, 4096)
 
@@ -41,18 +44,19 @@ QUANTISERS = {"w8a16": oracle.quantize_rows,
 
 
 class Setup:
-    def __init__(self, path, act):
-        print(f"qwen3-0.6b setup path={path} act={act}", flush=True)
+    def __init__(self, path, act, shape=SHAPE):
+        print(f"{shape['name']} setup path={path} act={act}", flush=True)
         self.path = path
+        self.shape = shape
         n_pages = MAXCTX // 16
-        self.cfg = loader.config_for(SHAPE, path=path, num_pages=n_pages, max_context=MAXCTX,
+        self.cfg = loader.config_for(shape, path=path, num_pages=n_pages, max_context=MAXCTX,
                                      act=act)
         self.ctx = Q.qdec_create(self.cfg, 0)
-        self.w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        self.w = synth.bf16_model(shape, seed=0, device=DEV)
         loader.upload_weights(self.ctx, self.w, DEV)
         self.table = synth.block_table(n_pages, n_pages, seed=2)
         Q.qdec_kv_set_block_table(self.ctx, self.table)
-        kv = synth.kv_prefill(SHAPE, MAXCTX - 1, seed=1, device=DEV)
+        kv = synth.kv_prefill(shape, MAXCTX - 1, seed=1, device=DEV)
         loader.prefill_kv(self.ctx, kv)
         hw = synth.host_weights(self.w)
         if path in QUANTISERS:
@@ -64,7 +68,7 @@ class Setup:
             q, s = quant(oracle.bf16_bits_to_f64(hw["embed"]).astype(np.float32))
             hw["lm_head"], hw["lm_scale"] = q, s
         self.hw = hw
-        self.om = oracle.Model(dict(SHAPE, act_bf16=int(act == "bf16"), kv_bf16=1, logits_bf16=1),
+        self.om = oracle.Model(dict(shape, act_bf16=int(act == "bf16"), kv_bf16=1, logits_bf16=1),
                                hw, max_ctx=MAXCTX)
         for l, (k, v) in enumerate(kv):
             self.om.k_cache[l][: MAXCTX - 1] = k.float().cpu().numpy()
@@ -93,22 +97,34 @@ class Setup:
         Q.qdec_destroy(self.ctx)
 
 
-def _check(got, ref, act, ref32):
+def _distances(got, ref, ref32, what=""):
     gh, gl, ga = got
     rh, rl, ra = ref
     rel = np.linalg.norm(gh - rh) / np.linalg.norm(rh)
     lmax = np.max(np.abs(gl - rl))
     d32 = np.linalg.norm(ref32[0] - rh) / np.linalg.norm(rh)
     l32 = np.max(np.abs(ref32[1] - rl))
-    print(f"hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle {ra}  "
-          f"(plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
+    print(f"{what} hidden rel-L2 {rel:.3e}  logits max-abs {lmax:.3e}  argmax gpu {ga} oracle "
+          f"{ra}  (plain-fp32 oracle: {d32:.3e}, {l32:.3e})", flush=True)
+    return rel, lmax, d32, l32
+
+
+def _argmax_valid(got, ref):
+    rl = ref[1]
+    assert rl[got[2]] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+
+
+def _check(got, ref, act, ref32, what=""):
+    """The fixed bar (hidden relative L2 <= 1.5e-2, logits max-abs <= 5e-2), plus for fp32
+    activations the tighter bar derived from the arithmetic."""
+    rel, lmax, d32, l32 = _distances(got, ref, ref32, what)
+    assert rel <= 1.5e-2
+    assert lmax <= 5e-2
     if act == "f32":
+        gl, rl = got[1], ref[1]
         assert rel <= max(1e-4, 4 * d32)
         assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max() + 4 * l32)
-    else:
-        assert rel <= max(1.5e-2, 2 * d32)
-        assert lmax <= max(5e-2, 2 * l32)
-    assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
+    _argmax_valid(got, ref)
 
 
 def _oracle_pair(om, pos, tok_id):
@@ -122,10 +138,11 @@ def _oracle_pair(om, pos, tok_id):
 _SETUPS = {}
 
 
-def setup(path, act):
-    if (path, act) not in _SETUPS:
-        _SETUPS[(path, act)] = Setup(path, act)
-    return _SETUPS[(path, act)]
+def setup(path, act, shape=SHAPE):
+    key = (path, act, shape["n_layers"])
+    if key not in _SETUPS:
+        _SETUPS[key] = Setup(path, act, shape)
+    return _SETUPS[key]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -136,14 +153,11 @@ def _close_setups():
     _SETUPS.clear()
 
 
-# bf16 weights with fp32 activations (bf16 as storage only) at every context; bf16 activations
-# at op boundaries (the 16-bit activation policy) and the int8 per-row weights at both ends.
+# fp32 activations (bf16, int8 and int4 as storage formats) at the full 28 layers: the fixed bar
+# and the tighter derived one
 CASES = ([("bf16", "f32", T) for T in CONTEXTS] +
-         [("bf16", "bf16", 512), ("bf16", "bf16", 4096), ("w8a16", "bf16", 512),
-          ("w8a16", "bf16", 4096), ("w8a16", "f32", 4096),
-          # group-wise int8 and int4 weights (128-value groups)
-          ("w8a16g", "f32", 4096), ("w4a16", "f32", 512), ("w4a16", "f32", 4096),
-          ("w4a16", "bf16", 4096)])
+         [("w8a16", "f32", 512), ("w8a16", "f32", 4096), ("w8a16g", "f32", 4096),
+          ("w4a16", "f32", 512), ("w4a16", "f32", 4096)])
 
 
 @pytest.mark.parametrize("path,act,T", CASES)
@@ -153,6 +167,38 @@ def test_step_matches_oracle(path, act, T):
     got = s.step(T - 1)
     ref32, ref = _oracle_pair(s.om, T - 1, s.tok_id)
     _check(got, ref, act, ref32)
+
+
+# bf16 activations on the full-width 2-layer model: the fixed bar
+CASES_BF16_ACT = [(path, T) for path in ("bf16", "w8a16", "w8a16g", "w4a16")
+                  for T in (512, 4096)]
+
+
+@pytest.mark.parametrize("path,T", CASES_BF16_ACT)
+def test_bf16_activations_two_layers_fixed_bar(path, T):
+    print(f"qwen3-0.6b widths, 2 layers, {path} act=bf16 T={T}", flush=True)
+    s = setup(path, "bf16", SHAPE2)
+    got = s.step(T - 1)
+    ref32, ref = _oracle_pair(s.om, T - 1, s.tok_id)
+    _check(got, ref, "bf16", ref32, "2 layers")
+
+
+# bf16 activations over all 28 layers: evidence that the GPU lands where a plain fp32
+# implementation of the method does (compounding bf16 flips put both near the fixed bar)
+CASES_28_BF16_ACT = [("bf16", 512), ("bf16", 4096), ("w8a16", 512), ("w8a16", 4096),
+                     ("w4a16", 4096)]
+
+
+@pytest.mark.parametrize("path,T", CASES_28_BF16_ACT)
+def test_bf16_activations_28_layers_track_plain_fp32(path, T):
+    print(f"qwen3-0.6b 28 layers {path} act=bf16 T={T}", flush=True)
+    s = setup(path, "bf16")
+    got = s.step(T - 1)
+    ref32, ref = _oracle_pair(s.om, T - 1, s.tok_id)
+    rel, lmax, d32, l32 = _distances(got, ref, ref32, "28 layers")
+    assert rel <= 2 * d32
+    assert lmax <= 2 * l32
+    _argmax_valid(got, ref)
 
 
 def test_graph_replay_bit_identical():
@@ -193,7 +239,7 @@ def _tdt(codes):
 
 @pytest.mark.parametrize("path", ["w8a16", "w8a16g", "w4a16"])
 def test_quantised_codes_bit_exact(path):
-    w8 = setup(path, "bf16" if path == "w8a16" else "f32")
+    w8 = setup(path, "f32")
     for layer in (0, 27):
         for which, key in ((Q.W_QKV, "qkv"), (Q.W_O, "o"), (Q.W_GATE_UP, "gate_up"),
                            (Q.W_DOWN, "down")):
@@ -244,3 +290,66 @@ def test_graph_replay_at_many_positions():
         Q.qdec_graph_reset(s.ctx)
     finally:
         s.close()
+
+
+def test_fused_append_sentinel_pool_bf16():
+    """bf16 K/V pools of 300 pages (more than the 256 the block table maps) filled with a
+    sentinel; positions 0..2046 written through the block table, then one decode step at pos
+    2047 (the append inside the attention kernel of every layer).  Afterwards, in every layer:
+    the pre-filled slots hold their values bit for bit, the slot of (pos 2047) holds the oracle's
+    appended row up to one bf16 step, and every other slot of both pools still holds the
+    sentinel bit for bit -- the step wrote exactly one row per layer, where the block table
+    says."""
+    T, n_pages, n_logical = 2048, 300, 256
+    cfg = loader.config_for(SHAPE, path="bf16", num_pages=n_pages, max_context=MAXCTX)
+    ctx = Q.qdec_create(cfg, 0)
+    try:
+        L, hkv, d = SHAPE["n_layers"], SHAPE["n_kv_heads"], SHAPE["head_dim"]
+        w = synth.bf16_model(SHAPE, seed=0, device=DEV)
+        loader.upload_weights(ctx, w, DEV)
+        table = synth.block_table(n_pages, n_logical, seed=9)
+        Q.qdec_kv_set_block_table(ctx, table)
+        sentinel = torch.tensor(-7.25, dtype=torch.bfloat16)
+        pool0 = torch.full((n_pages, hkv, 16, d), -7.25, dtype=torch.bfloat16, device=DEV)
+        for layer in range(L):
+            kp, vp = Q.qdec_kv_pool_ptr(ctx, layer)
+            Q.qdec_op_copy(kp, pool0, pool0.numel() * 2)
+            Q.qdec_op_copy(vp, pool0, pool0.numel() * 2)
+        kv = synth.kv_prefill(SHAPE, T - 1, seed=1, device=DEV)
+        loader.prefill_kv(ctx, kv)
+        tok_id = synth.token_id(SHAPE["vocab"], seed=3)
+        tok = torch.tensor([tok_id], dtype=torch.int32, device=DEV)
+        hidden = torch.empty(SHAPE["hidden"], device=DEV)
+        Q.qdec_decode_step(ctx, Q.make_step(T - 1, token_id=tok, hidden_out=hidden))
+        torch.cuda.synchronize()
+        om = oracle.Model(dict(SHAPE, act_bf16=0, kv_bf16=1, logits_bf16=1),
+                          synth.host_weights(w), max_ctx=T)
+        for l, (k, v) in enumerate(kv):
+            om.k_cache[l][: T - 1] = k.float().cpu().numpy()
+            om.v_cache[l][: T - 1] = v.float().cpu().numpy()
+        om.step(T - 1, token=tok_id, want_logits=False)
+        sbits = int(synth.bf16_to_bits(sentinel))
+        pre = oracle.pool_scatter(np.ones((T - 1, hkv, d), dtype=np.float32), 0, table, n_pages,
+                                  16) != 0
+        new = oracle.pool_scatter(np.ones((1, hkv, d), dtype=np.float32), T - 1, table, n_pages,
+                                  16) != 0
+        untouched = ~(pre | new)
+        assert new.sum() == hkv * d and not np.any(pre & new)
+        buf = torch.empty((n_pages, hkv, 16, d), dtype=torch.bfloat16, device=DEV)
+        for layer in range(L):
+            kp, vp = Q.qdec_kv_pool_ptr(ctx, layer)
+            for p, rows, cache in ((kp, kv[layer][0], om.k_cache[layer]),
+                                   (vp, kv[layer][1], om.v_cache[layer])):
+                Q.qdec_op_copy(buf, p, buf.numel() * 2)
+                torch.cuda.synchronize()
+                bits = synth.bf16_to_bits(buf)
+                assert np.all(bits[untouched] == sbits), layer
+                exp_pre = oracle.pool_scatter(synth.bf16_to_bits(rows), 0, table, n_pages, 16)
+                np.testing.assert_array_equal(bits[pre], exp_pre[pre])
+                got_new = oracle.bf16_bits_to_f64(bits[new])
+                ref_new = oracle.pool_scatter(cache[T - 1:T], T - 1, table, n_pages, 16)[new]
+                atol = 1e-4 * np.abs(ref_new).max()
+                assert np.all(np.abs(got_new - ref_new) <= np.abs(ref_new) * 2.0**-7 + atol), layer
+        del kv, w
+    finally:
+        Q.qdec_destroy(ctx)

@@ -177,6 +177,61 @@ def test_kv_cache_holds_the_appended_rows(tiny):
         assert torch.equal(back_k, kk) and torch.equal(back_v, kk + 0.5)
 
 
+def _fill_pools(ctx, n_layers, num_pages, hkv, d, value, dtype):
+    t = torch.full((num_pages, hkv, 16, d), value, dtype=dtype, device=DEV)
+    for layer in range(n_layers):
+        kp, vp = Q.qdec_kv_pool_ptr(ctx, layer)
+        Q.qdec_op_copy(kp, t, t.numel() * t.element_size())
+        Q.qdec_op_copy(vp, t, t.numel() * t.element_size())
+    torch.cuda.synchronize()
+
+
+def _read_pool(ctx, layer, num_pages, hkv, d, dtype):
+    kp, vp = Q.qdec_kv_pool_ptr(ctx, layer)
+    out = []
+    for p in (kp, vp):
+        t = torch.empty((num_pages, hkv, 16, d), dtype=dtype, device=DEV)
+        Q.qdec_op_copy(t, p, t.numel() * t.element_size())
+        out.append(t)
+    torch.cuda.synchronize()
+    return [t.cpu().numpy() for t in out]
+
+
+def test_fused_append_writes_exactly_one_slot_per_layer_and_step():
+    """Both pools of every layer start filled with a sentinel; after the 47 steps of the run
+    (prompt, then greedy ids fed back on the device) every slot the oracle's scatter does not
+    address still holds the sentinel bit for bit, and every slot it addresses -- the step's own
+    append inside the attention kernel, one (layer, position) row per step -- holds the oracle's
+    row for that position (max-abs 1e-4)."""
+    t = Tiny()
+    try:
+        cfg = t.cfg
+        L, hkv, d, n_pages = cfg["n_layers"], cfg["n_kv_heads"], cfg["head_dim"], t.m["num_pages"]
+        sentinel = -7.25
+        _fill_pools(t.ctx, L, n_pages, hkv, d, sentinel, torch.float32)
+        hs, ls, ids = t.run()
+        n = len(t.m["prompt"]) + N_GEN - 1
+        om = oracle.Model(dict(cfg, act_bf16=0, kv_bf16=0), t.m["weights"], max_ctx=64)
+        prompt = [int(x) for x in t.m["prompt"]]
+        nxt = None
+        for pos in range(n):
+            tok = prompt[pos] if pos < len(prompt) else nxt
+            _, _, am = om.step(pos, token=tok, want_logits=pos >= len(prompt) - 1)
+            nxt = am
+        bt = t.m["block_table"]
+        written = oracle.pool_scatter(np.ones((n, hkv, d), dtype=np.float32), 0, bt, n_pages,
+                                      16) != 0
+        assert written.sum() == n * hkv * d
+        for layer in range(L):
+            kp, vp = _read_pool(t.ctx, layer, n_pages, hkv, d, torch.float32)
+            for pool, cache in ((kp, om.k_cache[layer]), (vp, om.v_cache[layer])):
+                exp = oracle.pool_scatter(cache[:n], 0, bt, n_pages, 16)
+                assert np.all(pool[~written] == np.float32(sentinel)), layer
+                assert np.max(np.abs(pool[written] - exp[written])) <= 1e-4, layer
+    finally:
+        t.close()
+
+
 def test_step_errors_are_reported_not_run(tiny):
     st = Q.make_step(64, token_id=tiny.tok, hidden_out=tiny.hid)
     with pytest.raises(Q.QdecError) as e:

@@ -11,10 +11,11 @@ Recipe: 2 layers, 4 Q / 2 KV heads, D 64, FFN 512, vocab 2048 tied; random-init 
 N(0, 0.02) stored bf16 (seed 5) and quantised on the device to int4 with a scale per 128 values
 (the oracle quantises the same bf16 values), gammas 1 + N(0, 0.1); KV positions 0..46 pre-filled
 with N(0, 1) bf16 values through a random permutation of 4 pages; a step at pos 47, eager and
-graph-replayed.  Bar: the one the Qwen3-0.6B-shape test derives from the arithmetic (hidden
-relative L2 and logits against the oracle, scaled by the distance of the oracle's own plain-fp32
-mode), the greedy id a maximiser of the oracle's logits up to bf16 rounding, graph replay
-bit-identical to the eager step.
+graph-replayed.  Bar: the fixed bar of the bf16 path (hidden relative L2 <= 1.5e-2, logits
+max-abs <= 5e-2 against the fp64 oracle) with either activation precision; with fp32
+activations also the tighter bar the Qwen3-0.6B-shape test derives from the arithmetic (scaled
+by the distance of the oracle's own plain-fp32 mode); the greedy id a maximiser of the oracle's
+logits up to bf16 rounding; graph replay bit-identical to the eager step.
 """
 import numpy as np
 import pytest
@@ -90,12 +91,11 @@ def test_step_matches_oracle(hidden, act):
         l32 = np.max(np.abs(r32[1] - rl))
         print(f"hidden rel-L2 {rel:.3e} (plain fp32 {d32:.3e}); logits max-abs "
               f"{np.max(np.abs(gl - rl)):.3e} (plain fp32 {l32:.3e})", flush=True)
+        assert rel <= 1.5e-2
+        assert np.max(np.abs(gl - rl)) <= 5e-2
         if act == "f32":
             assert rel <= max(1e-4, 4 * d32)
             assert np.all(np.abs(gl - rl) <= 2.0**-7 * np.abs(rl) + 1e-5 * np.abs(rl).max() + 4 * l32)
-        else:
-            assert rel <= max(1.5e-2, 2 * d32)
-            assert np.max(np.abs(gl - rl)) <= max(5e-2, 2 * l32)
         assert rl[ga] >= rl.max() - 2 * 2.0**-8 * abs(rl.max())
     finally:
         Q.qdec_destroy(ctx)
