@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1540,13 +1541,13 @@ QDEC_API qdec_status qdec_op_attention_workspace(int32_t ctx_len, int32_t n_q_he
   return QDEC_OK;
 }
 
-QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const void* k_pool,
-                                       const void* v_pool, int32_t kv_dtype,
-                                       const int32_t* block_table, int32_t ctx_len,
-                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
-                                       int32_t page_size, int32_t partition_size, void* workspace,
-                                       size_t workspace_bytes, void* out, int32_t out_dtype,
-                                       void* stream) {
+// Validates an op-level attention call and derives its partition length and count.
+static qdec_status op_attention_check(const void* q, int32_t q_dtype, const void* k_pool,
+                                      const void* v_pool, int32_t kv_dtype,
+                                      const int32_t* block_table, int32_t ctx_len,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t page_size, int32_t partition_size, const void* out,
+                                      int32_t out_dtype, int* part, int* np) {
   if (!q || !k_pool || !v_pool || !block_table || !out) return fail(nullptr, QDEC_E_INVAL, "NULL pointer");
   if (head_dim != 64 && head_dim != 128) return fail(nullptr, QDEC_E_UNSUPPORTED, "head_dim");
   if (page_size != kPage) return fail(nullptr, QDEC_E_UNSUPPORTED, "page_size must be 16");
@@ -1560,14 +1561,22 @@ QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const voi
       (out_dtype != QDEC_F32 && out_dtype != QDEC_BF16))
     return fail(nullptr, QDEC_E_INVAL, "bad dtype");
   if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(nullptr, QDEC_E_INVAL, "pools must be 16-byte aligned");
-  const int part = op_part(ctx_len, n_q_heads, n_kv_heads, partition_size);
-  const int np = n_parts_for(ctx_len, part);
-  if (np > kMaxMergeParts)
+  *part = op_part(ctx_len, n_q_heads, n_kv_heads, partition_size);
+  *np = n_parts_for(ctx_len, *part);
+  if (*np > kMaxMergeParts)
     return fail(nullptr, QDEC_E_UNSUPPORTED, "more than %d partitions", kMaxMergeParts);
+  return QDEC_OK;
+}
+
+// Enqueues the split-KV kernel (and the merge, with several partitions) of a checked call; the
+// partials go to workspace (laid out as attn_ws describes).
+static qdec_status op_attention_launch(const void* q, int32_t q_dtype, const void* k_pool,
+                                       const void* v_pool, int32_t kv_dtype,
+                                       const int32_t* block_table, int32_t ctx_len,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int part, int np, void* workspace, void* out,
+                                       int32_t out_dtype, void* stream) {
   const AttnWs ws = attn_ws(n_q_heads, np, head_dim);
-  if (np > 1 && (!workspace || workspace_bytes < (size_t)ws.bytes || !aligned(workspace, 256)))
-    return fail(nullptr, QDEC_E_INVAL, "workspace of %lld bytes (256-byte aligned) required",
-                (long long)ws.bytes);
   AttnArgs a{};
   a.q = q;
   a.q_bf16 = q_dtype == QDEC_BF16;
@@ -1595,6 +1604,88 @@ QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const voi
   if (e == hipSuccess && np > 1) e = launch_attention_merge(head_dim, a, s);
   if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "attention launch: %s", hipGetErrorString(e));
   return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const void* k_pool,
+                                       const void* v_pool, int32_t kv_dtype,
+                                       const int32_t* block_table, int32_t ctx_len,
+                                       int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                       int32_t page_size, int32_t partition_size, void* workspace,
+                                       size_t workspace_bytes, void* out, int32_t out_dtype,
+                                       void* stream) {
+  int part = 0, np = 0;
+  qdec_status r = op_attention_check(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len,
+                                     n_q_heads, n_kv_heads, head_dim, page_size, partition_size,
+                                     out, out_dtype, &part, &np);
+  if (r != QDEC_OK) return r;
+  const AttnWs ws = attn_ws(n_q_heads, np, head_dim);
+  if (np > 1 && (!workspace || workspace_bytes < (size_t)ws.bytes || !aligned(workspace, 256)))
+    return fail(nullptr, QDEC_E_INVAL, "workspace of %lld bytes (256-byte aligned) required",
+                (long long)ws.bytes);
+  return op_attention_launch(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len,
+                             n_q_heads, n_kv_heads, head_dim, part, np, workspace, out, out_dtype,
+                             stream);
+}
+
+// ---- the allocation-free variant of qdec_op_attention ---------------------------------------
+// Its split-KV partials live in `scratch`, a file-scope device array of kNoAllocScratchBytes that
+// every GPU the library runs on holds for the life of the process.  In host code the array's
+// name is only a stand-in: the device address of each GPU's copy comes from hipGetSymbolAddress,
+// taken once per device (with that device current) on the first call there, and only that
+// address is ever handed to a kernel.  Calls on one GPU share its copy, so calls that overlap on
+// one GPU race; nothing in it needs clearing (every slot a call reads, the same call writes first).
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+// Device address of the current device's copy of `scratch`.
+static qdec_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(nullptr, QDEC_E_UNSUPPORTED, "device %d beyond the %d the scratch table covers",
+                dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(nullptr, QDEC_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return QDEC_OK;
+}
+
+QDEC_API qdec_status qdec_op_attention_noalloc(const void* q, int32_t q_dtype, const void* k_pool,
+                                               const void* v_pool, int32_t kv_dtype,
+                                               const int32_t* block_table, int32_t ctx_len,
+                                               int32_t n_q_heads, int32_t n_kv_heads,
+                                               int32_t head_dim, int32_t page_size,
+                                               int32_t partition_size, void* out,
+                                               int32_t out_dtype, void* stream) {
+  int part = 0, np = 0;
+  qdec_status r = op_attention_check(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len,
+                                     n_q_heads, n_kv_heads, head_dim, page_size, partition_size,
+                                     out, out_dtype, &part, &np);
+  if (r != QDEC_OK) return r;
+  const AttnWs ws = attn_ws(n_q_heads, np, head_dim);
+  if (np > 1 && (size_t)ws.bytes > kNoAllocScratchBytes)
+    return fail(nullptr, QDEC_E_RANGE,
+                "split-KV partials of %lld bytes exceed the %zu-byte static scratch (fewer query "
+                "heads, a shorter context or longer partitions fit)",
+                (long long)ws.bytes, kNoAllocScratchBytes);
+  void* sp = nullptr;
+  if (np > 1 && (r = scratch_address(&sp)) != QDEC_OK) return r;
+  return op_attention_launch(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len,
+                             n_q_heads, n_kv_heads, head_dim, part, np, sp, out, out_dtype, stream);
 }
 
 QDEC_API qdec_status qdec_op_argmax(const void* x, int32_t x_dtype, int64_t n, int32_t* out,

@@ -117,6 +117,8 @@ _SIGS = {
     "qdec_op_attention_workspace": [_I32, _I32, _I32, _I32, C.POINTER(_SZ)],
     "qdec_op_attention": [_P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ,
                           _P, _I32, _P],
+    "qdec_op_attention_noalloc": [_P, _I32, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32,
+                                  _I32, _P, _I32, _P],
     "qdec_op_argmax": [_P, _I32, _I64, _P, _P],
     "qdec_op_copy": [_P, _P, _I64, _P],
 }
@@ -397,6 +399,14 @@ def qdec_op_attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len
     _call("qdec_op_attention", _p(q), q_dtype, _p(k_pool), _p(v_pool), kv_dtype, _p(block_table),
           ctx_len, n_q_heads, n_kv_heads, head_dim, page_size, partition_size, _p(workspace),
           workspace_bytes, _p(out), out_dtype, _p(stream))
+
+
+def qdec_op_attention_noalloc(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, ctx_len,
+                              n_q_heads, n_kv_heads, head_dim, partition_size, out, out_dtype,
+                              page_size=16, stream=None):
+    _call("qdec_op_attention_noalloc", _p(q), q_dtype, _p(k_pool), _p(v_pool), kv_dtype,
+          _p(block_table), ctx_len, n_q_heads, n_kv_heads, head_dim, page_size, partition_size,
+          _p(out), out_dtype, _p(stream))
 
 
 def qdec_op_argmax(x, x_dtype, n, out, stream=None):

@@ -458,6 +458,21 @@ qdec_status qdec_op_attention(const void* q, int32_t q_dtype, const void* k_pool
                               void* workspace, size_t workspace_bytes, void* out,
                               int32_t out_dtype, void* stream);
 
+/* qdec_op_attention without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The split-KV partials go to a static device scratch array of 16 MiB that each GPU the library
+ * runs on holds until the process ends; the call itself allocates nothing.  Runs on the current
+ * device (stream must belong to it); the first call on a device looks up that device's scratch
+ * address.  Calls that overlap on one GPU share its scratch and race: order them on one stream or
+ * serialise them.  QDEC_E_RANGE when the partials (Hq x partitions x (D + 2) x 4 bytes, the size
+ * qdec_op_attention_workspace reports) exceed 16 MiB; other arguments as qdec_op_attention. */
+qdec_status qdec_op_attention_noalloc(const void* q, int32_t q_dtype, const void* k_pool,
+                                      const void* v_pool, int32_t kv_dtype,
+                                      const int32_t* block_table, int32_t ctx_len,
+                                      int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                      int32_t page_size, int32_t partition_size, void* out,
+                                      int32_t out_dtype, void* stream);
+
 /* Index of the largest of n values of x_dtype (F32|BF16), lowest index on ties, NaN ignored
  * (-1 if every value is NaN); out: device int32. */
 qdec_status qdec_op_argmax(const void* x, int32_t x_dtype, int64_t n, int32_t* out, void* stream);
