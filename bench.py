@@ -54,6 +54,11 @@ def parse():
     p.add_argument("--no-legs", action="store_true",
                    help="skip the other decode workloads (0.6B W8A16 and W8A16 LM head, 8B bf16 "
                         "and W4A16)")
+    p.add_argument("--trace", choices=["stream", "offload"], default=None,
+                   help="run only this workload (for profiler runs): layer streaming or "
+                        "attention over host-resident K/V")
+    p.add_argument("--trace-steps", type=int, default=10)
+    p.add_argument("--trace-slots", type=int, default=2)
     p.add_argument("--no-ops", action="store_true",
                    help="skip the op-level workloads (attention stress, W8A16 GEMV, copy)")
     p.add_argument("--eager-only", type=int, default=0, metavar="N",
@@ -392,6 +397,137 @@ def ops_bench():
     us = per_launch_us(lambda i: Q.qdec_op_copy(b, a, nb, stream=s.cuda_stream), 4)
     out["copy_1gib"] = {"us": round(us, 1), "gbps_read_plus_write": round(2 * nb / us / 1e3, 1)}
     return out
+
+
+def streaming_bench(shape, slots_list=(1, 2, 3, -1), T=4096, steps=5):
+    """Layer streaming: every layer's projections in pinned host memory, `slots` device slots,
+    eager steps of the decode workload (bf16 weights, context T); each step copies every layer
+    over the host link once (slots = -1: the kernels read the mapped host copy themselves, no
+    copies).  Timed with events around `steps` steps after 2 warm-up steps,
+    beside a pinned host-to-device copy of the same bytes (the link's rate here) and the resident
+    eager step."""
+    import torch
+
+    from decode_step_04_amd import loader, synth
+    from decode_step_04_amd import qdec as Q
+
+    dev = "cuda"
+    n_pages = (T + 15) // 16
+    w = synth.bf16_model(shape, seed=0, device=dev)
+    kv = synth.kv_prefill(shape, T - 1, seed=1, device=dev)
+    tok = torch.tensor([synth.token_id(shape["vocab"], seed=3)], dtype=torch.int32, device=dev)
+    lg = torch.empty(shape["vocab"], dtype=torch.bfloat16, device=dev)
+    am = torch.empty(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {"model": shape["name"], "context": T, "weights": "bf16", "runs": []}
+    layer_bytes = None
+    for slots in (0,) + tuple(slots_list):
+        cfg = loader.config_for(shape, path="bf16", num_pages=n_pages, max_context=T,
+                                weight_slots=slots)
+        ctx = Q.qdec_create(cfg, 0)
+        try:
+            loader.upload_weights(ctx, w, dev)
+            Q.qdec_kv_set_block_table(ctx, synth.block_table(n_pages, n_pages, seed=2))
+            loader.prefill_kv(ctx, kv)
+            info = Q.qdec_info_get(ctx)
+            if layer_bytes is None:  # one layer's projections (the info counts all layers)
+                layer_bytes = (info.layer_matrix_bytes + info.layer_scale_bytes) // shape["n_layers"]
+            st = Q.make_step(T - 1, token_id=tok, logits_out=lg, argmax_out=am)
+            for _ in range(2):
+                Q.qdec_decode_step(ctx, st)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                Q.qdec_decode_step(ctx, st)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            row = {"slots": {0: "resident", -1: "direct"}.get(slots, slots),
+                   "ms_per_step": round(ms, 3),
+                   "device_mib": round(info.device_bytes / 2**20, 1)}
+            if slots:
+                nbytes = layer_bytes * shape["n_layers"]
+                row["host_bytes_per_step"] = nbytes
+                row["link_gbps"] = round(nbytes / ms / 1e6, 2)
+            out["runs"].append(row)
+        finally:
+            Q.qdec_destroy(ctx)
+    # the host link's rate for the same bytes: one pinned copy of every layer's block
+    nbytes = layer_bytes * shape["n_layers"]
+    h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        d.copy_(h, non_blocking=True)
+    torch.cuda.synchronize()
+    e0.record()
+    d.copy_(h, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1)
+    out["h2d_copy_ms"] = round(copy_ms, 3)
+    out["h2d_copy_gbps"] = round(nbytes / copy_ms / 1e6, 2)
+    for r in out["runs"]:
+        if r["slots"] != "resident":
+            r["of_copy"] = round(copy_ms / r["ms_per_step"], 3)
+    del w, kv, h, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def trace_workload(args):
+    """Only one workload, for profiler runs: `stream` = eager decode steps of the 0.6B shape
+    with every layer streamed through --trace-slots slots; `offload` = attention over
+    host-resident K/V (32 Q / 8 KV heads, D 128, 32K positions, 4096-position tiles, 2 buffers)."""
+    import torch
+
+    from decode_step_04_amd import loader, synth
+    from decode_step_04_amd import qdec as Q
+
+    dev = "cuda"
+    if args.trace == "stream":
+        shape, T = synth.QWEN3_0P6B, 4096
+        n_pages = T // 16
+        cfg = loader.config_for(shape, path="bf16", num_pages=n_pages, max_context=T,
+                                weight_slots=args.trace_slots)
+        ctx = Q.qdec_create(cfg, 0)
+        w = synth.bf16_model(shape, seed=0, device=dev)
+        loader.upload_weights(ctx, w, dev)
+        Q.qdec_kv_set_block_table(ctx, synth.block_table(n_pages, n_pages, seed=2))
+        loader.prefill_kv(ctx, synth.kv_prefill(shape, T - 1, seed=1, device=dev))
+        tok = torch.tensor([synth.token_id(shape["vocab"], seed=3)], dtype=torch.int32, device=dev)
+        am = torch.empty(1, dtype=torch.int32, device=dev)
+        st = Q.make_step(T - 1, token_id=tok, argmax_out=am)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.trace_steps):
+            Q.qdec_decode_step(ctx, st)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.trace_steps
+        Q.qdec_destroy(ctx)
+        print(json.dumps({"trace": "stream", "slots": args.trace_slots,
+                          "steps": args.trace_steps, "ms_per_step": round(ms, 3)}))
+    else:
+        hq, hkv, d, T = 32, 8, 128, 32768
+        pages = T // 16
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(11)
+        hk = torch.empty((pages, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty((pages, hkv, 16, d), dtype=torch.bfloat16, pin_memory=True)
+        hk.copy_(torch.randn((pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+        hv.copy_(torch.randn((pages, hkv, 16, d), generator=gen, device=dev).to(torch.bfloat16))
+        q = synth.attention_stress(8192, device=dev)[0]
+        att = torch.empty((hq, d), device=dev)
+        o = Q.qdec_offload_create(hq, hkv, d, Q.BF16, T, 4096, args.trace_slots, 0)
+        cs = torch.cuda.current_stream().cuda_stream
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.trace_steps):
+            Q.qdec_offload_attention(o, q, Q.F32, hk, hv, T, att, Q.F32, cs)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.trace_steps
+        Q.qdec_offload_destroy(o)
+        print(json.dumps({"trace": "offload", "slots": args.trace_slots, "tile": 4096,
+                          "context": T, "calls": args.trace_steps, "ms_per_call": round(ms, 3)}))
 
 
 def host_cpu():
@@ -759,6 +895,9 @@ def main():
     if args.copy_calib:
         copy_calibration()
         return
+    if args.trace:
+        trace_workload(args)
+        return
 
     import torch
 
@@ -781,6 +920,8 @@ def main():
     shape = synth.QWEN3_0P6B if args.model == "0.6b" else synth.DENSE_8B
     prefill = prefill_bench(shape, args.prefill_tokens) if args.prefill_tokens > 0 else None
     ops = None if args.no_ops else ops_bench()
+    if ops is not None:
+        ops["weight_streaming"] = streaming_bench(synth.QWEN3_0P6B)
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": head["steps"], "warmup": head["warmup"], "ms_per_step": head["ms_per_step"],

@@ -56,7 +56,10 @@ hipError_t launch_quantize_groups(const void* w, int src_bf16, int bits, void* q
 hipError_t launch_kv_copy(void* pool, void* linear, const int32_t* block_table, int pos0, int n,
                           int n_kv_heads, int head_dim, int elem, int to_pool, hipStream_t s);
 hipError_t launch_rope_table(float* table, int max_pos, int head_dim, float theta, hipStream_t s);
-hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+// bytes % 16 == 0; at most max_wgs work-groups (4096 fill the chip; a few dozen saturate the host
+// link when src is mapped host memory)
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s,
+                       int max_wgs = 4096);
 hipError_t launch_convert(void* dst, int dst_type, const void* src, int src_type, int64_t n,
                           hipStream_t s);
 hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y, int y_bf16,

@@ -412,11 +412,11 @@ __global__ __launch_bounds__(256) void k_copy(uint4* __restrict__ dst,
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s, int max_wgs) {
   const int64_t n16 = bytes / 16;
   if (n16 <= 0) return hipSuccess;
   int64_t wgs = (n16 + 255) / 256;
-  if (wgs > 256 * 16) wgs = 256 * 16;
+  if (wgs > max_wgs) wgs = max_wgs;
   hipLaunchKernelGGL(k_copy, dim3((unsigned)wgs), dim3(256), 0, s, static_cast<uint4*>(dst),
                      static_cast<const uint4*>(src), n16);
   return hipGetLastError();

@@ -38,6 +38,8 @@ thread_local std::string g_err;  // last error of context-free calls on this thr
 // partitions to merge).
 inline int target_wgs(int /*n_q_heads*/, int /*n_kv_heads*/) { return 256; }
 constexpr int kMaxTargetWgs = 256;
+// work-groups of the copy kernel that fills a weight slot from mapped host memory
+constexpr int kSlotCopyWgs = 64;
 constexpr int kNumSlots = 11;
 
 qdec_status fail(std::string* dst, qdec_status s, const char* fmt, ...) {
@@ -100,6 +102,25 @@ int64_t block_table_entries(const qdec_config& c) {
   return std::max<int64_t>(c.num_pages, model_max_parts(c) * (model_part_tokens(c) / kPage));
 }
 
+// One record of the offload schedule (kinds as in qdec_offload_schedule).
+struct OffloadOp {
+  int kind, tile, slot, other;
+};
+enum { OFF_WAIT_FREE = 0, OFF_COPY = 1, OFF_WAIT_READY = 2, OFF_COMPUTE = 3, OFF_MERGE = 4 };
+
+// Tile i uses buffer i % n_slots.  Its copy may start once the compute of the tile that last used
+// that buffer (i - n_slots) has finished, and its compute once its own copy has finished.
+void offload_schedule(int n_tiles, int n_slots, std::vector<OffloadOp>* ops) {
+  ops->clear();
+  for (int i = 0; i < n_tiles; ++i) {
+    const int slot = i % n_slots;
+    if (i >= n_slots) ops->push_back({OFF_WAIT_FREE, i, slot, i - n_slots});
+    ops->push_back({OFF_COPY, i, slot, -1});
+    ops->push_back({OFF_WAIT_READY, i, slot, i});
+    ops->push_back({OFF_COMPUTE, i, slot, -1});
+  }
+  ops->push_back({OFF_MERGE, -1, -1, -1});
+}
 }  // namespace
 
 struct qdec_ctx {
@@ -137,6 +158,18 @@ struct qdec_ctx {
   void* sample_ws = nullptr;  // temperature / top-p sampling (vocab <= 2^18)
   int am_parts = 0;
   StepDesc* desc = nullptr;
+  // layer streaming (weight_slots > 0): the layers' projection Mats point into host_layers
+  // (pinned host memory, one block of layer_block bytes per layer); slots[s] holds the device
+  // Mats of slot s (one block each, the same layout)
+  std::vector<Layer> slots;
+  bool direct_weights = false;  // weight_slots = -1: kernels read the mapped host copy; slots[0]
+                                // is only the upload staging area
+  void* host_layers = nullptr;
+  char* host_layers_dev = nullptr;  // the device's address of host_layers (its mapping)
+  int64_t layer_block = 0;
+  hipStream_t copy_stream = nullptr;
+  std::vector<hipEvent_t> ev_copied, ev_computed;  // per slot: data ready, buffer free
+  std::vector<OffloadOp> wops;
   std::vector<uint8_t> uploaded;  // (n_layers + 1) x kNumSlots; row n_layers = global slots
   std::string err;
   // graph of everything after the embedding kernel
@@ -250,6 +283,12 @@ static qdec_status validate(const qdec_config* c, std::string* why) {
   if (model_max_parts(*c) > kMaxMergeParts)
     return fail(why, QDEC_E_UNSUPPORTED, "more than %d split-KV partitions at max_context",
                 kMaxMergeParts);
+  if (c->weight_slots < -1 || c->weight_slots > c->n_layers)
+    return fail(why, QDEC_E_INVAL, "weight_slots %d out of [-1, n_layers = %d]", c->weight_slots,
+                c->n_layers);
+  if (c->weight_slots != 0 && c->max_prefill > 0)
+    return fail(why, QDEC_E_UNSUPPORTED, "host-resident layers (weight_slots != 0) run decode "
+                "steps only: max_prefill must be 0");
   {
     const int wp = wt_of(c->proj_dtype);
     const int wl = wt_of(c->lm_head_dtype);
@@ -289,8 +328,14 @@ static void fill_info(const qdec_config& c, qdec_info* o) {
   o->max_partitions = (int32_t)mp;
   const int ae = elem_size(c.act_dtype), ie = elem_size(c.io_dtype);
   const bool lm_alias = c.tied_lm_head && c.lm_head_dtype == c.io_dtype;
+  // host-resident layers (weight_slots != 0) keep their projections in pinned host memory and
+  // hold max(1, slots) layer-sized device blocks instead
+  const int64_t nslot = c.weight_slots < 0 ? 1 : c.weight_slots;
+  const int64_t layer_dev = c.weight_slots == 0
+                                ? o->layer_matrix_bytes + o->layer_scale_bytes
+                                : nslot * ((o->layer_matrix_bytes + o->layer_scale_bytes) / L);
   o->device_bytes = v * d * ie + (lm_alias ? 0 : o->lm_head_bytes) + d * 4 +
-                    o->layer_matrix_bytes + o->layer_scale_bytes + L * norms * 4 + o->kv_pool_bytes +
+                    layer_dev + L * norms * 4 + o->kv_pool_bytes +
                     block_table_entries(c) * 4 + (int64_t)c.max_context * (hd / 2) * 8 + d * 4 +
                     (hq + 2 * hkv) * hd * 4 + 2 * hq * hd * ae + f * ae + v * ie +
                     hq * mp * hd * 4 + hq * mp * 8 + (int64_t)sizeof(StepDesc) +
@@ -381,6 +426,10 @@ static void release(qdec_ctx* c) {
   if (c->graph) (void)hipGraphDestroy(c->graph);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  for (hipEvent_t e : c->ev_copied) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->ev_computed) (void)hipEventDestroy(e);
+  if (c->host_layers) (void)hipHostFree(c->host_layers);
   for (void* p : c->allocs) (void)hipFree(p);
   delete c;
 }
@@ -444,11 +493,77 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
   TRY(c->alloc(&c->final_norm, d * 4, "final norm"));
   c->layers.resize((size_t)L);
   const int64_t pool_bytes = (int64_t)cfg->num_pages * kPage * hkv * hd * elem_size(cfg->kv_dtype);
+  // one layer's projections (codes, then scales, each 256-byte aligned) carved out of a block
+  auto carve = [&](Layer& ly, char* base) {
+    int64_t off = 0;
+    auto one = [&](Mat& m, int64_t rows, int64_t cols) {
+      m.rows = rows;
+      m.cols = cols;
+      m.dtype = cfg->proj_dtype;
+      m.data = base ? base + off : nullptr;
+      off += (code_bytes(m.dtype, rows, cols) + 255) / 256 * 256;
+      m.scale = (base && is_quant(m.dtype)) ? reinterpret_cast<float*>(base + off) : nullptr;
+      off += (scale_count(m.dtype, rows, cols) * 4 + 255) / 256 * 256;
+    };
+    one(ly.qkv, (hq + 2 * hkv) * hd, d);
+    one(ly.o, d, hq * hd);
+    one(ly.gu, 2 * f, d);
+    one(ly.down, d, f);
+    return off;
+  };
+  if (cfg->weight_slots != 0) {
+    Layer probe;
+    c->layer_block = carve(probe, nullptr);
+    const size_t host_bytes = (size_t)c->layer_block * (size_t)L;
+    hipError_t eh = hipHostMalloc(&c->host_layers, host_bytes, hipHostMallocDefault);
+    if (eh != hipSuccess) {
+      (void)hipGetLastError();
+      c->host_layers = nullptr;
+      fail(&c->err, QDEC_E_NOMEM, "hipHostMalloc of %zu bytes for the streamed layers: %s",
+           host_bytes, hipGetErrorString(eh));
+      g_err = c->err;
+      release(c);
+      return QDEC_E_NOMEM;
+    }
+    c->direct_weights = cfg->weight_slots < 0;
+    c->slots.resize(c->direct_weights ? 1 : (size_t)cfg->weight_slots);
+    for (auto& sl : c->slots) {
+      char* blk = nullptr;
+      TRY(c->alloc(&blk, c->layer_block, "weight slot"));
+      carve(sl, blk);
+    }
+    // the device's address of the pinned host block: the slot copies read it (streaming), or
+    // the kernels do (direct)
+    void* mapped = nullptr;
+    TRY(c->hip(hipHostGetDevicePointer(&mapped, c->host_layers, 0),
+               "hipHostGetDevicePointer (host-resident layers)"));
+    if (!mapped || !aligned(mapped, 256)) {
+      fail(&c->err, QDEC_E_HIP, "host-resident layers have no aligned device mapping");
+      g_err = c->err;
+      release(c);
+      return QDEC_E_HIP;
+    }
+    c->host_layers_dev = static_cast<char*>(mapped);
+    char* host_base = c->direct_weights ? c->host_layers_dev : static_cast<char*>(c->host_layers);
+    for (int64_t l = 0; l < L; ++l)
+      carve(c->layers[(size_t)l], host_base + l * c->layer_block);
+    TRY(c->hip(hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking),
+               "hipStreamCreateWithFlags (weight copies)"));
+    for (int i = 0; i < (c->direct_weights ? 0 : cfg->weight_slots); ++i) {
+      hipEvent_t a = nullptr, b = nullptr;
+      TRY(c->hip(hipEventCreateWithFlags(&a, hipEventDisableTiming), "hipEventCreate"));
+      c->ev_copied.push_back(a);
+      TRY(c->hip(hipEventCreateWithFlags(&b, hipEventDisableTiming), "hipEventCreate"));
+      c->ev_computed.push_back(b);
+    }
+  }
   for (auto& ly : c->layers) {
-    TRY(make_mat(ly.qkv, (hq + 2 * hkv) * hd, d, cfg->proj_dtype, "QKV"));
-    TRY(make_mat(ly.o, d, hq * hd, cfg->proj_dtype, "O"));
-    TRY(make_mat(ly.gu, 2 * f, d, cfg->proj_dtype, "gate-up"));
-    TRY(make_mat(ly.down, d, f, cfg->proj_dtype, "down"));
+    if (cfg->weight_slots == 0) {
+      TRY(make_mat(ly.qkv, (hq + 2 * hkv) * hd, d, cfg->proj_dtype, "QKV"));
+      TRY(make_mat(ly.o, d, hq * hd, cfg->proj_dtype, "O"));
+      TRY(make_mat(ly.gu, 2 * f, d, cfg->proj_dtype, "gate-up"));
+      TRY(make_mat(ly.down, d, f, cfg->proj_dtype, "down"));
+    }
     TRY(c->alloc(&ly.in_norm, d * 4, "norm"));
     TRY(c->alloc(&ly.post_norm, d * 4, "norm"));
     if (cfg->qk_norm) {
@@ -500,6 +615,7 @@ QDEC_API qdec_status qdec_create(const qdec_config* cfg, int32_t device, qdec_ct
 QDEC_API qdec_status qdec_info_get(const qdec_ctx* ctx, qdec_info* out) {
   if (!ctx || !out) return fail(nullptr, QDEC_E_INVAL, "NULL argument");
   fill_info(ctx->cfg, out);
+  out->device_bytes = ctx->device_bytes;  // what this context did allocate
   return QDEC_OK;
 }
 
@@ -573,6 +689,33 @@ static qdec_status fill_mat(qdec_ctx* c, Mat& m, const void* src, int src_dtype,
                 "convert kernel");
 }
 
+// Layer streaming: a layer's projection lives in pinned host memory.  Uploads go through the
+// same projection of slot 0 (device staging, where conversion and quantisation run), then to
+// the host copy; the call waits for both, since slot 0 is reused.
+static bool streamed(const qdec_ctx* c, int which) {
+  return !c->slots.empty() && (which == QDEC_W_QKV || which == QDEC_W_O ||
+                               which == QDEC_W_GATE_UP || which == QDEC_W_DOWN);
+}
+static Mat& stage_of(qdec_ctx* c, int which) {
+  Layer& s0 = c->slots[0];
+  return which == QDEC_W_QKV ? s0.qkv : which == QDEC_W_O ? s0.o : which == QDEC_W_GATE_UP ? s0.gu
+                                                                                          : s0.down;
+}
+static qdec_status stage_to_host(qdec_ctx* c, const Mat& stage, Mat& host, hipStream_t s) {
+  // (the host copy's address may be its device mapping: the runtime resolves the direction)
+  qdec_status st = c->hip(hipMemcpyAsync(host.data, stage.data,
+                                         (size_t)code_bytes(stage.dtype, stage.rows, stage.cols),
+                                         hipMemcpyDefault, s),
+                          "hipMemcpyAsync (streamed layer to host)");
+  if (st == QDEC_OK && stage.scale)
+    st = c->hip(hipMemcpyAsync(host.scale, stage.scale,
+                               (size_t)scale_count(stage.dtype, stage.rows, stage.cols) * 4,
+                               hipMemcpyDefault, s),
+                "hipMemcpyAsync (streamed layer scales to host)");
+  if (st == QDEC_OK) st = c->hip(hipStreamSynchronize(s), "hipStreamSynchronize (upload)");
+  return st;
+}
+
 QDEC_API qdec_status qdec_upload(qdec_ctx* c, int32_t layer, int32_t which, const void* src,
                                  int32_t src_dtype, int64_t rows, int64_t cols,
                                  int32_t src_is_device, void* stream) {
@@ -609,6 +752,13 @@ QDEC_API qdec_status qdec_upload(qdec_ctx* c, int32_t layer, int32_t which, cons
     return fail(&c->err, QDEC_E_UNSUPPORTED, "int8 rows need cols %% 16 == 0");
   if (is_grouped(m->dtype) && m->cols % kQGroup)
     return fail(&c->err, QDEC_E_UNSUPPORTED, "group-wise rows need cols %% 128 == 0");
+  if (streamed(c, which)) {
+    Mat& stage = stage_of(c, which);
+    st = fill_mat(c, stage, src, src_dtype, src_is_device, s);
+    if (st == QDEC_OK) st = stage_to_host(c, stage, *m, s);
+    if (st == QDEC_OK) c->slot(lrow, which) = 1;
+    return st;
+  }
   st = fill_mat(c, *m, src, src_dtype, src_is_device, s);
   if (st != QDEC_OK) return st;
   c->slot(lrow, which) = 1;
@@ -638,12 +788,14 @@ QDEC_API qdec_status qdec_upload_quantized(qdec_ctx* c, int32_t layer, int32_t w
   if (rows != er || cols != ec) return fail(&c->err, QDEC_E_INVAL, "shape mismatch");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = c->hip(hipSetDevice(c->device), "hipSetDevice")) != QDEC_OK) return st;
-  if ((st = copy_in(c, m->data, codes, code_bytes(m->dtype, rows, cols), src_is_device, s)) !=
+  Mat* dst = streamed(c, which) ? &stage_of(c, which) : m;
+  if ((st = copy_in(c, dst->data, codes, code_bytes(m->dtype, rows, cols), src_is_device, s)) !=
       QDEC_OK)
     return st;
-  if ((st = copy_in(c, m->scale, scales, scale_count(m->dtype, rows, cols) * 4, src_is_device,
+  if ((st = copy_in(c, dst->scale, scales, scale_count(m->dtype, rows, cols) * 4, src_is_device,
                     s)) != QDEC_OK)
     return st;
+  if (dst != m && (st = stage_to_host(c, *dst, *m, s)) != QDEC_OK) return st;
   c->slot(is_global(which) ? c->cfg.n_layers : layer, which) = 1;
   return QDEC_OK;
 }
@@ -823,11 +975,15 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
   const bool ab = c->act_bf16();
   const int wt = wt_of(k.proj_dtype);
   const Layer& ly = c->layers[(size_t)l];
+  // the projections: the layer's own, or (layer streaming) those of its slot l % N
+  const Layer& wm = (c->slots.empty() || c->direct_weights)
+                        ? ly
+                        : c->slots[(size_t)(l % (int64_t)c->slots.size())];
   switch (cls) {
     case QDEC_K_QKV: {
       GemvArgs g{};
-      g.w = ly.qkv.data;
-      g.scale = ly.qkv.scale;
+      g.w = wm.qkv.data;
+      g.scale = wm.qkv.scale;
       g.x = c->x;
       g.gamma = ly.in_norm;
       g.eps = k.rms_eps;
@@ -867,8 +1023,8 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
     }
     case QDEC_K_O_PROJ: {
       GemvArgs o{};
-      o.w = ly.o.data;
-      o.scale = ly.o.scale;
+      o.w = wm.o.data;
+      o.scale = wm.o.scale;
       o.x = c->attn;
       o.x_bf16 = ab;
       o.resid = c->x;
@@ -878,8 +1034,8 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
     }
     case QDEC_K_GATE_UP: {
       GemvArgs gu{};
-      gu.w = ly.gu.data;
-      gu.scale = ly.gu.scale;
+      gu.w = wm.gu.data;
+      gu.scale = wm.gu.scale;
       gu.x = c->x;
       gu.gamma = ly.post_norm;
       gu.eps = k.rms_eps;
@@ -892,8 +1048,8 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
     }
     case QDEC_K_DOWN: {
       GemvArgs dn{};
-      dn.w = ly.down.data;
-      dn.scale = ly.down.scale;
+      dn.w = wm.down.data;
+      dn.scale = wm.down.scale;
       dn.x = c->act;
       dn.x_bf16 = ab;
       dn.resid = c->x;
@@ -958,13 +1114,55 @@ static qdec_status enqueue_layers(qdec_ctx* c, const qdec_step* st, int pos, hip
     if ((rs = c->hip(launch_class(c, st, cls, l, grid_parts, s), #cls)) != QDEC_OK) return rs; \
     ps_.done();                                                                           \
   } while (0)
-  for (int64_t l = 0; l < c->cfg.n_layers; ++l) {
+  auto layer = [&](int64_t l) -> qdec_status {
     LAUNCH(QDEC_K_QKV, l);
     LAUNCH(QDEC_K_ATTENTION, l);
     if (graph || np > 1) LAUNCH(QDEC_K_MERGE, l);
     LAUNCH(QDEC_K_O_PROJ, l);
     LAUNCH(QDEC_K_GATE_UP, l);
     LAUNCH(QDEC_K_DOWN, l);
+    return QDEC_OK;
+  };
+  if (c->slots.empty() || c->direct_weights) {
+    for (int64_t l = 0; l < c->cfg.n_layers; ++l)
+      if ((rs = layer(l)) != QDEC_OK) return rs;
+  } else {
+    // Layer streaming ([ETE], the "Layer streaming" passage): layer l runs from slot l % N.  Its
+    // copy (host block of layer l -> slot) waits for the compute that last used the slot
+    // (buffer free: layer l - N of this step, or for the first N layers the previous step's last
+    // user of the slot), and its kernels wait for that copy (data ready).
+    offload_schedule((int)c->cfg.n_layers, (int)c->slots.size(), &c->wops);
+    for (const OffloadOp& op : c->wops) {
+      hipError_t e = hipSuccess;
+      switch (op.kind) {
+        case OFF_WAIT_FREE:
+          e = hipStreamWaitEvent(c->copy_stream, c->ev_computed[(size_t)op.slot], 0);
+          break;
+        case OFF_COPY: {
+          if (op.tile < (int)c->slots.size())  // the previous step's last use of the slot
+            e = hipStreamWaitEvent(c->copy_stream, c->ev_computed[(size_t)op.slot], 0);
+          // the library's copy kernel on 64 work-groups reads the mapped host block: enough
+          // requests in flight for the link, and a kernel launch, not a DMA transfer, between
+          // two copies
+          const Layer& dst = c->slots[(size_t)op.slot];
+          const char* src = c->host_layers_dev + op.tile * c->layer_block;
+          if (e == hipSuccess)
+            e = launch_copy(dst.qkv.data, src, c->layer_block, c->copy_stream, kSlotCopyWgs);
+          if (e == hipSuccess) e = hipEventRecord(c->ev_copied[(size_t)op.slot], c->copy_stream);
+          break;
+        }
+        case OFF_WAIT_READY:
+          e = hipStreamWaitEvent(s, c->ev_copied[(size_t)op.slot], 0);
+          break;
+        case OFF_COMPUTE:
+          if ((rs = layer(op.tile)) != QDEC_OK) return rs;
+          e = hipEventRecord(c->ev_computed[(size_t)op.slot], s);
+          break;
+        default:
+          break;
+      }
+      if ((rs = c->hip(e, "layer streaming")) != QDEC_OK) return rs;
+    }
   }
   if (st->logits_out || st->argmax_out) {
     LAUNCH(QDEC_K_LM_HEAD, 0);
@@ -1143,6 +1341,9 @@ QDEC_API qdec_status qdec_graph_reset(qdec_ctx* c) {
 
 QDEC_API qdec_status qdec_graph_capture(qdec_ctx* c, const qdec_step* templ, void* stream) {
   if (!c) return fail(nullptr, QDEC_E_INVAL, "ctx is NULL");
+  if (!c->slots.empty() && !c->direct_weights)
+    return fail(&c->err, QDEC_E_UNSUPPORTED,
+                "layer streaming (weight_slots > 0) runs its steps eagerly: no graph capture");
   qdec_status r = check_step(c, templ, false);
   if (r != QDEC_OK) return r;
   qdec_graph_reset(c);
@@ -1711,28 +1912,8 @@ QDEC_API qdec_status qdec_op_copy(void* dst, const void* src, int64_t bytes, voi
 // attention over host-resident K/V: tiles copied into device buffers, double-buffered
 // =====================================================================================
 
-namespace {
-// One record of the offload schedule (kinds as in qdec_offload_schedule).
-struct OffloadOp {
-  int kind, tile, slot, other;
-};
-enum { OFF_WAIT_FREE = 0, OFF_COPY = 1, OFF_WAIT_READY = 2, OFF_COMPUTE = 3, OFF_MERGE = 4 };
-
-// Tile i uses buffer i % n_slots.  Its copy may start once the compute of the tile that last used
-// that buffer (i - n_slots) has finished, and its compute once its own copy has finished.
-void offload_schedule(int n_tiles, int n_slots, std::vector<OffloadOp>* ops) {
-  ops->clear();
-  for (int i = 0; i < n_tiles; ++i) {
-    const int slot = i % n_slots;
-    if (i >= n_slots) ops->push_back({OFF_WAIT_FREE, i, slot, i - n_slots});
-    ops->push_back({OFF_COPY, i, slot, -1});
-    ops->push_back({OFF_WAIT_READY, i, slot, i});
-    ops->push_back({OFF_COMPUTE, i, slot, -1});
-  }
-  ops->push_back({OFF_MERGE, -1, -1, -1});
-}
-}  // namespace
-
+// (the copy / compute schedule, offload_schedule, is defined with the context above: layer
+// streaming uses it too)
 struct qdec_offload {
   qdec_offload_config cfg{};
   int part = 0;               // partition length
@@ -1941,6 +2122,14 @@ QDEC_API qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int3
     if (e != hipSuccess) return fail(nullptr, QDEC_E_HIP, "offload attention: %s", hipGetErrorString(e));
     return QDEC_OK;
   }
+  // the tiles are copied by the library's copy kernel reading the pinned pages through their
+  // device mapping (a kernel launch between two tiles instead of a DMA transfer's setup)
+  if (hipHostGetDevicePointer(&dk, const_cast<void*>(host_k), 0) != hipSuccess ||
+      hipHostGetDevicePointer(&dv, const_cast<void*>(host_v), 0) != hipSuccess || !dk || !dv ||
+      !aligned(dk, 16) || !aligned(dv, 16)) {
+    (void)hipGetLastError();
+    return fail(nullptr, QDEC_E_INVAL, "host_k and host_v must be device-mapped pinned memory");
+  }
   chk(hipEventRecord(o->start, s));
   chk(hipStreamWaitEvent(o->copy_stream, o->start, 0));
   offload_schedule(n_tiles, c.n_slots, &o->ops);
@@ -1956,10 +2145,10 @@ QDEC_API qdec_status qdec_offload_attention(qdec_offload* o, const void* q, int3
         break;
       case OFF_COPY: {
         const int64_t src = t0 / kPage * o->page_bytes, bytes = pages * o->page_bytes;
-        chk(hipMemcpyAsync(o->dev_k + op.slot * buf_bytes, static_cast<const char*>(host_k) + src,
-                           (size_t)bytes, hipMemcpyHostToDevice, o->copy_stream));
-        chk(hipMemcpyAsync(o->dev_v + op.slot * buf_bytes, static_cast<const char*>(host_v) + src,
-                           (size_t)bytes, hipMemcpyHostToDevice, o->copy_stream));
+        chk(launch_copy(o->dev_k + op.slot * buf_bytes, static_cast<const char*>(dk) + src,
+                        bytes, o->copy_stream, kSlotCopyWgs));
+        chk(launch_copy(o->dev_v + op.slot * buf_bytes, static_cast<const char*>(dv) + src,
+                        bytes, o->copy_stream, kSlotCopyWgs));
         chk(hipEventRecord(o->copied[op.slot], o->copy_stream));
         break;
       }

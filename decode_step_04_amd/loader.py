@@ -17,14 +17,17 @@ LM_ONLY_PATHS = {"bf16-w8head": Q.I8_ROW}
 
 
 def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
-               partition_size: int = 0, act: str = None, max_prefill: int = 0) -> Q.qdec_config:
+               partition_size: int = 0, act: str = None, max_prefill: int = 0,
+               weight_slots: int = 0) -> Q.qdec_config:
     """path: 'fp32' (fp32 everything), 'bf16' (bf16 weights, embedding, logits and KV), 'w8a16'
     (int8 per-row projections and LM head, bf16 embedding, logits and KV), 'w8a16g' (int8 with a
     scale per 128-value group), 'w4a16' (int4 with a scale per 128-value group) or 'bf16-w8head'
     (bf16 projections, int8 per-row LM head, bf16 embedding, logits and KV).  act: 'f32' or 'bf16',
     the precision of activations crossing op boundaries; default 'f32' for every path (the weight
     and cache formats are storage formats; activations are a few KiB per step, so their precision
-    costs no bandwidth), 'bf16' rounds them to 16 bits at every op boundary."""
+    costs no bandwidth), 'bf16' rounds them to 16 bits at every op boundary.  weight_slots: 0 keeps
+    every layer's projections in device memory; N >= 1 streams them from pinned host memory
+    through N device slots."""
     if path == "fp32":
         proj = lm = io = kv = Q.F32
         act = act or "f32"
@@ -48,7 +51,7 @@ def config_for(shape: dict, *, path: str, num_pages: int, max_context: int,
         vocab=shape["vocab"], tied_lm_head=int(shape["tied"]), qk_norm=int(shape["qk_norm"]),
         rms_eps=shape["eps"], rope_theta=shape["theta"], proj_dtype=proj, lm_head_dtype=lm,
         io_dtype=io, act_dtype=act, kv_dtype=kv, page_size=16, num_pages=num_pages, max_context=max_context,
-        partition_size=partition_size, max_prefill=max_prefill)
+        partition_size=partition_size, max_prefill=max_prefill, weight_slots=weight_slots)
 
 
 def _dt(t):

@@ -11,6 +11,10 @@ Usage (the CSV files are those rocprofv3 writes with --output-format csv):
   python -m decode_step_04_amd.profiling stats --trace run_kernel_trace.csv --n-layers 28 \
       --command "<the command that made the trace>" > summary.md
 
+  python -m decode_step_04_amd.profiling overlap --kernels run_kernel_trace.csv \
+      --copies run_memory_copy_trace.csv --title "<workload>" --command "<command>"
+      (or --copy-kernel k_copy instead of --copies when a kernel makes the copies)
+
   python -m decode_step_04_amd.profiling traffic --n-layers 28 --workload <name> \
       --fetch fetch_counter_collection.csv --write write_counter_collection.csv \
       --calib-fetch cf_counter_collection.csv --calib-write cw_counter_collection.csv \
@@ -162,6 +166,89 @@ def cmd_traffic(a):
     print(json.dumps(res, indent=1))
 
 
+def _intervals(path, name=None, exclude=None):
+    """(start, end) ns of the rows of a rocprofv3 trace CSV (kernel or memory-copy trace); for a
+    kernel trace, only the kernels whose name contains `name`, or all but those containing
+    `exclude`."""
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if not (r.get("Start_Timestamp") and r.get("End_Timestamp")):
+                continue
+            kn = r.get("Kernel_Name", "")
+            if name is not None and name not in kn:
+                continue
+            if exclude is not None and exclude in kn:
+                continue
+            out.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    return sorted(out)
+
+
+def _union(iv):
+    merged = []
+    for a, b in sorted(iv):
+        if merged and a <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], b)
+        else:
+            merged.append([a, b])
+    return merged
+
+
+def _length(m):
+    return sum(b - a for a, b in m)
+
+
+def _intersect(x, y):
+    i = j = 0
+    tot = 0
+    while i < len(x) and j < len(y):
+        a, b = max(x[i][0], y[j][0]), min(x[i][1], y[j][1])
+        if a < b:
+            tot += b - a
+        if x[i][1] < y[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def overlap(kernels, copies, skip=0.2):
+    """Copy / compute overlap over the window from the first copy to the last one, the first
+    `skip` fraction of that window dropped (warm-up): busy time of each engine (union of its
+    intervals), their intersection, and the fractions of each hidden under the other."""
+    c_all = _union(copies)
+    if not c_all:
+        return None
+    t0, t1 = c_all[0][0], c_all[-1][1]
+    t0 += int((t1 - t0) * skip)
+    clip = lambda m: [[max(a, t0), min(b, t1)] for a, b in m if b > t0 and a < t1]  # noqa: E731
+    k, c = clip(_union(kernels)), clip(c_all)
+    both = _intersect(k, c)
+    wall = t1 - t0
+    return {"window_us": wall / 1e3, "kernel_busy_us": _length(k) / 1e3,
+            "copy_busy_us": _length(c) / 1e3, "both_busy_us": both / 1e3,
+            "copy_hidden_under_kernels": both / max(1, _length(c)),
+            "kernels_hidden_under_copies": both / max(1, _length(k)),
+            "either_busy_frac": (_length(k) + _length(c) - both) / max(1, wall),
+            "copies": sum(1 for a, b in copies if b > t0 and a < t1),
+            "kernels": sum(1 for a, b in kernels if b > t0 and a < t1)}
+
+
+def cmd_overlap(a):
+    if a.copy_kernel:  # copies made by a kernel: split the kernel trace by name
+        res = overlap(_intervals(a.kernels, exclude=a.copy_kernel),
+                      _intervals(a.kernels, name=a.copy_kernel), a.skip)
+    else:
+        res = overlap(_intervals(a.kernels), _intervals(a.copies), a.skip)
+    print(f"# Copy / compute overlap: {a.title}\n\nCommand: `{a.command}`\n")
+    if res is None:
+        print("no memory copies in the trace")
+        return
+    print("| quantity | value |\n|---|---|")
+    for k, v in res.items():
+        print(f"| {k} | {v:.3f} |" if isinstance(v, float) else f"| {k} | {v} |")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -174,8 +261,16 @@ def main(argv=None):
         t.add_argument("--" + k.replace("_", "-"), required=True)
     t.add_argument("--calib-bytes", type=int, required=True)
     t.add_argument("--n-layers", type=int, required=True)
+    o = sub.add_parser("overlap")
+    o.add_argument("--kernels", required=True)
+    o.add_argument("--copies", default=None, help="memory-copy trace CSV")
+    o.add_argument("--copy-kernel", default=None,
+                   help="the copies are dispatches of this kernel in the kernel trace")
+    o.add_argument("--title", default="")
+    o.add_argument("--command", default="")
+    o.add_argument("--skip", type=float, default=0.2)
     a = p.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "overlap": cmd_overlap}[a.cmd](a)
 
 
 if __name__ == "__main__":

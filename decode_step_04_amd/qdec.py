@@ -40,7 +40,8 @@ class qdec_config(C.Structure):
                 ("lm_head_dtype", C.c_int32), ("io_dtype", C.c_int32), ("act_dtype", C.c_int32),
                 ("kv_dtype", C.c_int32),
                 ("page_size", C.c_int32), ("num_pages", C.c_int32), ("max_context", C.c_int32),
-                ("partition_size", C.c_int32), ("max_prefill", C.c_int32)]
+                ("partition_size", C.c_int32), ("max_prefill", C.c_int32),
+                ("weight_slots", C.c_int32)]
 
 
 class qdec_step(C.Structure):

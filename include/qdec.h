@@ -97,6 +97,17 @@ typedef struct qdec_config {
   int32_t max_prefill;    /* most tokens one qdec_prefill call takes (its buffers are allocated
                            * at create); 0 = no prefill.  Prefill needs bf16 projections, io and
                            * KV. */
+  int32_t weight_slots;   /* Where the layers' projections live.  0: device memory.  N in
+                           * [1, n_layers]: layer streaming ([ETE], the "Layer streaming" passage):
+                           * every layer's projections live in pinned host memory that the context
+                           * allocates, and N device slots hold N layers at a time - layer l
+                           * computes from slot l % N, a copy stream fills the slot for layer l+N
+                           * once layer l has finished with it (buffer free), and layer l's kernels
+                           * wait for their slot's copy (data ready); steps then run eagerly (no
+                           * graph capture).  -1: the same pinned host copy, read by the kernels
+                           * through its device mapping (no copies, no slots; graph capture
+                           * allowed).  Gammas, embedding and LM head stay in device memory.
+                           * Host-resident layers take no prefill (max_prefill 0). */
 } qdec_config;
 
 /* Supported dtype combinations (checked by qdec_config_validate):
@@ -160,7 +171,8 @@ typedef struct qdec_info {
   int64_t lm_head_bytes;           /* LM head as stored, scales included */
   int64_t kv_bytes_per_layer_token;
   int64_t kv_pool_bytes;           /* n_layers * 2 * num_pages * page_size * Hkv * D * elem */
-  int64_t device_bytes;            /* everything qdec_create allocates for this config */
+  int64_t device_bytes;            /* device memory qdec_create allocates for this config (from
+                                      qdec_info_get: what the context did allocate) */
   int32_t partition_tokens;        /* split-KV partition length in effect */
   int32_t max_partitions;          /* ceil(max_context / partition_tokens) */
 } qdec_info;
@@ -222,14 +234,18 @@ qdec_status qdec_info_get(const qdec_ctx* ctx, qdec_info* out);
  * (QDEC_F32 or QDEC_BF16), contiguous; rows/cols must equal the slot's shape.  `layer` selects the
  * block for per-layer slots (ignored for global ones).  A host source (src_is_device = 0) is
  * accepted only when no conversion is needed.  Uploading QDEC_W_EMBED with tied_lm_head also
- * fills the LM head (quantising it when lm_head_dtype is quantised).  Asynchronous on `stream`. */
+ * fills the LM head (quantising it when lm_head_dtype is quantised).  Asynchronous on `stream`,
+ * except for a projection of a host-resident layer (weight_slots != 0): that one is converted in
+ * device staging memory and copied to the layer's pinned host copy before the call returns, so it
+ * must not overlap a decode step. */
 qdec_status qdec_upload(qdec_ctx* ctx, int32_t layer, int32_t which, const void* src,
                         int32_t src_dtype, int64_t rows, int64_t cols, int32_t src_is_device,
                         void* stream);
 
 /* Copies pre-quantised codes and fp32 scales, in the layouts of the slot's dtype (qdec_dtype),
  * into a quantised slot (I8_ROW, I8_G128 or I4_G128); QDEC_E_INVAL for another slot dtype or a
- * shape mismatch.  Asynchronous on `stream`; a host source is copied synchronously. */
+ * shape mismatch.  Asynchronous on `stream`; a host source is copied synchronously; a projection
+ * of a host-resident layer goes through device staging to the layer's host copy, synchronously. */
 qdec_status qdec_upload_quantized(qdec_ctx* ctx, int32_t layer, int32_t which, const void* codes,
                                   const float* scales, int64_t rows, int64_t cols,
                                   int32_t src_is_device, void* stream);
@@ -239,8 +255,10 @@ qdec_status qdec_upload_i8(qdec_ctx* ctx, int32_t layer, int32_t which, const in
                            const float* scales, int64_t rows, int64_t cols, int32_t src_is_device,
                            void* stream);
 
-/* Device pointers of a stored weight slot (for read-back in tests): *data receives the matrix as
- * stored, *scales the fp32 scales (NULL unless quantised). */
+/* Pointers of a stored weight slot (for read-back in tests): *data receives the matrix as stored,
+ * *scales the fp32 scales (NULL unless quantised).  Device pointers, except for the projections
+ * of a host-resident layer (weight_slots != 0), whose storage is the context's pinned host copy
+ * (its device mapping when weight_slots = -1). */
 qdec_status qdec_weight_ptr(const qdec_ctx* ctx, int32_t layer, int32_t which, void** data,
                             float** scales);
 
