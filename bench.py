@@ -54,9 +54,11 @@ def parse():
     p.add_argument("--no-legs", action="store_true",
                    help="skip the other decode workloads (0.6B W8A16 and W8A16 LM head, 8B bf16 "
                         "and W4A16)")
-    p.add_argument("--trace", choices=["stream", "offload"], default=None,
-                   help="run only this workload (for profiler runs): layer streaming or "
-                        "attention over host-resident K/V")
+    p.add_argument("--trace", choices=["stream", "offload", "attention"], default=None,
+                   help="run only this workload (for profiler runs): layer streaming, attention "
+                        "over host-resident K/V, or the attention stress op")
+    p.add_argument("--trace-ctx", type=int, default=131072,
+                   help="context of the attention-stress trace workload")
     p.add_argument("--trace-steps", type=int, default=10)
     p.add_argument("--trace-slots", type=int, default=2)
     p.add_argument("--no-ops", action="store_true",
@@ -484,6 +486,37 @@ def trace_workload(args):
     from decode_step_04_amd import qdec as Q
 
     dev = "cuda"
+    if args.trace == "attention":
+        # the attention stress workload: 32 Q / 8 KV heads, D 128, bf16 K/V, automatic partitions
+        T = args.trace_ctx
+        q, kl, vl, bt = synth.attention_stress(T, device=dev)
+        n_pages = len(bt)
+        hkv, d = 8, 128
+        kp = torch.empty((n_pages, hkv, 16, d), dtype=torch.bfloat16, device=dev)
+        vp = torch.empty_like(kp)
+        kp.view(n_pages * hkv * 16, d)[:] = 0
+        # place logical rows through the table (device gather of the page order)
+        btd = torch.from_numpy(bt).to(dev).long()
+        kpad = torch.zeros((n_pages * 16, hkv, d), dtype=torch.bfloat16, device=dev)
+        vpad = torch.zeros_like(kpad)
+        kpad[:T] = kl
+        vpad[:T] = vl
+        kp[btd] = kpad.view(n_pages, 16, hkv, d).permute(0, 2, 1, 3)
+        vp[btd] = vpad.view(n_pages, 16, hkv, d).permute(0, 2, 1, 3)
+        ws_bytes = Q.qdec_op_attention_workspace(T, 32, d, args.partition)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        out = torch.empty((32, d), device=dev)
+        btd32 = btd.to(torch.int32)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.trace_steps):
+            Q.qdec_op_attention(q, Q.F32, kp, vp, Q.BF16, btd32, T, 32, hkv, d, args.partition,
+                                ws, ws.numel(), out, Q.F32)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / args.trace_steps
+        print(json.dumps({"trace": "attention", "context": T, "calls": args.trace_steps,
+                          "us_per_call": round(us, 2)}))
+        return
     if args.trace == "stream":
         shape, T = synth.QWEN3_0P6B, 4096
         n_pages = T // 16

@@ -109,6 +109,102 @@ __device__ __forceinline__ void combine_rows(float (&m)[G], float (&l)[G], float
   }
 }
 
+// ---- transposed scores (D = 128, bf16 K/V: 16 lanes per token, 4 tokens per lane and page) ----
+// After the per-lane partial dot products, a lane holds NV = 4G partial scores (head h, token
+// slot i at index 4h + i), each a partial sum over the lane's 8 dims.  A transpose-reduce over
+// the 16 lanes of a row halves the values at each of four lane pairings (xor 8, 7, 3, 1, deciding
+// by bit 3, 2, 1, 0 of the lane in the row which half a lane keeps), so that every lane ends
+// with complete scores of its own (head, slot) -- one softmax exponential per score instead of
+// one in each of the 16 lanes of the token.  With fewer than 16 values the last pairings are
+// plain sums, and lanes that differ only in those bits hold duplicates.
+template <int G>
+struct TrGeo {
+  static constexpr int NV = 4 * G;                                   // partial scores per lane
+  static constexpr int H = NV >= 16 ? 4 : NV == 8 ? 3 : NV == 4 ? 2 : 1;  // halving pairings
+  static constexpr int NVF = NV >> H;                                // complete scores per lane
+  static constexpr int DUP = (1 << (4 - H)) - 1;                     // duplicate-lane bits
+  static constexpr int GS = (4 / NVF) << (4 - H);                    // lanes of one head in a row
+  // lane in the row holding score index v, and its slot there
+  static constexpr int lane_of(int v) { return (v / NVF) << (4 - H); }
+  static constexpr int slot_of(int v) { return v % NVF; }
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "head groups of 1, 2, 4 or 8");
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// One pairing of the transpose-reduce over the first CNT values: lanes x and x ^ (pairing) both
+// form a + a' and b + b' for each pair (a, b) = (v[k], v[CNT/2 + k]), and keep the first when
+// `hi` is clear; with CNT <= 1 the single value is summed with its partner's.
+template <int CTRL, int CNT, int N>
+__device__ __forceinline__ void tr_step(float (&v)[N], bool hi) {
+  if constexpr (CNT > 1) {
+    constexpr int HF = CNT / 2;
+#pragma unroll
+    for (int k = 0; k < HF; ++k) {
+      const float sa = v[k] + dpp_f<CTRL>(v[k]);
+      const float sb = v[HF + k] + dpp_f<CTRL>(v[HF + k]);
+      v[k] = hi ? sb : sa;
+    }
+  } else {
+    v[0] += dpp_f<CTRL>(v[0]);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void transpose_reduce16(float (&v)[NV], int c) {
+  tr_step<0x128, NV>(v, (c & 8) != 0);        // xor 8
+  tr_step<0x141, NV / 2>(v, (c & 4) != 0);    // xor 7 (half mirror)
+  tr_step<0x1B, NV / 4>(v, (c & 2) != 0);     // xor 3 (quad mirror)
+  tr_step<0xB1, NV / 8>(v, (c & 1) != 0);     // xor 1
+}
+
+// The score of index v (head v / 4, slot v % 4) for every lane of the row: read from the lane
+// of the row that owns it (DPP row broadcast, gfx950 row_newbcast).  v is a compile-time index
+// after unrolling.
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp_f<0x150 + L>(x);
+}
+
+template <int G>
+__device__ __forceinline__ float bcast_slot(const float (&sv)[4 * G], int v) {
+  using Tg = TrGeo<G>;
+  const int ln = Tg::lane_of(v), k = Tg::slot_of(v);
+  const float x = Tg::NVF == 1 ? sv[0] : (k == 0 ? sv[0] : sv[1]);
+  switch (ln) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);
+    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);
+    case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);
+    case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);
+    default: return row_bcast<15>(x);
+  }
+}
+
+// maximum over aligned groups of GS lanes of a row (GS = 1, 2, 4, 8 or 16)
+template <int GS>
+__device__ __forceinline__ float group_max_any(float v) {
+  if constexpr (GS >= 2) v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if constexpr (GS >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if constexpr (GS >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (GS >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+
 constexpr int kAttnWaves = 4;  // waves per work-group of k_attn (8 measured slower at both shapes)
 constexpr int kAttnThreads = kAttnWaves * kWave;
 
@@ -120,6 +216,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   constexpr int NW = kAttnWaves, NT = kAttnThreads;
   constexpr int NPH = kMaxPartTokens / kPage / NW;  // block-table entries per wave, read ahead
   constexpr int QT = (G + NW - 1) / NW;             // query heads per wave in the prologue
+  // transposed scores: 128-dim bf16 pages (16 lanes per token) and head groups of 1, 2, 4, 8
+  constexpr bool TR = D == 128 && KVB && (G == 1 || G == 2 || G == 4 || G == 8);
   __shared__ float sq[G][D];        // scaled query heads
   __shared__ float skv[2][D];       // K and V of the new token (as stored)
   __shared__ float sm_acc[NW][G][D];
@@ -292,99 +390,246 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) q[h][e] = sq[h][dsub + e];
-  float m[G], l[G], acc[G][EPL];
+  // Fully unrolled page loops below: every step's code follows the previous one's with no loop
+  // back-edge, so each wait counts exactly the loads in flight (a loop makes the compiler drain
+  // all loads before entering it).  One page per step: request the wave's next page (on the last
+  // page the current one again, served by the caches, so that no load sits under a branch), then
+  // compute the current one; the two register sets alternate between the steps (copying an
+  // in-flight load's registers would make the compiler wait for it).
+  if constexpr (TR) {
+    // Transposed scores (TrGeo): each lane owns NVF complete scores -- head hL, token slots
+    // iK[k] of its row -- so the softmax runs once per score.  The running maximum of each head
+    // is shared by the whole wave (page maxima are reduced over the head's lanes and the rows),
+    // so the accumulators of the four rows need no rescaling against each other, and a page
+    // whose maxima do not grow skips the rescaling altogether (a wave-uniform branch).  The
+    // appended token (pos) is left out of the pages and folded in once afterwards.
+    using Tg = TrGeo<G>;
+    constexpr int NV = Tg::NV, NVF = Tg::NVF;
+    const int c = lane & 15;                       // lane in its 16-lane row; trow = lane >> 4
+    const int vbase = (c >> (4 - Tg::H)) * NVF;    // score index of slot 0 of this lane
+    const int hL = vbase >> 2;                     // its head
+    const bool nondup = (c & Tg::DUP) == 0;        // counts its scores (duplicates do not)
+    auto first_lane = [](int h) { return Tg::lane_of(4 * h); };
+    float mL = -1e30f, lL = 0.f, acc[G][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -1e30f;
-    l[h] = 0.f;
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    const int tlim = has_new ? pos : tok1;         // the appended token comes after the pages
 
-  // One page per step: request the wave's next page (on the last page the current one again,
-  // served by the caches, so that no load sits under a branch), then compute the current one.
-  // The two register sets alternate between the steps; copying an in-flight load's registers
-  // would make the compiler wait for it.
-  auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
-                       uint4 (&nv)[NI], int& tn, int ph1) {
-    request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
-    // scores from K first; V is still arriving (loads complete in order)
-    float s[G][NI];
+    auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
+                         uint4 (&nv)[NI], int& tn, int ph1) {
+      request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
+      // partial scores over the lane's 8 dims, then the transpose-reduce over the row
+      float sv[NV];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float kf[EPL];
-      widen16<KVB, EPL>(ck[i], kf);
-      const int tok = pg * kPage + i * TPI + trow;
-      if (has_new && tok == pos) {  // the appended slot: use the values just computed
+      for (int i = 0; i < NI; ++i) {
+        float kf[EPL];
+        widen16<KVB, EPL>(ck[i], kf);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) kf[e] = skv[0][dsub + e];
+        for (int h = 0; h < G; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
+          sv[4 * h + i] = p;
+        }
       }
+      transpose_reduce16<NV>(sv, c);
+      float pmax = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        const int tok = pg * kPage + ((vbase + k) & 3) * TPI + trow;
+        sv[k] = tok < tlim ? sv[k] : -INFINITY;
+        pmax = fmaxf(pmax, sv[k]);
+      }
+      pmax = group_max_any<Tg::GS>(pmax);
+      {
+        float lo, hi;
+        lane_pair<16>(pmax, lo, hi);
+        pmax = fmaxf(lo, hi);
+        lane_pair<32>(pmax, lo, hi);
+        pmax = fmaxf(lo, hi);
+      }
+      const float mnew = fmaxf(mL, pmax);
+      if (__builtin_amdgcn_ballot_w64(mnew > mL) != 0) {  // wave-uniform
+        const float cL = fast_exp2(mL - mnew);
+        lL *= cL;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ch = lane_value(cL, first_lane(h));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= ch;
+        }
+        mL = mnew;
+      }
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        sv[k] = fast_exp2(sv[k] - mL);
+        lL += sv[k];
+      }
+      // P V: the probability of (head h, slot i) comes from the lane of the row that owns it
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vf[EPL];
+        widen16<KVB, EPL>(cv[i], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pb = bcast_slot<G>(sv, 4 * h + i);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pb, vf[e], acc[h][e]);
+        }
+      }
+      pg += NW;
+    };
+#pragma unroll
+    for (int jj = 0; jj < NPH; ++jj) {
+      if (pg >= pg1) break;
+      const int ph1 = jj + 1 < NPH ? phys[jj + 1 < NPH ? jj + 1 : 0] : 0;
+      if (jj % 2 == 0)
+        page_step(k0, v0, t0, k1, v1, t1, ph1);
+      else
+        page_step(k1, v1, t1, k0, v0, t0, ph1);
+    }
+    // the appended token, folded into wave 0's state (its K and V as stored, from LDS)
+    if (has_new && wave == 0) {
+      float sh[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float p = 0.f;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
-        p = lanes_sum<LPT>(p);
-        s[h][i] = (tok < tok1) ? p : -INFINITY;
+        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], skv[0][dsub + e], p);
+        sh[h] = lanes_sum<16>(p);
+      }
+      float sL = sh[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) sL = hL == h ? sh[h] : sL;
+      const float mnew = fmaxf(mL, sL);
+      const float cL = fast_exp2(mL - mnew), pL = fast_exp2(sL - mnew);
+      lL = fmaf(lL, cL, lane == first_lane(hL) ? pL : 0.f);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ch = lane_value(cL, first_lane(h));
+        const float ph = trow == 0 ? lane_value(pL, first_lane(h)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(acc[h][e], ch, ph * skv[1][dsub + e]);
+      }
+      mL = mnew;
+    }
+    // the four rows share each head's maximum: their accumulators add up as they are
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float lo, hi;
+        lane_pair<16>(acc[h][e], lo, hi);
+        lane_pair<32>(lo + hi, lo, hi);
+        acc[h][e] = lo + hi;
+      }
+    float lh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) lh[h] = wave_sum(hL == h && nondup ? lL : 0.f);
+    if (trow == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_acc[wave][h][dsub + e] = acc[h][e];
       }
     }
+    if (lane == 0) {
 #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm_m[wave][h] = lane_value(mL, first_lane(h));
+        sm_l[wave][h] = lh[h];
+      }
+    }
+  } else {
+    float m[G], l[G], acc[G][EPL];
+  #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float mx = m[h];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, s[h][i]);
-      const float c = fast_exp2(m[h] - mx);
-      l[h] *= c;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        s[h][i] = fast_exp2(s[h][i] - mx);
-        l[h] += s[h][i];
-      }
-      m[h] = mx;
+      m[h] = -1e30f;
+      l[h] = 0.f;
+  #pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float vf[EPL];
-      widen16<KVB, EPL>(cv[i], vf);
-      const int tok = pg * kPage + i * TPI + trow;
-      if (has_new && tok == pos) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vf[e] = skv[1][dsub + e];
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[h][i], vf[e], acc[h][e]);
-    }
-    pg += NW;
-  };
-  // Fully unrolled over the at most NPH pages of the wave: every step's code follows the
-  // previous one's with no loop back-edge, so each wait counts exactly the loads in flight (a
-  // loop makes the compiler drain all loads before entering it).
-#pragma unroll
-  for (int jj = 0; jj < NPH; ++jj) {
-    if (pg >= pg1) break;
-    const int ph1 = jj + 1 < NPH ? phys[jj + 1 < NPH ? jj + 1 : 0] : 0;
-    if (jj % 2 == 0)
-      page_step(k0, v0, t0, k1, v1, t1, ph1);
-    else
-      page_step(k1, v1, t1, k0, v0, t0, ph1);
-  }
 
-  // combine the token rows of the wave (lanes with equal dims), exact rescaling
-  if constexpr (LPT <= 8) combine_rows<8, G, EPL>(m, l, acc);
-  if constexpr (LPT <= 16) combine_rows<16, G, EPL>(m, l, acc);
-  combine_rows<32, G, EPL>(m, l, acc);
-  if (trow == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][h][dsub + e] = acc[h][e];
-      if (lane == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
+    auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
+                         uint4 (&nv)[NI], int& tn, int ph1) {
+      request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
+      // scores from K first; V is still arriving (loads complete in order)
+      float s[G][NI];
+  #pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float kf[EPL];
+        widen16<KVB, EPL>(ck[i], kf);
+        const int tok = pg * kPage + i * TPI + trow;
+        if (has_new && tok == pos) {  // the appended slot: use the values just computed
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) kf[e] = skv[0][dsub + e];
+        }
+  #pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float p = 0.f;
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
+          p = lanes_sum<LPT>(p);
+          s[h][i] = (tok < tok1) ? p : -INFINITY;
+        }
+      }
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float mx = m[h];
+  #pragma unroll
+        for (int i = 0; i < NI; ++i) mx = fmaxf(mx, s[h][i]);
+        const float c = fast_exp2(m[h] - mx);
+        l[h] *= c;
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= c;
+  #pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          s[h][i] = fast_exp2(s[h][i] - mx);
+          l[h] += s[h][i];
+        }
+        m[h] = mx;
+      }
+  #pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vf[EPL];
+        widen16<KVB, EPL>(cv[i], vf);
+        const int tok = pg * kPage + i * TPI + trow;
+        if (has_new && tok == pos) {
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) vf[e] = skv[1][dsub + e];
+        }
+  #pragma unroll
+        for (int h = 0; h < G; ++h)
+  #pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[h][i], vf[e], acc[h][e]);
+      }
+      pg += NW;
+    };
+  #pragma unroll
+    for (int jj = 0; jj < NPH; ++jj) {
+      if (pg >= pg1) break;
+      const int ph1 = jj + 1 < NPH ? phys[jj + 1 < NPH ? jj + 1 : 0] : 0;
+      if (jj % 2 == 0)
+        page_step(k0, v0, t0, k1, v1, t1, ph1);
+      else
+        page_step(k1, v1, t1, k0, v0, t0, ph1);
+    }
+
+    // combine the token rows of the wave (lanes with equal dims), exact rescaling
+    if constexpr (LPT <= 8) combine_rows<8, G, EPL>(m, l, acc);
+    if constexpr (LPT <= 16) combine_rows<16, G, EPL>(m, l, acc);
+    combine_rows<32, G, EPL>(m, l, acc);
+    if (trow == 0) {
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+  #pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_acc[wave][h][dsub + e] = acc[h][e];
+        if (lane == 0) {
+          sm_m[wave][h] = m[h];
+          sm_l[wave][h] = l[h];
+        }
       }
     }
   }
