@@ -634,6 +634,13 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
     // fewer than kStreamLoads loads per round (short int8 rows): request the next round ahead
     // so that a wave still keeps about that many in flight
     p.pipe = kStreamPipe || p.r * pairs * p.maxch < kStreamLoads * lmul;
+    // a streamed bf16 gate-up pair: one row pair per wave with the next round requested ahead
+    // (measured on the 8B-class gate-up, 24576 x 4096: 34.8 against 36.4 us for two pairs per
+    // wave without lookahead; the single-row LM head is faster without it, 205 against 229 us)
+    if (wtype == W_BF16 && pairs == 2) {
+      p.r = 1;
+      p.pipe = true;
+    }
     wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
     if (wgs > kStreamWgs) wgs = kStreamWgs;
   } else {
