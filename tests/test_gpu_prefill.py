@@ -115,6 +115,18 @@ def test_prefill_attention_matches_oracle(d, hq, hkv, pos0, P):
     of the same bf16 q, K and V per query.  Bar: the output is rounded to bf16 and the
     probabilities are rounded to bf16 as the second product's operand, so |got - ref| <=
     2^-7 |ref| + 4e-3 (values ~N(0, 1))."""
+    _check_prefill_attention(d, hq, hkv, pos0, P)
+
+
+@pytest.mark.parametrize("d,hq,hkv", [(128, 16, 8), (128, 32, 8)])
+@pytest.mark.parametrize("pos0,P", [(0, 2048), (3000, 1000), (0, 4097)])
+def test_prefill_attention_long_prompts(d, hq, hkv, pos0, P):
+    """Prompts of many query blocks (paired heavy with light in one work-group) over contexts
+    of several page chunks, at the same bar."""
+    _check_prefill_attention(d, hq, hkv, pos0, P)
+
+
+def _check_prefill_attention(d, hq, hkv, pos0, P):
     print(f"prefill attention d={d} hq={hq} hkv={hkv} pos0={pos0} P={P}", flush=True)
     T = pos0 + P
     g = torch.Generator(device=DEV).manual_seed(T * 7 + d + hq + P)
