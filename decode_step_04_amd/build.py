@@ -24,7 +24,9 @@ SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
            ("gemv.hip", "gemv_i4g", ["-DQD_GEMV_PART=4"]),
            ("gemv.hip", "gemv_dispatch", ["-DQD_GEMV_PART=-1"]),
            ("attention.hip", "attention", []), ("misc.hip", "misc", []),
-           ("prefill.hip", "prefill", []), ("sample.hip", "sample", []),
+           ("prefill.hip", "prefill", []),
+           ("prefill_attn.hip", "prefill_attn", ["-mno-amdgpu-ieee", "-fno-honor-nans"]),
+           ("sample.hip", "sample", []),
            ("runtime.hip", "runtime", [])]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

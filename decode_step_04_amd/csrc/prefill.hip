@@ -26,7 +26,6 @@ namespace qd {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float pf_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8 load_frag(const uint16_t* p) {
@@ -374,235 +373,6 @@ hipError_t launch_prefill_rope(int head_dim, const PrefillRopeArgs& a, hipStream
   else
     hipLaunchKernelGGL((k_prefill_rope<128>), grid, dim3(64), 0, s, a);
   return hipGetLastError();
-}
-
-// ---- causal GQA attention of P new tokens over the paged cache, on the matrix cores --------------
-// FlashAttention-style ([ETE], the batched-prefill next step; the (m, l, acc) state of
-// [Qwen3-runtime] §9.1 / [ETE] online softmax, per query row).  A wave owns 16 rows, each a
-// (query, head of the KV group) pair, query-major; a work-group of 4 waves takes 64 rows of kv
-// head g (BQ = 64 / G queries).  Keys go in blocks of 64 (four pages): every thread loads 16-byte
-// chunks of K and V two blocks ahead into registers and writes them row-major into one of two LDS
-// buffers; one barrier per block.
-//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = 16 keys x 32 dims of K from LDS (16 contiguous
-//     bytes per lane), B = the wave's 16 query rows (held in registers).  Lane l receives keys
-//     4(l/16) + e of each 16-key tile for query row l % 16, so each lane holds 16 of the block's
-//     64 keys for one row: the row maximum and sum are 16 local values and two lane swaps
-//     (v_permlane16/32_swap), and the rescale of a row's accumulator uses the lane's own factor.
-//   P = 2^(S - m) is rounded to bf16 (the MFMA operand type; the denominator adds the rounded
-//     values, so O / l stays a normalised average) and is already the B operand of
-//     O^T += V^T P^T: lane l's 8 values of a 32-key half are keys 4(l/16) + e and 16 + 4(l/16) + e,
-//     and the A operand (V^T, 16 dims x the same 8 keys) comes from the row-major V tile through
-//     ds_read_b64_tr_b16.  In each 16-lane group that instruction returns to lane i element
-//     i % 4 of the 8 bytes addressed by lane 4e + i / 4, as its e-th value (checked on MI355X):
-//     lanes 4e .. 4e+3 address the 16 dims of key row e, so lane i gets dim i of 4 key rows.
-//   The output O^T lands with lane l holding dims 4(l/16) + e of query row l % 16.
-// A work-group takes query blocks nb-1-x and x (the causal work of the pair is the same for every
-// x), heaviest first; the work-group index runs kv head fastest, so with 8 XCDs dispatched round
-// robin one kv head's work-groups share an XCD (and its L2 copy of that head's K and V).
-// LDS rows are D + 8 bf16 (272 bytes for D = 128): the 16-byte fragment reads of 16 consecutive
-// key rows and the 8-byte transposed reads of 16 key rows fall in distinct bank groups.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
-  constexpr int BQ = 64 / G;     // queries per query block
-  constexpr int ROWS = BQ * G;   // active rows (64 unless G does not divide 64)
-  constexpr int KB = 64;         // keys per block
-  constexpr int KS = D / 32;     // MFMA k-steps over D
-  constexpr int ND = D / 16;     // 16-dim tiles of the output
-  constexpr int KP = D + 8;      // LDS row stride of K and V, in bf16
-  constexpr int CPK = D / 8;     // 16-byte chunks per key row
-  constexpr int CL = KB * CPK / 256;  // chunks of K (and of V) per thread per block
-  __shared__ __align__(16) uint16_t kt[2][KB][KP];
-  __shared__ __align__(16) uint16_t vt[2][KB][KP];
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int r16 = lane & 15, q4 = lane >> 4;
-  const int hq = a.n_q_heads, hkv = a.n_kv_heads;
-  const int g = (int)(blockIdx.x % (unsigned)hkv);
-  const int x = (int)(blockIdx.x / (unsigned)hkv);
-  const int nb = (a.p + BQ - 1) / BQ;
-  const float NEG = -INFINITY;
-  const int64_t head_stride = (int64_t)kPage * D;  // one head's page tile, in elements
-  const int row = wave * 16 + r16;                 // this lane's query row in the block
-
-  for (int pass = 0; pass < 2; ++pass) {
-    const int qb = pass == 0 ? nb - 1 - x : x;
-    if (pass == 1) {
-      if (qb >= nb - 1 - x) break;  // an odd count's middle block runs once (uniform)
-      __syncthreads();              // every wave is done with the LDS tiles of the first block
-    }
-    const int t0 = qb * BQ;
-    const int nq = min(BQ, a.p - t0);              // valid queries of the block (>= 1)
-    const int kend = a.pos0 + t0 + nq;             // keys 0 .. kend-1 are visible
-    const int last = kend - 1;
-    const int qfirst = a.pos0 + t0;                // position of the block's first query
-    const bool active = row < ROWS && row / G < nq;
-    const int qpos = active ? qfirst + row / G : -1;   // an inactive row sees no key
-    bf8 qf[KS];
-    {
-      const int qa = min(row < ROWS ? row / G : 0, nq - 1), ha = row % G;
-      const uint16_t* qrow = a.q + ((int64_t)(t0 + qa) * hq + g * G + ha) * D + 8 * q4;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = load_frag(qrow + 32 * ks);
-    }
-    // m: the row's running maximum (log2 units); lp: this lane's part of the row's denominator
-    float m = -1e30f, lp = 0.f;
-    f32x4 o[ND];
-#pragma unroll
-    for (int nd = 0; nd < ND; ++nd) o[nd] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nblk = (kend + KB - 1) / KB;
-    // page numbers without a memory round trip in the loop: lane l holds page l of the current
-    // chunk of 64 pages (16 blocks); the next chunk is loaded a whole chunk ahead.  Pages past the
-    // last visible one are clamped to it (every entry below npages is valid).
-    const int npages = (kend + kPage - 1) / kPage;
-    int pc = a.block_table[min(lane, npages - 1)], pn = 0;
-    // this thread's chunk u of a block: 16 bytes at dim 8 (idx % CPK) of key idx / CPK, idx =
-    // t + 256 u; keys past `last` are clamped.  A wave's chunks lie in one page, so the page
-    // number is a wave-uniform read of the lane-held chunk.
-    u32x4 kc0[CL], vc0[CL], kc1[CL], vc1[CL];
-    auto fetch = [&](int kb, u32x4 (&kc)[CL], u32x4 (&vc)[CL]) __attribute__((always_inline)) {
-      const int key0 = kb * KB;
-#pragma unroll
-      for (int u = 0; u < CL; ++u) {
-        const int idx = t + 256 * u, kl = idx / CPK, c = idx % CPK;
-        const int key = min(key0 + kl, last);
-        const int pidx = __builtin_amdgcn_readfirstlane(key / kPage) & 63;
-        const int64_t ph = __builtin_amdgcn_readlane(pc, pidx);
-        const int64_t off = (ph * hkv + g) * head_stride + (int64_t)(key % kPage) * D + 8 * c;
-        kc[u] = *reinterpret_cast<const u32x4*>(a.k_pool + off);
-        vc[u] = *reinterpret_cast<const u32x4*>(a.v_pool + off);
-      }
-    };
-    auto stage = [&](int buf, const u32x4 (&kc)[CL], const u32x4 (&vc)[CL])
-                     __attribute__((always_inline)) {
-#pragma unroll
-      for (int u = 0; u < CL; ++u) {
-        const int idx = t + 256 * u, kl = idx / CPK, c = idx % CPK;
-        *reinterpret_cast<u32x4*>(&kt[buf][kl][8 * c]) = kc[u];
-        *reinterpret_cast<u32x4*>(&vt[buf][kl][8 * c]) = vc[u];
-      }
-    };
-    auto block = [&](int kb, u32x4 (&kc)[CL], u32x4 (&vc)[CL]) __attribute__((always_inline)) {
-      const int key0 = kb * KB;
-      const int buf = kb & 1;
-      if ((kb & 15) == 0 && kb + 16 < nblk)   // wave-uniform
-        pn = a.block_table[min(((kb >> 4) + 1) * 64 + lane, npages - 1)];
-      if (((kb + 2) & 15) == 0) pc = pn;       // the block fetched next opens a new chunk
-      stage(buf, kc, vc);
-      if (kb + 2 < nblk) fetch(kb + 2, kc, vc);
-      __syncthreads();
-      // S^T for the four 16-key tiles
-      f32x4 sc[4];
-#pragma unroll
-      for (int kt4 = 0; kt4 < 4; ++kt4) {
-        sc[kt4] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          sc[kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              load_frag(&kt[buf][16 * kt4 + r16][32 * ks + 8 * q4]), qf[ks], sc[kt4], 0, 0, 0);
-      }
-      // online softmax of row `row` over keys key0 + 16 kt4 + 4 q4 + e: the maximum on the
-      // unscaled scores (qscale > 0), the scale folded into the exponent's fma
-      if (key0 + KB - 1 > qfirst) {
-#pragma unroll
-        for (int kt4 = 0; kt4 < 4; ++kt4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (key0 + 16 * kt4 + 4 * q4 + e > qpos) sc[kt4][e] = NEG;
-      }
-      float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
-#pragma unroll
-      for (int kt4 = 1; kt4 < 4; ++kt4)
-        mx = fmaxf(mx, fmaxf(fmaxf(sc[kt4][0], sc[kt4][1]), fmaxf(sc[kt4][2], sc[kt4][3])));
-      float lo, hi;
-      lane_pair<16>(mx, lo, hi);
-      mx = fmaxf(lo, hi);
-      lane_pair<32>(mx, lo, hi);
-      mx = fmaxf(lo, hi) * a.qscale;
-      const float mn = fmaxf(m, mx);
-      const float corr = pf_exp2(m - mn);
-      const bool grew = mn != m;
-      m = mn;
-      bf8 pb[2];
-      float ps = 0.f;
-#pragma unroll
-      for (int kt4 = 0; kt4 < 4; ++kt4)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const __bf16 b = (__bf16)pf_exp2(fmaf(sc[kt4][e], a.qscale, -mn));
-          pb[kt4 >> 1][4 * (kt4 & 1) + e] = b;
-          ps += (float)b;
-        }
-      lp = fmaf(lp, corr, ps);
-      if (__ballot(grew) != 0) {  // wave-uniform; when no row's maximum grew every factor is 1
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) o[nd] *= corr;
-      }
-      // O^T += V^T P^T, one 32-key half at a time
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kr = 32 * h + 4 * q4 + (r16 >> 2);
-#pragma unroll
-        for (int nd = 0; nd < ND; ++nd) {
-          const int dc = 16 * nd + 4 * (r16 & 3);
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(&vt[buf][kr][dc]));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(&vt[buf][kr + 16][dc]));
-          const bf8 va = __builtin_bit_cast(
-              bf8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[h], o[nd], 0, 0, 0);
-        }
-      }
-    };
-    fetch(0, kc0, vc0);
-    if (nblk > 1) fetch(1, kc1, vc1);
-    for (int kb = 0; kb < nblk; kb += 2) {
-      block(kb, kc0, vc0);
-      if (kb + 1 >= nblk) break;
-      block(kb + 1, kc1, vc1);
-    }
-
-    float lo, hi;
-    lane_pair<16>(lp, lo, hi);
-    const float l2 = lo + hi;
-    lane_pair<32>(l2, lo, hi);
-    const float lsum = lo + hi;
-    if (active) {
-      const float inv = 1.0f / lsum;
-      uint16_t* orow = a.out + ((int64_t)(t0 + row / G) * hq + g * G + row % G) * D + 4 * q4;
-#pragma unroll
-      for (int nd = 0; nd < ND; ++nd) {
-        uint2 w;
-        w.x = (uint32_t)f32_to_bf16(o[nd][0] * inv) | ((uint32_t)f32_to_bf16(o[nd][1] * inv) << 16);
-        w.y = (uint32_t)f32_to_bf16(o[nd][2] * inv) | ((uint32_t)f32_to_bf16(o[nd][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + 16 * nd) = w;
-      }
-    }
-  }
-}
-
-template <int D>
-static hipError_t launch_pa(int group, const PrefillAttnArgs& a, hipStream_t s) {
-  const unsigned hk = (unsigned)a.n_kv_heads;
-  switch (group) {
-#define QD_PA(G)                                                                           \
-  case G:                                                                                  \
-    hipLaunchKernelGGL((k_prefill_attn<D, G>),                                             \
-                       dim3((unsigned)(((a.p + 64 / G - 1) / (64 / G) + 1) / 2) * hk), dim3(256), \
-                       0, s, a);                                                           \
-    break;
-    QD_PA(1) QD_PA(2) QD_PA(3) QD_PA(4) QD_PA(5) QD_PA(6) QD_PA(7) QD_PA(8)
-#undef QD_PA
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_prefill_attn(int head_dim, int group, const PrefillAttnArgs& a, hipStream_t s) {
-  if (a.p <= 0) return hipSuccess;
-  return head_dim == 64 ? launch_pa<64>(group, a, s) : launch_pa<128>(group, a, s);
 }
 
 }  // namespace qd
