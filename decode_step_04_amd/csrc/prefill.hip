@@ -130,27 +130,32 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
-// k_gemm_lds: the same product and epilogues with the operand tiles staged in LDS.  A work-group
-// of 4 waves computes BM rows (128 or 64) against BN weight rows (128 or 64): per K step of 64 it
-// loads A[BM x 64] and W[BN x 64] into one of two LDS buffers (16-byte loads, 8 threads per
-// 128-byte row segment) while the MFMAs read the other; one barrier per step.  The next step's
-// loads are issued before the current step's MFMAs and stored after them.  At most 54 KB of LDS
-// and ~180 registers keep two work-groups on a CU, so one's load latency hides under the other's
-// MFMAs.  LDS rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of any 8
-// consecutive lanes (rows r .. r+7 at one k offset) fall in distinct banks.  Wave w owns rows
-// (w / 2) BM/2 .. +BM/2-1 and weight rows (w % 2) BN/2 .. +BN/2-1 of the tile.  For SWIGLU a wave's
-// BN/2 weight rows are BN/4 gate rows and the matching BN/4 up rows, so g and u of an output meet
-// in the same lanes.
-template <int EPI, int BM, int BN>
+// k_gemm_lds: the same product and epilogues with the operand tiles staged in LDS, on
+// v_mfma_f32_32x32x16_bf16 (on MI355X it sustains about 1.3x the rate of the 16x16x32 form: 2.15
+// against 1.62 PFLOP/s in a register-only loop).  For one 32 x 32 x 16 step lane l supplies
+// A[row l % 32][k 8(l/32) .. +7] and W[row l % 32][k 8(l/32) .. +7] and receives
+// C[row 8(r/4) + 4(l/32) + r % 4][col l % 32], r < 16 (layout checked on MI355X).  A work-group
+// of 4 waves computes BM rows (128 or 64) against BN weight rows (128 or 64) in K steps of 64.
+// Each thread moves 16-byte chunks (8 threads per 128-byte row segment) of A[BM x 64] and
+// W[BN x 64]: a step's chunks are requested PF steps ahead into one of PF register sets and
+// written into one of two LDS buffers the step before their MFMAs; one barrier per step.  LDS
+// rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of 16 consecutive rows at
+// one k offset fall in distinct banks.  Wave w owns rows (w / 2) BM/2 .. +BM/2-1 and weight rows
+// (w % 2) BN/2 .. +BN/2-1 of the tile.  For SWIGLU (BN = 128) a wave's 64 weight rows are 32 gate
+// rows and the matching 32 up rows, so g and u of an output meet in the same lanes.
+template <int EPI, int BM, int BN, int PF>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   constexpr int BK = 64, LDR = BK + 8;
   constexpr int WM = BM / 2, WN = BN / 2;   // rows and weight rows per wave
-  constexpr int NI = WM / 16, NJ = WN / 16; // their 16-row blocks
+  constexpr int NI = WM / 32, NJ = WN / 32; // their 32-row blocks
   constexpr int AL = BM * BK / 8 / 256;     // 16-byte loads per thread per step
   constexpr int BL = BN * BK / 8 / 256;
+  static_assert(EPI != EPI_SWIGLU || NJ == 2, "SWIGLU pairs one gate and one up block per wave");
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
   __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * LDR];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * LDR];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int M = a.m, N = a.n, K = a.k;
   const int m0 = blockIdx.y * BM;
   const int nout = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per work-group
@@ -169,82 +174,98 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
       return min(n0 + row, N - 1);
     }
   };
-  u32x4 ra[AL], rb[BL];
-  auto gload = [&](int k) __attribute__((always_inline)) {
+  const uint16_t* pa[AL];
+  const uint16_t* pb[BL];
+#pragma unroll
+  for (int r = 0; r < AL; ++r) pa[r] = A + (int64_t)min(m0 + trow + 32 * r, M - 1) * K + tkc;
+#pragma unroll
+  for (int r = 0; r < BL; ++r) pb[r] = W + (int64_t)wrow(trow + 32 * r) * K + tkc;
+  u32x4 ra[PF][AL], rb[PF][BL];
+  auto gload = [&](int set, int kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < AL; ++r) ra[set][r] = *reinterpret_cast<const u32x4*>(pa[r] + kt * BK);
+#pragma unroll
+    for (int r = 0; r < BL; ++r) rb[set][r] = *reinterpret_cast<const u32x4*>(pb[r] + kt * BK);
+  };
+  auto lstore = [&](int set, int st) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < AL; ++r)
-      ra[r] = *reinterpret_cast<const u32x4*>(
-          A + (int64_t)min(m0 + trow + 32 * r, M - 1) * K + k + tkc);
+      *reinterpret_cast<u32x4*>(&sa[st][(trow + 32 * r) * LDR + tkc]) = ra[set][r];
 #pragma unroll
     for (int r = 0; r < BL; ++r)
-      rb[r] = *reinterpret_cast<const u32x4*>(W + (int64_t)wrow(trow + 32 * r) * K + k + tkc);
+      *reinterpret_cast<u32x4*>(&sb[st][(trow + 32 * r) * LDR + tkc]) = rb[set][r];
   };
-  auto lstore = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int r = 0; r < AL; ++r)
-      *reinterpret_cast<u32x4*>(&sa[st][(trow + 32 * r) * LDR + tkc]) = ra[r];
-#pragma unroll
-    for (int r = 0; r < BL; ++r)
-      *reinterpret_cast<u32x4*>(&sb[st][(trow + 32 * r) * LDR + tkc]) = rb[r];
-  };
-  f32x4 acc[NI][NJ];
+  f32x16 acc[NI][NJ];
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int arow = (wave >> 1) * WM + r16, brow = (wave & 1) * WN + r16;
-  const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  const int r32 = lane & 31, kq = (lane >> 5) * 8;
+  const int arow = (wave >> 1) * WM + r32, brow = (wave & 1) * WN + r32;
+  auto compute = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
+    for (int ks = 0; ks < BK; ks += 16) {
       bf16x8 fa[NI], fb[NJ];
 #pragma unroll
       for (int i = 0; i < NI; ++i)
         fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               &sa[st][(arow + 16 * i) * LDR + ks + kq]));
+                                               &sa[st][(arow + 32 * i) * LDR + ks + kq]));
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         fb[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                               &sb[st][(brow + 16 * j) * LDR + ks + kq]));
+                                               &sb[st][(brow + 32 * j) * LDR + ks + kq]));
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(st ^ 1);
-    __syncthreads();
+  };
+  // step kt lives in register set kt % PF from its request until it is written to LDS; steps
+  // 0 .. PF-1 are requested first, step 0 goes to LDS, and its set takes step PF
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+    if (s < nk) gload(s, s);
+  lstore(0, 0);
+  if (PF < nk) gload(0, PF);
+  __syncthreads();
+  for (int k0 = 0; k0 < nk; k0 += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int kt = k0 + s;
+      if (kt >= nk) break;
+      compute(kt & 1);
+      const int nx = kt + 1, set = (s + 1) % PF;   // step nx is in register set nx % PF
+      if (nx < nk) {
+        lstore(set, nx & 1);
+        if (nx + PF < nk) gload(set, nx + PF);
+      }
+      __syncthreads();
+    }
   }
 
-  // epilogue: lane holds C[row 16 i + 4 (l/16) + e of the wave][weight row 16 j + l % 16]
+  // epilogue: lane holds C[row 32 i + 8 (r/4) + 4 (l/32) + r % 4 of the wave][weight row
+  // 32 j + l % 32]
   const int mw = m0 + (wave >> 1) * WM;
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int m = mw + 16 * i + 4 * (lane >> 4) + e;
+    for (int r = 0; r < 16; ++r) {
+      const int m = mw + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (m >= M) continue;
       if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
-          const int n = n0 + (wave & 1) * (WN / 2) + 16 * j + r16;
-          if (n >= N) continue;
-          const float g = acc[i][j][e], u = acc[i][j + NJ / 2][e];
-          const float v = g / (1.0f + expf(-g)) * u;
-          static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
-        }
+        const int n = n0 + (wave & 1) * (WN / 2) + r32;
+        if (n >= N) continue;
+        const float g = acc[i][0][r], u = acc[i][1][r];
+        const float v = g / (1.0f + expf(-g)) * u;
+        static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
       } else {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int n = n0 + (wave & 1) * WN + 16 * j + r16;
+          const int n = n0 + (wave & 1) * WN + 32 * j + r32;
           if (n >= N) continue;
-          const float v = acc[i][j][e];
+          const float v = acc[i][j][r];
           if constexpr (EPI == EPI_RESID)
             a.resid[(int64_t)m * N + n] += v;
           else if (a.y_bf16)
@@ -257,7 +278,8 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   }
 }
 
-// The largest tile that still gives two work-groups per CU (512), else the smallest.
+// The largest tile that still gives two work-groups per CU (512), else the smallest (SWIGLU tiles
+// keep 128 weight rows: 64 gate and 64 up).
 template <int EPI>
 static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
   const int64_t wide = EPI == EPI_SWIGLU ? 2 : 1;  // weight rows per output column
@@ -267,12 +289,20 @@ static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
   auto grid = [&](int bm, int bn) {
     return dim3((unsigned)((a.n * wide + bn - 1) / bn), (unsigned)((a.m + bm - 1) / bm));
   };
-  if (wgs(128, 128) >= 512)
-    hipLaunchKernelGGL((k_gemm_lds<EPI, 128, 128>), grid(128, 128), dim3(256), 0, s, a);
-  else if (wgs(64, 128) >= 512)
-    hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128>), grid(64, 128), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 64>), grid(64, 64), dim3(256), 0, s, a);
+#ifdef QD_GEMM_SWEEP
+  QD_GEMM_SWEEP
+#endif
+  if (EPI == EPI_SWIGLU || wgs(128, 128) >= 512) {
+    if (EPI == EPI_SWIGLU && wgs(128, 128) < 512)
+      hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128, 1>), grid(64, 128), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_lds<EPI, 128, 128, 1>), grid(128, 128), dim3(256), 0, s, a);
+  } else if constexpr (EPI != EPI_SWIGLU) {
+    if (wgs(64, 128) >= 512)
+      hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128, 1>), grid(64, 128), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 64, 1>), grid(64, 64), dim3(256), 0, s, a);
+  }
 }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
