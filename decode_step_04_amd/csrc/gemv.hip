@@ -660,8 +660,9 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
     // over R = 2/4/8, 512-4096 work-groups and both round modes for six matrix shapes)
     const bool big = wbytes > kStreamBytes;
     const int64_t cap = big ? 2048 : 1024;
-    // rows of three or more chunks per wave (K >= 8192 split four ways): one row per wave,
-    // the next round requested ahead (measured 8.8 against 9.5 us at 4096 x 12288)
+    // wave slices of three or more 1024-value chunks (over 2048 values, e.g. K = 12288 split four
+    // ways): one row per wave, the next round requested ahead (measured 8.8 against 9.5 us at
+    // 4096 x 12288)
     for (p.r = p.maxch >= 3 ? 1 : big ? 4 : 2;; p.r /= 2) {  // fewer when over the budget
       const int64_t need = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
       wgs = need < cap ? need : cap;
