@@ -161,14 +161,6 @@ struct GemvArgs {
 };
 
 // Prefill GEMM Y[m x n] = A[m x k] . W[n x k]^T with bf16 A and W (row-major, k contiguous).
-struct GemmArgs {
-  const void* a;          // [m x k] bf16
-  const void* w;          // [n x k] bf16 ([2n x k] for SwiGLU: gate rows, then up rows)
-  void* y;                // EPI_STORE: [m x n] fp32 or bf16; EPI_SWIGLU: [m x n] bf16
-  int32_t y_bf16;
-  float* resid;           // EPI_RESID: resid[m x n] += A W^T
-  int32_t m, n, k;        // k % 32 == 0
-};
 
 struct AttnArgs {
   // fused (model) path: the query heads and the new K/V come from the QKV projection output
@@ -230,6 +222,16 @@ struct PrefillRopeArgs {
   uint16_t* v_pool;
   const int32_t* block_table;
   int32_t pos0, p, n_q_heads, n_kv_heads;
+};
+
+struct GemmArgs {
+  const void* a;          // [m x k] bf16
+  const void* w;          // [n x k] bf16 ([2n x k] for SwiGLU: gate rows, then up rows)
+  void* y;                // EPI_STORE: [m x n] fp32 or bf16; EPI_SWIGLU: [m x n] bf16
+  int32_t y_bf16;
+  float* resid;           // EPI_RESID: resid[m x n] += A W^T
+  int32_t m, n, k;        // k % 32 == 0
+  PrefillRopeArgs rope;   // EPI_ROPE: where the rows go (its qkv field is unused)
 };
 
 struct PrefillAttnArgs {

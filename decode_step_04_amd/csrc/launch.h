@@ -11,7 +11,9 @@
 
 namespace qd {
 
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+// EPI_ROPE (prefill QKV, head_dim 128): the Q/K norm, RoPE and paged K/V append of
+// k_prefill_rope applied to each 128-column tile (one head) of the product in the epilogue
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_ROPE = 3 };
 
 // The RMSNorm prologue stages x * gamma in LDS: norm GEMVs take inputs of at most this length.
 constexpr int64_t kGemvNormMaxK = 16384;

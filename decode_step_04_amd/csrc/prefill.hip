@@ -130,6 +130,67 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
   }
 }
 
+// EPI_ROPE epilogue: the product tile (BM tokens x one 128-dim head of the QKV row) goes to LDS;
+// wave w then takes tokens w BM/4 .. +BM/4-1, lane l the RoPE pair (l, l + 64), and stores Q as
+// bf16 rows or K / V into the paged pool, as k_prefill_rope does (the same operations in the
+// same order, so the values are identical).
+template <int BM, int BN, int WM, int WN, int NI, int NJ, typename Acc>
+__device__ __forceinline__ void rope_epilogue(const GemmArgs& a, const Acc (&acc)[NI][NJ],
+                                              float* tile, int m0, int n0, int wave, int lane) {
+  constexpr int TS = BN + 4, HALF = 64, D = 128;
+  const int r32 = lane & 31;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (wave >> 1) * WM + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = (wave & 1) * WN + 32 * j + r32;
+        tile[row * TS + col] = acc[i][j][r];
+      }
+  __syncthreads();
+  const PrefillRopeArgs& ra = a.rope;
+  const int hq = ra.n_q_heads, hkv = ra.n_kv_heads;
+  const int hh = n0 / D;               // head of the QKV row: Q heads, then K, then V
+  const bool is_q = hh < hq, is_v = hh >= hq + hkv;
+  const int g = is_q ? 0 : (is_v ? hh - hq - hkv : hh - hq);
+  const float* gam = is_v ? nullptr : (is_q ? ra.q_gamma : ra.k_gamma);
+  const float g0 = gam != nullptr ? gam[lane] : 0.f, g1 = gam != nullptr ? gam[lane + HALF] : 0.f;
+  for (int rr = wave * (BM / 4); rr < (wave + 1) * (BM / 4); ++rr) {
+    const int t = m0 + rr;
+    if (t >= a.m) break;  // wave-uniform
+    float x0 = tile[rr * TS + lane], x1 = tile[rr * TS + lane + HALF];
+    const int pos = ra.pos0 + t;
+    if (is_v) {
+      const int64_t phys = ra.block_table[pos / kPage];
+      const int64_t off = ((phys * hkv + g) * kPage + pos % kPage) * D + lane;
+      ra.v_pool[off] = f32_to_bf16(x0);
+      ra.v_pool[off + HALF] = f32_to_bf16(x1);
+      continue;
+    }
+    if (gam != nullptr) {
+      const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
+      const float rinv = 1.0f / sqrtf(ss / (float)D + ra.eps);
+      x0 = x0 * rinv * g0;
+      x1 = x1 * rinv * g1;
+    }
+    const float2 cs = reinterpret_cast<const float2*>(ra.table)[(int64_t)pos * HALF + lane];
+    const float y0 = x0 * cs.x - x1 * cs.y;
+    const float y1 = x1 * cs.x + x0 * cs.y;
+    if (is_q) {
+      const int64_t o = ((int64_t)t * hq + hh) * D + lane;
+      ra.q_out[o] = f32_to_bf16(y0);
+      ra.q_out[o + HALF] = f32_to_bf16(y1);
+    } else {
+      const int64_t phys = ra.block_table[pos / kPage];
+      const int64_t off = ((phys * hkv + g) * kPage + pos % kPage) * D + lane;
+      ra.k_pool[off] = f32_to_bf16(y0);
+      ra.k_pool[off + HALF] = f32_to_bf16(y1);
+    }
+  }
+}
+
 // k_gemm_lds: the same product and epilogues with the operand tiles staged in LDS, on
 // v_mfma_f32_32x32x16_bf16 (on MI355X it sustains about 1.3x the rate of the 16x16x32 form: 2.15
 // against 1.62 PFLOP/s in a register-only loop).  For one 32 x 32 x 16 step lane l supplies
@@ -142,7 +203,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 // rows are padded to 72 bf16 (144 bytes): the 16-byte fragment reads of 16 consecutive rows at
 // one k offset fall in distinct banks.  Wave w owns rows (w / 2) BM/2 .. +BM/2-1 and weight rows
 // (w % 2) BN/2 .. +BN/2-1 of the tile.  For SWIGLU (BN = 128) a wave's 64 weight rows are 32 gate
-// rows and the matching 32 up rows, so g and u of an output meet in the same lanes.
+// rows and the matching 32 up rows, so g and u of an output meet in the same lanes.  For ROPE
+// (BN = 128 = head_dim) the fp32 tile is staged in LDS and each wave takes BM / 4 of its rows
+// (tokens), one at a time, with the lane layout and arithmetic of k_prefill_rope.
 template <int EPI, int BM, int BN, int PF>
 __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   constexpr int BK = 64, LDR = BK + 8;
@@ -150,10 +213,14 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   constexpr int NI = WM / 32, NJ = WN / 32; // their 32-row blocks
   constexpr int AL = BM * BK / 8 / 256;     // 16-byte loads per thread per step
   constexpr int BL = BN * BK / 8 / 256;
+  constexpr int TS = BN + 4;                // ROPE: fp32 row stride of the staged tile
   static_assert(EPI != EPI_SWIGLU || NJ == 2, "SWIGLU pairs one gate and one up block per wave");
+  static_assert(EPI != EPI_ROPE || BN == 128, "ROPE tiles are one 128-dim head");
+  static_assert(EPI != EPI_ROPE || BM * TS * 4 <= 2 * (BM + BN) * LDR * 2, "ROPE tile in LDS");
   typedef float f32x16 __attribute__((ext_vector_type(16)));
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][BN * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * LDR];
+  uint16_t (*sa)[BM * LDR] = reinterpret_cast<uint16_t (*)[BM * LDR]>(smem);
+  uint16_t (*sb)[BN * LDR] = reinterpret_cast<uint16_t (*)[BN * LDR]>(smem + 2 * BM * LDR);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int M = a.m, N = a.n, K = a.k;
@@ -245,6 +312,11 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
     }
   }
 
+  if constexpr (EPI == EPI_ROPE) {
+    rope_epilogue<BM, BN, WM, WN, NI, NJ>(a, acc, reinterpret_cast<float*>(smem), m0, n0, wave,
+                                          lane);
+    return;
+  }
   // epilogue: lane holds C[row 32 i + 8 (r/4) + 4 (l/32) + r % 4 of the wave][weight row
   // 32 j + l % 32]
   const int mw = m0 + (wave >> 1) * WM;
@@ -292,12 +364,12 @@ static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
 #ifdef QD_GEMM_SWEEP
   QD_GEMM_SWEEP
 #endif
-  if (EPI == EPI_SWIGLU || wgs(128, 128) >= 512) {
-    if (EPI == EPI_SWIGLU && wgs(128, 128) < 512)
+  if (EPI == EPI_SWIGLU || EPI == EPI_ROPE || wgs(128, 128) >= 512) {
+    if ((EPI == EPI_SWIGLU || EPI == EPI_ROPE) && wgs(128, 128) < 512)
       hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128, 1>), grid(64, 128), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((k_gemm_lds<EPI, 128, 128, 1>), grid(128, 128), dim3(256), 0, s, a);
-  } else if constexpr (EPI != EPI_SWIGLU) {
+  } else if constexpr (EPI != EPI_SWIGLU && EPI != EPI_ROPE) {
     if (wgs(64, 128) >= 512)
       hipLaunchKernelGGL((k_gemm_lds<EPI, 64, 128, 1>), grid(64, 128), dim3(256), 0, s, a);
     else
@@ -312,10 +384,15 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
     switch (epi) {
       case EPI_STORE: launch_gemm_lds<EPI_STORE>(a, s); break;
       case EPI_RESID: launch_gemm_lds<EPI_RESID>(a, s); break;
+      case EPI_ROPE:
+        if (a.n % 128) return hipErrorInvalidValue;
+        launch_gemm_lds<EPI_ROPE>(a, s);
+        break;
       default: launch_gemm_lds<EPI_SWIGLU>(a, s); break;
     }
     return hipGetLastError();
   }
+  if (epi == EPI_ROPE) return hipErrorInvalidValue;
   const int ncols = epi == EPI_SWIGLU ? 64 : 128;
   const dim3 grid((unsigned)((a.n + ncols - 1) / ncols), (unsigned)((a.m + 127) / 128));
   switch (epi) {

@@ -1249,7 +1249,6 @@ QDEC_API qdec_status qdec_prefill(qdec_ctx* c, const int32_t* token_ids, int32_t
     g.y_bf16 = 0;
     g.n = nqkv;
     g.k = d;
-    P_TRY(launch_gemm(EPI_STORE, g, s), "prefill qkv gemm");
     PrefillRopeArgs pr{};
     pr.qkv = c->pqkv;
     pr.q_gamma = ly.q_norm;
@@ -1264,7 +1263,13 @@ QDEC_API qdec_status qdec_prefill(qdec_ctx* c, const int32_t* token_ids, int32_t
     pr.p = n;
     pr.n_q_heads = hq;
     pr.n_kv_heads = hkv;
-    P_TRY(launch_prefill_rope(hd, pr, s), "prefill rope/append");
+    if (hd == 128 && d % 64 == 0) {  // one 128-column tile per head: norm, RoPE, append in the epilogue
+      g.rope = pr;
+      P_TRY(launch_gemm(EPI_ROPE, g, s), "prefill qkv gemm + rope/append");
+    } else {
+      P_TRY(launch_gemm(EPI_STORE, g, s), "prefill qkv gemm");
+      P_TRY(launch_prefill_rope(hd, pr, s), "prefill rope/append");
+    }
     PrefillAttnArgs pa{};
     pa.q = static_cast<const uint16_t*>(c->pq);
     pa.k_pool = static_cast<const uint16_t*>(ly.k_pool);
