@@ -131,9 +131,11 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
 }
 
 // EPI_ROPE epilogue: the product tile (BM tokens x one 128-dim head of the QKV row) goes to LDS;
-// wave w then takes tokens w BM/4 .. +BM/4-1, lane l the RoPE pair (l, l + 64), and stores Q as
-// bf16 rows or K / V into the paged pool, as k_prefill_rope does (the same operations in the
-// same order, so the values are identical).
+// wave w then takes tokens w BM/4 .. +BM/4-1.  The RMSNorm sums of squares of those rows are
+// split over the lanes (64 / (BM/4) lanes per row, each a contiguous slice, then combined), so
+// each row's 1/sqrt is computed once; then row by row lane l takes the RoPE pair (l, l + 64) with
+// the row's factor read from the lane that holds it, and stores Q as bf16 rows or K / V into the
+// paged pool (the operations of k_prefill_rope, the sum of squares in another order).
 template <int BM, int BN, int WM, int WN, int NI, int NJ, typename Acc>
 __device__ __forceinline__ void rope_epilogue(const GemmArgs& a, const Acc (&acc)[NI][NJ],
                                               float* tile, int m0, int n0, int wave, int lane) {
@@ -157,34 +159,57 @@ __device__ __forceinline__ void rope_epilogue(const GemmArgs& a, const Acc (&acc
   const int g = is_q ? 0 : (is_v ? hh - hq - hkv : hh - hq);
   const float* gam = is_v ? nullptr : (is_q ? ra.q_gamma : ra.k_gamma);
   const float g0 = gam != nullptr ? gam[lane] : 0.f, g1 = gam != nullptr ? gam[lane + HALF] : 0.f;
-  for (int rr = wave * (BM / 4); rr < (wave + 1) * (BM / 4); ++rr) {
-    const int t = m0 + rr;
+  // every row's (cos, sin) and page number are requested before the first row is processed
+  // (rows past the end read the last row's, and store nothing)
+  constexpr int RPW = BM / 4;
+  constexpr int LPR = 64 / RPW, SPAN = D / LPR;   // lanes per row, columns per lane
+  const int r0 = wave * RPW;
+  float2 cs[RPW];
+  int pg[RPW];
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int pos = ra.pos0 + min(m0 + r0 + q, a.m - 1);
+    cs[q] = reinterpret_cast<const float2*>(ra.table)[(int64_t)pos * HALF + lane];
+    pg[q] = ra.block_table[pos / kPage];
+  }
+  // lane l sums the squares of columns (l / RPW) SPAN .. +SPAN-1 of row r0 + l % RPW; the LPR
+  // partial sums of a row are combined (lanes l, l + RPW, ...) and lane q < RPW keeps row q's
+  // 1 / rms
+  float rinv = 1.f;
+  if (gam != nullptr) {  // uniform
+    const float* tr = tile + (r0 + (lane % RPW)) * TS + (lane / RPW) * SPAN;
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < SPAN; ++c) ss = fmaf(tr[c], tr[c], ss);
+    if constexpr (LPR >= 4) ss += __shfl_xor(ss, 2 * RPW);
+    ss += __shfl_xor(ss, RPW);
+    rinv = 1.0f / sqrtf(ss / (float)D + ra.eps);
+  }
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) {
+    const int rr = r0 + q, t = m0 + rr;
     if (t >= a.m) break;  // wave-uniform
     float x0 = tile[rr * TS + lane], x1 = tile[rr * TS + lane + HALF];
     const int pos = ra.pos0 + t;
+    const int64_t off = (((int64_t)pg[q] * hkv + g) * kPage + pos % kPage) * D + lane;
     if (is_v) {
-      const int64_t phys = ra.block_table[pos / kPage];
-      const int64_t off = ((phys * hkv + g) * kPage + pos % kPage) * D + lane;
       ra.v_pool[off] = f32_to_bf16(x0);
       ra.v_pool[off + HALF] = f32_to_bf16(x1);
       continue;
     }
     if (gam != nullptr) {
-      const float ss = wave_sum(fmaf(x0, x0, x1 * x1));
-      const float rinv = 1.0f / sqrtf(ss / (float)D + ra.eps);
-      x0 = x0 * rinv * g0;
-      x1 = x1 * rinv * g1;
+      const float ri = __builtin_bit_cast(
+          float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rinv), q));
+      x0 = x0 * ri * g0;
+      x1 = x1 * ri * g1;
     }
-    const float2 cs = reinterpret_cast<const float2*>(ra.table)[(int64_t)pos * HALF + lane];
-    const float y0 = x0 * cs.x - x1 * cs.y;
-    const float y1 = x1 * cs.x + x0 * cs.y;
+    const float y0 = x0 * cs[q].x - x1 * cs[q].y;
+    const float y1 = x1 * cs[q].x + x0 * cs[q].y;
     if (is_q) {
       const int64_t o = ((int64_t)t * hq + hh) * D + lane;
       ra.q_out[o] = f32_to_bf16(y0);
       ra.q_out[o + HALF] = f32_to_bf16(y1);
     } else {
-      const int64_t phys = ra.block_table[pos / kPage];
-      const int64_t off = ((phys * hkv + g) * kPage + pos % kPage) * D + lane;
       ra.k_pool[off] = f32_to_bf16(y0);
       ra.k_pool[off + HALF] = f32_to_bf16(y1);
     }
