@@ -134,6 +134,52 @@ __device__ __forceinline__ float dot16(typename WTraits<WT>::Vec w, const float*
   return acc;
 }
 
+// Wave sums of NR = 1, 2, 4 or 8 per-lane values at once: lane l receives the sum over all 64
+// lanes of v[l / (64 / NR)].  Each halving stage keeps half the rows per lane and adds the
+// partner's copy: v_permlane32_swap(A, B) leaves A's lower and B's lower half in the first result
+// and A's upper and B's upper half in the second, so their sum is A's pair sum in lanes 0-31 and
+// B's in lanes 32-63 (v_permlane16_swap the same for 16-lane rows, a DPP rotate by 8 for the last
+// stage); the rest is an ordinary sum over the 64 / NR lanes of a group.  NR rows cost about
+// 1.25 NR + 4 operations instead of NR full reductions.
+template <int NR>
+__device__ __forceinline__ float reduce_rows(float (&v)[NR]) {
+  static_assert(NR == 1 || NR == 2 || NR == 4 || NR == 8, "rows per reduction");
+  if constexpr (NR == 1) {
+    return wave_sum(v[0]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NR / 2; ++k) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[k]),
+                                                      __float_as_uint(v[k + NR / 2]), false, false);
+      v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (NR >= 4) {
+#pragma unroll
+      for (int k = 0; k < NR / 4; ++k) {
+        const auto r = __builtin_amdgcn_permlane16_swap(
+            __float_as_uint(v[k]), __float_as_uint(v[k + NR / 4]), false, false);
+        v[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+    }
+    if constexpr (NR == 8) {  // lanes with bit 3 clear keep v[0], the others v[1]
+      const bool hi8 = (__lane_id() & 8) != 0;
+      const float recv = dpp<0x128>(hi8 ? v[0] : v[1]);
+      v[0] = (hi8 ? v[1] : v[0]) + recv;
+    }
+    float t = v[0];
+    if constexpr (NR == 2) {
+      t = group_sum<16>(t);
+      float lo, hi;
+      lane_pair<16>(t, lo, hi);
+      return lo + hi;
+    } else if constexpr (NR == 4) {
+      return group_sum<16>(t);
+    } else {
+      return group_sum<8>(t);
+    }
+  }
+}
+
 __device__ __forceinline__ bool argmax_better(float vb, int ib, float va, int ia) {
   if (ib < 0) return false;
   if (ia < 0) return true;
@@ -251,9 +297,13 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
       }
     }
   };
-  // epilogue operands of lane r's row in group gg (lanes >= R read row 0 of the group)
+  // after the row reduction lane l holds row l / GL of the round (reduce_rows); lane r GL takes
+  // row r of the group, and lanes that hold no gate row read row 0
+  constexpr int GL = kWave / NR;
+  const int myrow = lane / GL;
+  // epilogue operands of this lane's row in group gg
   auto load_epi = [&](int64_t gg, float& res, float& s1, float& s2) {
-    const int64_t row = row_of(gg, lane < R ? lane : 0);
+    const int64_t row = row_of(gg, myrow < R ? myrow : 0);
     if constexpr (EPI == EPI_RESID) res = a.resid[row];
     if constexpr (WT == W_I8) {
       s1 = a.scale[row];
@@ -444,37 +494,27 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) acc[r] *= 0x1p24f;
     }
-    float tot[NR];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) tot[r] = wave_sum(acc[r]);
+    float mine = reduce_rows<NR>(acc);  // this lane: the total of row myrow of the round
     if (split > 1) {
-      if (lane == 0)
-#pragma unroll
-        for (int r = 0; r < NR; ++r) red_acc[wave][r] = tot[r];
+      if (lane % GL == 0) red_acc[wave][myrow] = mine;
       __syncthreads();
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float t = 0.f;
-        for (int s2 = 0; s2 < split; ++s2) t += red_acc[grp * split + s2][r];
-        tot[r] = t;
-      }
+      float t = 0.f;
+      for (int s2 = 0; s2 < split; ++s2) t += red_acc[grp * split + s2][myrow];
+      mine = t;
       // red_acc is reused by the work-group's next round, if it has one (uniform: every wave of
       // the work-group runs the same rounds)
       if ((rnd + gridDim.x) * gpw < ngroups) __syncthreads();
     }
-    // lane r takes row r of the group
-    float vg = tot[0], vu = 0.f;
-#pragma unroll
-    for (int r = 1; r < R; ++r)
-      if (lane == r) vg = tot[r];
+    // lane r GL takes row r of the group; for SWIGLU the up row R + r is 32 lanes further on
+    float vg = mine, vu = 0.f;
     if constexpr (EPI == EPI_SWIGLU) {
-      vu = tot[R];
-#pragma unroll
-      for (int r = 1; r < R; ++r)
-        if (lane == r) vu = tot[R + r];
+      float lo, hi;
+      lane_pair<32>(mine, lo, hi);
+      vg = lo;
+      vu = hi;
     }
-    const int64_t row = gg * R + lane;
-    if (active && sub == 0 && lane < R && row < n) {
+    const int64_t row = gg * R + myrow;
+    if (active && sub == 0 && lane % GL == 0 && myrow < R && row < n) {
       float v = vg;
       if constexpr (WT == W_I8) v *= c_s1;
       if constexpr (EPI == EPI_SWIGLU) {
