@@ -633,6 +633,7 @@ constexpr int64_t kStreamBytes = int64_t(64) << 20;
 constexpr int64_t kStreamWgs = 512;
 constexpr bool kStreamPipe = false;
 constexpr int kStreamLoads = 8;
+constexpr int64_t kStreamInFlight = int64_t(16) << 20;
 constexpr int64_t kI4Bytes = int64_t(4) << 20;  // int4 matrices above this take their own plan
 
 static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
@@ -682,7 +683,17 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
       p.pipe = true;
     }
     wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
-    if (wgs > kStreamWgs) wgs = kStreamWgs;
+    int64_t cap = kStreamWgs;
+    if (wtype == W_I8) {
+      // per-row int8: enough work-groups for about kStreamInFlight bytes of rows in flight (a
+      // work-group round reads gpw row groups of R rows, two rounds with lookahead).  Measured
+      // on 130560 x 1536 (no lookahead): 512 work-groups (12 MiB) 37.3 us, 768 34.3 us, 1024
+      // 35.5 us; 151936 x 1024 (lookahead, 16 MiB at 512) is fastest at 512
+      const int64_t per_wg = (int64_t)gpw * p.r * pairs * (k * bits / 8) * (p.pipe ? 2 : 1);
+      cap = (kStreamInFlight / per_wg + 128) / 256 * 256;
+      cap = cap < kStreamWgs ? kStreamWgs : cap > 2 * kStreamWgs ? 2 * kStreamWgs : cap;
+    }
+    if (wgs > cap) wgs = cap;
   } else {
     p.r = pick_r(16);
     wgs = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
