@@ -20,14 +20,19 @@
 //     rotates K of head g, stores K and V at (bt[pos/16], pos%16) -- the paged append -- and uses
 //     the same values in registers for that slot.
 //   - Page loop ([Qwen3-runtime] §10.1-10.2): each wave takes every 4th page; a 16 x D page tile
-//     of one head is contiguous and read with one 16-byte load per lane per 1 KiB, so lane l
-//     holds EPL consecutive dims of one token per load (token row l / LPT).  Scores are reduced
-//     over the LPT lanes of a token with DPP; each token row keeps fp32 (m, l, acc) per head
-//     ([ETE], the online-softmax passage) and all G heads use the same K/V registers, so each
-//     K/V byte is read once for the whole query group ([Qwen3-runtime] §2.5).
-//   - Rows, then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With one partition
-//     the normalised output is written directly (the short path of §10.1); otherwise the
-//     unnormalised state goes to scratch for k_attn_merge.
+//     of one head is contiguous, read with 16-byte loads (non-temporal: every byte is used once,
+//     so it is not kept in the caches), and all G heads use the same K/V registers, so each K/V
+//     byte is read once for the whole query group ([Qwen3-runtime] §2.5).  fp32 (m, l, acc)
+//     state per head ([ETE], the online-softmax passage).
+//       * D = 128 with bf16 K/V and G = 1, 2, 4 or 8 (the model shapes): the dot products run on
+//         the matrix cores, with the fp32 query and probabilities each split into two bf16
+//         parts (the comment at the loop gives the layout).
+//       * Other shapes (fp32 K/V, D = 64, other G): lane l holds EPL consecutive dims of one
+//         token per load (token row l / LPT); scores are reduced over the LPT lanes of a token
+//         with DPP and each token row keeps its own state.
+//   - Rows (generic path), then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With
+//     one partition the normalised output is written directly (the short path of §10.1);
+//     otherwise the unnormalised state goes to scratch for k_attn_merge.
 // k_attn_merge: one work-group per (query head, 32 dims): M = max m_p, w_p = 2^(m_p - M),
 // out = sum w_p acc_p / sum w_p l_p.
 //
@@ -72,6 +77,13 @@ __device__ __forceinline__ void widen16(const uint4 w, float (&f)[EPL]) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Matrix-core operands (bf16 K/V, D = 128)
+typedef __bf16 mf_bf8 __attribute__((ext_vector_type(8)));
+typedef short mf_s4 __attribute__((ext_vector_type(4)));
+typedef float mf_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mf_u4 __attribute__((ext_vector_type(4)));
+
+
 // Per-head RMSNorm (when `norm`) and rotate-half RoPE of one D-vector by one wave; lane l holds
 // the pair (x0, x1) = (v[l], v[l + D/2]) and its gammas (g0, g1) (zeros for l >= D/2) and gets
 // the rotated pair.
@@ -109,122 +121,49 @@ __device__ __forceinline__ void combine_rows(float (&m)[G], float (&l)[G], float
   }
 }
 
-// ---- transposed scores (D = 128, bf16 K/V: 16 lanes per token, 4 tokens per lane and page) ----
-// After the per-lane partial dot products, a lane holds NV = 4G partial scores (head h, token
-// slot i at index 4h + i), each a partial sum over the lane's 8 dims.  A transpose-reduce over
-// the 16 lanes of a row halves the values at each of four lane pairings (xor 8, 7, 3, 1, deciding
-// by bit 3, 2, 1, 0 of the lane in the row which half a lane keeps), so that every lane ends
-// with complete scores of its own (head, slot) -- one softmax exponential per score instead of
-// one in each of the 16 lanes of the token.  With fewer than 16 values the last pairings are
-// plain sums, and lanes that differ only in those bits hold duplicates.
-template <int G>
-struct TrGeo {
-  static constexpr int NV = 4 * G;                                   // partial scores per lane
-  static constexpr int H = NV >= 16 ? 4 : NV == 8 ? 3 : NV == 4 ? 2 : 1;  // halving pairings
-  static constexpr int NVF = NV >> H;                                // complete scores per lane
-  static constexpr int DUP = (1 << (4 - H)) - 1;                     // duplicate-lane bits
-  static constexpr int GS = (4 / NVF) << (4 - H);                    // lanes of one head in a row
-  // lane in the row holding score index v, and its slot there
-  static constexpr int lane_of(int v) { return (v / NVF) << (4 - H); }
-  static constexpr int slot_of(int v) { return v % NVF; }
-  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "head groups of 1, 2, 4 or 8");
-};
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// One pairing of the transpose-reduce over the first CNT values: lanes x and x ^ (pairing) both
-// form a + a' and b + b' for each pair (a, b) = (v[k], v[CNT/2 + k]), and keep the first when
-// `hi` is clear; with CNT <= 1 the single value is summed with its partner's.
-template <int CTRL, int CNT, int N>
-__device__ __forceinline__ void tr_step(float (&v)[N], bool hi) {
-  if constexpr (CNT > 1) {
-    constexpr int HF = CNT / 2;
-#pragma unroll
-    for (int k = 0; k < HF; ++k) {
-      const float sa = v[k] + dpp_f<CTRL>(v[k]);
-      const float sb = v[HF + k] + dpp_f<CTRL>(v[HF + k]);
-      v[k] = hi ? sb : sa;
-    }
-  } else {
-    v[0] += dpp_f<CTRL>(v[0]);
-  }
-}
-
-template <int NV>
-__device__ __forceinline__ void transpose_reduce16(float (&v)[NV], int c) {
-  tr_step<0x128, NV>(v, (c & 8) != 0);        // xor 8
-  tr_step<0x141, NV / 2>(v, (c & 4) != 0);    // xor 7 (half mirror)
-  tr_step<0x1B, NV / 4>(v, (c & 2) != 0);     // xor 3 (quad mirror)
-  tr_step<0xB1, NV / 8>(v, (c & 1) != 0);     // xor 1
-}
-
-// The score of index v (head v / 4, slot v % 4) for every lane of the row: read from the lane
-// of the row that owns it (DPP row broadcast, gfx950 row_newbcast).  v is a compile-time index
-// after unrolling.
-template <int L>
-__device__ __forceinline__ float row_bcast(float x) {
-  return dpp_f<0x150 + L>(x);
-}
-
-template <int G>
-__device__ __forceinline__ float bcast_slot(const float (&sv)[4 * G], int v) {
-  using Tg = TrGeo<G>;
-  const int ln = Tg::lane_of(v), k = Tg::slot_of(v);
-  const float x = Tg::NVF == 1 ? sv[0] : (k == 0 ? sv[0] : sv[1]);
-  switch (ln) {
-    case 0: return row_bcast<0>(x);
-    case 1: return row_bcast<1>(x);
-    case 2: return row_bcast<2>(x);
-    case 3: return row_bcast<3>(x);
-    case 4: return row_bcast<4>(x);
-    case 5: return row_bcast<5>(x);
-    case 6: return row_bcast<6>(x);
-    case 7: return row_bcast<7>(x);
-    case 8: return row_bcast<8>(x);
-    case 9: return row_bcast<9>(x);
-    case 10: return row_bcast<10>(x);
-    case 11: return row_bcast<11>(x);
-    case 12: return row_bcast<12>(x);
-    case 13: return row_bcast<13>(x);
-    case 14: return row_bcast<14>(x);
-    default: return row_bcast<15>(x);
-  }
-}
-
-// maximum over aligned groups of GS lanes of a row (GS = 1, 2, 4, 8 or 16)
-template <int GS>
-__device__ __forceinline__ float group_max_any(float v) {
-  if constexpr (GS >= 2) v = fmaxf(v, dpp_f<kDppXor1>(v));
-  if constexpr (GS >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
-  if constexpr (GS >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
-  if constexpr (GS >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
-  return v;
-}
-
 constexpr int kAttnWaves = 4;  // waves per work-group of k_attn (8 measured slower at both shapes)
 constexpr int kAttnThreads = kAttnWaves * kWave;
 
+// The matrix-core page loop of the plain (not fused) kernel fits in 128 registers for groups of
+// 1, 2 and 4: four work-groups per CU instead of three (long contexts launch more than three per
+// CU).  The fused kernel would spill at that bound, and G = 8 is held to three by its LDS.
 template <int D, bool KVB, int G, bool FUSED>
-__global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
+constexpr int attn_waves_per_simd() {
+  return !FUSED && D == 128 && KVB && (G == 1 || G == 2 || G == 4) ? 4 : 1;
+}
+
+template <int D, bool KVB, int G, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((
+    amdgpu_waves_per_eu(attn_waves_per_simd<D, KVB, G, FUSED>()))) void k_attn(AttnArgs a) {
   using Gm = Geo<D, KVB>;
   constexpr int EPL = Gm::EPL, LPT = Gm::LPT, TPI = Gm::TPI, NI = Gm::NI, ELEM = Gm::ELEM;
   constexpr int HALF = D / 2;
   constexpr int NW = kAttnWaves, NT = kAttnThreads;
   constexpr int NPH = kMaxPartTokens / kPage / NW;  // block-table entries per wave, read ahead
   constexpr int QT = (G + NW - 1) / NW;             // query heads per wave in the prologue
-  // transposed scores: 128-dim bf16 pages (16 lanes per token) and head groups of 1, 2, 4, 8
-  constexpr bool TR = D == 128 && KVB && (G == 1 || G == 2 || G == 4 || G == 8);
+  // matrix-core pages: 128-dim bf16 pages and head groups of 1, 2, 4 or 8
+  constexpr bool MF = D == 128 && KVB && (G == 1 || G == 2 || G == 4 || G == 8);
+  constexpr int VROW = D + 16;      // LDS row of a staged V page, in bf16 (288 bytes)
   __shared__ float sq[G][D];        // scaled query heads
+  __shared__ __attribute__((aligned(16))) uint16_t svp[MF ? NW * kPage * VROW : 1];
+  // matrix-core pages: the scaled query heads split into bf16 hi = bf16(q) and lo = bf16(q - hi)
+  __shared__ __attribute__((aligned(16))) uint16_t sqb[MF ? G : 1][2][D];
+  auto put_q = [&](int h, int d, float x) {
+    sq[h][d] = x;
+    if constexpr (MF) {
+      const uint16_t hb = f32_to_bf16(x);
+      sqb[h][0][d] = hb;
+      sqb[h][1][d] = f32_to_bf16(x - bf16_to_f32(hb));
+    }
+  };
   __shared__ float skv[2][D];       // K and V of the new token (as stored)
   __shared__ float sm_acc[NW][G][D];
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index as a scalar: its block-table entries, pages and token ranges are then
+  // wave-uniform values (scalar loads and registers, uniform branches)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hkv = a.n_kv_heads;
   const int g = blockIdx.x % hkv;
   const int pi = blockIdx.x / hkv;
@@ -311,17 +250,25 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   int t0, t1;  // physical page of each set
   int pg = pg_first + wave;
   const int gh = live ? g : 0;
+  // Matrix-core pages read K as the A operand of v_mfma_f32_16x16x32_bf16: load ks of lane l is
+  // token l % 16, dims 32 ks + 8 (l / 16) .. + 7 (64 contiguous bytes per token and load).
+  const int64_t kmf = ((int64_t)(lane & 15) * D + 8 * (lane >> 4)) * ELEM;
   // The address is computed from a page number chosen by a select (not a select of two
   // addresses), so the compiler cannot fold a re-request into a copy of another set's registers.
+  // Non-temporal loads: each byte of the pages is read once (measured 10 % faster at 128K
+  // positions than cached loads).
+  auto load16 = [](const char* p) {
+    const mf_u4 x = __builtin_nontemporal_load(reinterpret_cast<const mf_u4*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+  };
   auto request = [&](uint4 (&kd)[NI], uint4 (&vd)[NI], int& td, int ph) {
     td = ph;
     const int64_t tile = ((int64_t)ph * hkv + gh) * tile_bytes;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      kd[i] = *reinterpret_cast<const uint4*>(kbase + tile + (int64_t)(i * kWave + lane) * 16);
+      kd[i] = load16(kbase + tile + (MF ? kmf + 64 * i : (int64_t)(i * kWave + lane) * 16));
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      vd[i] = *reinterpret_cast<const uint4*>(vbase + tile + (int64_t)(i * kWave + lane) * 16);
+    for (int i = 0; i < NI; ++i) vd[i] = load16(vbase + tile + (int64_t)(i * kWave + lane) * 16);
   };
   // a surplus partition reads page 0 of head 0 (cached after the first), not HBM
   request(k0, v0, t0, live ? phys[0] : 0);
@@ -348,8 +295,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         y1 = round_bf16(y1);
       }
       if (h < G && lane < HALF) {
-        sq[h][lane] = y0 * a.qscale;
-        sq[h][lane + HALF] = y1 * a.qscale;
+        put_q(h, lane, y0 * a.qscale);
+        put_q(h, lane + HALF, y1 * a.qscale);
       }
     }
     float y0, y1;
@@ -378,7 +325,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < QP; ++t) {
       const int i = threadIdx.x + NT * t;
-      if (i < G * D) sq[i / D][i % D] = qop[t] * a.qscale;
+      if (i < G * D) put_q(i / D, i % D, qop[t] * a.qscale);
     }
   }
   __syncthreads();
@@ -396,53 +343,61 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
   // page the current one again, served by the caches, so that no load sits under a branch), then
   // compute the current one; the two register sets alternate between the steps (copying an
   // in-flight load's registers would make the compiler wait for it).
-  if constexpr (TR) {
-    // Transposed scores (TrGeo): each lane owns NVF complete scores -- head hL, token slots
-    // iK[k] of its row -- so the softmax runs once per score.  The running maximum of each head
-    // is shared by the whole wave (page maxima are reduced over the head's lanes and the rows),
-    // so the accumulators of the four rows need no rescaling against each other, and a page
-    // whose maxima do not grow skips the rescaling altogether (a wave-uniform branch).  The
-    // appended token (pos) is left out of the pages and folded in once afterwards.
-    using Tg = TrGeo<G>;
-    constexpr int NV = Tg::NV, NVF = Tg::NVF;
-    const int c = lane & 15;                       // lane in its 16-lane row; trow = lane >> 4
-    const int vbase = (c >> (4 - Tg::H)) * NVF;    // score index of slot 0 of this lane
-    const int hL = vbase >> 2;                     // its head
-    const bool nondup = (c & Tg::DUP) == 0;        // counts its scores (duplicates do not)
-    auto first_lane = [](int h) { return Tg::lane_of(4 * h); };
-    float mL = -1e30f, lL = 0.f, acc[G][EPL];
+  if constexpr (MF) {
+    // Matrix-core pages.  Scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (A = the page's 16 tokens
+    // x 32 dims, B = 32 dims x 16 columns), then O^T += V^T P^T on v_mfma_f32_16x16x16_bf16
+    // (A = 16 dims x the page's 16 tokens, B = P^T).  The query and the probabilities are fp32,
+    // the operands bf16: each is split into a rounded part and the rounded rest (x = hi + lo to
+    // about 2^-17 relative), and column 2h of B carries hi of head h, column 2h + 1 lo of head h
+    // (columns from 2G on are zero).  Lane l receives the scores of tokens 4 (l / 16) + j (j < 4) of
+    // column l % 16; a lane adds its partner column's value (DPP lane xor 1, applied to every lane:
+    // a DPP read under a lane-dependent branch would see its partner disabled), so both lanes of
+    // a head hold its complete scores and run the same softmax, each producing its own part of
+    // P -- which is already the B operand of the second product (its keys are 4 (l / 16) + j, the
+    // same tokens).  The running maximum of a head is reduced over the four
+    // rows, so the whole page shares it.  V is staged row-major in the wave's LDS tile and read as
+    // V^T with ds_read_b64_tr_b16.  O^T lands with lane l holding dims 16 T + 4 (l / 16) + j of
+    // column l % 16; the hi and lo columns are added at the end.  The appended token (pos) is
+    // folded in once afterwards, in fp32.
+    const int c = lane & 15, r = lane >> 4;
+    const bool hi_col = (c & 1) == 0, used = c < 2 * G;
+    const int hc = used ? c >> 1 : 0;              // head of this lane's column
+    uint16_t* vw = svp + wave * kPage * VROW;
+    // this lane's B operand of the scores: dims 32 ks + 8 (l / 16) .. + 7 of its column's part
+    // (columns from 2G on repeat head 0; their scores are never used)
+    const uint16_t* qrow = &sqb[hc][c & 1][8 * r];
+    float mL = -1e30f, lL = 0.f;
+    mf_f4 acc[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    for (int t = 0; t < 8; ++t) acc[t] = mf_f4{0.f, 0.f, 0.f, 0.f};
     const int tlim = has_new ? pos : tok1;         // the appended token comes after the pages
 
     auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
                          uint4 (&nv)[NI], int& tn, int ph1) {
+      // the query operand is re-read from LDS on every page (an empty asm with a memory
+      // clobber keeps the compiler from holding it in registers across the pages)
+      asm volatile("" ::: "memory");
       request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
-      // partial scores over the lane's 8 dims, then the transpose-reduce over the row
-      float sv[NV];
+      mf_f4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float kf[EPL];
-        widen16<KVB, EPL>(ck[i], kf);
+      for (int ks = 0; ks < 4; ++ks)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(mf_bf8, mf_u4{ck[ks].x, ck[ks].y, ck[ks].z, ck[ks].w}),
+            __builtin_bit_cast(mf_bf8, *reinterpret_cast<const mf_u4*>(qrow + 32 * ks)), st, 0,
+            0, 0);
+      // V row-major into the wave's tile: load i of lane l is token 4 i + l / 16, dims 8 (l % 16)
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float p = 0.f;
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<mf_u4*>(vw + (4 * i + r) * VROW + 8 * c) =
+            mf_u4{cv[i].x, cv[i].y, cv[i].z, cv[i].w};
+      float s[4], pmax = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
-          sv[4 * h + i] = p;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const float x = st[j] + dpp<kDppXor1>(st[j]);
+        const int tok = pg * kPage + 4 * r + j;
+        s[j] = (used && tok < tlim) ? x : -INFINITY;
+        pmax = fmaxf(pmax, s[j]);
       }
-      transpose_reduce16<NV>(sv, c);
-      float pmax = -INFINITY;
-#pragma unroll
-      for (int k = 0; k < NVF; ++k) {
-        const int tok = pg * kPage + ((vbase + k) & 3) * TPI + trow;
-        sv[k] = tok < tlim ? sv[k] : -INFINITY;
-        pmax = fmaxf(pmax, sv[k]);
-      }
-      pmax = group_max_any<Tg::GS>(pmax);
       {
         float lo, hi;
         lane_pair<16>(pmax, lo, hi);
@@ -455,29 +410,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
         const float cL = fast_exp2(mL - mnew);
         lL *= cL;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float ch = lane_value(cL, first_lane(h));
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] *= ch;
-        }
+        for (int t = 0; t < 8; ++t) acc[t] *= cL;
         mL = mnew;
       }
+      mf_s4 pb;
 #pragma unroll
-      for (int k = 0; k < NVF; ++k) {
-        sv[k] = fast_exp2(sv[k] - mL);
-        lL += sv[k];
+      for (int j = 0; j < 4; ++j) {
+        const float p = fast_exp2(s[j] - mL);     // 0 for masked tokens and unused columns
+        lL += p;
+        const float ph = round_bf16(p);
+        pb[j] = (short)f32_to_bf16(hi_col ? ph : p - ph);
       }
-      // P V: the probability of (head h, slot i) comes from the lane of the row that owns it
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float vf[EPL];
-        widen16<KVB, EPL>(cv[i], vf);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pb = bcast_slot<G>(sv, 4 * h + i);
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pb, vf[e], acc[h][e]);
-        }
+      for (int t = 0; t < 8; ++t) {
+        const mf_s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) mf_s4*)(vw + (4 * r + (c >> 2)) * VROW + 16 * t +
+                                                       4 * (c & 3)));
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[t], 0, 0, 0);
       }
       pg += NW;
     };
@@ -490,56 +439,44 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn(AttnArgs a) {
       else
         page_step(k1, v1, t1, k0, v0, t0, ph1);
     }
-    // the appended token, folded into wave 0's state (its K and V as stored, from LDS)
+    // the appended token, folded into wave 0's state in fp32 (its K and V as stored, from LDS):
+    // lane l forms the partial dot product over dims 32 (l / 16) .. + 31, summed over the rows
     if (has_new && wave == 0) {
-      float sh[G];
+      float sp = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], skv[0][dsub + e], p);
-        sh[h] = lanes_sum<16>(p);
-      }
-      float sL = sh[0];
-#pragma unroll
-      for (int h = 1; h < G; ++h) sL = hL == h ? sh[h] : sL;
+      for (int e = 0; e < 32; ++e) sp = fmaf(sq[hc][32 * r + e], skv[0][32 * r + e], sp);
+      float lo, hi;
+      lane_pair<16>(sp, lo, hi);
+      lane_pair<32>(lo + hi, lo, hi);
+      const float sL = used ? lo + hi : -INFINITY;
       const float mnew = fmaxf(mL, sL);
       const float cL = fast_exp2(mL - mnew), pL = fast_exp2(sL - mnew);
-      lL = fmaf(lL, cL, lane == first_lane(hL) ? pL : 0.f);
+      lL = fmaf(lL, cL, r == 0 ? pL : 0.f);
+      const float pv = hi_col ? pL : 0.f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ch = lane_value(cL, first_lane(h));
-        const float ph = trow == 0 ? lane_value(pL, first_lane(h)) : 0.f;
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(acc[h][e], ch, ph * skv[1][dsub + e]);
-      }
+        for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(acc[t][j], cL, pv * skv[1][16 * t + 4 * r + j]);
       mL = mnew;
     }
-    // the four rows share each head's maximum: their accumulators add up as they are
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float lo, hi;
-        lane_pair<16>(acc[h][e], lo, hi);
-        lane_pair<32>(lo + hi, lo, hi);
-        acc[h][e] = lo + hi;
-      }
-    float lh[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) lh[h] = wave_sum(hL == h && nondup ? lL : 0.f);
-    if (trow == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) sm_acc[wave][h][dsub + e] = acc[h][e];
-      }
+    float lsum;
+    {
+      float lo, hi;
+      lane_pair<16>(lL, lo, hi);
+      lane_pair<32>(lo + hi, lo, hi);
+      lsum = lo + hi;
     }
-    if (lane == 0) {
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        sm_m[wave][h] = lane_value(mL, first_lane(h));
-        sm_l[wave][h] = lh[h];
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[t][j] += dpp<kDppXor1>(acc[t][j]);
+    if (hi_col && used) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<mf_f4*>(&sm_acc[wave][hc][16 * t + 4 * r]) = acc[t];
+      if (r == 0) {
+        sm_m[wave][hc] = mL;
+        sm_l[wave][hc] = lsum;
       }
     }
   } else {
