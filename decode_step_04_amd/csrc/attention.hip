@@ -20,19 +20,21 @@
 //     rotates K of head g, stores K and V at (bt[pos/16], pos%16) -- the paged append -- and uses
 //     the same values in registers for that slot.
 //   - Page loop ([Qwen3-runtime] §10.1-10.2): each wave takes every 4th page; a 16 x D page tile
-//     of one head is contiguous, read with 16-byte loads (non-temporal: every byte is used once,
-//     so it is not kept in the caches), and all G heads use the same K/V registers, so each K/V
-//     byte is read once for the whole query group ([Qwen3-runtime] §2.5).  fp32 (m, l, acc)
-//     state per head ([ETE], the online-softmax passage).
-//       * D = 128 with bf16 K/V and G = 1, 2, 4 or 8 (the model shapes): the dot products run on
-//         the matrix cores, with the fp32 query and probabilities each split into two bf16
-//         parts (the comment at the loop gives the layout).
+//     of one head is contiguous and read with 16-byte loads, and all G heads use the same K/V
+//     registers, so each K/V byte is read once for the whole query group ([Qwen3-runtime] §2.5).
+//     fp32 (m, l, acc) state per head ([ETE], the online-softmax passage).  Three page loops:
+//       * D = 128, bf16 K/V, G = 4 or 8: the dot products run on the matrix cores, with the fp32
+//         query and probabilities each split into two bf16 parts (the comment at the loop gives
+//         the layout); non-temporal page loads (every byte is used once).
+//       * D = 128, bf16 K/V, G = 1 or 2: transposed scores on the vector ALUs (TrGeo) -- with one
+//         or two heads the per-page VALU work is small and its shorter dependency chain measured
+//         faster than the matrix-core loop.
 //       * Other shapes (fp32 K/V, D = 64, other G): lane l holds EPL consecutive dims of one
 //         token per load (token row l / LPT); scores are reduced over the LPT lanes of a token
 //         with DPP and each token row keeps its own state.
-//   - Rows (generic path), then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With
-//     one partition the normalised output is written directly (the short path of §10.1);
-//     otherwise the unnormalised state goes to scratch for k_attn_merge.
+//   - Rows, then waves (LDS), are combined exactly ([Qwen3-runtime] §9.1).  With one partition
+//     the normalised output is written directly (the short path of §10.1); otherwise the
+//     unnormalised state goes to scratch for k_attn_merge.
 // k_attn_merge: one work-group per (query head, 32 dims): M = max m_p, w_p = 2^(m_p - M),
 // out = sum w_p acc_p / sum w_p l_p.
 //
@@ -121,15 +123,106 @@ __device__ __forceinline__ void combine_rows(float (&m)[G], float (&l)[G], float
   }
 }
 
+// ---- transposed scores (D = 128, bf16 K/V: 16 lanes per token, 4 tokens per lane and page) ----
+// After the per-lane partial dot products, a lane holds NV = 4G partial scores (head h, token
+// slot i at index 4h + i), each a partial sum over the lane's 8 dims.  A transpose-reduce over
+// the 16 lanes of a row halves the values at each of four lane pairings (xor 8, 7, 3, 1, deciding
+// by bit 3, 2, 1, 0 of the lane in the row which half a lane keeps), so that every lane ends
+// with complete scores of its own (head, slot) -- one softmax exponential per score instead of
+// one in each of the 16 lanes of the token.  With fewer than 16 values the last pairings are
+// plain sums, and lanes that differ only in those bits hold duplicates.
+template <int G>
+struct TrGeo {
+  static constexpr int NV = 4 * G;                                   // partial scores per lane
+  static constexpr int H = NV >= 16 ? 4 : NV == 8 ? 3 : NV == 4 ? 2 : 1;  // halving pairings
+  static constexpr int NVF = NV >> H;                                // complete scores per lane
+  static constexpr int DUP = (1 << (4 - H)) - 1;                     // duplicate-lane bits
+  static constexpr int GS = (4 / NVF) << (4 - H);                    // lanes of one head in a row
+  // lane in the row holding score index v, and its slot there
+  static constexpr int lane_of(int v) { return (v / NVF) << (4 - H); }
+  static constexpr int slot_of(int v) { return v % NVF; }
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "head groups of 1, 2, 4 or 8");
+};
+
+
+// One pairing of the transpose-reduce over the first CNT values: lanes x and x ^ (pairing) both
+// form a + a' and b + b' for each pair (a, b) = (v[k], v[CNT/2 + k]), and keep the first when
+// `hi` is clear; with CNT <= 1 the single value is summed with its partner's.
+template <int CTRL, int CNT, int N>
+__device__ __forceinline__ void tr_step(float (&v)[N], bool hi) {
+  if constexpr (CNT > 1) {
+    constexpr int HF = CNT / 2;
+#pragma unroll
+    for (int k = 0; k < HF; ++k) {
+      const float sa = v[k] + dpp<CTRL>(v[k]);
+      const float sb = v[HF + k] + dpp<CTRL>(v[HF + k]);
+      v[k] = hi ? sb : sa;
+    }
+  } else {
+    v[0] += dpp<CTRL>(v[0]);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void transpose_reduce16(float (&v)[NV], int c) {
+  tr_step<0x128, NV>(v, (c & 8) != 0);        // xor 8
+  tr_step<0x141, NV / 2>(v, (c & 4) != 0);    // xor 7 (half mirror)
+  tr_step<0x1B, NV / 4>(v, (c & 2) != 0);     // xor 3 (quad mirror)
+  tr_step<0xB1, NV / 8>(v, (c & 1) != 0);     // xor 1
+}
+
+// The score of index v (head v / 4, slot v % 4) for every lane of the row: read from the lane
+// of the row that owns it (DPP row broadcast, gfx950 row_newbcast).  v is a compile-time index
+// after unrolling.
+template <int L>
+__device__ __forceinline__ float row_bcast(float x) {
+  return dpp<0x150 + L>(x);
+}
+
+template <int G>
+__device__ __forceinline__ float bcast_slot(const float (&sv)[4 * G], int v) {
+  using Tg = TrGeo<G>;
+  const int ln = Tg::lane_of(v), k = Tg::slot_of(v);
+  const float x = Tg::NVF == 1 ? sv[0] : (k == 0 ? sv[0] : sv[1]);
+  switch (ln) {
+    case 0: return row_bcast<0>(x);
+    case 1: return row_bcast<1>(x);
+    case 2: return row_bcast<2>(x);
+    case 3: return row_bcast<3>(x);
+    case 4: return row_bcast<4>(x);
+    case 5: return row_bcast<5>(x);
+    case 6: return row_bcast<6>(x);
+    case 7: return row_bcast<7>(x);
+    case 8: return row_bcast<8>(x);
+    case 9: return row_bcast<9>(x);
+    case 10: return row_bcast<10>(x);
+    case 11: return row_bcast<11>(x);
+    case 12: return row_bcast<12>(x);
+    case 13: return row_bcast<13>(x);
+    case 14: return row_bcast<14>(x);
+    default: return row_bcast<15>(x);
+  }
+}
+
+// maximum over aligned groups of GS lanes of a row (GS = 1, 2, 4, 8 or 16)
+template <int GS>
+__device__ __forceinline__ float group_max_any(float v) {
+  if constexpr (GS >= 2) v = fmaxf(v, dpp<kDppXor1>(v));
+  if constexpr (GS >= 4) v = fmaxf(v, dpp<kDppXor2>(v));
+  if constexpr (GS >= 8) v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  if constexpr (GS >= 16) v = fmaxf(v, dpp<kDppMirror>(v));
+  return v;
+}
+
 constexpr int kAttnWaves = 4;  // waves per work-group of k_attn (8 measured slower at both shapes)
 constexpr int kAttnThreads = kAttnWaves * kWave;
 
 // The matrix-core page loop of the plain (not fused) kernel fits in 128 registers for groups of
-// 1, 2 and 4: four work-groups per CU instead of three (long contexts launch more than three per
-// CU).  The fused kernel would spill at that bound, and G = 8 is held to three by its LDS.
+// 4: four work-groups per CU instead of three (long contexts launch more than three per CU).  The
+// fused kernel would spill at that bound, and G = 8 is held to three by its LDS.
 template <int D, bool KVB, int G, bool FUSED>
 constexpr int attn_waves_per_simd() {
-  return !FUSED && D == 128 && KVB && (G == 1 || G == 2 || G == 4) ? 4 : 1;
+  return !FUSED && D == 128 && KVB && G == 4 ? 4 : 1;
 }
 
 template <int D, bool KVB, int G, bool FUSED>
@@ -141,8 +234,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
   constexpr int NW = kAttnWaves, NT = kAttnThreads;
   constexpr int NPH = kMaxPartTokens / kPage / NW;  // block-table entries per wave, read ahead
   constexpr int QT = (G + NW - 1) / NW;             // query heads per wave in the prologue
-  // matrix-core pages: 128-dim bf16 pages and head groups of 1, 2, 4 or 8
-  constexpr bool MF = D == 128 && KVB && (G == 1 || G == 2 || G == 4 || G == 8);
+  // 128-dim bf16 pages: matrix-core pages for head groups of 4 and 8; transposed scores on the
+  // vector ALUs for groups of 1 and 2 (at that width the VALU work per page is small and the
+  // shorter dependency chain per page wins)
+  constexpr bool MF = D == 128 && KVB && (G == 4 || G == 8);
+  constexpr bool TR = D == 128 && KVB && (G == 1 || G == 2);
   constexpr int VROW = D + 16;      // LDS row of a staged V page, in bf16 (288 bytes)
   __shared__ float sq[G][D];        // scaled query heads
   __shared__ __attribute__((aligned(16))) uint16_t svp[MF ? NW * kPage * VROW : 1];
@@ -157,13 +253,17 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
     }
   };
   __shared__ float skv[2][D];       // K and V of the new token (as stored)
+  // matrix-core pages of the fused kernel: the same K and V as bf16, patched into their page
+  __shared__ __attribute__((aligned(16))) uint16_t skvb[MF && FUSED ? 2 : 1][D];
   __shared__ float sm_acc[NW][G][D];
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
 
-  // the wave index as a scalar: its block-table entries, pages and token ranges are then
-  // wave-uniform values (scalar loads and registers, uniform branches)
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Matrix-core pages take the wave index as a scalar: its block-table entries, pages and token
+  // ranges are then wave-uniform values (scalar loads and registers, uniform branches), which
+  // the 128-register budget needs.  (The other paths measured faster without.)
+  const int lane = threadIdx.x & 63;
+  const int wave = MF ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int hkv = a.n_kv_heads;
   const int g = blockIdx.x % hkv;
   const int pi = blockIdx.x / hkv;
@@ -255,10 +355,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
   const int64_t kmf = ((int64_t)(lane & 15) * D + 8 * (lane >> 4)) * ELEM;
   // The address is computed from a page number chosen by a select (not a select of two
   // addresses), so the compiler cannot fold a re-request into a copy of another set's registers.
-  // Non-temporal loads: each byte of the pages is read once (measured 10 % faster at 128K
-  // positions than cached loads).
+  // Matrix-core pages use non-temporal loads: each byte of the pages is read once (measured 10 %
+  // faster at 128K positions than cached loads; on the transposed-score path they measured
+  // slower inside the decode step).
   auto load16 = [](const char* p) {
-    const mf_u4 x = __builtin_nontemporal_load(reinterpret_cast<const mf_u4*>(p));
+    const mf_u4 x = MF ? __builtin_nontemporal_load(reinterpret_cast<const mf_u4*>(p))
+                       : *reinterpret_cast<const mf_u4*>(p);
     return make_uint4(x[0], x[1], x[2], x[3]);
   };
   auto request = [&](uint4 (&kd)[NI], uint4 (&vd)[NI], int& td, int ph) {
@@ -320,6 +422,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
       }
       skv[0][lane] = y0; skv[0][lane + HALF] = y1;
       skv[1][lane] = v0; skv[1][lane + HALF] = v1;
+      if constexpr (MF && FUSED) {
+        skvb[0][lane] = f32_to_bf16(y0); skvb[0][lane + HALF] = f32_to_bf16(y1);
+        skvb[1][lane] = f32_to_bf16(v0); skvb[1][lane + HALF] = f32_to_bf16(v1);
+      }
     }
   } else {
 #pragma unroll
@@ -357,8 +463,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
     // same tokens).  The running maximum of a head is reduced over the four
     // rows, so the whole page shares it.  V is staged row-major in the wave's LDS tile and read as
     // V^T with ds_read_b64_tr_b16.  O^T lands with lane l holding dims 16 T + 4 (l / 16) + j of
-    // column l % 16; the hi and lo columns are added at the end.  The appended token (pos) is
-    // folded in once afterwards, in fp32.
+    // column l % 16; the hi and lo columns are added at the end.  The appended token (pos) goes
+    // through the same products: on its page, its K and V as stored (from LDS) replace what the
+    // page load returned (the load may have been issued before the append).
     const int c = lane & 15, r = lane >> 4;
     const bool hi_col = (c & 1) == 0, used = c < 2 * G;
     const int hc = used ? c >> 1 : 0;              // head of this lane's column
@@ -370,7 +477,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
     mf_f4 acc[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[t] = mf_f4{0.f, 0.f, 0.f, 0.f};
-    const int tlim = has_new ? pos : tok1;         // the appended token comes after the pages
+    const int pg_new = has_new ? pos / kPage : -1;  // page of the appended token (wave-uniform)
+    const int slot_new = pos % kPage;
 
     auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
                          uint4 (&nv)[NI], int& tn, int ph1) {
@@ -378,24 +486,30 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
       // clobber keeps the compiler from holding it in registers across the pages)
       asm volatile("" ::: "memory");
       request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
+      mf_u4 kk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kk[ks] = mf_u4{ck[ks].x, ck[ks].y, ck[ks].z, ck[ks].w};
+      if (FUSED && pg == pg_new) {
+        // the appended token's K replaces its row (lanes l % 16 == slot)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const mf_u4 x = *reinterpret_cast<const mf_u4*>(&skvb[0][32 * ks + 8 * r]);
+          kk[ks] = c == slot_new ? x : kk[ks];
+        }
+      }
       mf_f4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(mf_bf8, mf_u4{ck[ks].x, ck[ks].y, ck[ks].z, ck[ks].w}),
+            __builtin_bit_cast(mf_bf8, kk[ks]),
             __builtin_bit_cast(mf_bf8, *reinterpret_cast<const mf_u4*>(qrow + 32 * ks)), st, 0,
             0, 0);
-      // V row-major into the wave's tile: load i of lane l is token 4 i + l / 16, dims 8 (l % 16)
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-        *reinterpret_cast<mf_u4*>(vw + (4 * i + r) * VROW + 8 * c) =
-            mf_u4{cv[i].x, cv[i].y, cv[i].z, cv[i].w};
       float s[4], pmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float x = st[j] + dpp<kDppXor1>(st[j]);
         const int tok = pg * kPage + 4 * r + j;
-        s[j] = (used && tok < tlim) ? x : -INFINITY;
+        s[j] = (used && tok < tok1) ? x : -INFINITY;
         pmax = fmaxf(pmax, s[j]);
       }
       {
@@ -421,6 +535,18 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
         const float ph = round_bf16(p);
         pb[j] = (short)f32_to_bf16(hi_col ? ph : p - ph);
       }
+      // V row-major into the wave's tile: load i of lane l is token 4 i + l / 16, dims 8 (l % 16)
+      // (then the appended token's row, written after, so it wins).  Staged only now: the wait
+      // for V's loads would otherwise hold up the scores, which need only K (the empty asm keeps
+      // the compiler from moving the stores up).
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<mf_u4*>(vw + (4 * i + r) * VROW + 8 * c) =
+            mf_u4{cv[i].x, cv[i].y, cv[i].z, cv[i].w};
+      if (FUSED && pg == pg_new && r == 0)
+        *reinterpret_cast<mf_u4*>(vw + slot_new * VROW + 8 * c) =
+            *reinterpret_cast<const mf_u4*>(&skvb[1][8 * c]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const mf_s4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -438,26 +564,6 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
         page_step(k0, v0, t0, k1, v1, t1, ph1);
       else
         page_step(k1, v1, t1, k0, v0, t0, ph1);
-    }
-    // the appended token, folded into wave 0's state in fp32 (its K and V as stored, from LDS):
-    // lane l forms the partial dot product over dims 32 (l / 16) .. + 31, summed over the rows
-    if (has_new && wave == 0) {
-      float sp = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) sp = fmaf(sq[hc][32 * r + e], skv[0][32 * r + e], sp);
-      float lo, hi;
-      lane_pair<16>(sp, lo, hi);
-      lane_pair<32>(lo + hi, lo, hi);
-      const float sL = used ? lo + hi : -INFINITY;
-      const float mnew = fmaxf(mL, sL);
-      const float cL = fast_exp2(mL - mnew), pL = fast_exp2(sL - mnew);
-      lL = fmaf(lL, cL, r == 0 ? pL : 0.f);
-      const float pv = hi_col ? pL : 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[t][j] = fmaf(acc[t][j], cL, pv * skv[1][16 * t + 4 * r + j]);
-      mL = mnew;
     }
     float lsum;
     {
@@ -477,6 +583,152 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
       if (r == 0) {
         sm_m[wave][hc] = mL;
         sm_l[wave][hc] = lsum;
+      }
+    }
+  } else if constexpr (TR) {
+    // Transposed scores (TrGeo): each lane owns NVF complete scores -- head hL, token slots
+    // iK[k] of its row -- so the softmax runs once per score.  The running maximum of each head
+    // is shared by the whole wave (page maxima are reduced over the head's lanes and the rows),
+    // so the accumulators of the four rows need no rescaling against each other, and a page
+    // whose maxima do not grow skips the rescaling altogether (a wave-uniform branch).  The
+    // appended token (pos) is left out of the pages and folded in once afterwards.
+    using Tg = TrGeo<G>;
+    constexpr int NV = Tg::NV, NVF = Tg::NVF;
+    const int c = lane & 15;                       // lane in its 16-lane row; trow = lane >> 4
+    const int vbase = (c >> (4 - Tg::H)) * NVF;    // score index of slot 0 of this lane
+    const int hL = vbase >> 2;                     // its head
+    const bool nondup = (c & Tg::DUP) == 0;        // counts its scores (duplicates do not)
+    auto first_lane = [](int h) { return Tg::lane_of(4 * h); };
+    float mL = -1e30f, lL = 0.f, acc[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    const int tlim = has_new ? pos : tok1;         // the appended token comes after the pages
+
+    auto page_step = [&](const uint4 (&ck)[NI], const uint4 (&cv)[NI], int tc, uint4 (&nk)[NI],
+                         uint4 (&nv)[NI], int& tn, int ph1) {
+      request(nk, nv, tn, (pg + NW < pg1) ? ph1 : tc);
+      // partial scores over the lane's 8 dims, then the transpose-reduce over the row
+      float sv[NV];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float kf[EPL];
+        widen16<KVB, EPL>(ck[i], kf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float p = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], kf[e], p);
+          sv[4 * h + i] = p;
+        }
+      }
+      transpose_reduce16<NV>(sv, c);
+      float pmax = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        const int tok = pg * kPage + ((vbase + k) & 3) * TPI + trow;
+        sv[k] = tok < tlim ? sv[k] : -INFINITY;
+        pmax = fmaxf(pmax, sv[k]);
+      }
+      pmax = group_max_any<Tg::GS>(pmax);
+      {
+        float lo, hi;
+        lane_pair<16>(pmax, lo, hi);
+        pmax = fmaxf(lo, hi);
+        lane_pair<32>(pmax, lo, hi);
+        pmax = fmaxf(lo, hi);
+      }
+      const float mnew = fmaxf(mL, pmax);
+      if (__builtin_amdgcn_ballot_w64(mnew > mL) != 0) {  // wave-uniform
+        const float cL = fast_exp2(mL - mnew);
+        lL *= cL;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ch = lane_value(cL, first_lane(h));
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= ch;
+        }
+        mL = mnew;
+      }
+#pragma unroll
+      for (int k = 0; k < NVF; ++k) {
+        sv[k] = fast_exp2(sv[k] - mL);
+        lL += sv[k];
+      }
+      // P V: the probability of (head h, slot i) comes from the lane of the row that owns it
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vf[EPL];
+        widen16<KVB, EPL>(cv[i], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pb = bcast_slot<G>(sv, 4 * h + i);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pb, vf[e], acc[h][e]);
+        }
+      }
+      pg += NW;
+    };
+#pragma unroll
+    for (int jj = 0; jj < NPH; ++jj) {
+      if (pg >= pg1) break;
+      const int ph1 = jj + 1 < NPH ? phys[jj + 1 < NPH ? jj + 1 : 0] : 0;
+      if (jj % 2 == 0)
+        page_step(k0, v0, t0, k1, v1, t1, ph1);
+      else
+        page_step(k1, v1, t1, k0, v0, t0, ph1);
+    }
+    // the appended token, folded into wave 0's state (its K and V as stored, from LDS)
+    if (has_new && wave == 0) {
+      float sh[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) p = fmaf(q[h][e], skv[0][dsub + e], p);
+        sh[h] = lanes_sum<16>(p);
+      }
+      float sL = sh[0];
+#pragma unroll
+      for (int h = 1; h < G; ++h) sL = hL == h ? sh[h] : sL;
+      const float mnew = fmaxf(mL, sL);
+      const float cL = fast_exp2(mL - mnew), pL = fast_exp2(sL - mnew);
+      lL = fmaf(lL, cL, lane == first_lane(hL) ? pL : 0.f);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float ch = lane_value(cL, first_lane(h));
+        const float ph = trow == 0 ? lane_value(pL, first_lane(h)) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(acc[h][e], ch, ph * skv[1][dsub + e]);
+      }
+      mL = mnew;
+    }
+    // the four rows share each head's maximum: their accumulators add up as they are
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float lo, hi;
+        lane_pair<16>(acc[h][e], lo, hi);
+        lane_pair<32>(lo + hi, lo, hi);
+        acc[h][e] = lo + hi;
+      }
+    float lh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) lh[h] = wave_sum(hL == h && nondup ? lL : 0.f);
+    if (trow == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sm_acc[wave][h][dsub + e] = acc[h][e];
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm_m[wave][h] = lane_value(mL, first_lane(h));
+        sm_l[wave][h] = lh[h];
       }
     }
   } else {
