@@ -16,9 +16,10 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqdec.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # (source, object, extra flags): gemv.hip is built once per weight type and once for its
-# dispatcher, in parallel.  attention.hip keeps matrix-core accumulators in ordinary vector
-# registers (with them in the accumulation registers every rescale of the running sums would
-# copy them out and back); prefill_attn.hip is built without IEEE mode and NaN semantics.
+# dispatcher, in parallel.  attention.hip and prefill.hip keep matrix-core accumulators in
+# ordinary vector registers (in the accumulation registers every rescale of the attention's
+# running sums would copy them out and back, and the GEMM tiles would need more registers in
+# all); prefill_attn.hip is built without IEEE mode and NaN semantics.
 SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
            ("gemv.hip", "gemv_bf16", ["-DQD_GEMV_PART=1"]),
            ("gemv.hip", "gemv_i8", ["-DQD_GEMV_PART=2"]),
@@ -26,7 +27,7 @@ SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
            ("gemv.hip", "gemv_i4g", ["-DQD_GEMV_PART=4"]),
            ("gemv.hip", "gemv_dispatch", ["-DQD_GEMV_PART=-1"]),
            ("attention.hip", "attention", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]), ("misc.hip", "misc", []),
-           ("prefill.hip", "prefill", []),
+           ("prefill.hip", "prefill", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
            ("prefill_attn.hip", "prefill_attn", ["-mno-amdgpu-ieee", "-fno-honor-nans"]),
            ("sample.hip", "sample", []),
            ("runtime.hip", "runtime", [])]

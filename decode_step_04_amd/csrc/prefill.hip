@@ -18,6 +18,8 @@
 // next step's 8 fragments into a second register set before issuing the current 16 MFMAs.
 // Epilogues: STORE (fp32), RESID (adds into an fp32 [M x N] residual), SWIGLU (the tile's 128
 // weight rows are 64 gate rows and the matching 64 up rows; bf16 silu(g) * u).
+#include <utility>
+
 #include "common.h"
 #include "launch.h"
 
@@ -375,6 +377,189 @@ __global__ __launch_bounds__(256) void k_gemm_lds(GemmArgs a) {
   }
 }
 
+// k_gemm_dma: the STORE, RESID and SWIGLU products with the operand tiles moved straight from
+// global memory into LDS (gfx950 global_load_lds_dwordx4: each lane names its own 16-byte source,
+// the wave's 64 chunks land at consecutive 16-byte slots of a wave-uniform LDS address), so no
+// register staging, no LDS store instructions and no VGPRs held for tiles in flight.
+//   - Tiles of K are 64 wide (128-byte rows, 8 chunks).  Row r of a tile keeps its chunk c at slot
+//     c ^ ((r / 2) % 8): the 32 x 32 x 16 fragment read of 16 consecutive rows at one k offset then
+//     covers all 64 banks once (two rows per 256 bytes, eight slot positions).
+//   - NS stages, each its own __shared__ array (the compiler tracks direct-to-LDS loads per LDS
+//     object, so reading one stage does not wait for the loads into the others).  Step kt waits
+//     for its own stage with an explicit vmcnt (the loads of the NS - 2 later tiles may stay in
+//     flight), meets the other waves at a plain s_barrier (a __syncthreads would drain every load
+//     in flight), requests tile kt + NS - 1 into the stage freed by step kt - 1, and computes.
+//     Past the last tile the requests re-read the last one, so the count of loads in flight is
+//     the same at every step.
+//   - The loop body is U steps (the compiler drains all loads at the loop head, once per U).
+//   - Wave w of a WGM x WGN grid owns rows (w / WGN) BM/WGM .. and weight rows (w % WGN) BN/WGN ..;
+//     the epilogues are those of k_gemm_lds (SWIGLU needs 64 weight rows per wave: 32 gate, 32 up).
+// Measured on MI355X (2048 rows, N 24576, K 4096, fp32 out, weights cold in HBM): 426 us with
+// 256 x 256 tiles and 8 waves, against about 555 us for 128 x 128 tiles (either kernel).  With
+// 128 x 128 and smaller tiles it is no faster than register staging inside the prefill.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt field");
+  // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (15 << 8) | ((VM >> 4) << 14));
+}
+
+// Stage S of a tile kind (ID: 0 for A, 1 for W) of SZ bf16: one LDS object per stage.
+template <int ID, int S, int SZ>
+__device__ __forceinline__ uint16_t* gemm_stage() {
+  __shared__ __attribute__((aligned(1024))) uint16_t buf[SZ];
+  return buf;
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N-1, in order
+template <class F, int... I>
+__device__ __forceinline__ void for_each_const(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int EPI, int BM, int BN, int NS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_dma(GemmArgs a) {
+  constexpr int BK = 64, CPR = BK * 2 / 16, RPB = 64 / CPR, RPP = 256 / (BK * 2);
+  constexpr int NW = WGM * WGN;
+  constexpr int AL = BM / RPB / NW, BL = BN / RPB / NW;   // 1 KiB loads per wave per tile
+  constexpr int WM = BM / WGM, WN = BN / WGN, NI = WM / 32, NJ = WN / 32;
+  constexpr int U = NS == 3 ? 18 : 16;                     // steps per loop iteration
+  static_assert(NS >= 2 && NS <= 4, "two to four stages");
+  static_assert(AL * RPB * NW == BM && BL * RPB * NW == BN && NI >= 1 && NJ >= 1, "tile split");
+  static_assert(EPI == EPI_STORE || EPI == EPI_RESID || EPI == EPI_SWIGLU, "epilogue");
+  static_assert(EPI != EPI_SWIGLU || NJ == 2, "SWIGLU pairs one gate and one up block per wave");
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int M = a.m, N = a.n, K = a.k;
+  const int m0 = blockIdx.y * BM;
+  const int nout = EPI == EPI_SWIGLU ? BN / 2 : BN;   // output columns per work-group
+  const int n0 = blockIdx.x * nout;
+  const int nk = K / BK;
+  const uint16_t* A = static_cast<const uint16_t*>(a.a);
+  const uint16_t* W = static_cast<const uint16_t*>(a.w);
+  auto wrow = [&](int row) __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const int h = row / WN, q = row % WN;
+      const int col = min(n0 + h * (WN / 2) + q % (WN / 2), N - 1);
+      return q < WN / 2 ? col : N + col;
+    } else {
+      return min(n0 + row, N - 1);
+    }
+  };
+  // this lane's chunk of load r: tile row (r NW + wave) RPB + lane / CPR, slot lane % CPR, which
+  // holds source chunk slot ^ swizzle(row); rows past the end are clamped (results discarded)
+  const int lrow = lane / CPR, slot = lane % CPR;
+  const uint16_t* pa[AL];
+  const uint16_t* pb[BL];
+#pragma unroll
+  for (int r = 0; r < AL; ++r) {
+    const int row = (r * NW + wave) * RPB + lrow;
+    pa[r] = A + (int64_t)min(m0 + row, M - 1) * K + (slot ^ ((row / RPP) % CPR)) * 8;
+  }
+#pragma unroll
+  for (int r = 0; r < BL; ++r) {
+    const int row = (r * NW + wave) * RPB + lrow;
+    pb[r] = W + (int64_t)wrow(row) * K + (slot ^ ((row / RPP) % CPR)) * 8;
+  }
+  auto request = [&](auto stage, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    uint16_t* sa = gemm_stage<0, S, BM * BK>();
+    uint16_t* sb = gemm_stage<1, S, BN * BK>();
+    kt = min(kt, nk - 1);
+#pragma unroll
+    for (int r = 0; r < AL; ++r)
+      __builtin_amdgcn_global_load_lds((const void*)(pa[r] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(sa + (r * NW + wave) * 512),
+                                       16, 0, 0);
+#pragma unroll
+    for (int r = 0; r < BL; ++r)
+      __builtin_amdgcn_global_load_lds((const void*)(pb[r] + kt * BK),
+                                       (__attribute__((address_space(3))) void*)(sb + (r * NW + wave) * 512),
+                                       16, 0, 0);
+  };
+  f32x16 acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
+  const int r32 = lane & 31, kq = lane >> 5;
+  const int arow = (wave / WGN) * WM + r32, brow = (wave % WGN) * WN + r32;
+  auto frag = [&](const uint16_t* base, int row, int ks) __attribute__((always_inline)) {
+    const int c = (2 * ks + kq) ^ ((row / RPP) % CPR);
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + row * BK + 8 * c));
+  };
+  auto compute = [&](auto stage) __attribute__((always_inline)) {
+    constexpr int S = decltype(stage)::value;
+    const uint16_t* sa = gemm_stage<0, S, BM * BK>();
+    const uint16_t* sb = gemm_stage<1, S, BN * BK>();
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 fa[NI], fb[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) fa[i] = frag(sa, arow + 32 * i, ks);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) fb[j] = frag(sb, brow + 32 * j, ks);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  for_each_const([&](auto st) { request(st, decltype(st)::value); },
+                 std::make_integer_sequence<int, NS - 1>{});
+  for (int k0 = 0; k0 < nk; k0 += U) {
+    bool done = false;
+    for_each_const(
+        [&](auto u) {
+          constexpr int UI = decltype(u)::value;
+          const int kt = k0 + UI;
+          done = done || kt >= nk;
+          if (done) return;
+          wait_vmcnt<(NS - 2) * (AL + BL)>();   // this step's tile has landed (this wave's part)
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_s_barrier();         // ... every wave's part, and step kt - 1 is done
+          asm volatile("" ::: "memory");
+          request(std::integral_constant<int, (UI + NS - 1) % NS>{}, kt + NS - 1);
+          compute(std::integral_constant<int, UI % NS>{});
+        },
+        std::make_integer_sequence<int, U>{});
+  }
+
+  // epilogue: lane holds C[row 32 i + 8 (r/4) + 4 (l/32) + r % 4 of the wave][weight row
+  // 32 j + l % 32]
+  const int mw = m0 + (wave / WGN) * WM;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = mw + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m >= M) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int n = n0 + (wave % WGN) * (WN / 2) + r32;
+        if (n >= N) continue;
+        const float g = acc[i][0][r], u = acc[i][1][r];
+        const float v = g / (1.0f + expf(-g)) * u;
+        static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = n0 + (wave % WGN) * WN + 32 * j + r32;
+          if (n >= N) continue;
+          const float v = acc[i][j][r];
+          if constexpr (EPI == EPI_RESID)
+            a.resid[(int64_t)m * N + n] += v;
+          else if (a.y_bf16)
+            static_cast<uint16_t*>(a.y)[(int64_t)m * N + n] = f32_to_bf16(v);
+          else
+            static_cast<float*>(a.y)[(int64_t)m * N + n] = v;
+        }
+      }
+    }
+  }
+}
+
 // The largest tile that still gives two work-groups per CU (512), else the smallest (SWIGLU tiles
 // keep 128 weight rows: 64 gate and 64 up).
 template <int EPI>
@@ -402,18 +587,38 @@ static void launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
   }
 }
 
+// Products with at least 512 tiles of 256 x 256 (weight rows per output column: 2 for SWIGLU) take
+// the direct-to-LDS kernel with 8 waves (128 KiB of LDS: one work-group per CU); the others keep
+// the register-staged kernel, which measured as fast or faster on them in the prefill (smaller
+// tiles are bound by the latency of the first weight bytes, not by the operand traffic).
+template <int EPI>
+static bool launch_gemm_dma(const GemmArgs& a, hipStream_t s) {
+  const int64_t wide = EPI == EPI_SWIGLU ? 2 : 1;
+  const int64_t tiles = ((a.n * wide + 255) / 256) * (int64_t)((a.m + 255) / 256);
+  if (tiles < 512) return false;
+  const dim3 grid((unsigned)((a.n * wide + 255) / 256), (unsigned)((a.m + 255) / 256));
+  hipLaunchKernelGGL((k_gemm_dma<EPI, 256, 256, 2, 2, 4>), grid, dim3(512), 0, s, a);
+  return true;
+}
+
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.m <= 0 || a.n <= 0) return hipSuccess;
   if (a.k % 32 || a.k < 32) return hipErrorInvalidValue;
   if (a.k % 64 == 0) {
     switch (epi) {
-      case EPI_STORE: launch_gemm_lds<EPI_STORE>(a, s); break;
-      case EPI_RESID: launch_gemm_lds<EPI_RESID>(a, s); break;
+      case EPI_STORE:
+        if (!launch_gemm_dma<EPI_STORE>(a, s)) launch_gemm_lds<EPI_STORE>(a, s);
+        break;
+      case EPI_RESID:
+        if (!launch_gemm_dma<EPI_RESID>(a, s)) launch_gemm_lds<EPI_RESID>(a, s);
+        break;
       case EPI_ROPE:
         if (a.n % 128) return hipErrorInvalidValue;
         launch_gemm_lds<EPI_ROPE>(a, s);
         break;
-      default: launch_gemm_lds<EPI_SWIGLU>(a, s); break;
+      default:
+        if (!launch_gemm_dma<EPI_SWIGLU>(a, s)) launch_gemm_lds<EPI_SWIGLU>(a, s);
+        break;
     }
     return hipGetLastError();
   }
