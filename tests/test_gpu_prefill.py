@@ -82,6 +82,51 @@ def test_gemm_swiglu_epilogue(m, f, k):
     assert _bf16_ulp_ok(synth.bf16_to_f32(y)[rows], exact, extra=1e-5).all()
 
 
+# Products with at least 512 tiles of 256 x 256 run on the direct-to-LDS kernel (8 waves, swizzled
+# LDS stages); these shapes reach it, with ragged rows and columns.  Sampled rows, every column.
+def _sample_rows(m, n_rows=40, seed=2):
+    return np.unique(np.concatenate([np.random.default_rng(seed).choice(m, min(m, n_rows), replace=False),
+                                     [0, m - 1]]))
+
+
+@pytest.mark.parametrize("m,n,k", [(2048, 16384, 512), (2000, 16400, 256)])
+def test_gemm_large_tiles_store_and_resid(m, n, k):
+    print(f"gemm large tiles m={m} n={n} k={k}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(m + 3 * n + k)
+    a = torch.randn((m, k), generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((n, k), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    y32 = torch.empty((m, n), device=DEV)
+    ybf = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    r0 = torch.randn((m, n), generator=g, device=DEV)
+    r = r0.clone()
+    Q.qdec_op_gemm(a, w, y32, Q.F32, None, Q.GEMM_STORE, m, n, k)
+    Q.qdec_op_gemm(a, w, ybf, Q.BF16, None, Q.GEMM_STORE, m, n, k)
+    Q.qdec_op_gemm(a, w, None, Q.F32, r, Q.GEMM_RESID, m, n, k)
+    torch.cuda.synchronize()
+    rows = _sample_rows(m)
+    exact = _rows_exact(_bits(a), _bits(w), rows)
+    assert np.max(np.abs(y32.cpu().numpy()[rows] - exact)) <= 1e-4
+    assert _bf16_ulp_ok(synth.bf16_to_f32(ybf)[rows], exact).all()
+    resid_exact = exact + r0.cpu().numpy()[rows].astype(np.float64)
+    assert np.max(np.abs(r.cpu().numpy()[rows] - resid_exact)) <= 1e-4
+
+
+@pytest.mark.parametrize("m,f,k", [(2001, 8200, 512), (2048, 12288, 4096)])
+def test_gemm_large_tiles_swiglu(m, f, k):
+    """Includes the 8B-class prefill's gate-up product (2048 tokens, FFN 12288, hidden 4096)."""
+    print(f"gemm large tiles swiglu m={m} f={f} k={k}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(m * 5 + f + k)
+    a = torch.randn((m, k), generator=g, device=DEV).to(torch.bfloat16)
+    w = (torch.randn((2 * f, k), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    y = torch.empty((m, f), device=DEV, dtype=torch.bfloat16)
+    Q.qdec_op_gemm(a, w, y, Q.BF16, None, Q.GEMM_SWIGLU, m, f, k)
+    torch.cuda.synchronize()
+    rows = _sample_rows(m, 24)
+    gu = _rows_exact(_bits(a), _bits(w), rows)
+    exact = oracle.silu(gu[:, :f]) * gu[:, f:]
+    assert _bf16_ulp_ok(synth.bf16_to_f32(y)[rows], exact, extra=1e-5).all()
+
+
 def test_gemm_rejects_bad_arguments():
     a = torch.zeros((4, 64), device=DEV, dtype=torch.bfloat16)
     w = torch.zeros((8, 64), device=DEV, dtype=torch.bfloat16)
