@@ -24,7 +24,7 @@ SOURCES = [("gemv.hip", "gemv_f32", ["-DQD_GEMV_PART=0"]),
            ("gemv.hip", "gemv_bf16", ["-DQD_GEMV_PART=1"]),
            ("gemv.hip", "gemv_i8", ["-DQD_GEMV_PART=2"]),
            ("gemv.hip", "gemv_i8g", ["-DQD_GEMV_PART=3"]),
-           ("gemv.hip", "gemv_i4g", ["-DQD_GEMV_PART=4"]),
+           ("gemv.hip", "gemv_i4g", ["-DQD_GEMV_PART=4", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
            ("gemv.hip", "gemv_dispatch", ["-DQD_GEMV_PART=-1"]),
            ("attention.hip", "attention", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]), ("misc.hip", "misc", []),
            ("prefill.hip", "prefill", ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]),
