@@ -36,9 +36,13 @@
 // A work-group takes query blocks nb-1-x and x (the causal work of the pair is the same for every
 // x), heaviest first; the work-group index runs kv head fastest, so with 8 XCDs dispatched round
 // robin one kv head's work-groups share an XCD (and its L2 copy of that head's K and V).
-// LDS rows: K D + 8 bf16 (272 bytes for D = 128: the 16-byte fragment reads of 16 consecutive
-// key rows cover all banks once), V D + 16 (288 bytes: the 8-byte transposed reads of a 16-lane
-// group cover 4 rows x 32 contiguous bytes, each row 32 bytes further along the banks).
+// LDS rows (D = 128): K and V both D + 16 bf16, 288 bytes.  Measured with rocprofv3's
+// SQ_LDS_BANK_CONFLICT on MI355X (2048-token prefill, 0.6B shape): K rows of 272 bytes -- which
+// would put 16 consecutive rows' 16-byte reads on distinct banks -- stalled the LDS for about
+// two thirds of its active cycles, 288 bytes for none (the kernel 6.6 % faster); V rows of 272 or
+// 320 bytes doubled the stalls, and 288 bytes (the 8-byte transposed reads of a 16-lane group then
+// cover 4 rows x 32 contiguous bytes, each row 32 bytes further along the banks) had none.  For
+// D = 64, K rows stay D + 8.
 #include "common.h"
 #include "launch.h"
 
@@ -73,7 +77,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   constexpr int KB = 64;         // keys per block
   constexpr int KS = D / 32;     // MFMA k-steps over D
   constexpr int ND = D / 16;     // 16-dim tiles of the output
-  constexpr int KP = D + 8;      // LDS row stride of K, in bf16
+  constexpr int KP = D == 128 ? D + 16 : D + 8;  // LDS row stride of K, in bf16
   constexpr int VP = D + 16;     // LDS row stride of V, in bf16
   constexpr int CPK = D / 8;     // 16-byte chunks per key row
   constexpr int CL = 2 * KB * CPK / 512;  // chunks of K (and of V) per thread per step
