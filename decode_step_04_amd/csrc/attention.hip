@@ -242,8 +242,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((
   constexpr int VROW = D + 16;      // LDS row of a staged V page, in bf16 (288 bytes)
   __shared__ float sq[G][D];        // scaled query heads
   __shared__ __attribute__((aligned(16))) uint16_t svp[MF ? NW * kPage * VROW : 1];
-  // matrix-core pages: the scaled query heads split into bf16 hi = bf16(q) and lo = bf16(q - hi)
-  __shared__ __attribute__((aligned(16))) uint16_t sqb[MF ? G : 1][2][D];
+  // matrix-core pages: the scaled query heads split into bf16 hi = bf16(q) and lo = bf16(q - hi).
+  // Rows of 288 bytes: with 256 (a whole bank cycle) every column's 16-byte operand read of a
+  // k-step sat on the same four banks.  rocprofv3's SQ_LDS_BANK_CONFLICT at G = 4 (8B shape, 8K
+  // positions): 426K stall cycles per launch with 256-byte rows, 98K with 288; the launch time
+  // did not change (the page loop waits on memory, not on the LDS)
+  constexpr int QROW = MF ? D + 16 : D;
+  __shared__ __attribute__((aligned(16))) uint16_t sqb[MF ? G : 1][2][QROW];
   auto put_q = [&](int h, int d, float x) {
     sq[h][d] = x;
     if constexpr (MF) {
