@@ -469,6 +469,62 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float* x, const float* ga
   }
 }
 
+// The same row norm with the row held in registers: thread t loads the float4s t + 256 j of x
+// and gamma (16-byte loads, x read once), and writes 4 outputs per store (8 bytes of bf16).  Each
+// output is the same expression as k_rmsnorm's; only the sum of squares is added in another
+// order.  Rows of n % 4 == 0 values up to 1024 V, with 16-byte aligned x rows and gamma and y rows
+// aligned for the store.  (Measured on MI355X, 2048 rows of 1024: 5.4 us for k_rmsnorm, whose
+// scalar loop reads each value twice.)
+template <int V>
+__global__ __launch_bounds__(256) void k_rmsnorm_v(const float* x, const float* gamma, float eps,
+                                                   void* y, int y_bf16, int n) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n4 = n / 4;
+  const float4* x4 = reinterpret_cast<const float4*>(x + (int64_t)blockIdx.x * n);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  float4 v[V], g[V];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = tid + 256 * j;
+    v[j] = g[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < n4) {
+      v[j] = x4[i];
+      g[j] = g4[i];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    ss = fmaf(v[j].x, v[j].x, ss);
+    ss = fmaf(v[j].y, v[j].y, ss);
+    ss = fmaf(v[j].z, v[j].z, ss);
+    ss = fmaf(v[j].w, v[j].w, ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float rinv = 1.0f / sqrtf(tot / (float)n + eps);
+  char* yr = static_cast<char*>(y) + (int64_t)blockIdx.x * n * (y_bf16 ? 2 : 4);
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n4) {
+      const float h0 = v[j].x * rinv * g[j].x, h1 = v[j].y * rinv * g[j].y;
+      const float h2 = v[j].z * rinv * g[j].z, h3 = v[j].w * rinv * g[j].w;
+      if (y_bf16) {
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+        w.y = (uint32_t)f32_to_bf16(h2) | ((uint32_t)f32_to_bf16(h3) << 16);
+        reinterpret_cast<uint2*>(yr)[i] = w;
+      } else {
+        reinterpret_cast<float4*>(yr)[i] = make_float4(h0, h1, h2, h3);
+      }
+    }
+  }
+}
+
 hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y, int y_bf16,
                           int n, hipStream_t s) {
   return launch_rmsnorm_rows(x, gamma, eps, y, y_bf16, n, 1, s);
@@ -477,7 +533,19 @@ hipError_t launch_rmsnorm(const float* x, const float* gamma, float eps, void* y
 hipError_t launch_rmsnorm_rows(const float* x, const float* gamma, float eps, void* y, int y_bf16,
                                int n, int rows, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm, dim3((unsigned)rows), dim3(256), 0, s, x, gamma, eps, y, y_bf16, n);
+  const auto al = [](const void* p, uintptr_t b) { return reinterpret_cast<uintptr_t>(p) % b == 0; };
+  const bool vec = n % 4 == 0 && n <= 8192 && al(x, 16) && al(gamma, 16) && al(y, y_bf16 ? 8 : 16);
+  const dim3 grid((unsigned)rows), block(256);
+  if (vec && n <= 1024)
+    hipLaunchKernelGGL((k_rmsnorm_v<1>), grid, block, 0, s, x, gamma, eps, y, y_bf16, n);
+  else if (vec && n <= 2048)
+    hipLaunchKernelGGL((k_rmsnorm_v<2>), grid, block, 0, s, x, gamma, eps, y, y_bf16, n);
+  else if (vec && n <= 4096)
+    hipLaunchKernelGGL((k_rmsnorm_v<4>), grid, block, 0, s, x, gamma, eps, y, y_bf16, n);
+  else if (vec)
+    hipLaunchKernelGGL((k_rmsnorm_v<8>), grid, block, 0, s, x, gamma, eps, y, y_bf16, n);
+  else
+    hipLaunchKernelGGL(k_rmsnorm, grid, block, 0, s, x, gamma, eps, y, y_bf16, n);
   return hipGetLastError();
 }
 

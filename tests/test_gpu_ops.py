@@ -220,16 +220,23 @@ def test_group_gemv_rejects_bad_arguments():
 
 # ---- RMSNorm, RoPE table, fused Q/K norm + RoPE + append ---------------------------------------------------
 
-def test_rmsnorm_op():
-    n = 1024
+# sizes on both sides of the row-in-registers kernel's limits (n % 4 == 0 and n <= 8192) and of
+# its 1024 / 2048 / 4096 / 8192 register tiers; 1000 and 12288 take the scalar kernel
+@pytest.mark.parametrize("n", [4, 64, 1000, 1024, 2048, 3076, 4096, 8192, 12288])
+@pytest.mark.parametrize("bf16_out", [False, True])
+def test_rmsnorm_op(n, bf16_out):
     g = torch.Generator(device=DEV).manual_seed(2)
     x = torch.randn(n, generator=g, device=DEV) * 3
     gam = 1 + 0.1 * torch.randn(n, generator=g, device=DEV)
-    y = torch.empty(n, device=DEV)
-    Q.qdec_op_rmsnorm(x, gam, 1e-6, y, Q.F32, n)
+    y = torch.empty(n, dtype=torch.bfloat16 if bf16_out else torch.float32, device=DEV)
+    Q.qdec_op_rmsnorm(x, gam, 1e-6, y, Q.BF16 if bf16_out else Q.F32, n)
     _sync()
     ref = oracle.rmsnorm(x.cpu().numpy(), gam.cpu().numpy(), 1e-6)
-    assert np.max(np.abs(y.cpu().numpy() - ref)) <= 1e-5
+    got = y.float().cpu().numpy()
+    if bf16_out:  # the fp32 result rounded to bf16: within half a bf16 spacing of the exact value
+        assert np.all(np.abs(got - ref) <= 1.01 * 2.0**-8 * np.abs(ref) + 1e-7)
+    else:
+        assert np.max(np.abs(got - ref)) <= 1e-5
 
 
 @pytest.mark.parametrize("d", [64, 128])
