@@ -36,13 +36,13 @@
 // A work-group takes query blocks nb-1-x and x (the causal work of the pair is the same for every
 // x), heaviest first; the work-group index runs kv head fastest, so with 8 XCDs dispatched round
 // robin one kv head's work-groups share an XCD (and its L2 copy of that head's K and V).
-// LDS rows (D = 128): K and V both D + 16 bf16, 288 bytes.  Measured with rocprofv3's
-// SQ_LDS_BANK_CONFLICT on MI355X (2048-token prefill, 0.6B shape): K rows of 272 bytes -- which
-// would put 16 consecutive rows' 16-byte reads on distinct banks -- stalled the LDS for about
-// two thirds of its active cycles, 288 bytes for none (the kernel 6.6 % faster); V rows of 272 or
-// 320 bytes doubled the stalls, and 288 bytes (the 8-byte transposed reads of a 16-lane group then
-// cover 4 rows x 32 contiguous bytes, each row 32 bytes further along the banks) had none.  For
-// D = 64, K rows stay D + 8.
+// LDS rows (D = 128): K and V both D + 16 bf16, 288 bytes, chosen by measurement with rocprofv3's
+// SQ_LDS_BANK_CONFLICT on MI355X (2048-token prefill, 0.6B shape).  K rows of 272 bytes, the
+// layout that is conflict-free if a 16-byte read is served 16 consecutive lanes at a time,
+// stalled the LDS for about two thirds of its active cycles; 288-byte rows stalled it for none
+// (the kernel 6.6 % faster).  V rows of 272 or 320 bytes doubled the stalls, and 288 bytes (the
+// 8-byte transposed reads of a 16-lane group then cover 4 rows x 32 contiguous bytes, each row 32
+// bytes further along the banks) had none.  For D = 64, K rows stay D + 8.
 #include "common.h"
 #include "launch.h"
 
