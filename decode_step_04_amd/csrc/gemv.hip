@@ -711,14 +711,26 @@ static GemvPlan plan_gemv(int wtype, int epi, int64_t n, int64_t k) {
     // over R = 2/4/8, 512-4096 work-groups and both round modes for six matrix shapes)
     const bool big = wbytes > kStreamBytes;
     const int64_t cap = big ? 2048 : 1024;
-    // wave slices of three or more 1024-value chunks (over 2048 values, e.g. K = 12288 split four
-    // ways): one row per wave, the next round requested ahead (measured 8.8 against 9.5 us at
-    // 4096 x 12288)
-    for (p.r = p.maxch >= 3 ? 1 : big ? 4 : 2;; p.r /= 2) {  // fewer when over the budget
-      const int64_t need = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
-      wgs = need < cap ? need : cap;
-      p.pipe = need > wgs;
-      if (p.r == 1 || p.r * pairs * p.maxch <= (p.pipe ? 8 : 16) * lmul) break;
+    // four rows per wave when that covers every row in a single round of at most 2048
+    // work-groups (no lookahead, no second round).  Measured on MI355X in the 8B-class w4a16 step
+    // (fp32 inputs): QKV 6144 x 4096 7.5 -> 6.7 us, O 4096 x 4096 5.3 -> 4.8, down 4096 x 12288
+    // 10.6 -> 9.3, the step 1.87 -> 1.77 ms; where four rows still take several rounds it measured
+    // slower (24576 x 4096 STORE: 14.1 -> 16.0 us), so the rule below applies there
+    const int64_t need4 = ((n + 3) / 4 + gpw - 1) / gpw;
+    if (!big && need4 <= 2048 && 4 * pairs * p.maxch <= 16 * lmul) {
+      p.r = 4;
+      wgs = need4;
+      p.pipe = false;
+    } else {
+      // wave slices of three or more 1024-value chunks (over 2048 values, e.g. K = 12288 split
+      // four ways): one row per wave, the next round requested ahead (measured 8.8 against 9.5
+      // us at 4096 x 12288)
+      for (p.r = p.maxch >= 3 ? 1 : big ? 4 : 2;; p.r /= 2) {  // fewer when over the budget
+        const int64_t need = ((n + p.r - 1) / p.r + gpw - 1) / gpw;
+        wgs = need < cap ? need : cap;
+        p.pipe = need > wgs;
+        if (p.r == 1 || p.r * pairs * p.maxch <= (p.pipe ? 8 : 16) * lmul) break;
+      }
     }
   }
   p.wgs = (unsigned)(wgs < 1 ? 1 : wgs);
