@@ -155,6 +155,8 @@ struct GemvArgs {
   float* hidden_copy;     // optional: work-group 0 copies the raw input x here
   float* part_val;        // optional (EPI_STORE): per-work-group largest rounded output ...
   int32_t* part_idx;      // ... and its lowest row index (-1 when none)
+  int32_t part_cap;       // entries of part_val / part_idx: the launcher refuses a plan with more
+                          // work-groups (each writes the entry of its index)
   int64_t n;              // output rows
   int64_t k;              // input length
   int32_t split;          // waves sharing one row group along K (set by the launcher)

@@ -916,6 +916,8 @@ hipError_t launch_wt(int epi, bool norm, GemvArgs a, hipStream_t s) {
   }
   const GemvPlan p = plan_gemv(WT, epi, a.n, a.k);
   if (!p.ok || (norm && a.k > kGemvNormMaxK)) return hipErrorInvalidValue;
+  // every work-group writes the argmax partial of its index: never past the buffer's end
+  if (a.part_val && (int64_t)p.wgs > (int64_t)a.part_cap) return hipErrorInvalidValue;
   a.split = p.split;
   const bool xb = a.x_bf16 != 0;
   if (norm && xb) return hipErrorInvalidValue;

@@ -1072,6 +1072,7 @@ static hipError_t launch_class(qdec_ctx* c, const qdec_step* st, int cls, int64_
       if (st->argmax_out) {  // the sampler takes its maximum from these too
         h.part_val = c->am_val;
         h.part_idx = c->am_idx;
+        h.part_cap = c->am_parts;
       }
       h.n = k.vocab;
       h.k = d;
@@ -1322,6 +1323,7 @@ QDEC_API qdec_status qdec_prefill(qdec_ctx* c, const int32_t* token_ids, int32_t
     if (argmax_out) {
       h.part_val = c->am_val;
       h.part_idx = c->am_idx;
+      h.part_cap = c->am_parts;
     }
     h.n = k.vocab;
     h.k = d;
