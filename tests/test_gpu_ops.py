@@ -137,8 +137,11 @@ def _group_codes_torch(codes):
 
 @pytest.mark.parametrize("wdt", [Q.I8_G128, Q.I4_G128])
 @pytest.mark.parametrize("xdt", [Q.BF16, Q.F32])
+# (6144, 4096), (4096, 4096) and (4096, 12288): int4 matrices over 4 MiB that take four rows per
+# wave in a single round; (24576, 4096): one that still takes several rounds
 @pytest.mark.parametrize("n,k", [(1, 128), (37, 256), (1001, 1152), (4096, 1024), (515, 3072),
-                                 (64, 12288), (3, 32768), (4096, 12288)])
+                                 (64, 12288), (3, 32768), (4096, 12288), (6144, 4096),
+                                 (4096, 4096), (24576, 4096)])
 def test_group_gemv_matches_oracle(wdt, xdt, n, k):
     print(f"group gemv wdt={wdt} xdt={xdt} n={n} k={k}", flush=True)
     g = torch.Generator(device=DEV).manual_seed(n * 11 + k + wdt)
